@@ -1,0 +1,399 @@
+"""Plain fp64 CPU oracle for cascade token/head pruned attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+run this module: only the tests, the smoke entry and the benchmark's CPU
+baseline leg use it. It shares no code with the HIP library.
+
+Source: "SpAtten: Efficient Sparse Attention Architecture with Cascade Token
+and Head Pruning" (Wang, Zhang, Han; arXiv 2012.09852), as summarised on the
+paperlayer.ai page for that paper. Section names below are that page's.
+
+Every function follows a definition directly, with numpy doing the
+arithmetic in float64. Where a value is stored in bf16 by the GPU path
+(x between layers, Q, K, V, the head outputs O and the K/V cache), the
+`bf16` flag rounds to bf16 (round to nearest even) at exactly those points
+and nowhere else. Decisions that turn a float into an integer are taken in
+the precision the kernels take them in: top-k compares fp32 keys, and the
+int8 quantizer runs in fp32.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+
+def bf16_round(a) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even).
+
+    bf16 keeps 8 significant bits and fp32's exponent range. For normal
+    numbers the quantum is 2**(e - 8) where frexp gives a = m * 2**e,
+    m in [0.5, 1); below 2**-126 the quantum is fixed at 2**-133.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    e = np.maximum(e, -125)
+    q = np.ldexp(np.ones_like(a), e - 8)
+    return np.rint(a / q) * q
+
+
+def _store(a, bf16: bool):
+    return bf16_round(a) if bf16 else np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# attention (page: section II, "Attention mechanism")
+# --------------------------------------------------------------------------
+
+
+def softmax_rows(S: np.ndarray) -> np.ndarray:
+    """Row-wise softmax; -inf entries get probability 0."""
+    m = np.max(S, axis=-1, keepdims=True)
+    E = np.exp(S - m)
+    return E / np.sum(E, axis=-1, keepdims=True)
+
+
+def head_attention(Q, K, V, causal: bool, row_block: int = 512):
+    """One head: S = Q K^T / sqrt(dh), causal mask j > i (indices are in
+    ascending original-position order, so this is the positional mask),
+    P = row softmax(S), O = P V.
+
+    Returns O [n, dh], column sums of P [n], row log-sum-exp [n].
+    Works in row blocks so that n x n is never held for long sequences.
+    """
+    n, dh = Q.shape
+    scale = 1.0 / math.sqrt(dh)
+    O = np.empty((n, V.shape[1]))
+    col = np.zeros(K.shape[0])
+    lse = np.empty(n)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        S = (Q[r0:r1] @ K.T) * scale
+        if causal:
+            i = np.arange(r0, r1)[:, None]
+            j = np.arange(K.shape[0])[None, :]
+            S = np.where(j > i, -np.inf, S)
+        m = np.max(S, axis=1, keepdims=True)
+        E = np.exp(S - m)
+        l = np.sum(E, axis=1, keepdims=True)
+        P = E / l
+        O[r0:r1] = P @ V
+        col += P.sum(axis=0)
+        lse[r0:r1] = (m + np.log(l))[:, 0]
+    return O, col, lse
+
+
+# --------------------------------------------------------------------------
+# cascade token and head pruning (page: section II "Cascade pruning",
+# "B. Motivation" token pruning, "A. Cascade Token Pruning")
+# --------------------------------------------------------------------------
+
+
+def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool):
+    """One attention-only residual layer over the kept tokens and heads of
+    one sequence.
+
+    x:     [n, D] kept token rows (values already in storage precision)
+    w:     dict of wq, wk, wv, wo, each [D, D] in x @ W layout
+    heads: kept head ids, ascending
+
+    Returns (x_new [n, D], token-importance increment [n] = sum over kept
+    heads and queries of P, head-importance increment {h: sum |O_h|},
+    per-head LSE {h: [n]}).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, D = x.shape
+    dh = head_dim
+    delta = np.zeros((n, D))
+    dcol = np.zeros(n)
+    dg = {}
+    lse = {}
+    for h in heads:
+        c = slice(h * dh, (h + 1) * dh)
+        Q = _store(x @ w["wq"][:, c].astype(np.float64), bf16)
+        K = _store(x @ w["wk"][:, c].astype(np.float64), bf16)
+        V = _store(x @ w["wv"][:, c].astype(np.float64), bf16)
+        O, col, l = head_attention(Q, K, V, causal)
+        dcol += col
+        dg[h] = float(np.abs(O).sum())
+        lse[h] = l
+        delta += _store(O, bf16) @ w["wo"][c, :].astype(np.float64)
+    return _store(x + delta, bf16), dcol, dg, lse
+
+
+# --------------------------------------------------------------------------
+# top-k (page: "B. Top-k Engine"): the k largest scores, reported in input
+# order. Ranking is on the fp32 value, ties broken towards the lower index.
+# --------------------------------------------------------------------------
+
+
+def order_key(v) -> np.ndarray:
+    """Monotone map from fp32 to uint32: larger value -> larger key.
+    Negative numbers have all bits flipped, non-negative ones the sign bit
+    set, so -0.0 orders just below +0.0."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    neg = (u >> 31) == 1
+    return np.where(neg, u ^ 0xFFFFFFFF, u ^ 0x80000000).astype(np.int64)
+
+
+def topk(scores, k: int) -> np.ndarray:
+    """Indices of the k largest fp32 scores by (key desc, index asc),
+    returned in ascending index order."""
+    key = order_key(scores)
+    n = key.shape[0]
+    assert 0 < k <= n
+    order = np.lexsort((np.arange(n), -key))
+    return np.sort(order[:k]).astype(np.int32)
+
+
+def kth_value(scores, k: int) -> np.float32:
+    """The score of the k-th ranked element (fp32)."""
+    s = np.asarray(scores, dtype=np.float32)
+    key = order_key(s)
+    order = np.lexsort((np.arange(s.shape[0]), -key))
+    return s[order[k - 1]]
+
+
+def compact(arr, idx) -> np.ndarray:
+    """Rows of arr at the survivor indices, in the given order."""
+    return np.asarray(arr)[np.asarray(idx)]
+
+
+# --------------------------------------------------------------------------
+# progressive quantization (page: section III "Progressive Quantization",
+# IV "Quantization Support", E "Progressive Quantization")
+# --------------------------------------------------------------------------
+
+
+def quantize_rows(x):
+    """Per-row symmetric int8 in fp32 arithmetic.
+
+    s = fp32(max |x|) / 127; q = clamp(round_half_even(x / s), -127, 127);
+    a row of zeros gets s = 0 and q = 0.
+    Returns (q int8 [..., D], s float32 [...]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    q = np.rint(x / safe[..., None]).astype(np.float32)
+    q = np.where(s[..., None] == 0, np.float32(0.0), q)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q, s
+
+
+def split_planes(q):
+    """int8 code -> (msb, lsb): msb = q >> 4 (arithmetic, -8..7),
+    lsb = q & 15 (0..15); 16*msb + lsb == q."""
+    q = np.asarray(q, dtype=np.int8).astype(np.int16)
+    msb = (q >> 4).astype(np.int8)
+    lsb = (q & 15).astype(np.uint8)
+    return msb, lsb
+
+
+def pack_nibbles(v):
+    """Two 4-bit fields per byte: element 2j in the low nibble, element
+    2j+1 in the high nibble (two's complement bits kept as is)."""
+    b = (np.asarray(v).astype(np.int16) & 0xF).astype(np.uint8)
+    return (b[..., 0::2] | (b[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(p, signed: bool):
+    p = np.asarray(p, dtype=np.uint8)
+    lo = (p & 0xF).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    if signed:
+        lo = np.where(lo >= 8, lo - 16, lo)
+        hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int16)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def quantize_kv(x):
+    """Full quantization of K or V rows [..., D] into the two planes.
+    Returns packed msb [..., D/2] u8, packed lsb [..., D/2] u8, scale [...] f32."""
+    q, s = quantize_rows(x)
+    msb, lsb = split_planes(q)
+    return pack_nibbles(msb), pack_nibbles(lsb), s
+
+
+def dequant(msb_p, lsb_p, scale, full: bool):
+    """Value of the stored cache: scale*16*msb (MSBs only, LSBs taken as
+    zero) or scale*(16*msb + lsb) (both planes)."""
+    m = unpack_nibbles(msb_p, signed=True).astype(np.float64)
+    v = 16.0 * m
+    if full:
+        v = v + unpack_nibbles(lsb_p, signed=False).astype(np.float64)
+    return v * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def pq_head_attention(q, Kmsb, Kfull, Vmsb, Vfull, threshold: float):
+    """One decode query row of one head under progressive quantization.
+
+    First pass scores against the MSB-only keys. If the largest probability
+    is below the threshold the distribution is flat: the row is recomputed
+    with both planes for K and V. Returns (o, p, recomputed, max_p_msb).
+    """
+    dh = q.shape[0]
+    p = softmax_rows((Kmsb @ q) / math.sqrt(dh))
+    c = float(np.max(p))
+    if c < threshold:
+        p = softmax_rows((Kfull @ q) / math.sqrt(dh))
+        return p @ Vfull, p, True, c
+    return p @ Vmsb, p, False, c
+
+
+# --------------------------------------------------------------------------
+# whole stacks
+# --------------------------------------------------------------------------
+
+
+def run_prefill(cfg, inputs: dict, seqs=None,
+                adopt: Optional[Callable] = None) -> dict:
+    """Cascade over cfg.n_layers layers for each sequence in `seqs`.
+
+    Start: all tokens and heads kept, token importance a = 0, head
+    importance g = 0. After layer l (l < L) the next layer keeps
+    topk(a, n_{l+1}) tokens, with x, a and the original positions compacted
+    to them; when the head count drops, kept heads become
+    heads[topk(g[heads], h_{l+1})].
+
+    adopt(kind, b, l, oracle_idx, scores) may return another valid selection
+    (used by tests to follow the GPU's choice among near-ties).
+    """
+    bf16 = cfg.dtype == "bf16"
+    B = cfg.batch
+    seqs = range(B) if seqs is None else seqs
+    D, dh = cfg.model_dim, cfg.head_dim
+    out = {}
+    for b in seqs:
+        x = np.asarray(inputs["x"][b], dtype=np.float64)
+        pos = np.arange(cfg.tokens[0], dtype=np.int32)
+        heads = np.arange(cfg.n_heads, dtype=np.int32)
+        a = np.zeros(cfg.tokens[0])
+        g = np.zeros(cfg.n_heads)
+        trace = []
+        for l in range(cfg.n_layers):
+            assert x.shape[0] == cfg.tokens[l] and len(heads) == cfg.heads[l]
+            x, dcol, dg, lse = prefill_layer(x, inputs["layers"][l], heads, dh, cfg.causal, bf16)
+            a = a + dcol
+            for h, v in dg.items():
+                g[h] += v
+            rec = {"pos": pos.copy(), "heads": heads.copy(), "a": a.copy(), "g": g.copy(),
+                   "x": x.copy()}
+            if l + 1 < cfg.n_layers:
+                if cfg.heads[l + 1] != len(heads):
+                    gk = g[heads].astype(np.float32)
+                    sel = topk(gk, cfg.heads[l + 1])
+                    if adopt is not None:
+                        sel = adopt("head", b, l, sel, gk)
+                    heads = heads[sel]
+                a32 = a.astype(np.float32)
+                idx = topk(a32, cfg.tokens[l + 1])
+                if adopt is not None:
+                    idx = adopt("token", b, l, idx, a32)
+                rec["sel"] = idx
+                x, a, pos = compact(x, idx), compact(a, idx), compact(pos, idx)
+            trace.append(rec)
+        out[b] = {"x": x, "pos": pos, "heads": heads, "a": a, "g": g, "trace": trace}
+    return out
+
+
+def decode_layer(x, w: dict, cache: dict, heads_n: int, head_dim: int, bf16: bool,
+                 quantized: bool, threshold: float):
+    """One decode layer for one sequence. The new token's k and v are
+    appended to the cache, then the query attends over every cache entry
+    (no mask). Returns (x_new, p [H, Lc], recompute flags [H])."""
+    H, dh = heads_n, head_dim
+    x = np.asarray(x, dtype=np.float64)
+    q = _store(x @ w["wq"].astype(np.float64), bf16).reshape(H, dh)
+    k = _store(x @ w["wk"].astype(np.float64), bf16)
+    v = _store(x @ w["wv"].astype(np.float64), bf16)
+    if quantized:
+        km, kl, ks = quantize_kv(k.astype(np.float32))
+        vm, vl, vs = quantize_kv(v.astype(np.float32))
+        for name, val in (("k_msb", km), ("k_lsb", kl), ("k_scale", ks),
+                          ("v_msb", vm), ("v_lsb", vl), ("v_scale", vs)):
+            cache[name] = np.concatenate([cache[name], np.asarray(val)[None]], axis=0)
+        Km = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], False).reshape(-1, H, dh)
+        Kf = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], True).reshape(-1, H, dh)
+        Vm = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], False).reshape(-1, H, dh)
+        Vf = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], True).reshape(-1, H, dh)
+    else:
+        cache["k"] = np.concatenate([cache["k"], k.reshape(1, H, dh)], axis=0)
+        cache["v"] = np.concatenate([cache["v"], v.reshape(1, H, dh)], axis=0)
+    Lc = cache["k_scale"].shape[0] if quantized else cache["k"].shape[0]
+    P = np.zeros((H, Lc))
+    rec = np.zeros(H, dtype=bool)
+    cmax = np.zeros(H)
+    delta = np.zeros(x.shape[0])
+    for h in range(H):
+        if quantized:
+            o, p, r, c = pq_head_attention(q[h], Km[:, h], Kf[:, h], Vm[:, h], Vf[:, h], threshold)
+            rec[h] = r
+            cmax[h] = c
+        else:
+            p = softmax_rows((cache["k"][:, h] @ q[h]) / math.sqrt(dh))
+            o = p @ cache["v"][:, h]
+        P[h] = p
+        delta += _store(o, bf16) @ w["wo"][h * dh:(h + 1) * dh, :].astype(np.float64)
+    return _store(x + delta, bf16), P, rec, cmax
+
+
+def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
+               steps: Optional[int] = None) -> dict:
+    """Generation (page: section II, attention-based NLP models): one new
+    token per step against cached K/V. Token importance a accumulates the
+    probabilities each cache entry receives, over heads, layers and steps;
+    a new entry starts at 0. After every layer of step 1 has run, the cache
+    of every layer keeps topk(a over L0+1 entries, cache_keep) entries."""
+    bf16 = cfg.dtype == "bf16"
+    seqs = range(cfg.batch) if seqs is None else seqs
+    steps = cfg.steps if steps is None else steps
+    H, dh = cfg.n_heads, cfg.head_dim
+    out = {}
+    for b in seqs:
+        caches = []
+        for l in range(cfg.n_layers):
+            Lw = inputs["layers"][l]
+            K0 = np.asarray(Lw["k_cache"][b], dtype=np.float64)
+            V0 = np.asarray(Lw["v_cache"][b], dtype=np.float64)
+            if cfg.quantized:
+                km, kl, ks = quantize_kv(K0.reshape(K0.shape[0], -1).astype(np.float32))
+                vm, vl, vs = quantize_kv(V0.reshape(V0.shape[0], -1).astype(np.float32))
+                caches.append({"k_msb": km, "k_lsb": kl, "k_scale": ks,
+                               "v_msb": vm, "v_lsb": vl, "v_scale": vs})
+            else:
+                caches.append({"k": K0, "v": V0})
+        a = np.zeros(cfg.cache_len)
+        xs, recs, sel = [], [], None
+        for s in range(steps):
+            x = np.asarray(inputs["x_steps"][s][b], dtype=np.float64)
+            a = np.concatenate([a, [0.0]])
+            step_rec = []
+            for l in range(cfg.n_layers):
+                x, P, rec, cmax = decode_layer(x, inputs["layers"][l], caches[l], H, dh, bf16,
+                                               cfg.quantized, cfg.pq_threshold)
+                a = a + P.sum(axis=0)
+                step_rec.append((rec, cmax))
+            xs.append(x)
+            recs.append(step_rec)
+            if s == 0:
+                a32 = a.astype(np.float32)
+                idx = topk(a32, cfg.cache_keep)
+                if adopt is not None:
+                    idx = adopt("cache", b, 0, idx, a32)
+                sel = idx
+                for c in caches:
+                    for name in c:
+                        c[name] = compact(c[name], idx)
+                a = compact(a, idx)
+        out[b] = {"x_steps": np.stack(xs), "a": a, "sel": sel, "recompute": recs}
+    return out

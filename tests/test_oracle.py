@@ -1,0 +1,411 @@
+"""Pins for the CPU oracle: values and properties fixed by the pages and by
+mathematics, independent of the oracle's own formulas.
+
+Cited definitions (SpAtten, paperlayer.ai summary of arXiv 2012.09852):
+attention = section II "Attention mechanism"; token importance = column
+sums of probabilities ("B. Motivation", "A. Cascade Token Pruning"); head
+importance = cumulative |attention output| (section II "Cascade pruning");
+top-k = "B. Top-k Engine"; MSB/LSB planes = section III "Progressive
+Quantization" and IV "Quantization Support".
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spatten_ref as R
+from oracle.topk_engine import topk_engine, zero_eliminate
+from workloads import TINY, make_prefill_inputs, random_scores, scaled
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _sdpa(Q, K, V, causal):
+    """torch's attention in fp64 on the CPU (library cross-check)."""
+    q = torch.from_numpy(np.asarray(Q, np.float64))[None, None]
+    k = torch.from_numpy(np.asarray(K, np.float64))[None, None]
+    v = torch.from_numpy(np.asarray(V, np.float64))[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+    return o[0, 0].numpy()
+
+
+def _torch_probs(Q, K, causal):
+    q = torch.from_numpy(np.asarray(Q, np.float64))
+    k = torch.from_numpy(np.asarray(K, np.float64))
+    s = q @ k.T / math.sqrt(Q.shape[1])
+    if causal:
+        s = s.masked_fill(torch.ones_like(s, dtype=torch.bool).triu(1), float("-inf"))
+    return torch.softmax(s, dim=-1).numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+# ----------------------------------------------------------------- bf16
+
+
+def test_bf16_golden():
+    for c in _gold("bf16_ties.json")["cases"]:
+        assert R.bf16_round(c["x"]) == c["r"], c
+
+
+def test_bf16_matches_torch_cast_on_fp32_inputs():
+    rng = np.random.default_rng(1)
+    a = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(2000) * 1e-39]).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(R.bf16_round(a.astype(np.float64)), ref)
+
+
+# ----------------------------------------------------------------- attention
+
+
+def test_attention_golden_two_tokens():
+    g = _gold("attention_2tok.json")
+    Q, K, V = (np.array(g[k]) for k in ("Q", "K", "V"))
+    for mode, causal in (("bidirectional", False), ("causal", True)):
+        O, col, lse = R.head_attention(Q, K, V, causal)
+        np.testing.assert_allclose(O, g[mode]["O"], atol=1e-12)
+        np.testing.assert_allclose(col, g[mode]["colsum"], atol=1e-12)
+        np.testing.assert_allclose(lse, g[mode]["lse"], atol=1e-12)
+        assert abs(np.abs(O).sum() - g[mode]["abs_o_sum"]) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,dh", [(1, 8), (7, 4), (37, 16), (130, 32)])
+def test_attention_vs_torch_sdpa(n, dh, causal):
+    rng = np.random.default_rng(n * 100 + dh)
+    Q, K, V = (rng.standard_normal((n, dh)) * 2 for _ in range(3))
+    O, col, lse = R.head_attention(Q, K, V, causal, row_block=16)
+    np.testing.assert_allclose(O, _sdpa(Q, K, V, causal), rtol=1e-12, atol=1e-12)
+    P, L = _torch_probs(Q, K, causal)
+    np.testing.assert_allclose(col, P.sum(axis=0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, L, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_attention_brute_force_loops():
+    rng = np.random.default_rng(5)
+    for n, dh in ((1, 1), (3, 2), (8, 4)):
+        Q, K, V = (rng.standard_normal((n, dh)) for _ in range(3))
+        O, col, _ = R.head_attention(Q, K, V, causal=False)
+        for i in range(n):
+            e = [math.exp(sum(Q[i, c] * K[j, c] for c in range(dh)) / math.sqrt(dh))
+                 for j in range(n)]
+            z = sum(e)
+            for c in range(dh):
+                assert abs(O[i, c] - sum(e[j] / z * V[j, c] for j in range(n))) < 1e-12
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(6)
+    n, dh = 23, 8
+    K, V = rng.standard_normal((n, dh)), rng.standard_normal((n, dh))
+    Z = np.zeros((n, dh))
+    # Q = 0: uniform probabilities; bidirectional column sums are n_q / n = 1
+    O, col, lse = R.head_attention(Z, K, V, causal=False)
+    np.testing.assert_allclose(O, np.tile(V.mean(axis=0), (n, 1)), atol=1e-12)
+    np.testing.assert_allclose(col, 1.0, atol=1e-12)
+    np.testing.assert_allclose(lse, math.log(n), atol=1e-12)
+    # causal, Q = 0: row i is uniform over j <= i, so column j sums to H_n - H_j
+    O, col, _ = R.head_attention(Z, K, V, causal=True)
+    harm = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(col, harm[n] - harm[np.arange(n)], atol=1e-12)
+    np.testing.assert_allclose(O[0], V[0], atol=1e-12)           # causal row 0 sees only key 0
+    # n = 1: O = V
+    O, col, _ = R.head_attention(K[:1], K[:1], V[:1], causal=False)
+    np.testing.assert_allclose(O, V[:1], atol=1e-15)
+    np.testing.assert_allclose(col, [1.0], atol=1e-15)
+
+
+def test_attention_permutation_equivariance():
+    rng = np.random.default_rng(7)
+    n, dh = 19, 8
+    Q, K, V = (rng.standard_normal((n, dh)) for _ in range(3))
+    perm = rng.permutation(n)
+    O, col, _ = R.head_attention(Q, K, V, causal=False)
+    O2, col2, _ = R.head_attention(Q[perm], K[perm], V[perm], causal=False)
+    np.testing.assert_allclose(O2, O[perm], atol=1e-12)
+    np.testing.assert_allclose(col2, col[perm], atol=1e-12)
+
+
+# ----------------------------------------------------------------- layer
+
+
+def _tiny_weights(D, rng):
+    return {k: rng.standard_normal((D, D)) / math.sqrt(D) for k in ("wq", "wk", "wv", "wo")}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_layer_matches_torch_dense_mha(causal):
+    rng = np.random.default_rng(8)
+    n, H, dh = 29, 4, 8
+    D = H * dh
+    x = rng.standard_normal((n, D))
+    w = _tiny_weights(D, rng)
+    xn, dcol, dg, _ = R.prefill_layer(x, w, range(H), dh, causal, bf16=False)
+    # the same layer through torch: per-head SDPA, concatenate, project
+    t = {k: torch.from_numpy(v) for k, v in w.items()}
+    tx = torch.from_numpy(x)
+    q = (tx @ t["wq"]).reshape(n, H, dh).transpose(0, 1).contiguous()
+    k = (tx @ t["wk"]).reshape(n, H, dh).transpose(0, 1).contiguous()
+    v = (tx @ t["wv"]).reshape(n, H, dh).transpose(0, 1).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+    ref = tx + o.transpose(0, 1).reshape(n, D) @ t["wo"]
+    np.testing.assert_allclose(xn, ref.numpy(), rtol=1e-11, atol=1e-11)
+    assert abs(dcol.sum() - H * n) < 1e-9                        # each row sums to 1
+    gref = o.abs().sum(dim=(1, 2)).numpy()
+    np.testing.assert_allclose([dg[h] for h in range(H)], gref, rtol=1e-12)
+
+
+def test_layer_q_zero_closed_form_and_kept_heads():
+    rng = np.random.default_rng(9)
+    n, H, dh = 17, 4, 8
+    D = H * dh
+    x = rng.standard_normal((n, D))
+    w = _tiny_weights(D, rng)
+    w["wq"] = np.zeros((D, D))
+    heads = [1, 3]
+    _, dcol, dg, _ = R.prefill_layer(x, w, heads, dh, False, bf16=False)
+    np.testing.assert_allclose(dcol, len(heads), atol=1e-12)      # h * n_q / n per column
+    assert sorted(dg) == heads
+    _, dcol, _, _ = R.prefill_layer(x, w, heads, dh, True, bf16=False)
+    harm = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(dcol, len(heads) * (harm[n] - harm[np.arange(n)]), atol=1e-12)
+
+
+def test_layer_constant_v_head_importance():
+    rng = np.random.default_rng(10)
+    n, H, dh = 11, 2, 4
+    D = H * dh
+    row = rng.standard_normal(D)
+    x = np.tile(row, (n, 1))                                     # identical rows
+    w = _tiny_weights(D, rng)
+    _, _, dg, _ = R.prefill_layer(x, w, range(H), dh, False, bf16=False)
+    v = row @ w["wv"]
+    for h in range(H):
+        assert abs(dg[h] - n * np.abs(v[h * dh:(h + 1) * dh]).sum()) < 1e-10
+
+
+def test_layer_bf16_storage_points_are_bf16():
+    rng = np.random.default_rng(11)
+    n, H, dh = 9, 2, 8
+    D = H * dh
+    x = R.bf16_round(rng.standard_normal((n, D)))
+    w = {k: R.bf16_round(v) for k, v in _tiny_weights(D, rng).items()}
+    xn, _, _, _ = R.prefill_layer(x, w, range(H), dh, False, bf16=True)
+    np.testing.assert_array_equal(xn, R.bf16_round(xn))
+
+
+# ----------------------------------------------------------------- top-k
+
+
+def test_topk_golden():
+    g = _gold("topk_ties.json")
+    s = np.array(g["scores"], dtype=np.float32)
+    for c in g["cases"]:
+        idx = R.topk(s, c["k"])
+        assert idx.tolist() == c["idx"]
+        kv = R.kth_value(s, c["k"])
+        assert kv == c["kth"] and math.copysign(1.0, kv) == math.copysign(1.0, c["kth"])
+        assert topk_engine(s, c["k"]).tolist() == c["idx"]
+
+
+def _ranks_above(a, i, j):
+    """True if element i outranks element j: larger value, -0.0 below +0.0,
+    equal values broken by lower index. Uses float comparisons only."""
+    vi, vj = float(a[i]), float(a[j])
+    if vi != vj:
+        return vi > vj
+    si, sj = math.copysign(1.0, vi), math.copysign(1.0, vj)
+    if si != sj:
+        return si > sj
+    return i < j
+
+
+def test_topk_brute_force_subsets():
+    rng = np.random.default_rng(12)
+    for trial in range(60):
+        n = int(rng.integers(1, 10))
+        kind = ["normal", "ties", "signed_zero"][trial % 3]
+        a = random_scores(n, seed=trial, kind=kind)
+        for k in range(1, n + 1):
+            valid = [S for S in itertools.combinations(range(n), k)
+                     if all(_ranks_above(a, i, j) for i in S for j in range(n) if j not in S)]
+            assert len(valid) == 1
+            assert R.topk(a, k).tolist() == list(valid[0])
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed_zero", "uniform"])
+def test_topk_matches_engine_and_properties(kind):
+    rng = np.random.default_rng(13)
+    for trial in range(12):
+        n = int(rng.integers(1, 300))
+        a = random_scores(n, seed=100 + trial, kind=kind)
+        for k in sorted({1, n, int(rng.integers(1, n + 1))}):
+            idx = R.topk(a, k)
+            assert idx.tolist() == topk_engine(a, k).tolist()
+            assert len(idx) == k and np.all(np.diff(idx) > 0)
+            rest = np.setdiff1d(np.arange(n), idx)
+            if len(rest):
+                key = R.order_key(a)
+                assert key[idx].min() >= key[rest].max()
+
+
+def test_zero_eliminator_keeps_order():
+    rng = np.random.default_rng(14)
+    for n in (1, 2, 5, 16, 33, 100):
+        keep = rng.random(n) < 0.4
+        assert zero_eliminate(list(range(n)), keep) == list(np.flatnonzero(keep))
+
+
+def test_order_key_monotone():
+    vals = np.array([-np.inf, -3.0, -1e-40, -0.0, 0.0, 1e-40, 2.0, np.inf], dtype=np.float32)
+    k = R.order_key(vals)
+    assert np.all(np.diff(k) > 0)
+
+
+def test_compact_is_fancy_indexing():
+    a = np.arange(30).reshape(10, 3)
+    idx = np.array([1, 4, 9])
+    np.testing.assert_array_equal(R.compact(a, idx), a[[1, 4, 9]])
+    np.testing.assert_array_equal(R.compact(a, np.arange(10)), a)
+
+
+# ----------------------------------------------------------------- quantizer
+
+
+def test_quantize_golden_rows():
+    for row in _gold("quantize_rows.json")["rows"]:
+        x = np.array(row["x"], dtype=np.float32)[None]
+        q, s = R.quantize_rows(x)
+        assert float(s[0]) == row["scale"]
+        assert q[0].tolist() == row["q"]
+        msb, lsb = R.split_planes(q[0])
+        assert msb.tolist() == row["msb"] and lsb.tolist() == row["lsb"]
+        pm, pl, ps = R.quantize_kv(x)
+        assert pm[0].tolist() == row["msb_bytes"] and pl[0].tolist() == row["lsb_bytes"]
+
+
+def test_nibble_round_trip_exhaustive():
+    q = np.arange(-128, 128, dtype=np.int16).astype(np.int8)
+    msb, lsb = R.split_planes(q)
+    assert np.all((msb >= -8) & (msb <= 7)) and np.all((lsb >= 0) & (lsb <= 15))
+    np.testing.assert_array_equal(16 * msb.astype(np.int32) + lsb.astype(np.int32), q.astype(np.int32))
+    # packing: every pair of codes survives pack/unpack
+    a, b = np.meshgrid(q, q)
+    pairs = np.stack([a.ravel(), b.ravel()], axis=1)
+    m, l = R.split_planes(pairs)
+    um = R.unpack_nibbles(R.pack_nibbles(m), signed=True)
+    ul = R.unpack_nibbles(R.pack_nibbles(l), signed=False)
+    np.testing.assert_array_equal(16 * um + ul, pairs.astype(np.int16))
+
+
+def test_quantizer_error_bound_and_extremes():
+    rng = np.random.default_rng(15)
+    x = (rng.standard_normal((500, 64)) * rng.random((500, 1)) * 10).astype(np.float32)
+    q, s = R.quantize_rows(x)
+    err = np.abs(x.astype(np.float64) - s[:, None].astype(np.float64) * q)
+    assert np.all(err <= s[:, None].astype(np.float64) * 0.5 * (1 + 1e-6))
+    amax_at = np.argmax(np.abs(x), axis=1)
+    np.testing.assert_array_equal(np.abs(q[np.arange(500), amax_at]), 127)
+    assert q.min() >= -127
+
+
+# ----------------------------------------------------------------- progressive quantization
+
+
+def test_pq_threshold_extremes():
+    rng = np.random.default_rng(16)
+    Lc, dh = 57, 16
+    K = rng.standard_normal((Lc, dh)).astype(np.float32)
+    V = rng.standard_normal((Lc, dh)).astype(np.float32)
+    km, kl, ks = R.quantize_kv(K)
+    vm, vl, vs = R.quantize_kv(V)
+    Km, Kf = R.dequant(km, kl, ks, False), R.dequant(km, kl, ks, True)
+    Vm, Vf = R.dequant(vm, vl, vs, False), R.dequant(vm, vl, vs, True)
+    # full dequantisation is exactly scale * int8 code
+    q8, s8 = R.quantize_rows(K)
+    np.testing.assert_array_equal(Kf, q8.astype(np.float64) * s8[:, None].astype(np.float64))
+    q = rng.standard_normal(dh) * 2
+    o, p, rec, _ = R.pq_head_attention(q, Km, Kf, Vm, Vf, threshold=0.0)
+    assert not rec
+    np.testing.assert_allclose(o, _sdpa(q[None], Km, Vm, False)[0], atol=1e-12)
+    o, p, rec, _ = R.pq_head_attention(q, Km, Kf, Vm, Vf, threshold=1.01)
+    assert rec
+    np.testing.assert_allclose(o, _sdpa(q[None], Kf, Vf, False)[0], atol=1e-12)
+    np.testing.assert_allclose(p.sum(), 1.0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- stacks
+
+
+def test_run_prefill_keep_all_equals_repeated_dense_layers():
+    cfg = scaled(TINY, tokens=(64, 64), heads=(4, 4))
+    inp = make_prefill_inputs(cfg)
+    out = R.run_prefill(cfg, inp)[0]
+    x = inp["x"][0].astype(np.float64)
+    for l in range(2):
+        x, _, _, _ = R.prefill_layer(x, inp["layers"][l], range(4), 32, False, False)
+    np.testing.assert_allclose(out["x"], x, atol=1e-12)
+    np.testing.assert_array_equal(out["pos"], np.arange(64))
+    assert abs(out["a"].sum() - 2 * 4 * 64) < 1e-9
+
+
+def test_run_prefill_tiny_cascade_invariants():
+    cfg = TINY
+    inp = make_prefill_inputs(cfg)
+    out = R.run_prefill(cfg, inp)[0]
+    t0, t1 = out["trace"]
+    assert abs(t0["a"].sum() - 4 * 64) < 1e-9
+    sel = t0["sel"]
+    assert len(sel) == 32 and np.all(np.diff(sel) > 0)
+    np.testing.assert_array_equal(t1["pos"], sel)
+    # layer-2 mass = kept layer-1 mass + heads * kept queries
+    assert abs(out["a"].sum() - (t0["a"][sel].sum() + 4 * 32)) < 1e-9
+    # the kept tokens are the 32 largest of layer-1 importance
+    rest = np.setdiff1d(np.arange(64), sel)
+    assert t0["a"][sel].min() >= t0["a"][rest].max()
+
+
+def test_run_prefill_head_cut():
+    cfg = scaled(TINY, n_layers=3, tokens=(48, 40, 32), heads=(4, 4, 2))
+    inp = make_prefill_inputs(cfg)
+    out = R.run_prefill(cfg, inp)[0]
+    t1 = out["trace"][1]
+    heads = out["trace"][2]["heads"]
+    assert len(heads) == 2 and np.all(np.diff(heads) > 0)
+    rest = np.setdiff1d(np.arange(4), heads)
+    assert t1["g"][heads].min() >= t1["g"][rest].max()
+
+
+def test_run_decode_small_invariants():
+    from workloads import GPT2_DECODE, make_decode_inputs
+    cfg = scaled(GPT2_DECODE, n_layers=2, batch=2, n_heads=2, head_dim=8, cache_len=20,
+                 cache_keep=8, steps=3)
+    inp = make_decode_inputs(cfg)
+    out = R.run_decode(cfg, inp)
+    for b in range(2):
+        o = out[b]
+        assert o["x_steps"].shape == (3, 16)
+        assert len(o["sel"]) == 8 and np.all(np.diff(o["sel"]) > 0)
+        # every step adds heads x layers probability mass; step 1 mass is 2x2
+        # over 21 entries, then compaction keeps part of it
+        assert o["a"].shape == (8 + 2,)
+
+
+def test_run_decode_pq_threshold_zero_never_recomputes():
+    from workloads import PQ_DECODE, make_decode_inputs
+    cfg = scaled(PQ_DECODE, n_layers=1, batch=1, n_heads=2, head_dim=8, cache_len=16,
+                 cache_keep=8, steps=2, pq_threshold=0.0)
+    out = R.run_decode(cfg, make_decode_inputs(cfg))[0]
+    assert not any(r.any() for step in out["recompute"] for r, _ in step)
+    cfg2 = scaled(cfg, pq_threshold=1.01)
+    out2 = R.run_decode(cfg2, make_decode_inputs(cfg2))[0]
+    assert all(r.all() for step in out2["recompute"] for r, _ in step)

@@ -1,0 +1,121 @@
+"""Workload definitions for cascade token/head pruned attention.
+
+Five workloads are defined, each a stack of attention-only residual layers
+(x += softmax(Q K^T / sqrt(dh)) V Wo, no FFN, no LayerNorm):
+
+  tiny        2 layers, B=1, T=64, H=4, dh=32, D=128, fp32; layer 2 keeps the
+              top-32 tokens by layer-1 cumulative importance.
+  bert_base   12 layers, B=32, T=512, H=12, dh=64, D=768, bf16 storage,
+              bidirectional; token keep fraction falls linearly from 1.0 at
+              layer 1 to 0.5 at layer 12; heads cut to the top-10 of 12 from
+              layer 4 by |O_h| importance.
+  gpt2_decode 12 layers, H=12, dh=64, B=64, 1024 cached tokens, 32 decode
+              steps; the cache is pruned to 40% of its length after step 1.
+  pq_decode   24 layers, H=16, dh=64, B=16, 2048 cached tokens, K/V stored as
+              4-bit MSB and LSB planes of a per-token int8 code; MSB-only
+              scoring first, recompute with LSBs for rows whose max
+              probability is below 0.1; cache keep 50%.
+  long_causal 4 layers, B=1, T=32768, H=32, dh=128, D=4096, bf16, causal;
+              25% of tokens kept after layer 1, heads top-24 of 32 from
+              layer 2.
+
+This module holds shapes and schedules only. Keep counts follow
+k = floor(f * N + 1/2) with N the original length, so fractions are absolute
+along the cascade.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from fractions import Fraction
+from typing import List, Optional
+
+
+def keep_count(frac: Fraction, n: int) -> int:
+    """floor(frac * n + 1/2), exact."""
+    v = Fraction(frac) * n + Fraction(1, 2)
+    return v.numerator // v.denominator
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    kind: str                 # "prefill" or "decode"
+    n_layers: int
+    batch: int
+    n_heads: int
+    head_dim: int
+    dtype: str                # "f32" or "bf16" (storage type; accumulation is fp32 on the GPU)
+    causal: bool = False
+    # prefill: tokens and heads processed by each layer
+    tokens: tuple = ()
+    heads: tuple = ()
+    # decode
+    cache_len: int = 0        # prior tokens in the cache (L0)
+    cache_keep: int = 0       # entries kept after step 1
+    steps: int = 0
+    quantized: bool = False
+    pq_threshold: float = 0.0
+    heavy_frac: float = 0.05
+    heavy_scale: float = 3.0
+
+    @property
+    def model_dim(self) -> int:
+        return self.n_heads * self.head_dim
+
+    @property
+    def seq_len(self) -> int:
+        return self.tokens[0] if self.kind == "prefill" else self.cache_len
+
+    @property
+    def cache_cap(self) -> int:
+        """Cache rows needed per sequence: L0 prior entries + one per step."""
+        return self.cache_len + self.steps
+
+    def token_layers(self) -> int:
+        """Tokens processed summed over layers (and steps for decode)."""
+        if self.kind == "prefill":
+            return self.batch * sum(self.tokens)
+        return self.batch * self.n_layers * self.steps
+
+
+def _linear_schedule(T: int, L: int, last_frac: Fraction) -> tuple:
+    # f_l = 1 - (1 - last_frac) * (l - 1) / (L - 1), l = 1..L
+    out = []
+    for l in range(1, L + 1):
+        f = 1 - (1 - last_frac) * Fraction(l - 1, L - 1)
+        out.append(keep_count(f, T))
+    return tuple(out)
+
+
+TINY = Config(
+    name="tiny", kind="prefill", n_layers=2, batch=1, n_heads=4, head_dim=32,
+    dtype="f32", causal=False, tokens=(64, 32), heads=(4, 4))
+
+BERT_BASE = Config(
+    name="bert_base", kind="prefill", n_layers=12, batch=32, n_heads=12, head_dim=64,
+    dtype="bf16", causal=False,
+    tokens=_linear_schedule(512, 12, Fraction(1, 2)),
+    heads=(12, 12, 12) + (10,) * 9)
+
+GPT2_DECODE = Config(
+    name="gpt2_decode", kind="decode", n_layers=12, batch=64, n_heads=12, head_dim=64,
+    dtype="bf16", cache_len=1024, cache_keep=keep_count(Fraction(2, 5), 1024), steps=32)
+
+PQ_DECODE = Config(
+    name="pq_decode", kind="decode", n_layers=24, batch=16, n_heads=16, head_dim=64,
+    dtype="bf16", cache_len=2048, cache_keep=keep_count(Fraction(1, 2), 2048), steps=32,
+    quantized=True, pq_threshold=0.1)
+
+LONG_CAUSAL = Config(
+    name="long_causal", kind="prefill", n_layers=4, batch=1, n_heads=32, head_dim=128,
+    dtype="bf16", causal=True,
+    tokens=(32768,) + (keep_count(Fraction(1, 4), 32768),) * 3,
+    heads=(32,) + (24,) * 3)
+
+CONFIGS = [TINY, BERT_BASE, GPT2_DECODE, PQ_DECODE, LONG_CAUSAL]
+BY_NAME = {c.name: c for c in CONFIGS}
+
+
+def scaled(cfg: Config, **kw) -> Config:
+    """A smaller variant of a workload for parity tests (same structure)."""
+    return replace(cfg, **kw)

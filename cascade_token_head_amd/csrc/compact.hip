@@ -1,0 +1,109 @@
+// Multi-tensor row gather: pruned tokens leave x, their importance scores,
+// positions and (for decode) every layer's K/V cache rows in one launch
+// (SpAtten, "A. Cascade Token Pruning": a pruned token's Q, K and V are
+// gone from every later head and layer).
+//
+// The pages route pruning's random row addresses through an on-chip
+// crossbar; here each destination row is a contiguous copy, split into
+// 16-byte units when the addresses allow, so consecutive lanes touch
+// consecutive bytes of the same row and HBM access stays coalesced.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "timing.hpp"
+
+namespace spatten {
+namespace {
+
+struct CompactTensor {
+  const char* src;
+  char* dst;
+  int64_t row_bytes, sbs, dbs;
+  int32_t vec_shift;
+};
+
+constexpr int kCompactMax = 48;
+
+struct CompactParams {
+  CompactTensor t[kCompactMax];
+};
+
+template <int V>
+struct VecT;
+template <> struct VecT<16> { using T = u32x4; };
+template <> struct VecT<8> { using T = uint64_t; };
+template <> struct VecT<4> { using T = uint32_t; };
+template <> struct VecT<2> { using T = uint16_t; };
+template <> struct VecT<1> { using T = uint8_t; };
+
+template <int V>
+__device__ __forceinline__ void copy_units(const CompactTensor& t, const int32_t* __restrict__ idx,
+                                           int k, int64_t total, int64_t start, int64_t step) {
+  using T = typename VecT<V>::T;
+  const int64_t upr = t.row_bytes / V;
+  for (int64_t u = start; u < total; u += step) {
+    const int64_t row = u / upr, part = u - row * upr;
+    const int64_t b = row / k, r = row - b * k;
+    const int64_t sr = idx[b * k + r];
+    const T* s = reinterpret_cast<const T*>(t.src + b * t.sbs + sr * t.row_bytes) + part;
+    T* d = reinterpret_cast<T*>(t.dst + b * t.dbs + r * t.row_bytes) + part;
+    *d = *s;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+compact_kernel(CompactParams p, const int32_t* __restrict__ idx, int batch, int k) {
+  const CompactTensor& t = p.t[blockIdx.y];
+  const int64_t total = int64_t(batch) * k * (t.row_bytes >> t.vec_shift);
+  const int64_t start = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t step = int64_t(gridDim.x) * blockDim.x;
+  switch (t.vec_shift) {
+    case 4: copy_units<16>(t, idx, k, total, start, step); break;
+    case 3: copy_units<8>(t, idx, k, total, start, step); break;
+    case 2: copy_units<4>(t, idx, k, total, start, step); break;
+    case 1: copy_units<2>(t, idx, k, total, start, step); break;
+    default: copy_units<1>(t, idx, k, total, start, step); break;
+  }
+}
+
+int vec_shift_for(const void* s, const void* d, int64_t rb, int64_t sbs, int64_t dbs) {
+  const uint64_t all = uint64_t(reinterpret_cast<uintptr_t>(s)) |
+                       uint64_t(reinterpret_cast<uintptr_t>(d)) | uint64_t(rb) |
+                       uint64_t(sbs) | uint64_t(dbs);
+  for (int sh = 4; sh > 0; --sh)
+    if ((all & ((uint64_t(1) << sh) - 1)) == 0) return sh;
+  return 0;
+}
+
+}  // namespace
+
+int launch_compact(int n_tensors, const void* const* src, void* const* dst,
+                   const int64_t* row_bytes, const int64_t* sbs, const int64_t* dbs,
+                   const int32_t* idx, int batch, int k, hipStream_t stream) {
+  if (n_tensors == 0 || batch == 0 || k == 0) return SPATTEN_OK;
+  for (int t0 = 0; t0 < n_tensors; t0 += kCompactMax) {
+    const int cnt = n_tensors - t0 < kCompactMax ? n_tensors - t0 : kCompactMax;
+    CompactParams p{};
+    int64_t max_units = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const int t = t0 + i;
+      CompactTensor& c = p.t[i];
+      c.src = static_cast<const char*>(src[t]);
+      c.dst = static_cast<char*>(dst[t]);
+      c.row_bytes = row_bytes[t];
+      c.sbs = sbs[t];
+      c.dbs = dbs[t];
+      c.vec_shift = vec_shift_for(src[t], dst[t], row_bytes[t], sbs[t], dbs[t]);
+      const int64_t units = int64_t(batch) * k * (row_bytes[t] >> c.vec_shift);
+      if (units > max_units) max_units = units;
+    }
+    int64_t blocks = ceil_div(max_units, 256);
+    if (blocks > 8192) blocks = 8192;
+    SPATTEN_TIMED("compact", stream,
+                  compact_kernel<<<dim3(unsigned(blocks), cnt), dim3(256), 0, stream>>>(p, idx,
+                                                                                    batch, k));
+    SPATTEN_LAUNCH_CHECK();
+  }
+  return SPATTEN_OK;
+}
+
+}  // namespace spatten

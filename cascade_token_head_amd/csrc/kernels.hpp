@@ -1,0 +1,100 @@
+// Internal launchers (not part of the C ABI). Each enqueues on `stream` and
+// returns a spatten_status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.hpp"
+
+namespace spatten {
+
+int launch_topk(const float* scores, int batch, int n, int64_t row_stride, int k,
+                int32_t* out_idx, float* kth, hipStream_t stream);
+
+int launch_compact(int n_tensors, const void* const* src, void* const* dst,
+                   const int64_t* row_bytes, const int64_t* sbs, const int64_t* dbs,
+                   const int32_t* idx, int batch, int k, hipStream_t stream);
+
+int launch_quantize(const void* kv, int dtype, int batch, int n, int dim, int64_t kv_bs,
+                    uint8_t* msb, uint8_t* lsb, float* scale, int64_t pbs, hipStream_t stream);
+
+// Projections. QKV: for each kept head slot s of sequence b the rows
+// head_idx[b, s]*dh .. +dh of wq/wk/wv (output-major) produce Q, K and V.
+//   prefill: Q, K -> [B, h, n_pad, dh]; V -> transposed [B, h, dh, n_pad]
+//   decode:  q -> q_out [B, D]; k, v -> k_out/v_out + b*kv_bs + s*dh + c
+struct QkvArgs {
+  int dtype, mode;
+  const void* x;
+  const void* w[3];
+  const int32_t* head_idx;
+  int batch, n, n_pad, h_kept, dh, D;
+  void* q;
+  void* k;
+  void* vt;
+  int64_t kv_bs;  // decode: elements between sequences in k/v outputs
+};
+int launch_qkv(const QkvArgs& a, hipStream_t stream);
+
+// Output projection with residual: x[b, m, :] += O[b, m, :] wo[:, gathered]^T
+struct OutArgs {
+  int dtype;
+  const void* o;  // [B, n, h_kept*dh]
+  const void* wo;
+  const int32_t* head_idx;
+  int batch, n, h_kept, dh, D;
+  void* x;
+};
+int launch_out(const OutArgs& a, hipStream_t stream);
+
+// Prefill attention with fused importance.
+struct AttnArgs {
+  int dtype, causal;
+  const void* q;
+  const void* k;
+  const void* vt;
+  int batch, h_kept, n, n_pad, dh;
+  void* o;        // [B, n, h_kept*dh]
+  float* lse;     // [B, h, n_pad]
+  float* colsum;  // [B, h, n_pad]
+  float* gpart;   // [B, h, nqb]
+  int nqb;
+};
+int launch_attention(const AttnArgs& a, hipStream_t stream);
+int launch_pad_zero(const AttnArgs& a, hipStream_t stream);
+
+// a[b, j] += sum_s colsum[b, s, j]; g[b, head_idx[b, s]] += sum_q gpart[b, s, q];
+// lse_out (optional) <- lse (row stride n).
+int launch_importance(const float* colsum, const float* gpart, const float* lse,
+                      const int32_t* head_idx, int batch, int h_kept, int H, int n, int n_pad,
+                      int nqb, float* a, float* g, float* lse_out, hipStream_t stream);
+
+// Decode attention over cache rows 0..lc-1 for every (b, h).
+struct DecodeArgs {
+  const void* q;  // [B, D] bf16
+  const void* k_cache;
+  const void* v_cache;  // [B, cap, D] bf16
+  const uint8_t* k_msb;
+  const uint8_t* k_lsb;
+  const float* k_scale;
+  const uint8_t* v_msb;
+  const uint8_t* v_lsb;
+  const float* v_scale;
+  int batch, H, dh, cap, lc, lc_pad, nchunk;
+  float threshold;
+  float* scores;  // [B, H, lc_pad]
+  float* mpart;
+  float* lpart;   // [B, H, nchunk]
+  float* opart;   // [B, H, nchunk, dh]
+  float* lse;     // [B, H]
+  float* cmax;    // [B, H]
+  int32_t* flags; // [B, H]
+  int32_t* queue; // [0] = count, then entries b*H + h
+  void* o;        // [B, D] bf16
+  float* a;       // [B, cap]
+  int32_t* recompute;  // optional [B, H]
+};
+int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream);
+
+}  // namespace spatten

@@ -1,0 +1,92 @@
+// Tile constants and workspace layout shared by the HIP-free validator and
+// the kernels. Plain C++ (no HIP headers) so that the argument checks can be
+// built and tested with the host compiler alone.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/spatten.h"
+
+#if defined(__HIPCC__)
+#define SPATTEN_HD __host__ __device__
+#else
+#define SPATTEN_HD
+#endif
+
+namespace spatten {
+
+// Prefill token rows of Q, K, V^T are padded per (sequence, head) to this
+// multiple so attention tiles never read past a head's slab.
+constexpr int kTokPad = 128;
+// Prefill attention: queries per workgroup in the forward (O, LSE) kernel
+// and keys per workgroup in the column-sum kernel (bf16 MFMA path).
+constexpr int kAttnQBlock = 128;
+constexpr int kAttnKBlock = 256;
+// fp32 attention: query rows per workgroup.
+constexpr int kAttnF32Rows = 8;
+// Decode: cache entries per split-K chunk.
+constexpr int kDecChunk = 64;
+
+SPATTEN_HD inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+SPATTEN_HD inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Byte offsets of every scratch array inside the caller's workspace.
+struct PrefillWs {
+  int64_t n_pad, nqb;
+  size_t q, k, vt, o, lse, colsum, gpart, total;
+};
+
+struct DecodeWs {
+  int64_t lc, lc_pad, nchunk;
+  size_t q, knew, vnew, scores, mpart, lpart, opart, lse, cmax, flags, queue, o, total;
+};
+
+inline size_t dtype_bytes(int dt) { return dt == SPATTEN_BF16 ? 2 : 4; }
+
+inline PrefillWs prefill_ws(const spatten_layer_desc& d) {
+  PrefillWs w{};
+  const int64_t B = d.batch, n = d.n_tokens, h = d.n_heads_kept, dh = d.head_dim;
+  const size_t es = dtype_bytes(d.dtype);
+  w.n_pad = round_up(n, kTokPad);
+  const int64_t rows = d.dtype == SPATTEN_BF16 ? kAttnQBlock : kAttnF32Rows;
+  w.nqb = ceil_div(n, rows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.q = take(B * h * w.n_pad * dh * es);
+  w.k = take(B * h * w.n_pad * dh * es);
+  w.vt = take(B * h * w.n_pad * dh * es);
+  w.o = take(B * n * h * dh * es);
+  w.lse = take(B * h * w.n_pad * 4);
+  w.colsum = take(B * h * w.n_pad * 4);
+  w.gpart = take(B * h * w.nqb * 4);
+  w.total = off;
+  return w;
+}
+
+inline DecodeWs decode_ws(const spatten_layer_desc& d) {
+  DecodeWs w{};
+  const int64_t B = d.batch, H = d.n_heads, dh = d.head_dim, D = H * dh;
+  w.lc = int64_t(d.cache_len) + 1;
+  w.lc_pad = round_up(w.lc, kDecChunk);
+  w.nchunk = w.lc_pad / kDecChunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.q = take(B * D * 2);
+  w.knew = take(B * D * 2);
+  w.vnew = take(B * D * 2);
+  w.scores = take(B * H * w.lc_pad * 4);
+  w.mpart = take(B * H * w.nchunk * 4);
+  w.lpart = take(B * H * w.nchunk * 4);
+  w.opart = take(B * H * w.nchunk * dh * 4);
+  w.lse = take(B * H * 4);
+  w.cmax = take(B * H * 4);
+  w.flags = take(B * H * 4);
+  w.queue = take((B * H + 1) * 4);
+  w.o = take(B * D * 2);
+  w.total = off;
+  return w;
+}
+
+}  // namespace spatten

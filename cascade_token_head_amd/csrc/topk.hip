@@ -1,0 +1,167 @@
+// On-the-fly top-k by radix select (SpAtten, "B. Top-k Engine": find the
+// k-th largest as a threshold, filter, then eliminate the dropped entries
+// while keeping input order).
+//
+// One workgroup per row. Scores map to order-preserving uint32 keys (larger
+// value -> larger key; -0.0 below +0.0). Four MSD passes of 8 bits find the
+// exact key T of the k-th ranked element with LDS histograms; wave ballots
+// fold lanes that share a digit into one LDS atomic. A final pass in index
+// order keeps every key > T plus the first (k - #above) keys == T, and
+// writes each survivor at its prefix-count position, computed with wave
+// ballots and a cross-wave scan - the GPU form of the order-preserving zero
+// eliminator.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "timing.hpp"
+
+namespace spatten {
+namespace {
+
+constexpr int kMaxWaves = 16;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u ^ 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
+
+// Block-wide exclusive scan of one count per wave; returns this wave's
+// offset and writes the block total to *total. Uses LDS `buf` of kMaxWaves.
+__device__ __forceinline__ int wave_offsets(int wave_count, int wave, int nwaves, int lane,
+                                            int* buf, int* total) {
+  if (lane == 0) buf[wave] = wave_count;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const int c = buf[w];
+    off += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off;
+}
+
+__global__ void __launch_bounds__(1024)
+topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, int k,
+                  int32_t* __restrict__ out_idx, float* __restrict__ kth_out) {
+  __shared__ uint32_t hist[256];
+  __shared__ int scan_buf[kMaxWaves];
+  __shared__ uint32_t sh_digit;
+  __shared__ int sh_krem;
+
+  const int b = blockIdx.x;
+  const float* s = scores + int64_t(b) * row_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+
+  uint32_t prefix = 0, mask = 0;
+  int krem = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += nthreads) hist[i] = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += nthreads) {
+      const int i = base + tid;
+      bool cand = false;
+      uint32_t dig = 0;
+      if (i < n) {
+        const uint32_t key = order_key(s[i]);
+        cand = (key & mask) == prefix;
+        dig = (key >> shift) & 255u;
+      }
+      // fold lanes that share a digit: up to four digit groups per wave
+      // become one atomic each, the rest add one by one
+      uint64_t rem = __ballot(cand);
+      for (int it = 0; it < 4 && rem; ++it) {
+        const int leader = __ffsll((long long)rem) - 1;
+        const uint32_t d0 = __shfl(dig, leader, 64);
+        const uint64_t grp = __ballot(cand && dig == d0) & rem;
+        if (lane == leader) atomicAdd(&hist[d0], uint32_t(__popcll(grp)));
+        rem &= ~grp;
+      }
+      if ((rem >> lane) & 1) atomicAdd(&hist[dig], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins 255-4l .. 252-4l (descending digit order)
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[255 - 4 * lane - j];
+        tot += c[j];
+      }
+      uint32_t incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const uint64_t hit = __ballot(incl >= uint32_t(krem));
+      const int first = __ffsll((long long)hit) - 1;
+      if (lane == first) {
+        uint32_t cum = incl - tot;
+        for (int j = 0; j < 4; ++j) {
+          if (cum + c[j] >= uint32_t(krem)) {
+            sh_digit = uint32_t(255 - 4 * lane - j);
+            sh_krem = krem - int(cum);
+            break;
+          }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    mask |= 255u << shift;
+    krem = sh_krem;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;  // key of the k-th ranked element
+  if (tid == 0 && kth_out) kth_out[b] = key_value(T);
+
+  // ordered selection: key > T, or key == T among the first krem ties
+  int32_t* out = out_idx + int64_t(b) * k;
+  int run_sel = 0, run_eq = 0;
+  for (int base = 0; base < n && run_sel < k; base += nthreads) {
+    const int i = base + tid;
+    uint32_t key = 0;
+    if (i < n) key = order_key(s[i]);
+    const bool gt = i < n && key > T;
+    const bool eq = i < n && key == T;
+    const uint64_t eqm = __ballot(eq);
+    int eq_tot;
+    const int eq_off = wave_offsets(__popcll(eqm), wave, nwaves, lane, scan_buf, &eq_tot);
+    const int eq_rank = run_eq + eq_off + __popcll(eqm & lanemask_lt(lane));
+    const bool sel = gt || (eq && eq_rank < krem);
+    const uint64_t selm = __ballot(sel);
+    int sel_tot;
+    const int sel_off = wave_offsets(__popcll(selm), wave, nwaves, lane, scan_buf, &sel_tot);
+    const int pos = run_sel + sel_off + __popcll(selm & lanemask_lt(lane));
+    if (sel && pos < k) out[pos] = i;
+    run_sel += sel_tot;
+    run_eq += eq_tot;
+  }
+}
+
+}  // namespace
+
+int launch_topk(const float* scores, int batch, int n, int64_t row_stride, int k,
+                int32_t* out_idx, float* kth, hipStream_t stream) {
+  if (batch == 0) return SPATTEN_OK;
+  int threads = 256;
+  if (n > 2048) threads = 512;
+  if (n > 8192) threads = 1024;
+  SPATTEN_TIMED("topk", stream,
+                topk_radix_kernel<<<dim3(batch), dim3(threads), 0, stream>>>(
+                    scores, n, row_stride, k, out_idx, kth));
+  SPATTEN_LAUNCH_CHECK();
+  return SPATTEN_OK;
+}
+
+}  // namespace spatten

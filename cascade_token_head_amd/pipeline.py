@@ -1,0 +1,208 @@
+"""Cascade drivers: sequences the four C-ABI calls over a stack of layers.
+
+All device memory is allocated up front (constructors), so `run()` /
+`step()` only enqueue library calls and can be captured in a HIP graph.
+
+Prefill (SpAtten section II "Cascade pruning"; "A. Cascade Token
+Pruning"): after layer l (l < L) the next layer keeps the top n_{l+1}
+tokens by cumulative importance; x, the importance scores and the original
+positions are compacted together, so pruned tokens are gone from every
+later layer. When the head count drops, the kept heads are re-ranked by
+cumulative head importance.
+
+Decode (section II, generation): one token per step against per-layer K/V
+caches; after every layer of step 1 the caches of all layers are pruned to
+the top cache_keep entries by cumulative importance.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import spatten as S
+
+
+def weights_to_device(layers: List[dict], dtype: torch.dtype, device="cuda") -> List[dict]:
+    """Per-layer x @ W weights ([D_in, D_out] arrays) -> output-major device
+    tensors (w[o, i]), the layout the library takes."""
+    out = []
+    for w in layers:
+        out.append({k: torch.as_tensor(w[k]).t().contiguous().to(device=device, dtype=dtype)
+                    for k in ("wq", "wk", "wv", "wo")})
+    return out
+
+
+class PrefillStack:
+    def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, tokens, heads,
+                 dtype: torch.dtype, causal: bool, weights: List[dict], device="cuda"):
+        assert len(tokens) == n_layers and len(heads) == n_layers
+        self.L, self.B, self.H, self.dh = n_layers, batch, n_heads, head_dim
+        self.D = n_heads * head_dim
+        self.tokens, self.heads = list(tokens), list(heads)
+        self.dtype, self.causal, self.w = dtype, causal, weights
+        self.es = torch.tensor([], dtype=dtype).element_size()
+        B, T, D, H = batch, tokens[0], self.D, n_heads
+        dev = device
+        self.xbuf = [torch.empty(B * T * D, dtype=dtype, device=dev) for _ in range(2)]
+        self.abuf = [torch.zeros(B * T, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.pbuf = [torch.empty(B * T, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.hbuf = [torch.empty(B * H, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.g = torch.zeros(B, H, dtype=torch.float32, device=dev)
+        self.g_kept = torch.empty(B * H, dtype=torch.float32, device=dev)
+        self.tok_idx = torch.empty(B * T, dtype=torch.int32, device=dev)
+        self.head_sel = torch.empty(B * H, dtype=torch.int32, device=dev)
+        self.descs = [S.make_desc(S.PREFILL, S.dtype_code(dtype), causal, B, tokens[l], H,
+                                  heads[l], head_dim) for l in range(n_layers)]
+        ws = max(S.workspace_bytes(d) for d in self.descs)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.lse = None
+        self.trace: Optional[list] = None
+
+    def load(self, x: torch.Tensor):
+        """Reset the cascade state and load x [B, T, D]."""
+        B, T, H = self.B, self.tokens[0], self.H
+        self.xbuf[0][: B * T * self.D].copy_(x.reshape(-1))
+        self.abuf[0].zero_()
+        self.g.zero_()
+        self.pbuf[0].copy_(torch.arange(T, dtype=torch.int32, device=self.g.device).repeat(B))
+        self.hbuf[0].copy_(torch.arange(H, dtype=torch.int32, device=self.g.device).repeat(B))
+
+    def run(self, record: bool = False):
+        """Run all layers; returns (x [B, n_L, D], pos [B, n_L], heads [B, h_L])."""
+        B, D, es = self.B, self.D, self.es
+        cur_t, cur_h = 0, 0
+        self.trace = [] if record else None
+        for l in range(self.L):
+            n, h = self.tokens[l], self.heads[l]
+            x = self.xbuf[cur_t][: B * n * D].view(B, n, D)
+            a = self.abuf[cur_t][: B * n].view(B, n)
+            hidx = self.hbuf[cur_h][: B * h].view(B, h)
+            lse = None
+            if record:
+                lse = torch.empty(B, h, n, dtype=torch.float32, device=x.device)
+                rec = {"x_in": x.clone(), "a_in": a.clone(), "g_in": self.g.clone(),
+                       "heads": hidx.clone(),
+                       "pos": self.pbuf[cur_t][: B * n].view(B, n).clone()}
+            w = self.w[l]
+            S.layer_forward(self.descs[l], x, w["wq"], w["wk"], w["wv"], w["wo"], hidx, a, self.g,
+                            self.ws, lse=lse)
+            if record:
+                rec.update({"x_out": x.clone(), "a_out": a.clone(), "g_out": self.g.clone(),
+                            "lse": lse})
+            if l + 1 < self.L:
+                h2, n2 = self.heads[l + 1], self.tokens[l + 1]
+                if h2 != h:
+                    gk = self.g_kept[: B * h].view(B, h)
+                    S.compact([(self.g, gk, 4, self.H * 4, h * 4)], hidx, h)
+                    sel = self.head_sel[: B * h2].view(B, h2)
+                    S.topk(gk, h2, out=sel)
+                    hnew = self.hbuf[cur_h ^ 1][: B * h2].view(B, h2)
+                    S.compact([(hidx, hnew, 4, h * 4, h2 * 4)], sel, h2)
+                    cur_h ^= 1
+                    if record:
+                        rec["head_sel"] = sel.clone()
+                idx = self.tok_idx[: B * n2].view(B, n2)
+                S.topk(a, n2, out=idx)
+                nt = cur_t ^ 1
+                S.compact([
+                    (x, self.xbuf[nt], D * es, n * D * es, n2 * D * es),
+                    (a, self.abuf[nt], 4, n * 4, n2 * 4),
+                    (self.pbuf[cur_t], self.pbuf[nt], 4, n * 4, n2 * 4),
+                ], idx, n2)
+                cur_t = nt
+                if record:
+                    rec["tok_sel"] = idx.clone()
+            if record:
+                self.trace.append(rec)
+        nL, hL = self.tokens[-1], self.heads[-1]
+        self.final = (self.xbuf[cur_t][: B * nL * D].view(B, nL, D),
+                      self.pbuf[cur_t][: B * nL].view(B, nL),
+                      self.hbuf[cur_h][: B * hL].view(B, hL),
+                      self.abuf[cur_t][: B * nL].view(B, nL))
+        return self.final
+
+
+class DecodeStack:
+    def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, cache_len: int,
+                 cache_keep: int, steps: int, weights: List[dict], quantized: bool = False,
+                 threshold: float = 0.0, dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        self.L, self.B, self.H, self.dh = n_layers, batch, n_heads, head_dim
+        self.D = D = n_heads * head_dim
+        self.L0, self.keep, self.steps = cache_len, cache_keep, steps
+        self.cap = cap = cache_len + steps
+        self.quantized, self.threshold, self.w, self.dtype = quantized, threshold, weights, dtype
+        B, dev = batch, device
+        self.caches = [[], []]
+        for side in range(2):
+            for _ in range(n_layers):
+                if quantized:
+                    c = {"k_msb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
+                         "k_lsb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
+                         "k_scale": torch.empty(B, cap, dtype=torch.float32, device=dev),
+                         "v_msb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
+                         "v_lsb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
+                         "v_scale": torch.empty(B, cap, dtype=torch.float32, device=dev)}
+                else:
+                    c = {"k_cache": torch.empty(B, cap, D, dtype=dtype, device=dev),
+                         "v_cache": torch.empty(B, cap, D, dtype=dtype, device=dev)}
+                self.caches[side].append(c)
+        self.abuf = [torch.zeros(B, cap, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.x = torch.empty(B, 1, D, dtype=dtype, device=dev)
+        self.head_idx = torch.arange(n_heads, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
+        self.g = torch.zeros(B, n_heads, dtype=torch.float32, device=dev)
+        self.recompute = torch.zeros(n_layers, B, n_heads, dtype=torch.int32, device=dev)
+        self.cache_sel = torch.empty(B, cache_keep, dtype=torch.int32, device=dev)
+        dmax = S.make_desc(S.DECODE, S.dtype_code(dtype), False, B, 1, n_heads, n_heads, head_dim,
+                           cap - 1, cap, quantized, threshold)
+        self.ws = torch.empty(max(S.workspace_bytes(dmax), 256), dtype=torch.uint8, device=dev)
+        self.side, self.len, self.s = 0, cache_len, 0
+
+    def load(self, k0: List[torch.Tensor], v0: List[torch.Tensor]):
+        """Initial caches, per layer [B, L0, H, dh] in dtype on the device."""
+        B, L0, D = self.B, self.L0, self.D
+        for l in range(self.L):
+            c = self.caches[0][l]
+            if self.quantized:
+                S.quantize_kv(k0[l].reshape(B, L0, D), c["k_msb"], c["k_lsb"], c["k_scale"])
+                S.quantize_kv(v0[l].reshape(B, L0, D), c["v_msb"], c["v_lsb"], c["v_scale"])
+            else:
+                c["k_cache"][:, :L0].copy_(k0[l].reshape(B, L0, D))
+                c["v_cache"][:, :L0].copy_(v0[l].reshape(B, L0, D))
+        for a in self.abuf:
+            a.zero_()
+        self.side, self.len, self.s = 0, L0, 0
+
+    def step(self, x: torch.Tensor) -> torch.Tensor:
+        """One decode step for x [B, D]; returns the step's output x [B, D]."""
+        B, H = self.B, self.H
+        self.x.view(B, self.D).copy_(x)
+        desc = S.make_desc(S.DECODE, S.dtype_code(self.dtype), False, B, 1, H, H, self.dh,
+                           self.len, self.cap, self.quantized, self.threshold)
+        a = self.abuf[self.side]
+        for l in range(self.L):
+            w, c = self.w[l], self.caches[self.side][l]
+            S.layer_forward(desc, self.x, w["wq"], w["wk"], w["wv"], w["wo"], self.head_idx, a,
+                            self.g, self.ws, recompute=self.recompute[l], **c)
+        self.len += 1
+        if self.s == 0:
+            self.prune()
+        self.s += 1
+        return self.x.view(B, self.D)
+
+    def prune(self):
+        """Keep the top `keep` cache entries (by cumulative importance) in
+        every layer, in one multi-tensor compaction."""
+        B, cap, k = self.B, self.cap, self.keep
+        a, a2 = self.abuf[self.side], self.abuf[self.side ^ 1]
+        S.topk(a, k, n=self.len, out=self.cache_sel)
+        pairs = [(a, a2, 4, cap * 4, cap * 4)]
+        for l in range(self.L):
+            src, dst = self.caches[self.side][l], self.caches[self.side ^ 1][l]
+            for name, t in src.items():
+                rb = t.stride(1) * t.element_size() if t.dim() == 3 else t.element_size()
+                bs = t.stride(0) * t.element_size()
+                pairs.append((t, dst[name], rb, bs, bs))
+        S.compact(pairs, self.cache_sel, k)
+        self.side ^= 1
+        self.len = k

@@ -1,0 +1,178 @@
+/*
+ * spatten.h - C ABI of libspatten.so: cascade token/head pruned attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "SpAtten: Efficient Sparse Attention Architecture
+ * with Cascade Token and Head Pruning" (Wang, Zhang, Han, arXiv 2012.09852)
+ * as summarised on its paperlayer.ai page; section names below are that
+ * page's.
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees or retains them. Small descriptor arrays (the per-tensor
+ *    tables of spatten_compact) are HOST memory read during the call.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream). Nothing synchronises the host; results are valid once the
+ *    stream has reached the enqueued work.
+ *  - Every function returns a spatten_status. Arguments are checked on the
+ *    host before anything is enqueued; a rejected call enqueues nothing.
+ *    SPATTEN_EHIP reports a failed launch (hipGetLastError) and leaves the
+ *    outputs unspecified. No function aborts or throws.
+ *  - Tensors are row-major and densely packed in their last dimension.
+ *    bf16 is IEEE bfloat16 stored as uint16.
+ *  - Weights use the output-major layout: w[o * D + i] multiplies input
+ *    feature i into output feature o (y = x w^T). Head h owns output rows
+ *    h*dh .. h*dh+dh-1 of wq, wk, wv and input columns h*dh .. h*dh+dh-1
+ *    of wo.
+ */
+#ifndef SPATTEN_H
+#define SPATTEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPATTEN_OK = 0,
+  SPATTEN_EINVAL = -1,       /* malformed argument (null pointer, size out of range, overlap) */
+  SPATTEN_EUNSUPPORTED = -2, /* well-formed but outside what the kernels implement */
+  SPATTEN_EWORKSPACE = -3,   /* workspace smaller than the size reported for this descriptor */
+  SPATTEN_EHIP = -4          /* a HIP launch failed */
+} spatten_status;
+
+typedef enum { SPATTEN_F32 = 0, SPATTEN_BF16 = 1 } spatten_dtype;
+typedef enum { SPATTEN_PREFILL = 0, SPATTEN_DECODE = 1 } spatten_mode;
+
+/* Shape of one layer call. */
+typedef struct {
+  int32_t mode;          /* spatten_mode */
+  int32_t dtype;         /* spatten_dtype of x, weights, caches (accumulation is fp32) */
+  int32_t causal;        /* prefill: 1 = token j is masked for query i when j > i */
+  int32_t batch;         /* B sequences */
+  int32_t n_tokens;      /* prefill: kept tokens per sequence (n_l); decode: 1 */
+  int32_t n_heads;       /* H; model dim D = H * head_dim */
+  int32_t n_heads_kept;  /* h_l kept heads (decode: must equal H) */
+  int32_t head_dim;      /* dh: 32, 64 or 128 */
+  int32_t cache_len;     /* decode: cache entries before this step's append */
+  int32_t cache_cap;     /* decode: cache rows allocated per sequence */
+  int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
+  float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
+} spatten_layer_desc;
+
+/*
+ * spatten_layer_forward - one attention-only residual layer over the kept
+ * tokens and heads (section II "Attention mechanism"), with cascade token
+ * and head importance accumulated on the fly (section II "Cascade
+ * pruning"; "A. Cascade Token Pruning").
+ *
+ *   For each sequence b and kept head slot s (head h = head_idx[b, s]):
+ *     Q_h, K_h, V_h = x w{q,k,v}[h rows]^T
+ *     P_h = row-softmax(Q_h K_h^T / sqrt(dh))   (causal: j > i masked)
+ *     O_h = P_h V_h
+ *     x  += sum_s O_h wo[:, h cols]^T           (residual, in place)
+ *     a[b, j] += sum_s sum_i P_h[i, j]          (token importance)
+ *     g[b, h] += sum_i sum_c |O_h[i, c]|        (head importance)
+ *
+ * Prefill: x is [B, n_tokens, D]; a is [B, n_tokens] fp32; g is [B, H]
+ *   fp32; k_cache..v_scale must be NULL. lse (optional, may be NULL) gets
+ *   the per-row log-sum-exp [B, h_kept, n_tokens] fp32.
+ * Decode: x is [B, 1, D] (this step's token). The token's k and v are
+ *   appended at cache row cache_len, then the query attends over rows
+ *   0..cache_len (no mask) and a[b, j] (a is [B, cache_cap]) accumulates
+ *   for those rows. Unquantized: k_cache, v_cache are [B, cache_cap, D]
+ *   in dtype. Quantized (progressive quantization, section III and
+ *   "E. ... Progressive Quantization"): k_msb, k_lsb, v_msb, v_lsb are
+ *   [B, cache_cap, D/2] u8 and k_scale, v_scale [B, cache_cap] fp32 as
+ *   written by spatten_quantize_kv; each (b, h) row is scored with MSB-only
+ *   values (scale*16*msb) and, when its largest probability is below
+ *   pq_threshold, recomputed with the full code scale*(16*msb + lsb) for
+ *   both K and V. recompute (optional, [B, H] int32) receives 1 for
+ *   recomputed rows. a accumulates the probabilities that produced O.
+ *   g is not used in decode and may be NULL. Decode needs head_dim 64,
+ *   H <= 32, bf16 and every head kept.
+ * head_idx: [B, h_kept] int32, strictly ascending head ids per sequence.
+ * workspace: device scratch of *workspace_bytes bytes, 256-byte aligned.
+ *   If workspace is NULL only *d is checked, the required size is stored in
+ *   *workspace_bytes and SPATTEN_OK is returned without enqueuing anything
+ *   (tensor pointers may then be NULL).
+ * Supported: prefill bf16 with head_dim 64 or 128, prefill fp32 with
+ *   n_tokens <= 1024; other shapes return SPATTEN_EUNSUPPORTED.
+ */
+int spatten_layer_forward(const spatten_layer_desc* d, void* x,
+                          const void* wq, const void* wk, const void* wv, const void* wo,
+                          const int32_t* head_idx, float* a, float* g,
+                          void* k_cache, void* v_cache,
+                          uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
+                          uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
+                          int32_t* recompute, float* lse,
+                          void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * spatten_topk - on-the-fly top-k ("B. Top-k Engine"): for each row b the
+ * k largest of scores[b*row_stride + 0 .. n-1], ranked by fp32 value with
+ * -0.0 below +0.0 and equal values broken towards the lower index
+ * (NaNs rank by their bit pattern). out_idx[b*k + 0 .. k-1] receives the
+ * selected indices in ascending order. kth_value (optional, [batch]) gets
+ * the k-th ranked score. Requires 1 <= k <= n, row_stride >= n; batch == 0
+ * is a no-op. No workspace.
+ */
+int spatten_topk(const float* scores, int32_t batch, int32_t n, int64_t row_stride,
+                 int32_t k, int32_t* out_idx, float* kth_value, void* stream);
+
+/*
+ * spatten_compact - multi-tensor row gather that drops pruned tokens from
+ * all following computation ("A. Cascade Token Pruning"):
+ *   for t < n_tensors, b < batch, r < k:
+ *     dst[t] + b*dst_batch_stride[t] + r*row_bytes[t]
+ *       <- src[t] + b*src_batch_stride[t] + idx[b*k + r]*row_bytes[t]
+ * (row_bytes bytes; strides in bytes). src, dst, row_bytes and the strides
+ * are HOST arrays of n_tensors entries holding device addresses. Each
+ * idx[b*k + r] must lie in [0, src rows) - the caller guarantees this
+ * (typically idx comes from spatten_topk). src and dst of one tensor must
+ * not overlap (checked over the span the call touches).
+ */
+int spatten_compact(int32_t n_tensors, const void* const* src, void* const* dst,
+                    const int64_t* row_bytes, const int64_t* src_batch_stride,
+                    const int64_t* dst_batch_stride, const int32_t* idx,
+                    int32_t batch, int32_t k, void* stream);
+
+/*
+ * spatten_quantize_kv - K/V rows to separately fetchable MSB and LSB
+ * planes (section III "Progressive Quantization"; IV "Quantization
+ * Support"). For each row of `dim` values, in fp32:
+ *   s = max|x| / 127;  q = clamp(round_half_even(x / s), -127, 127)
+ *   (s = 0 and q = 0 for an all-zero row)
+ *   msb = q >> 4 (arithmetic, -8..7), lsb = q & 15 (0..15)
+ *   msb byte j = (msb[2j] & 15) | (msb[2j+1] & 15) << 4, lsb likewise.
+ * kv: [batch, n, dim] in dtype with batch stride kv_batch_stride elements.
+ * msb, lsb: [batch, *, dim/2] u8 with batch stride plane_batch_stride rows;
+ * scale: [batch, *] fp32 with the same batch stride in rows. dim must be
+ * even. Pointers may be pre-offset to the first row to write.
+ */
+int spatten_quantize_kv(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,
+                        int64_t kv_batch_stride, uint8_t* msb, uint8_t* lsb, float* scale,
+                        int64_t plane_batch_stride, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* spatten_status_string(int status);
+
+/*
+ * Diagnostics (not part of the computation). spatten_debug_timing(1)
+ * brackets every kernel the library launches with two HIP events on the
+ * launching stream; spatten_debug_kernel_times() waits for them and reports,
+ * per kernel name, the summed event durations and the launch count, then
+ * forgets them. names receives up to max_kernels NUL-terminated names of
+ * name_len bytes each. Timing state is process-wide and not thread-safe.
+ */
+int spatten_debug_timing(int enable);
+int spatten_debug_kernel_times(int max_kernels, char* names, int name_len, double* total_ms,
+                               int* launches, int* n_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPATTEN_H */

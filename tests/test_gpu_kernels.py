@@ -1,0 +1,150 @@
+"""GPU parity: top-k, compaction and the int8 MSB/LSB quantizer, bit-exact
+against the oracle on identical inputs (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import spatten_ref as R
+from workloads import random_scores
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    from cascade_token_head_amd import spatten
+    spatten.load()
+    assert torch.cuda.is_available()
+    return spatten
+
+
+TOPK_CASES = [
+    # (batch, n, k, kind)
+    (1, 1, 1, "normal"), (3, 7, 3, "ties"), (1, 64, 32, "normal"), (2, 100, 1, "normal"),
+    (2, 100, 100, "ties"), (32, 512, 489, "normal"), (32, 489, 465, "uniform"),
+    (5, 300, 150, "signed_zero"), (4, 1025, 410, "normal"), (16, 2049, 1024, "normal"),
+    (3, 4097, 2000, "ties"), (1, 32768, 8192, "normal"), (2, 32768, 1, "uniform"),
+    (1, 32768, 32768, "ties"), (2, 12, 10, "normal"), (2, 32, 24, "uniform"),
+]
+
+
+@pytest.mark.parametrize("batch,n,k,kind", TOPK_CASES)
+def test_topk_bit_exact(S, batch, n, k, kind):
+    a = random_scores((batch, n), seed=n * 7 + k, kind=kind)
+    if kind == "normal" and n > 2:
+        a[:, 1] = a[:, 0]            # force a tie on the first pair
+    d = torch.from_numpy(a).cuda()
+    kth = torch.empty(batch, dtype=torch.float32, device="cuda")
+    idx = S.topk(d, k, kth=kth).cpu().numpy()
+    kv = kth.cpu().numpy()
+    for b in range(batch):
+        ref = R.topk(a[b], k)
+        np.testing.assert_array_equal(idx[b], ref, err_msg="row %d" % b)
+        rk = R.kth_value(a[b], k)
+        assert np.float32(kv[b]).view(np.uint32) == np.float32(rk).view(np.uint32)
+
+
+def test_topk_row_stride_and_prefix(S):
+    a = random_scores((4, 1056), seed=3)
+    d = torch.from_numpy(a).cuda()
+    idx = S.topk(d, 410, n=1025).cpu().numpy()
+    for b in range(4):
+        np.testing.assert_array_equal(idx[b], R.topk(a[b, :1025], 410))
+
+
+def test_topk_nan_orders_by_bits(S):
+    a = random_scores((2, 40), seed=4)
+    a[0, 5] = np.float32(np.nan)
+    a[1, 7] = -np.float32(np.nan)
+    d = torch.from_numpy(a).cuda()
+    idx = S.topk(d, 20).cpu().numpy()
+    for b in range(2):
+        np.testing.assert_array_equal(idx[b], R.topk(a[b], 20))
+
+
+def test_topk_rejects_bad_k(S):
+    d = torch.zeros(2, 10, device="cuda")
+    with pytest.raises(S.SpattenError):
+        S.topk(d, 11)
+    with pytest.raises(S.SpattenError):
+        S.topk(d, 0)
+
+
+def test_compact_multi_tensor_bit_exact(S):
+    rng = np.random.default_rng(0)
+    B, n, k = 3, 97, 41
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    tensors = [
+        rng.standard_normal((B, n, 768)).astype(np.float32),           # 16-byte rows
+        rng.integers(0, 255, (B, n, 6), dtype=np.uint8),               # 2-byte aligned rows
+        rng.integers(0, 255, (B, n, 3), dtype=np.uint8),               # byte rows
+        rng.standard_normal((B, n)).astype(np.float32),                 # 4-byte rows
+        rng.integers(0, 1 << 30, (B, n, 2), dtype=np.int32),           # 8-byte rows
+    ]
+    src = [torch.from_numpy(t).cuda() for t in tensors]
+    dst = [torch.zeros((B, k) + t.shape[2:], dtype=s.dtype, device="cuda") for t, s in zip(tensors, src)]
+    pairs = []
+    for s, d in zip(src, dst):
+        rb = s[0, 0].numel() * s.element_size()
+        pairs.append((s, d, rb, s.stride(0) * s.element_size(), d.stride(0) * d.element_size()))
+    S.compact(pairs, torch.from_numpy(idx).cuda(), k)
+    for t, d in zip(tensors, dst):
+        ref = np.stack([R.compact(t[b], idx[b]) for b in range(B)])
+        np.testing.assert_array_equal(d.cpu().numpy(), ref)
+
+
+def test_compact_identity_and_many_tensors(S):
+    B, n = 2, 33
+    srcs = [torch.arange(B * n * (i + 1), dtype=torch.int32, device="cuda").view(B, n, i + 1)
+            for i in range(60)]
+    dsts = [torch.empty_like(s) for s in srcs]
+    pairs = [(s, d, (i + 1) * 4, n * (i + 1) * 4, n * (i + 1) * 4)
+             for i, (s, d) in enumerate(zip(srcs, dsts))]
+    idx = torch.arange(n, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+    S.compact(pairs, idx, n)
+    for s, d in zip(srcs, dsts):
+        assert torch.equal(s, d)
+
+
+def test_compact_rejects_overlap(S):
+    t = torch.zeros(2, 10, 4, device="cuda")
+    idx = torch.zeros(2, 3, dtype=torch.int32, device="cuda")
+    with pytest.raises(S.SpattenError):
+        S.compact([(t, t, 16, 160, 160)], idx, 3)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("B,n,D", [(1, 1, 2), (2, 5, 8), (3, 17, 768), (2, 33, 1024), (1, 4, 1026)])
+def test_quantize_bit_exact(S, dtype, B, n, D):
+    rng = np.random.default_rng(B * 1000 + n * 10 + D)
+    x = (rng.standard_normal((B, n, D)) * rng.choice([1e-3, 1.0, 300.0], (B, n, 1))).astype(np.float32)
+    x[0, 0] = 0.0                                                    # all-zero row
+    if n > 2:
+        x[-1, 1, :] = np.float32(127.0) * np.sign(rng.standard_normal(D)).astype(np.float32) * 0.5
+    xt = torch.from_numpy(x).to(dtype)
+    xq = xt.float().numpy()                                          # values the kernel sees
+    cap = n + 3
+    msb = torch.zeros(B, cap, D // 2, dtype=torch.uint8, device="cuda")
+    lsb = torch.zeros_like(msb)
+    sc = torch.zeros(B, cap, dtype=torch.float32, device="cuda")
+    S.quantize_kv(xt.cuda(), msb, lsb, sc)
+    rm, rl, rs = R.quantize_kv(xq)
+    np.testing.assert_array_equal(msb[:, :n].cpu().numpy(), rm)
+    np.testing.assert_array_equal(lsb[:, :n].cpu().numpy(), rl)
+    np.testing.assert_array_equal(sc[:, :n].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert int(msb[:, n:].abs().sum()) == 0
+
+
+def test_quantize_offset_rows(S):
+    """Writing at a row offset (the decode append) leaves other rows alone."""
+    rng = np.random.default_rng(9)
+    B, D, cap, row = 4, 64, 10, 6
+    x = rng.standard_normal((B, 1, D)).astype(np.float32)
+    msb = torch.full((B, cap, D // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    lsb = torch.full_like(msb, 0xCD)
+    sc = torch.full((B, cap), -1.0, device="cuda")
+    S.quantize_kv(torch.from_numpy(x).cuda(), msb[:, row:], lsb[:, row:], sc[:, row:])
+    rm, rl, rs = R.quantize_kv(x)
+    np.testing.assert_array_equal(msb[:, row:row + 1].cpu().numpy(), rm)
+    np.testing.assert_array_equal(lsb[:, row:row + 1].cpu().numpy(), rl)
+    assert int((msb[:, :row] != 0xAB).sum()) == 0 and int((sc[:, row + 1:] != -1).sum()) == 0

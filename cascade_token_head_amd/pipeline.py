@@ -89,7 +89,7 @@ class PrefillStack:
                             self.ws, lse=lse)
             if record:
                 rec.update({"x_out": x.clone(), "a_out": a.clone(), "g_out": self.g.clone(),
-                            "lse": lse})
+                            "lse": lse, "ws": self.ws.clone()})
             if l + 1 < self.L:
                 h2, n2 = self.heads[l + 1], self.tokens[l + 1]
                 if h2 != h:
@@ -157,6 +157,7 @@ class DecodeStack:
                            cap - 1, cap, quantized, threshold)
         self.ws = torch.empty(max(S.workspace_bytes(dmax), 256), dtype=torch.uint8, device=dev)
         self.side, self.len, self.s = 0, cache_len, 0
+        self.trace = []
 
     def load(self, k0: List[torch.Tensor], v0: List[torch.Tensor]):
         """Initial caches, per layer [B, L0, H, dh] in dtype on the device."""
@@ -172,9 +173,13 @@ class DecodeStack:
         for a in self.abuf:
             a.zero_()
         self.side, self.len, self.s = 0, L0, 0
+        self.trace = []
 
-    def step(self, x: torch.Tensor) -> torch.Tensor:
-        """One decode step for x [B, D]; returns the step's output x [B, D]."""
+    def step(self, x: torch.Tensor, record: bool = False, hook=None) -> torch.Tensor:
+        """One decode step for x [B, D]; returns the step's output x [B, D].
+        With record=True the per-layer recompute flags of this step are kept
+        in self.trace. hook(phase, layer), if given, is called before
+        ("pre") and after ("post") each layer call."""
         B, H = self.B, self.H
         self.x.view(B, self.D).copy_(x)
         desc = S.make_desc(S.DECODE, S.dtype_code(self.dtype), False, B, 1, H, H, self.dh,
@@ -182,11 +187,19 @@ class DecodeStack:
         a = self.abuf[self.side]
         for l in range(self.L):
             w, c = self.w[l], self.caches[self.side][l]
+            if hook is not None:
+                hook("pre", l)
             S.layer_forward(desc, self.x, w["wq"], w["wk"], w["wv"], w["wo"], self.head_idx, a,
                             self.g, self.ws, recompute=self.recompute[l], **c)
+            if hook is not None:
+                hook("post", l)
         self.len += 1
+        if record:
+            self.trace.append({"recompute": self.recompute.clone()})
         if self.s == 0:
             self.prune()
+            if record:
+                self.trace[-1]["cache_sel"] = self.cache_sel.clone()
         self.s += 1
         return self.x.view(B, self.D)
 

@@ -238,17 +238,23 @@ def dequant(msb_p, lsb_p, scale, full: bool):
     return v * np.asarray(scale, dtype=np.float64)[..., None]
 
 
-def pq_head_attention(q, Kmsb, Kfull, Vmsb, Vfull, threshold: float):
+def pq_head_attention(q, Kmsb, Kfull, Vmsb, Vfull, threshold: float,
+                      decide: Optional[Callable] = None):
     """One decode query row of one head under progressive quantization.
 
     First pass scores against the MSB-only keys. If the largest probability
     is below the threshold the distribution is flat: the row is recomputed
     with both planes for K and V. Returns (o, p, recomputed, max_p_msb).
+    decide(c, default) may override the decision (tests use it to follow
+    the GPU among rows whose confidence is at the threshold).
     """
     dh = q.shape[0]
     p = softmax_rows((Kmsb @ q) / math.sqrt(dh))
     c = float(np.max(p))
-    if c < threshold:
+    flat = c < threshold
+    if decide is not None:
+        flat = decide(c, flat)
+    if flat:
         p = softmax_rows((Kfull @ q) / math.sqrt(dh))
         return p @ Vfull, p, True, c
     return p @ Vmsb, p, False, c
@@ -310,11 +316,42 @@ def run_prefill(cfg, inputs: dict, seqs=None,
     return out
 
 
+def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: bool,
+                     threshold: float, decide: Optional[Callable] = None):
+    """Attention of one decode query q [H, dh] over every entry of a cache
+    (no mask). Unquantized caches hold k, v [Lc, H, dh]; quantized ones the
+    packed planes and scales of K and V rows. Returns (o [H, dh],
+    p [H, Lc], recompute flags [H], MSB-pass max probability [H])."""
+    H, dh = heads_n, head_dim
+    if quantized:
+        Km = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], False).reshape(-1, H, dh)
+        Kf = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], True).reshape(-1, H, dh)
+        Vm = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], False).reshape(-1, H, dh)
+        Vf = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], True).reshape(-1, H, dh)
+        Lc = Km.shape[0]
+    else:
+        Lc = cache["k"].shape[0]
+    O = np.zeros((H, dh))
+    P = np.zeros((H, Lc))
+    rec = np.zeros(H, dtype=bool)
+    cmax = np.zeros(H)
+    for h in range(H):
+        if quantized:
+            dec = None if decide is None else (lambda c_, d_, h_=h: decide(h_, c_, d_))
+            O[h], P[h], rec[h], cmax[h] = pq_head_attention(q[h], Km[:, h], Kf[:, h], Vm[:, h],
+                                                            Vf[:, h], threshold, dec)
+        else:
+            P[h] = softmax_rows((cache["k"][:, h] @ q[h]) / math.sqrt(dh))
+            O[h] = P[h] @ cache["v"][:, h]
+    return O, P, rec, cmax
+
+
 def decode_layer(x, w: dict, cache: dict, heads_n: int, head_dim: int, bf16: bool,
-                 quantized: bool, threshold: float):
+                 quantized: bool, threshold: float, decide: Optional[Callable] = None):
     """One decode layer for one sequence. The new token's k and v are
     appended to the cache, then the query attends over every cache entry
-    (no mask). Returns (x_new, p [H, Lc], recompute flags [H])."""
+    (no mask). Returns (x_new, p [H, Lc], recompute flags [H], MSB-pass max
+    probability [H]). decide(h, c, default) may override a PQ decision."""
     H, dh = heads_n, head_dim
     x = np.asarray(x, dtype=np.float64)
     q = _store(x @ w["wq"].astype(np.float64), bf16).reshape(H, dh)
@@ -326,38 +363,24 @@ def decode_layer(x, w: dict, cache: dict, heads_n: int, head_dim: int, bf16: boo
         for name, val in (("k_msb", km), ("k_lsb", kl), ("k_scale", ks),
                           ("v_msb", vm), ("v_lsb", vl), ("v_scale", vs)):
             cache[name] = np.concatenate([cache[name], np.asarray(val)[None]], axis=0)
-        Km = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], False).reshape(-1, H, dh)
-        Kf = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], True).reshape(-1, H, dh)
-        Vm = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], False).reshape(-1, H, dh)
-        Vf = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], True).reshape(-1, H, dh)
     else:
         cache["k"] = np.concatenate([cache["k"], k.reshape(1, H, dh)], axis=0)
         cache["v"] = np.concatenate([cache["v"], v.reshape(1, H, dh)], axis=0)
-    Lc = cache["k_scale"].shape[0] if quantized else cache["k"].shape[0]
-    P = np.zeros((H, Lc))
-    rec = np.zeros(H, dtype=bool)
-    cmax = np.zeros(H)
+    O, P, rec, cmax = decode_attention(q, cache, H, dh, quantized, threshold, decide)
     delta = np.zeros(x.shape[0])
     for h in range(H):
-        if quantized:
-            o, p, r, c = pq_head_attention(q[h], Km[:, h], Kf[:, h], Vm[:, h], Vf[:, h], threshold)
-            rec[h] = r
-            cmax[h] = c
-        else:
-            p = softmax_rows((cache["k"][:, h] @ q[h]) / math.sqrt(dh))
-            o = p @ cache["v"][:, h]
-        P[h] = p
-        delta += _store(o, bf16) @ w["wo"][h * dh:(h + 1) * dh, :].astype(np.float64)
+        delta += _store(O[h], bf16) @ w["wo"][h * dh:(h + 1) * dh, :].astype(np.float64)
     return _store(x + delta, bf16), P, rec, cmax
 
 
 def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
-               steps: Optional[int] = None) -> dict:
+               steps: Optional[int] = None, pq_adopt: Optional[Callable] = None) -> dict:
     """Generation (page: section II, attention-based NLP models): one new
     token per step against cached K/V. Token importance a accumulates the
     probabilities each cache entry receives, over heads, layers and steps;
     a new entry starts at 0. After every layer of step 1 has run, the cache
-    of every layer keeps topk(a over L0+1 entries, cache_keep) entries."""
+    of every layer keeps topk(a over L0+1 entries, cache_keep) entries.
+    pq_adopt(b, s, l, h, c, default) may override a recompute decision."""
     bf16 = cfg.dtype == "bf16"
     seqs = range(cfg.batch) if seqs is None else seqs
     steps = cfg.steps if steps is None else steps
@@ -383,8 +406,11 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
             a = np.concatenate([a, [0.0]])
             step_rec = []
             for l in range(cfg.n_layers):
+                dec = None
+                if pq_adopt is not None:
+                    dec = (lambda h_, c_, d_, b_=b, s_=s, l_=l: pq_adopt(b_, s_, l_, h_, c_, d_))
                 x, P, rec, cmax = decode_layer(x, inputs["layers"][l], caches[l], H, dh, bf16,
-                                               cfg.quantized, cfg.pq_threshold)
+                                               cfg.quantized, cfg.pq_threshold, dec)
                 a = a + P.sum(axis=0)
                 step_rec.append((rec, cmax))
             xs.append(x)

@@ -409,3 +409,22 @@ def test_run_decode_pq_threshold_zero_never_recomputes():
     cfg2 = scaled(cfg, pq_threshold=1.01)
     out2 = R.run_decode(cfg2, make_decode_inputs(cfg2))[0]
     assert all(r.all() for step in out2["recompute"] for r, _ in step)
+
+
+def test_stack_amplifies_one_ulp_perturbation():
+    """The synthetic random-weight stack is chaotic: one bf16 step on one
+    input element grows by orders of magnitude within a few layers. This is
+    why stack parity is checked layer by layer on identical inputs."""
+    from workloads import BERT_BASE
+    cfg = scaled(BERT_BASE, batch=1, n_layers=6, tokens=(512,) * 6, heads=(12,) * 6)
+    inp = make_prefill_inputs(cfg)
+    base = R.run_prefill(cfg, inp)[0]
+    x2 = inp["x"].copy()
+    x2[0, 5, 7] = np.float32(R.bf16_round(x2[0, 5, 7] * (1 + 2.0 ** -7)))
+    pert = R.run_prefill(cfg, dict(inp, x=x2))[0]
+
+    def nrmse(l):
+        a, b = base["trace"][l]["x"], pert["trace"][l]["x"]
+        return np.sqrt(np.mean((a - b) ** 2) / np.mean(a * a))
+    assert nrmse(0) < 1e-3
+    assert nrmse(5) > 100 * nrmse(0)

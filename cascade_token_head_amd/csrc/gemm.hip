@@ -14,6 +14,8 @@
 #include "kernels.hpp"
 #include "timing.hpp"
 
+#include <cmath>
+
 namespace spatten {
 namespace {
 
@@ -209,6 +211,204 @@ gemm_bf16_kernel(GemmParams p) {
   }
 }
 
+// ------------------------------------------------------------------ bf16 MFMA, large tiles
+//
+// BM x BN x 64 workgroup tiles, four waves in a 2 x 2 grid, each wave
+// (BM/2) x (BN/2) with 32x32x16 MFMAs, so every LDS fragment feeds BN/64
+// or BM/64 MFMAs. LDS rows are 128 bytes with the 16-byte chunks XOR-
+// swizzled by the row index: the eight rows a group of lanes reads at one
+// k offset land in eight different bank groups without padding, and two
+// stages of a 256 x 256 tile fit in 128 KB. Epilogue index math is hoisted:
+// column terms once per MFMA column tile, row terms advanced incrementally.
+
+template <int MODE, int BM, int BN>
+__global__ void __launch_bounds__(256, (BM * BN <= 128 * 128) ? 2 : 1)
+gemm_tile_kernel(GemmParams p) {
+  constexpr int BKT = 64;
+  constexpr int WM = BM / 2, WN = BN / 2, TI = WM / 32, TJ = WN / 32;
+  constexpr int NA = BM * 8 / 256, NB = BN * 8 / 256;  // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BKT];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BKT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile_y = blockIdx.y, n0 = blockIdx.x * BN;
+  const int b_tile = p.seq_tiled ? tile_y / p.mt_per_seq : 0;
+  const int kc = tid & 7;  // 16-byte chunk along k this thread loads
+
+  const bf16_t* a_src[NA];
+  const bf16_t* w_src[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    RowMap rm = map_row(p, tile_y, r, BM);
+    if (!rm.valid) rm = p.seq_tiled ? RowMap{true, rm.b, p.n - 1} : RowMap{true, p.batch - 1, p.n - 1};
+    a_src[i] = static_cast<const bf16_t*>(p.A) + (int64_t(rm.b) * p.n + rm.m) * p.lda + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    int ncol = n0 + r;
+    if (ncol >= p.N) ncol = p.N - 1;
+    if (MODE == kOut)
+      w_src[i] = static_cast<const bf16_t*>(p.W0) + int64_t(ncol) * p.ldw + kc * 8;
+    else
+      w_src[i] = qkv_weight_row<bf16_t>(p, b_tile, ncol) + kc * 8;
+  }
+  // swizzled LDS slot of this thread's chunk in row r: r*64 + ((kc ^ (r&7)) * 8)
+  const int st_off = (((tid >> 3) & 7) ^ kc) * 8 + (tid >> 3) * BKT;
+
+  const int KT = p.K / BKT;
+  u32x4 ra[NA], rb[NB];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BKT;
+    int wk = k0;
+    if (MODE == kOut) {
+      const int s = k0 / p.dh;
+      wk = head_of(p, b_tile, s) * p.dh + (k0 - s * p.dh);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + k0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(w_src[i] + wk);
+  };
+  auto sstore = [&](int buf) {
+    // rows tid/8 + 32 i keep the same (row & 7), so one swizzled offset serves all i
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      *reinterpret_cast<u32x4*>(&As[buf][st_off + 32 * i * BKT]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      *reinterpret_cast<u32x4*>(&Bs[buf][st_off + 32 * i * BKT]) = rb[i];
+  };
+
+  floatx16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  const int fr = lane & 31, G = lane >> 5;
+  // fragment rows wm + 32 i + fr all share (row & 7) == (fr & 7)
+  const int fsw = fr & 7;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = ((2 * kk + G) ^ fsw) * 8;
+      bf16x8 af[TI], bfr[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&As[buf][(wm + 32 * i + fr) * BKT + ch]));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Bs[buf][(wn + 32 * j + fr) * BKT + ch]));
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: each 32 x 32 MFMA block goes through a 2 KB per-wave LDS
+  // stage (row-major, or transposed for V^T) and leaves as 16-byte stores.
+  const int hd = p.h_kept * p.dh;
+  const float inv_n = 1.0f / float(p.n);
+  bf16_t* stage = &As[0][0] + wave * 1024;
+  auto row_of = [&](int lr, int& b, int& m) -> bool {
+    if (p.seq_tiled) {
+      b = b_tile;
+      m = (tile_y - b_tile * p.mt_per_seq) * BM + lr;
+      return m < p.n;
+    }
+    const int g = tile_y * BM + lr;
+    b = int(float(g) * inv_n);
+    if (b * p.n > g) --b;
+    if ((b + 1) * p.n <= g) ++b;
+    m = g - b * p.n;
+    return g < p.M_total;
+  };
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int c0 = n0 + wn + 32 * j;  // first column of this block (uniform)
+    if (c0 >= p.N) continue;
+    const int which = MODE == kOut ? 0 : c0 / hd;
+    const bool trans = MODE == kQkvPrefill && which == 2;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int r0 = wm + 32 * i;  // first local row of this block
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 8 * (r >> 2) + 4 * G + (r & 3);
+        const int idx = trans ? fr * 32 + rr : rr * 32 + fr;
+        stage[idx] = f32_to_bf16(acc[i][j][r]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ch = lane + 64 * q;        // 128 chunks of 8 elements
+        const int a8 = ch >> 2, o8 = (ch & 3) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[a8 * 32 + o8]);
+        if (!trans) {
+          // a8 = row in block, o8 = column offset
+          int b, m;
+          if (!row_of(r0 + a8, b, m)) continue;
+          const int col = c0 + o8;
+          if (MODE == kOut) {
+            bf16_t* x = static_cast<bf16_t*>(p.out0) + (int64_t(b) * p.n + m) * p.D + col;
+            u32x4 xv = *reinterpret_cast<const u32x4*>(x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float lo = __uint_as_float(xv[e] << 16) + __uint_as_float(v[e] << 16);
+              const float hi = __uint_as_float(xv[e] & 0xffff0000u) +
+                               __uint_as_float(v[e] & 0xffff0000u);
+              xv[e] = pack_bf16x2(lo, hi);
+            }
+            *reinterpret_cast<u32x4*>(x) = xv;
+          } else {
+            const int rem = col - which * hd;
+            const int s_ = rem / p.dh, cc = rem - s_ * p.dh;
+            bf16_t* d = static_cast<bf16_t*>(which == 0 ? p.out0 : p.out1) +
+                        ((int64_t(b) * p.h_kept + s_) * p.n_pad + m) * p.dh + cc;
+            *reinterpret_cast<u32x4*>(d) = v;
+          }
+        } else {
+          // a8 = column in block, o8 = first of 8 consecutive rows
+          const int col = c0 + a8;
+          const int rem = col - 2 * hd;
+          const int s_ = rem / p.dh, cc = rem - s_ * p.dh;
+          int b, m, b7, m7;
+          const bool v0 = row_of(r0 + o8, b, m);
+          const bool v7 = row_of(r0 + o8 + 7, b7, m7);
+          bf16_t* base = static_cast<bf16_t*>(p.out2);
+          if (v0 && v7 && b7 == b && (m & 7) == 0) {
+            *reinterpret_cast<u32x4*>(base + ((int64_t(b) * p.h_kept + s_) * p.dh + cc) * p.n_pad + m) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              int be, me;
+              if (!row_of(r0 + o8 + e, be, me)) continue;
+              const uint32_t w32 = v[e >> 1];
+              base[((int64_t(be) * p.h_kept + s_) * p.dh + cc) * p.n_pad + me] =
+                  bf16_t((e & 1) ? (w32 >> 16) : (w32 & 0xffffu));
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 VALU
 
 constexpr int FT = 64, FK = 16;
@@ -270,9 +470,40 @@ gemm_f32_kernel(GemmParams p) {
   }
 }
 
+template <int MODE, int BMt, int BNt>
+int run_tile(GemmParams& p, hipStream_t stream, const char* name) {
+  if (!p.seq_tiled && p.M_total >= (1 << 24)) p.seq_tiled = 1;
+  int tiles_y;
+  if (p.seq_tiled) {
+    p.mt_per_seq = int(ceil_div(p.n, BMt));
+    tiles_y = p.mt_per_seq * p.batch;
+  } else {
+    p.mt_per_seq = 0;
+    tiles_y = int(ceil_div(p.M_total, BMt));
+  }
+  const dim3 grid(unsigned(ceil_div(p.N, BNt)), unsigned(tiles_y));
+  SPATTEN_TIMED(name, stream, gemm_tile_kernel<MODE, BMt, BNt><<<grid, 256, 0, stream>>>(p));
+  SPATTEN_LAUNCH_CHECK();
+  return SPATTEN_OK;
+}
+
+// Work estimate (tile-rows x tile-cols x relative cost) for picking a tile.
+inline double tile_cost(const GemmParams& p, int bm, int bn, double rel) {
+  const double my = p.seq_tiled ? double(ceil_div(p.n, bm)) * p.batch : double(ceil_div(p.M_total, bm));
+  const double nx = double(ceil_div(p.N, bn));
+  const double tiles = my * nx;
+  const double waves = std::ceil(tiles / 256.0);  // rounds of workgroups over 256 CUs
+  return waves * bm * bn * rel;
+}
+
 template <int MODE>
 int run_gemm(GemmParams& p, int dtype, hipStream_t stream) {
   const char* name = MODE == kOut ? "out_gemm" : "qkv_gemm";
+  if (dtype == SPATTEN_BF16 && MODE != kQkvDecode) {
+    // 128x128 tiles at two workgroups per CU hide load latency better than
+    // one 256x256 workgroup per CU (measured on MI355X).
+    return run_tile<MODE, 128, 128>(p, stream, name);
+  }
   const int tm = dtype == SPATTEN_BF16 ? BM : FT;
   const int tn = dtype == SPATTEN_BF16 ? BN : FT;
   int tiles_y;

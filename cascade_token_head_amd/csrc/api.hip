@@ -50,6 +50,7 @@ int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const vo
   aa.vt = ws + w.vt;
   aa.batch = d.batch;
   aa.h_kept = d.n_heads_kept;
+  aa.H = d.n_heads;
   aa.n = d.n_tokens;
   aa.n_pad = int(w.n_pad);
   aa.dh = d.head_dim;
@@ -58,11 +59,12 @@ int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const vo
   aa.colsum = reinterpret_cast<float*>(ws + w.colsum);
   aa.gpart = reinterpret_cast<float*>(ws + w.gpart);
   aa.nqb = int(w.nqb);
-  SPATTEN_TRY(launch_pad_zero(aa, st));
+  aa.nkb = int(w.nkb);
+  aa.head_idx = head_idx;
+  aa.a = a;
+  aa.g = g;
+  aa.lse_out = lse_out;
   SPATTEN_TRY(launch_attention(aa, st));
-  SPATTEN_TRY(launch_importance(aa.colsum, aa.gpart, aa.lse, head_idx, d.batch, d.n_heads_kept,
-                                d.n_heads, d.n_tokens, int(w.n_pad), int(w.nqb), a, g, lse_out,
-                                st));
   OutArgs oa{};
   oa.dtype = d.dtype;
   oa.o = ws + w.o;

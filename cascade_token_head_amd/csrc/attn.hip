@@ -39,6 +39,8 @@ attn_fwd_bf16(AttnArgs a) {
   constexpr int VS = KT + 8;    // LDS row stride of the V^T tile
   constexpr int NKC = KT * DH / 8 / 256;  // 16-byte K chunks per thread
   constexpr int NVC = DH * KT / 8 / 256;  // 16-byte V^T chunks per thread
+  constexpr int QW = 64;                  // queries per wave (two 32-query halves)
+  constexpr float kRescale = 8.0f;        // log2 headroom before O is rescaled
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KS];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][DH * VS];
   __shared__ float red[4];
@@ -47,29 +49,38 @@ attn_fwd_bf16(AttnArgs a) {
   const int G = lane >> 5, col = lane & 31;
   const int b = blockIdx.z, s = blockIdx.y;
   const int qb = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
-  const int q0 = qb * 128;
+  const int q0 = qb * kAttnQBlock;
+  const int wq0 = q0 + QW * wave;        // first query of this wave
   const int n = a.n, n_pad = a.n_pad;
   const int64_t bs = int64_t(b) * a.h_kept + s;
   const bf16_t* Q = static_cast<const bf16_t*>(a.q) + bs * n_pad * DH;
   const bf16_t* K = static_cast<const bf16_t*>(a.k) + bs * n_pad * DH;
   const bf16_t* VT = static_cast<const bf16_t*>(a.vt) + bs * DH * n_pad;
-  const int my_q = q0 + 32 * wave + col;
+  const bool wave_live = wq0 < n;
 
-  bf16x8 qf[DH / 16];
+  // Q operand (B of S^T = K Q^T): lane holds Q[query][16kk + 8G .. +8]
+  bf16x8 qf[2][DH / 16];
 #pragma unroll
-  for (int kk = 0; kk < DH / 16; ++kk)
-    qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(Q + int64_t(my_q) * DH + 16 * kk + 8 * G));
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk)
+      qf[u][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          Q + int64_t(wq0 + 32 * u + col) * DH + 16 * kk + 8 * G));
 
   const float sc = kLog2e / sqrtf(float(DH));
-  float m = -INFINITY, lsum = 0.0f;
-  floatx16 o[DH / 32];
+  float mref[2] = {-INFINITY, -INFINITY};  // max used as the exp2 reference (raw score units)
+  float lsum[2] = {0.0f, 0.0f};
+  floatx16 o[DH / 32][2];
 #pragma unroll
   for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][u][r] = 0.0f;
 
-  const int kend = CAUSAL ? min(n, q0 + 128) : n;
+  const int kend = CAUSAL ? min(n, q0 + kAttnQBlock) : n;
   const int ntiles = int(ceil_div(kend, KT));
+  const int wave_kend = CAUSAL ? min(n, wq0 + QW) : n;   // keys this wave can see
 
   u32x4 rk[NKC], rv[NVC];
   auto gload = [&](int it) {
@@ -84,6 +95,16 @@ attn_fwd_bf16(AttnArgs a) {
       const int c = tid + 256 * i;
       const int row = c >> 3, k8 = (c & 7) * 8;
       rv[i] = *reinterpret_cast<const u32x4*>(VT + int64_t(row) * n_pad + k0 + k8);
+      // keys past the end get exact zeros (their probabilities are 0, and
+      // the padding itself is never written)
+      if (k0 + KT > n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + k8 + 2 * e;
+          const uint32_t lo = key < n ? 0xffffu : 0u, hi = key + 1 < n ? 0xffff0000u : 0u;
+          rv[i][e] &= lo | hi;
+        }
+      }
     }
   };
   auto sstore = [&](int buf) {
@@ -111,89 +132,118 @@ attn_fwd_bf16(AttnArgs a) {
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1, k0 = it * KT;
     if (it + 1 < ntiles) gload(it + 1);
-    floatx16 st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[t][r] = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < DH / 16; ++kk) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &Ks[buf][(32 * t + kperm) * KS + 16 * kk + 8 * G]));
-        st[t] = mfma32x32x16(kf, qf[kk], st[t]);
-      }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 32 * t + 16 * G + i;
-        float v = st[t][i] * sc;
-        const bool masked = key >= n || (CAUSAL && key > my_q);
-        v = masked ? -INFINITY : v;
-        st[t][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = exp2f(m - m_new);
-    m = m_new;
-    lsum *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = exp2f(st[t][8 * u + 2 * j] - m);
-          const float p1 = exp2f(st[t][8 * u + 2 * j + 1] - m);
-          lsum += p0 + p1;
-          w[j] = pack_bf16x2(p0, p1);
-        }
-        pb[t][u] = as_bf16x8(w);
-      }
-#pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
+    if (wave_live && k0 < wave_kend) {
+      floatx16 st[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * u]));
-          o[dt] = mfma32x32x16(vf, pb[t][u], o[dt]);
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[t][u][r] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              &Ks[buf][(32 * t + kperm) * KS + 16 * kk + 8 * G]));
+#pragma unroll
+          for (int u = 0; u < 2; ++u) st[t][u] = mfma32x32x16(kf, qf[u][kk], st[t][u]);
         }
+      // masks only where the tile crosses the sequence end or the diagonal
+      const bool need_mask = (k0 + KT > n) || (CAUSAL && k0 + KT - 1 > wq0);
+      if (need_mask) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int my_q = wq0 + 32 * u + col;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + 32 * t + 16 * G + i;
+              const bool masked = key >= n || (CAUSAL && key > my_q);
+              st[t][u][i] = masked ? -INFINITY : st[t][u][i];
+            }
+        }
+      }
+      bf16x8 pb[2][2][2];  // [t][s][u]
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, st[t][u][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // move the reference only when a score would exceed it by 2^kRescale
+        const bool grow = tmax * sc > mref[u] * sc + kRescale || mref[u] == -INFINITY;
+        if (__ballot(grow)) {
+          const float m_new = grow ? fmaxf(mref[u], tmax) : mref[u];
+          const float alpha = mref[u] == -INFINITY ? 0.0f : fast_exp2((mref[u] - m_new) * sc);
+          mref[u] = m_new;
+          lsum[u] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][u][r] *= alpha;
+        }
+        const float msc = (mref[u] == -INFINITY ? 0.0f : mref[u]) * sc;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float p0 = fast_exp2(fmaf(st[t][u][8 * s2 + 2 * j], sc, -msc));
+              const float p1 = fast_exp2(fmaf(st[t][u][8 * s2 + 2 * j + 1], sc, -msc));
+              lsum[u] += p0 + p1;
+              w[j] = pack_bf16x2(p0, p1);
+            }
+            pb[t][s2][u] = as_bf16x8(w);
+          }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * s2]));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) o[dt][u] = mfma32x32x16(vf, pb[t][s2][u], o[dt][u]);
+          }
+    }
     if (it + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  lsum += __shfl_xor(lsum, 32, 64);
-  const float inv = 1.0f / lsum;
   float gsum = 0.0f;
-  if (my_q < n) {
-    bf16_t* orow = static_cast<bf16_t*>(a.o) + (int64_t(b) * n + my_q) * (a.h_kept * DH) + s * DH;
 #pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
+  for (int u = 0; u < 2; ++u) {
+    const int my_q = wq0 + 32 * u + col;
+    const float l = lsum[u] + __shfl_xor(lsum[u], 32, 64);
+    const float inv = 1.0f / l;
+    if (my_q < n) {
+      bf16_t* orow = static_cast<bf16_t*>(a.o) + (int64_t(b) * n + my_q) * (a.h_kept * DH) + s * DH;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * dt + 8 * q4 + 4 * G;
-        float v[4];
+      for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = o[dt][4 * q4 + e] * inv;
-          gsum += fabsf(v[e]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * dt + 8 * q4 + 4 * G;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = o[dt][u][4 * q4 + e] * inv;
+            gsum += fabsf(v[e]);
+          }
+          const uint64_t pk = uint64_t(pack_bf16x2(v[0], v[1])) |
+                              (uint64_t(pack_bf16x2(v[2], v[3])) << 32);
+          *reinterpret_cast<uint64_t*>(orow + d0) = pk;
         }
-        uint64_t pk = uint64_t(pack_bf16x2(v[0], v[1])) | (uint64_t(pack_bf16x2(v[2], v[3])) << 32);
-        *reinterpret_cast<uint64_t*>(orow + d0) = pk;
-      }
+      if (G == 0) a.lse[bs * n_pad + my_q] = mref[u] * sc + log2f(l);
+    }
   }
-  if (G == 0) a.lse[bs * n_pad + my_q] = m + log2f(lsum);
   gsum = wave_sum(gsum);
   if (lane == 0) red[wave] = gsum;
   __syncthreads();
@@ -281,17 +331,28 @@ attn_colsum_bf16(AttnArgs a) {
         for (int t = 0; t < 2; ++t) st[t] = mfma32x32x16(qa, kf[t][kk], st[t]);
       }
       // st[t][r]: query qt0 + 32u + 8(r/4) + 4G + r%4, key kw + 32t + col
+      const int qa = qt0 + 32 * u;
+      const bool need_mask = (qa + 31 >= n) || (CAUSAL && qa < kw + 64);
+      if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * u + 8 * (r >> 2) + 4 * G + (r & 3);
-        const int qi = qt0 + ql;
-        const float l2 = Ls[buf][ql];
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * u + 8 * (r >> 2) + 4 * G + (r & 3);
+          const int qi = qt0 + ql;
+          const float l2 = Ls[buf][ql];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int key = kw + 32 * t + col;
-          const float p = exp2f(st[t][r] * sc - l2);
-          const bool keep = qi < n && (!CAUSAL || key <= qi);
-          acc[t] += keep ? p : 0.0f;
+          for (int t = 0; t < 2; ++t) {
+            const int key = kw + 32 * t + col;
+            const float p = fast_exp2(fmaf(st[t][r], sc, -l2));
+            const bool keep = qi < n && (!CAUSAL || key <= qi);
+            acc[t] += keep ? p : 0.0f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float l2 = Ls[buf][32 * u + 8 * (r >> 2) + 4 * G + (r & 3)];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] += fast_exp2(fmaf(st[t][r], sc, -l2));
         }
       }
     }
@@ -375,56 +436,42 @@ attn_colsum_f32(AttnArgs a) {
   const int b = blockIdx.z, s = blockIdx.y;
   const int j = blockIdx.x * 256 + threadIdx.x;
   const int n = a.n, n_pad = a.n_pad, dh = a.dh;
-  if (j >= n) return;
   const int64_t bs = int64_t(b) * a.h_kept + s;
   const float* Q = static_cast<const float*>(a.q) + bs * n_pad * dh;
   const float* K = static_cast<const float*>(a.k) + bs * n_pad * dh;
   const float* L = a.lse + bs * n_pad;
   const float scale = kLog2e / sqrtf(float(dh));
-  float acc = 0.0f;
-  for (int i = CAUSAL ? j : 0; i < n; ++i) {
-    float d = 0.0f;
-    for (int c = 0; c < dh; ++c) d = fmaf(Q[int64_t(i) * dh + c], K[int64_t(j) * dh + c], d);
-    acc += exp2f(d * scale - L[i]);
-  }
-  a.colsum[bs * n_pad + j] = acc;
-}
-
-// ------------------------------------------------------------------ helpers
-
-// V^T columns n .. n_pad-1 must hold zeros: masked probabilities are exactly
-// 0 and multiply them in the P V product.
-template <typename T>
-__global__ void pad_zero_kernel(T* vt, int rows, int n, int n_pad) {
-  const int w = n_pad - n;
-  const int64_t total = int64_t(rows) * w;
-  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t r = e / w;
-    vt[r * n_pad + n + (e - r * w)] = T(0);
-  }
-}
-
-__global__ void __launch_bounds__(256)
-importance_kernel(const float* __restrict__ colsum, const float* __restrict__ gpart,
-                  const float* __restrict__ lse, const int32_t* __restrict__ head_idx,
-                  int h_kept, int H, int n, int n_pad, int nqb, float* __restrict__ a,
-                  float* __restrict__ g, float* __restrict__ lse_out) {
-  const int b = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
   if (j < n) {
     float acc = 0.0f;
-    for (int s = 0; s < h_kept; ++s) acc += colsum[(int64_t(b) * h_kept + s) * n_pad + j];
-    a[int64_t(b) * n + j] += acc;
-    if (lse_out)
-      for (int s = 0; s < h_kept; ++s)
-        lse_out[(int64_t(b) * h_kept + s) * n + j] = lse[(int64_t(b) * h_kept + s) * n_pad + j] * kLn2;
+    for (int i = CAUSAL ? j : 0; i < n; ++i) {
+      float d = 0.0f;
+      for (int c = 0; c < dh; ++c) d = fmaf(Q[int64_t(i) * dh + c], K[int64_t(j) * dh + c], d);
+      acc += fast_exp2(d * scale - L[i]);
+    }
+    a.colsum[bs * n_pad + j] = acc;
   }
-  if (blockIdx.x == 0 && threadIdx.x < h_kept) {
+}
+
+// a[b, j] += sum_s colsum[b, s, j] (heads in order: deterministic);
+// g[b, head_idx[b, s]] += sum_q gpart[b, s, q]; optional natural-log LSE copy.
+__global__ void __launch_bounds__(256)
+importance_kernel(AttnArgs a) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < a.n) {
+    float acc = 0.0f;
+    for (int s = 0; s < a.h_kept; ++s) acc += a.colsum[(int64_t(b) * a.h_kept + s) * a.n_pad + j];
+    a.a[int64_t(b) * a.n + j] += acc;
+    if (a.lse_out)
+      for (int s = 0; s < a.h_kept; ++s)
+        a.lse_out[(int64_t(b) * a.h_kept + s) * a.n + j] =
+            a.lse[(int64_t(b) * a.h_kept + s) * a.n_pad + j] * kLn2;
+  }
+  if (blockIdx.x == 0 && int(threadIdx.x) < a.h_kept) {
     const int s = threadIdx.x;
     float acc = 0.0f;
-    for (int q = 0; q < nqb; ++q) acc += gpart[(int64_t(b) * h_kept + s) * nqb + q];
-    g[int64_t(b) * H + head_idx[b * h_kept + s]] += acc;
+    for (int q = 0; q < a.nqb; ++q) acc += a.gpart[(int64_t(b) * a.h_kept + s) * a.nqb + q];
+    a.g[int64_t(b) * a.H + a.head_idx[b * a.h_kept + s]] += acc;
   }
 }
 
@@ -435,6 +482,9 @@ int run_bf16(const AttnArgs& a, hipStream_t stream) {
   SPATTEN_LAUNCH_CHECK();
   const dim3 g2(unsigned(ceil_div(a.n, kAttnKBlock)), a.h_kept, a.batch);
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_bf16<DH, CAUSAL><<<g2, 256, 0, stream>>>(a));
+  SPATTEN_LAUNCH_CHECK();
+  const dim3 g3(unsigned(ceil_div(a.n, 256)), a.batch);
+  SPATTEN_TIMED("importance", stream, importance_kernel<<<g3, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }
@@ -448,45 +498,19 @@ int run_f32(const AttnArgs& a, hipStream_t stream) {
   const dim3 g2(unsigned(ceil_div(a.n, 256)), a.h_kept, a.batch);
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_f32<CAUSAL><<<g2, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
+  const dim3 g3(unsigned(ceil_div(a.n, 256)), a.batch);
+  SPATTEN_TIMED("importance", stream, importance_kernel<<<g3, 256, 0, stream>>>(a));
+  SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }
 
 }  // namespace
-
-int launch_pad_zero(const AttnArgs& a, hipStream_t stream) {
-  if (a.n_pad == a.n) return SPATTEN_OK;
-  const int rows = a.batch * a.h_kept * a.dh;
-  const int64_t total = int64_t(rows) * (a.n_pad - a.n);
-  const int64_t nb = ceil_div(total, 256);
-  const unsigned blocks = unsigned(nb < 4096 ? nb : 4096);
-  if (a.dtype == SPATTEN_BF16)
-    SPATTEN_TIMED("pad_zero", stream,
-                  pad_zero_kernel<bf16_t><<<blocks, 256, 0, stream>>>(
-                      static_cast<bf16_t*>(const_cast<void*>(a.vt)), rows, a.n, a.n_pad));
-  else
-    SPATTEN_TIMED("pad_zero", stream,
-                  pad_zero_kernel<float><<<blocks, 256, 0, stream>>>(
-                      static_cast<float*>(const_cast<void*>(a.vt)), rows, a.n, a.n_pad));
-  SPATTEN_LAUNCH_CHECK();
-  return SPATTEN_OK;
-}
 
 int launch_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.dtype == SPATTEN_F32) return a.causal ? run_f32<true>(a, stream) : run_f32<false>(a, stream);
   if (a.dh == 64) return a.causal ? run_bf16<64, true>(a, stream) : run_bf16<64, false>(a, stream);
   if (a.dh == 128) return a.causal ? run_bf16<128, true>(a, stream) : run_bf16<128, false>(a, stream);
   return SPATTEN_EUNSUPPORTED;
-}
-
-int launch_importance(const float* colsum, const float* gpart, const float* lse,
-                      const int32_t* head_idx, int batch, int h_kept, int H, int n, int n_pad,
-                      int nqb, float* a, float* g, float* lse_out, hipStream_t stream) {
-  const dim3 grid(unsigned(ceil_div(n, 256)), batch);
-  SPATTEN_TIMED("importance", stream,
-                importance_kernel<<<grid, 256, 0, stream>>>(colsum, gpart, lse, head_idx, h_kept,
-                                                            H, n, n_pad, nqb, a, g, lse_out));
-  SPATTEN_LAUNCH_CHECK();
-  return SPATTEN_OK;
 }
 
 }  // namespace spatten

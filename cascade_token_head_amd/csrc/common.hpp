@@ -23,15 +23,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(uint32_t(v) << 16);
 }
 
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return bf16_t((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// gfx950 converts pairs with v_cvt_pk_bf16_f32 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const floatx2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return bf16_t(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // Loads/stores of T-typed element e of an untyped tensor.
@@ -56,6 +58,10 @@ template <>
 __device__ __forceinline__ void store_elem<bf16_t>(void* p, int64_t i, float v) {
   static_cast<bf16_t*>(p)[i] = f32_to_bf16(v);
 }
+
+// 2^x with the hardware v_exp_f32 (about 1 ulp; results below 2^-126 flush
+// to zero, exp2(-inf) = 0), without the library's subnormal range handling.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_sum(float v) {

@@ -125,7 +125,7 @@ decode_partial(DecodeArgs a) {
     if (KIND == kFull && !hflag[hh]) continue;
     const float v = S[hh][lane];
     const float m = wave_max(v);
-    const float e = exp2f(v - m);
+    const float e = fast_exp2(v - m);
     const float l = wave_sum(e);
     S[hh][lane] = e;
     if (lane == 0) {
@@ -190,7 +190,7 @@ decode_combine(DecodeArgs a, int phase) {
   M = wave_max(M);
   float L = 0.0f;
   for (int ci = lane; ci < a.nchunk; ci += 64)
-    L += a.lpart[bh * a.nchunk + ci] * exp2f(a.mpart[bh * a.nchunk + ci] - M);
+    L += a.lpart[bh * a.nchunk + ci] * fast_exp2(a.mpart[bh * a.nchunk + ci] - M);
   L = wave_sum(L);
   const float lse2 = M + log2f(L);
   const float cmax = 1.0f / L;  // largest probability: exp2(M - lse2)
@@ -218,7 +218,7 @@ decode_combine(DecodeArgs a, int phase) {
   for (int d = lane; d < a.dh; d += 64) {
     float acc = 0.0f;
     for (int ci = 0; ci < a.nchunk; ++ci)
-      acc += a.opart[(bh * a.nchunk + ci) * a.dh + d] * exp2f(a.mpart[bh * a.nchunk + ci] - M);
+      acc += a.opart[(bh * a.nchunk + ci) * a.dh + d] * fast_exp2(a.mpart[bh * a.nchunk + ci] - M);
     static_cast<bf16_t*>(a.o)[int64_t(b) * a.H * a.dh + h * a.dh + d] = f32_to_bf16(acc * inv);
   }
 }
@@ -233,7 +233,7 @@ decode_importance(DecodeArgs a) {
   if (j >= a.lc) return;
   float acc = 0.0f;
   for (int h = 0; h < a.H; ++h)
-    acc += exp2f(a.scores[(int64_t(b) * a.H + h) * a.lc_pad + j] - lse[h]);
+    acc += fast_exp2(a.scores[(int64_t(b) * a.H + h) * a.lc_pad + j] - lse[h]);
   a.a[int64_t(b) * a.cap + j] += acc;
 }
 

@@ -217,7 +217,7 @@ gemm_bf16_kernel(GemmParams p) {
 // (BM/2) x (BN/2) with 32x32x16 MFMAs, so every LDS fragment feeds BN/64
 // or BM/64 MFMAs. LDS rows are 128 bytes with the 16-byte chunks XOR-
 // swizzled by the row index: the eight rows a group of lanes reads at one
-// k offset land in eight different bank groups without padding, and two
+// k offset land in different bank groups without padding, and two
 // stages of a 256 x 256 tile fit in 128 KB. Epilogue index math is hoisted:
 // column terms once per MFMA column tile, row terms advanced incrementally.
 
@@ -254,12 +254,18 @@ gemm_tile_kernel(GemmParams p) {
     else
       w_src[i] = qkv_weight_row<bf16_t>(p, b_tile, ncol) + kc * 8;
   }
-  // swizzled LDS slot of this thread's chunk in row r: r*64 + ((kc ^ (r&7)) * 8)
-  const int st_off = (((tid >> 3) & 7) ^ kc) * 8 + (tid >> 3) * BKT;
+  // LDS rows are 128 bytes; gfx950 serves 16 lanes of a b128 access from 64
+  // banks, i.e. two rows per cycle, so chunk slots are XOR-swizzled by
+  // (row >> 1) & 7: the 16 rows a half-wave reads at one k offset then hit
+  // 16 distinct 16-byte bank groups. Slot of this thread's chunk in row r:
+  // r*64 + ((kc ^ ((r >> 1) & 7)) * 8).
+  const int st_off = (((tid >> 4) & 7) ^ kc) * 8 + (tid >> 3) * BKT;
 
   const int KT = p.K / BKT;
-  u32x4 ra[NA], rb[NB];
-  auto gload = [&](int kt) {
+  // two register staging sets: the tile stored into LDS at the start of
+  // iteration kt was requested two iterations earlier
+  u32x4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
+  auto gload = [&](u32x4* ra, u32x4* rb, int kt) {
     const int k0 = kt * BKT;
     int wk = k0;
     if (MODE == kOut) {
@@ -271,8 +277,8 @@ gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(w_src[i] + wk);
   };
-  auto sstore = [&](int buf) {
-    // rows tid/8 + 32 i keep the same (row & 7), so one swizzled offset serves all i
+  auto sstore = [&](const u32x4* ra, const u32x4* rb, int buf) {
+    // rows tid/8 + 32 i keep the same (row >> 1) & 7, so one swizzled offset serves all i
 #pragma unroll
     for (int i = 0; i < NA; ++i)
       *reinterpret_cast<u32x4*>(&As[buf][st_off + 32 * i * BKT]) = ra[i];
@@ -291,15 +297,10 @@ gemm_tile_kernel(GemmParams p) {
 
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
   const int fr = lane & 31, G = lane >> 5;
-  // fragment rows wm + 32 i + fr all share (row & 7) == (fr & 7)
-  const int fsw = fr & 7;
+  // fragment rows wm + 32 i + fr all share (row >> 1) & 7 == (fr >> 1) & 7
+  const int fsw = (fr >> 1) & 7;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ch = ((2 * kk + G) ^ fsw) * 8;
@@ -315,7 +316,24 @@ gemm_tile_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  };
+
+  gload(ra0, rb0, 0);
+  sstore(ra0, rb0, 0);
+  if (KT > 1) gload(ra0, rb0, 1);
+  if (KT > 2) gload(ra1, rb1, 2);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    // even step: compute tile kt from buffer 0, stage tile kt+1 into buffer 1
+    if (kt + 1 < KT) sstore(ra0, rb0, 1);
+    if (kt + 3 < KT) gload(ra0, rb0, kt + 3);
+    compute(0);
+    __syncthreads();
+    if (kt + 1 >= KT) break;
+    // odd step: compute tile kt+1 from buffer 1, stage tile kt+2 into buffer 0
+    if (kt + 2 < KT) sstore(ra1, rb1, 0);
+    if (kt + 4 < KT) gload(ra1, rb1, kt + 4);
+    compute(1);
     __syncthreads();
   }
 

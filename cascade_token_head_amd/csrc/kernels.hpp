@@ -48,27 +48,26 @@ struct OutArgs {
 };
 int launch_out(const OutArgs& a, hipStream_t stream);
 
-// Prefill attention with fused importance.
+// Prefill attention with fused importance: forward (O, row LSE, |O|
+// partials), key-major column sums, then a deterministic reduction into a
+// and g (and an optional natural-log LSE copy).
 struct AttnArgs {
   int dtype, causal;
   const void* q;
   const void* k;
   const void* vt;
-  int batch, h_kept, n, n_pad, dh;
-  void* o;        // [B, n, h_kept*dh]
-  float* lse;     // [B, h, n_pad]
-  float* colsum;  // [B, h, n_pad]
-  float* gpart;   // [B, h, nqb]
-  int nqb;
+  int batch, h_kept, H, n, n_pad, dh;
+  void* o;          // [B, n, h_kept*dh]
+  float* lse;       // [B, h, n_pad] (log2 units)
+  float* colsum;    // [B, h, n_pad]
+  float* gpart;     // [B, h, nqb]
+  int nqb, nkb;
+  const int32_t* head_idx;
+  float* a;         // [B, n]
+  float* g;         // [B, H]
+  float* lse_out;   // optional [B, h, n] (natural log)
 };
 int launch_attention(const AttnArgs& a, hipStream_t stream);
-int launch_pad_zero(const AttnArgs& a, hipStream_t stream);
-
-// a[b, j] += sum_s colsum[b, s, j]; g[b, head_idx[b, s]] += sum_q gpart[b, s, q];
-// lse_out (optional) <- lse (row stride n).
-int launch_importance(const float* colsum, const float* gpart, const float* lse,
-                      const int32_t* head_idx, int batch, int h_kept, int H, int n, int n_pad,
-                      int nqb, float* a, float* g, float* lse_out, hipStream_t stream);
 
 // Decode attention over cache rows 0..lc-1 for every (b, h).
 struct DecodeArgs {

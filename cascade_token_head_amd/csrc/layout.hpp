@@ -18,10 +18,10 @@ namespace spatten {
 
 // Prefill token rows of Q, K, V^T are padded per (sequence, head) to this
 // multiple so attention tiles never read past a head's slab.
-constexpr int kTokPad = 128;
+constexpr int kTokPad = 256;
 // Prefill attention: queries per workgroup in the forward (O, LSE) kernel
 // and keys per workgroup in the column-sum kernel (bf16 MFMA path).
-constexpr int kAttnQBlock = 128;
+constexpr int kAttnQBlock = 256;
 constexpr int kAttnKBlock = 256;
 // fp32 attention: query rows per workgroup.
 constexpr int kAttnF32Rows = 8;
@@ -35,6 +35,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // Byte offsets of every scratch array inside the caller's workspace.
 struct PrefillWs {
   int64_t n_pad, nqb;
+  int64_t nkb;
   size_t q, k, vt, o, lse, colsum, gpart, total;
 };
 
@@ -61,6 +62,7 @@ inline PrefillWs prefill_ws(const spatten_layer_desc& d) {
   w.lse = take(B * h * w.n_pad * 4);
   w.colsum = take(B * h * w.n_pad * 4);
   w.gpart = take(B * h * w.nqb * 4);
+  w.nkb = ceil_div(n, kAttnKBlock);
   w.total = off;
   return w;
 }

@@ -67,7 +67,7 @@ class PrefillWs:
     def __init__(self, B, n, h, dh, es, bf16):
         def a256(v):
             return (v + 255) // 256 * 256
-        n_pad = (n + 127) // 128 * 128
+        n_pad = (n + 255) // 256 * 256
         off = 0
         self.n_pad = n_pad
         sizes = [("q", B * h * n_pad * dh * es), ("k", B * h * n_pad * dh * es),

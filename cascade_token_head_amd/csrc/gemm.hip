@@ -427,6 +427,73 @@ gemm_tile_kernel(GemmParams p) {
   }
 }
 
+// ------------------------------------------------------------------ decode projections
+//
+// M = batch rows (at most 64): the weights are the traffic. A workgroup owns
+// 16 output columns for every row, so N/16 workgroups each stream their 16
+// weight rows once; operands go straight from global memory into 16x16x32
+// MFMA fragments (A: a row's 8 consecutive k; B: a weight row's 8
+// consecutive k). Waves take 16-row tiles; with fewer than four row tiles
+// they split K instead and add their partial sums through LDS.
+
+template <int MODE>
+__global__ void __launch_bounds__(256)
+gemm_skinny_kernel(GemmParams p) {
+  __shared__ floatx4 part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int RT = (p.M_total + 15) >> 4;            // 16-row tiles, 1..4
+  const int splits = RT == 1 ? 4 : (RT == 2 ? 2 : 1);
+  const bool active = wave < RT * splits;
+  const int rt = wave % RT, ks = wave / RT;
+  const int klen = p.K / splits, kbeg = ks * klen;
+  const int l16 = lane & 15, kq = (lane >> 4) * 8;
+
+  int row = rt * 16 + l16;
+  if (row >= p.M_total) row = p.M_total - 1;
+  const bf16_t* a_row = static_cast<const bf16_t*>(p.A) + int64_t(row) * p.lda + kq;
+  const int ncol = n0 + l16;
+  const bf16_t* w_row = MODE == kOut
+                            ? static_cast<const bf16_t*>(p.W0) + int64_t(ncol) * p.ldw + kq
+                            : qkv_weight_row<bf16_t>(p, 0, ncol) + kq;
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (active) {
+    for (int k0 = kbeg; k0 < kbeg + klen; k0 += 128) {
+      u32x4 av[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        av[u] = *reinterpret_cast<const u32x4*>(a_row + k0 + 32 * u);
+        bv[u] = *reinterpret_cast<const u32x4*>(w_row + k0 + 32 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc = mfma16x16x32(as_bf16x8(av[u]), as_bf16x8(bv[u]), acc);
+    }
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave >= RT) return;
+  for (int sp = 1; sp < splits; ++sp) acc += part[sp * RT + wave][lane];
+  // C fragment: lane holds rows 4*(lane/16) + i of the tile, column l16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = rt * 16 + 4 * (lane >> 4) + i;
+    if (b >= p.M_total) continue;
+    const float v = acc[i];
+    if (MODE == kOut) {
+      bf16_t* x = static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D + ncol;
+      *x = f32_to_bf16(bf16_to_f32(*x) + v);
+    } else {
+      const int hd = p.h_kept * p.dh;
+      const int which = ncol / hd;
+      const int rem = ncol - which * hd;
+      bf16_t* d = which == 0 ? static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D
+                             : static_cast<bf16_t*>(which == 1 ? p.out1 : p.out2) +
+                                   int64_t(b) * p.kv_bs;
+      d[rem] = f32_to_bf16(v);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 VALU
 
 constexpr int FT = 64, FK = 16;
@@ -517,6 +584,15 @@ inline double tile_cost(const GemmParams& p, int bm, int bn, double rel) {
 template <int MODE>
 int run_gemm(GemmParams& p, int dtype, hipStream_t stream) {
   const char* name = MODE == kOut ? "out_gemm" : "qkv_gemm";
+  const int rt = int(ceil_div(p.M_total, 16));
+  const int splits = rt == 1 ? 4 : (rt == 2 ? 2 : 1);
+  if (MODE != kQkvPrefill && dtype == SPATTEN_BF16 && !p.seq_tiled && p.M_total <= 64 &&
+      p.N % 16 == 0 && p.K % (128 * splits) == 0) {
+    SPATTEN_TIMED(name, stream,
+                  gemm_skinny_kernel<MODE><<<dim3(unsigned(p.N / 16)), 256, 0, stream>>>(p));
+    SPATTEN_LAUNCH_CHECK();
+    return SPATTEN_OK;
+  }
   if (dtype == SPATTEN_BF16 && MODE != kQkvDecode) {
     // 128x128 tiles at two workgroups per CU hide load latency better than
     // one 256x256 workgroup per CU (measured on MI355X).

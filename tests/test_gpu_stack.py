@@ -285,7 +285,9 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
                                    check_bf16_output(x_out[b], xr, what="x l%d b%d" % (l, b))[0])
             da = a_out[b, :lc] - snap["a_in"][b, :lc]
             ps = P.sum(axis=0)
-            assert np.max(np.abs(da - ps)) <= 2e-6 * H + 1e-5 * np.max(ps), (l, b)
+            # deep layers carry large scores (hundreds in log2 units); fp32
+            # exp(s - lse) then has ~1e-5..1e-4 relative error per entry
+            assert np.max(np.abs(da - ps)) <= 2e-6 * H + 1e-4 * np.max(ps), (l, b)
             if st.s == 0:
                 a_ora[b] += ps
 

@@ -112,12 +112,6 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
     qa.kv_bs = cap * D;
   }
   SPATTEN_TRY(launch_qkv(qa, st));
-  if (d.kv_quantized) {
-    SPATTEN_TRY(launch_quantize(ws + w.knew, SPATTEN_BF16, d.batch, 1, D, D, k_msb + row * (D / 2),
-                                k_lsb + row * (D / 2), k_scale + row, cap, st));
-    SPATTEN_TRY(launch_quantize(ws + w.vnew, SPATTEN_BF16, d.batch, 1, D, D, v_msb + row * (D / 2),
-                                v_lsb + row * (D / 2), v_scale + row, cap, st));
-  }
   DecodeArgs da{};
   da.q = ws + w.q;
   da.k_cache = k_cache;
@@ -128,6 +122,10 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
   da.v_msb = v_msb;
   da.v_lsb = v_lsb;
   da.v_scale = v_scale;
+  if (d.kv_quantized) {
+    da.knew = ws + w.knew;
+    da.vnew = ws + w.vnew;
+  }
   da.batch = d.batch;
   da.H = H;
   da.dh = dh;

@@ -93,6 +93,96 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Per-token symmetric int8 code of x under row scale s (s = max|x| / 127),
+// fp32 with IEEE division and round-half-to-even; a zero row codes to 0.
+__device__ __forceinline__ int quant_code(float x, float s) {
+  if (s == 0.0f) return 0;
+  float q = __builtin_rintf(x / s);
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return int(q);
+}
+
+// Eight contiguous values from a 16-byte aligned address, as fp32.
+__device__ __forceinline__ void load8_f32(const bf16_t* x, float* v) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(x);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_f32(const float* x, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(x)[0];
+  const float4 b = reinterpret_cast<const float4*>(x)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// One full wave quantizes a row of `dim` values (dim even) into its MSB and
+// LSB nibble planes (byte p: element 2p in the low nibble, 2p+1 in the high
+// one) and its scale. Rows of up to 2048 values in 8-value groups are held
+// in registers, so every load is issued before the first use.
+template <typename T>
+__device__ __forceinline__ void quantize_row_wave(const T* x, int dim, uint8_t* mrow,
+                                                  uint8_t* lrow, float* scale) {
+  const int lane = threadIdx.x & 63;
+  const int nch = dim >> 3;
+  const bool grouped = (dim & 7) == 0 && nch <= 4 * 64 &&
+                       (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(mrow) & 3) == 0 &&
+                       (reinterpret_cast<uintptr_t>(lrow) & 3) == 0;
+  if (grouped) {
+    float v[4][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) {
+        load8_f32(x + 8 * ch, v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) {
+        uint32_t mw = 0, lw = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int qc = quant_code(v[i][e], s);
+          mw |= uint32_t((qc >> 4) & 15) << (4 * e);
+          lw |= uint32_t(qc & 15) << (4 * e);
+        }
+        reinterpret_cast<uint32_t*>(mrow)[ch] = mw;
+        reinterpret_cast<uint32_t*>(lrow)[ch] = lw;
+      }
+    }
+    if (lane == 0) *scale = s;
+    return;
+  }
+  const int half = dim >> 1;
+  float amax = 0.0f;
+  for (int p = lane; p < half; p += 64) {
+    amax = fmaxf(amax, fabsf(load_elem<T>(x, 2 * p)));
+    amax = fmaxf(amax, fabsf(load_elem<T>(x, 2 * p + 1)));
+  }
+  amax = wave_max(amax);
+  const float s = amax / 127.0f;
+  for (int p = lane; p < half; p += 64) {
+    const int q0 = quant_code(load_elem<T>(x, 2 * p), s);
+    const int q1 = quant_code(load_elem<T>(x, 2 * p + 1), s);
+    mrow[p] = uint8_t(((q0 >> 4) & 15) | (((q1 >> 4) & 15) << 4));
+    lrow[p] = uint8_t((q0 & 15) | ((q1 & 15) << 4));
+  }
+  if (lane == 0) *scale = s;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }

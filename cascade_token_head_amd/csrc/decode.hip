@@ -6,13 +6,24 @@
 // recomputed when its largest probability is below a threshold).
 //
 // The cache is token-major [B, cap, D], so one cache row holds every head
-// of one token. A workgroup owns (sequence, 64-entry chunk) and streams the
-// chunk's rows once, coalesced: each thread owns one 8-dim column group
-// (one head's slice), reduces its partial dot with the 7 neighbouring lanes
-// of the same head, and accumulates p * v for its column group. Chunks are
-// combined per (b, h) in a second kernel (split-K over the cache length, so
-// a few hundred rows still fill 256 CUs). Scores stay in a small fp32 stash
-// so the importance kernel can form exact normalised probabilities.
+// of one token. decode_partial: a workgroup owns (sequence, 32-entry chunk)
+// and streams the chunk's K rows, then its V rows, once and coalesced. Each
+// thread owns one 8-dim column group (one head's slice) of every R-th row of
+// the chunk and issues all of its row loads before using any of them, so a
+// thread keeps up to 16 loads in flight; partial dots are reduced with the 7
+// neighbouring lanes of the same head. Chunks are combined per (sequence,
+// head): split-K over the cache length, so a few hundred rows still fill 256
+// CUs. Scores stay in a small fp32 stash so the importance pass can form the
+// exact normalised probabilities.
+//
+// Quantized caches: the MSB pass first codes this step's k and v rows into
+// the planes (in the workgroup that owns the new row), then scores and
+// accumulates with 16 * msb; decode_flag marks each (sequence, head) row
+// whose largest MSB-pass probability is below the threshold and appends it
+// to the recompute queue; decode_recompute runs one workgroup per (queued
+// row, chunk) over both planes of that head only. decode_finish combines
+// what is left, writes O and adds the probabilities that produced O to the
+// token importance.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -21,56 +32,43 @@ namespace spatten {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int CH = kDecChunk;
+constexpr int CH = kDecChunk;  // cache entries per chunk
+constexpr int KB = 16;         // rows per load batch
 constexpr int kMaxHeads = 32;
+constexpr int kRecomputeSlots = 128;
 
-enum { kBf16 = 0, kMsb = 1, kFull = 2 };
-
-// Eight cache values of column group c of row j before the row scale:
-// bf16 values, 16*msb (MSB plane only, LSBs taken as zero) or the full
-// code 16*msb + lsb.
-template <int KIND>
-__device__ __forceinline__ void load8(const DecodeArgs& a, bool is_v, int64_t row, int c, int D,
-                                      float* out) {
-  if (KIND == kBf16) {
-    const bf16_t* base = static_cast<const bf16_t*>(is_v ? a.v_cache : a.k_cache);
-    const u32x4 w = *reinterpret_cast<const u32x4*>(base + row * D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[2 * e] = __uint_as_float(w[e] << 16);
-      out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-    }
-  } else {
-    const uint8_t* mp = is_v ? a.v_msb : a.k_msb;
-    const uint32_t m = *reinterpret_cast<const uint32_t*>(mp + row * (D / 2) + 4 * c);
-    uint32_t l = 0;
-    if (KIND == kFull) {
-      const uint8_t* lp = is_v ? a.v_lsb : a.k_lsb;
-      l = *reinterpret_cast<const uint32_t*>(lp + row * (D / 2) + 4 * c);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int mn = int((m >> (4 * e)) & 15u);
-      const int ms = mn >= 8 ? mn - 16 : mn;
-      const int code = 16 * ms + (KIND == kFull ? int((l >> (4 * e)) & 15u) : 0);
-      out[e] = float(code);
-    }
-  }
-}
+enum { kBf16 = 0, kMsb = 1 };
 
 template <int KIND>
-__device__ __forceinline__ float row_scale(const DecodeArgs& a, bool is_v, int64_t row) {
-  if (KIND == kBf16) return 1.0f;
-  return (is_v ? a.v_scale : a.k_scale)[row];
+struct RawRow {
+  using T = u32x4;  // 8 bf16 values
+};
+template <>
+struct RawRow<kMsb> {
+  using T = uint32_t;  // 8 MSB nibbles
+};
+
+template <int KIND>
+__device__ __forceinline__ typename RawRow<KIND>::T load_row(const void* bf, const uint8_t* msb,
+                                                             int64_t row, int c, int D) {
+  if constexpr (KIND == kBf16)
+    return *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(bf) + row * D + 8 * c);
+  else
+    return *reinterpret_cast<const uint32_t*>(msb + row * (D / 2) + 4 * c);
 }
 
-// grid (nchunk, B); block = (D/8) * R threads
+// signed MSB nibble e of an 8-nibble word
+__device__ __forceinline__ float msb_val(uint32_t w, int e) {
+  const int mn = int((w >> (4 * e)) & 15u);
+  return float(mn >= 8 ? mn - 16 : mn);
+}
+
+// grid (nchunk, B); block = (D/8) * R threads, R rows of the chunk at a time
 template <int KIND>
 __global__ void __launch_bounds__(256)
 decode_partial(DecodeArgs a) {
+  using Raw = typename RawRow<KIND>::T;
   __shared__ float S[kMaxHeads][CH];
-  __shared__ int hflag[kMaxHeads];
   __shared__ float obuf[256 * 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, b = blockIdx.y;
@@ -80,81 +78,143 @@ decode_partial(DecodeArgs a) {
   const int h = (8 * c) / dh;
   const int j0 = chunk * CH;
   const int nwaves = blockDim.x >> 6;
+  const int kpt = CH / R;  // rows per thread
+  const int64_t rowb = int64_t(b) * a.cap;
 
-  if (KIND == kMsb && chunk == 0 && b == 0 && tid == 0) a.queue[0] = 0;
-  if (KIND == kFull) {
-    if (tid < H) hflag[tid] = a.flags[b * H + tid];
-    __syncthreads();
-    int any = 0;
-    for (int i = 0; i < H; ++i) any |= hflag[i];
-    if (!any) return;
+  if constexpr (KIND == kMsb) {
+    if (chunk == 0 && b == 0 && tid == 0) a.queue[0] = 0;
+    if (a.knew && chunk == (a.lc - 1) / CH) {
+      // this workgroup owns the new row: code it before reading it (waves 0
+      // and 1 are always full, since the block has at least 128 threads)
+      const int64_t nr = rowb + a.lc - 1;
+      if (wave == 0)
+        quantize_row_wave<bf16_t>(static_cast<const bf16_t*>(a.knew) + int64_t(b) * D, D,
+                                  a.k_msb + nr * (D / 2), a.k_lsb + nr * (D / 2), a.k_scale + nr);
+      else if (wave == 1)
+        quantize_row_wave<bf16_t>(static_cast<const bf16_t*>(a.vnew) + int64_t(b) * D, D,
+                                  a.v_msb + nr * (D / 2), a.v_lsb + nr * (D / 2), a.v_scale + nr);
+      __threadfence_block();
+      __syncthreads();
+    }
   }
-  const bool active = r < R && (KIND != kFull || hflag[h]);
 
   float q[8];
-  if (active) {
-    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + int64_t(b) * D + 8 * c;
+  {
+    const u32x4 w =
+        *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + int64_t(b) * D + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = bf16_to_f32(qp[e]);
+    for (int e = 0; e < 4; ++e) {
+      q[2 * e] = __uint_as_float(w[e] << 16);
+      q[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
   }
   const float sc = kLog2e / sqrtf(float(dh));
-  for (int jl = r; jl < CH; jl += R) {
-    const int j = j0 + jl;
-    float part = 0.0f;
-    float ks = 0.0f;
-    if (active && j < a.lc) {
-      float kv[8];
-      const int64_t row = int64_t(b) * a.cap + j;
-      load8<KIND>(a, false, row, c, D, kv);
+
+  // Rows past the cache end are read at row lc-1 (a valid address) and
+  // masked: their score is -inf, so their weight in P V is exactly 0.
+  auto row_of = [&](int tt) {
+    const int j = j0 + r + R * tt;
+    return rowb + (j < a.lc ? j : a.lc - 1);
+  };
+
+  // ---- scores
+  for (int t0 = 0; t0 < kpt; t0 += KB) {
+    Raw raw[KB];
+    float ks[KB];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf(q[e], kv[e], part);
-      ks = row_scale<KIND>(a, false, row);
+    for (int u = 0; u < KB; ++u) {
+      const int64_t row = row_of(t0 + u < kpt ? t0 + u : t0);
+      raw[u] = load_row<KIND>(a.k_cache, a.k_msb, row, c, D);
+      if constexpr (KIND == kMsb) ks[u] = a.k_scale[row];
     }
-    part += __shfl_xor(part, 1, 64);
-    part += __shfl_xor(part, 2, 64);
-    part += __shfl_xor(part, 4, 64);
-    if (r < R && (c & 7) == 0 && (KIND != kFull || hflag[h])) {
-      const float sv = j < a.lc ? part * ks * sc : -INFINITY;
-      S[h][jl] = sv;
-      if (j < a.lc) a.scores[(int64_t(b) * H + h) * a.lc_pad + j] = sv;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      float d = 0.0f;
+      if constexpr (KIND == kBf16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d = fmaf(q[2 * e], __uint_as_float(raw[u][e] << 16), d);
+          d = fmaf(q[2 * e + 1], __uint_as_float(raw[u][e] & 0xffff0000u), d);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(q[e], msb_val(raw[u], e), d);
+        d *= 16.0f;
+      }
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 4, 64);
+      if constexpr (KIND == kMsb) d *= ks[u];
+      const int jl = r + R * (t0 + u), j = j0 + jl;
+      if (t0 + u < kpt && (c & 7) == 0) {
+        const float sv = j < a.lc ? d * sc : -INFINITY;
+        S[h][jl] = sv;
+        if (j < a.lc) a.scores[(int64_t(b) * H + h) * a.lc_pad + j] = sv;
+      }
     }
   }
+
+  // V rows of the first batch are in flight across the softmax barrier
+  Raw vraw[KB];
+  float vs[KB];
+  auto load_v = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int64_t row = row_of(t0 + u < kpt ? t0 + u : t0);
+      vraw[u] = load_row<KIND>(a.v_cache, a.v_msb, row, c, D);
+      if constexpr (KIND == kMsb) vs[u] = a.v_scale[row];
+    }
+  };
+  load_v(0);
   __syncthreads();
-  // per-head chunk statistics; S becomes exp2(S - m)
-  for (int hh = wave; hh < H; hh += nwaves) {
-    if (KIND == kFull && !hflag[hh]) continue;
-    const float v = S[hh][lane];
-    const float m = wave_max(v);
+  // ---- per-head chunk statistics, two heads per wave (32 lanes each);
+  // S becomes exp2(S - m)
+  for (int hh = 2 * wave + (lane >> 5); hh < H; hh += 2 * nwaves) {
+    const int l32 = lane & 31;
+    const float v = S[hh][l32];
+    float m = v;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     const float e = fast_exp2(v - m);
-    const float l = wave_sum(e);
-    S[hh][lane] = e;
-    if (lane == 0) {
+    float l = e;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    S[hh][l32] = e;
+    if (l32 == 0) {
       const int64_t i = (int64_t(b) * H + hh) * a.nchunk + chunk;
       a.mpart[i] = m;
       a.lpart[i] = l;
     }
   }
   __syncthreads();
+  // ---- P V for this thread's column group
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (active) {
-    for (int jl = r; jl < CH; jl += R) {
-      const int j = j0 + jl;
-      if (j >= a.lc) break;
-      float vv[8];
-      const int64_t row = int64_t(b) * a.cap + j;
-      load8<KIND>(a, true, row, c, D, vv);
-      const float w = S[h][jl] * row_scale<KIND>(a, true, row);
+  for (int t0 = 0; t0 < kpt; t0 += KB) {
+    if (t0 > 0) load_v(t0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, vv[e], acc[e]);
+    for (int u = 0; u < KB; ++u) {
+      if (t0 + u >= kpt) break;
+      const float p = S[h][r + R * (t0 + u)];
+      if constexpr (KIND == kBf16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(p, __uint_as_float(vraw[u][e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(p, __uint_as_float(vraw[u][e] & 0xffff0000u), acc[2 * e + 1]);
+        }
+      } else {
+        const float w = 16.0f * p * vs[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, msb_val(vraw[u], e), acc[e]);
+      }
     }
   }
-  // reduce the R key phases of each column group
-  if (r > 0 && active) {
+  // reduce the R row phases of each column group
+  if (r > 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) obuf[((r - 1) * V + c) * 8 + e] = acc[e];
   }
   __syncthreads();
-  if (r == 0 && active) {
+  if (r == 0) {
     for (int rr = 1; rr < R; ++rr)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += obuf[((rr - 1) * V + c) * 8 + e];
@@ -165,76 +225,170 @@ decode_partial(DecodeArgs a) {
   }
 }
 
-// One wave per (b, h): combine chunk statistics into lse, max probability
-// and the normalised output row.
-//   phase 0: every row, write o.
-//   phase 1: every row; rows with max p < threshold are flagged and queued
-//            for recompute, the others write o.
-//   phase 2: queued rows only (after the recompute pass), write o.
-__global__ void __launch_bounds__(64)
-decode_combine(DecodeArgs a, int phase) {
-  const int lane = threadIdx.x;
-  int b, h;
-  if (phase == 2) {
-    if (int(blockIdx.x) >= a.queue[0]) return;
-    const int e = a.queue[1 + blockIdx.x];
-    b = e / a.H;
-    h = e - b * a.H;
-  } else {
-    b = blockIdx.x / a.H;
-    h = blockIdx.x - b * a.H;
-  }
+// One wave combines the chunk statistics of row (b, h) into its log2-sum-exp
+// (returned) and 1 / sum (the largest probability, exp2(M - lse2)); with
+// write_o it also writes the normalised bf16 output row (lane = dim, dh 64).
+// Lane i holds chunk i's rescale factor; the output pass broadcasts it with
+// readlane and keeps eight chunk loads in flight.
+__device__ float combine_row(const DecodeArgs& a, int b, int h, bool write_o, float* cmax) {
+  const int lane = threadIdx.x & 63;
   const int64_t bh = int64_t(b) * a.H + h;
+  const float* mp = a.mpart + bh * a.nchunk;
+  const float* lp = a.lpart + bh * a.nchunk;
   float M = -INFINITY;
-  for (int ci = lane; ci < a.nchunk; ci += 64) M = fmaxf(M, a.mpart[bh * a.nchunk + ci]);
+  for (int ci = lane; ci < a.nchunk; ci += 64) M = fmaxf(M, mp[ci]);
   M = wave_max(M);
   float L = 0.0f;
-  for (int ci = lane; ci < a.nchunk; ci += 64)
-    L += a.lpart[bh * a.nchunk + ci] * fast_exp2(a.mpart[bh * a.nchunk + ci] - M);
+  for (int ci = lane; ci < a.nchunk; ci += 64) L += lp[ci] * fast_exp2(mp[ci] - M);
   L = wave_sum(L);
-  const float lse2 = M + log2f(L);
-  const float cmax = 1.0f / L;  // largest probability: exp2(M - lse2)
-  bool write_o = true;
-  if (lane == 0) {
-    a.lse[bh] = lse2;
-    if (phase != 2) a.cmax[bh] = cmax;
-  }
-  if (phase == 1) {
-    const bool flag = cmax < a.threshold;
-    write_o = !flag;
-    if (lane == 0) {
-      a.flags[bh] = flag ? 1 : 0;
-      if (a.recompute) a.recompute[bh] = flag ? 1 : 0;
-      if (flag) {
-        const int slot = atomicAdd(a.queue, 1);
-        a.queue[1 + slot] = int(bh);
+  const float inv = 1.0f / L;
+  if (cmax) *cmax = inv;
+  if (write_o) {
+    const float* op = a.opart + bh * a.nchunk * a.dh + lane;
+    float acc = 0.0f;
+    for (int g0 = 0; g0 < a.nchunk; g0 += 64) {
+      const int cnt = a.nchunk - g0 < 64 ? a.nchunk - g0 : 64;
+      const float wl = lane < cnt ? fast_exp2(mp[g0 + lane] - M) : 0.0f;
+      for (int k = 0; k < cnt; k += 8) {
+        float ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ov[u] = k + u < cnt ? op[int64_t(g0 + k + u) * a.dh] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          acc += ov[u] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k + u));
       }
     }
-  } else if (phase == 0 && a.recompute && lane == 0) {
-    a.recompute[bh] = 0;
+    static_cast<bf16_t*>(a.o)[int64_t(b) * a.H * a.dh + h * a.dh + lane] = f32_to_bf16(acc * inv);
   }
-  if (!write_o) return;
-  const float inv = 1.0f / L;
-  for (int d = lane; d < a.dh; d += 64) {
-    float acc = 0.0f;
-    for (int ci = 0; ci < a.nchunk; ++ci)
-      acc += a.opart[(bh * a.nchunk + ci) * a.dh + d] * fast_exp2(a.mpart[bh * a.nchunk + ci] - M);
-    static_cast<bf16_t*>(a.o)[int64_t(b) * a.H * a.dh + h * a.dh + d] = f32_to_bf16(acc * inv);
+  return M + log2f(L);
+}
+
+// Quantized caches, after the MSB pass: one wave per (b, h). A row whose
+// largest MSB-pass probability is below the threshold is flagged and queued
+// for recompute; the others write O now.
+__global__ void __launch_bounds__(64)
+decode_flag(DecodeArgs a) {
+  const int b = blockIdx.x / a.H, h = blockIdx.x - b * a.H;
+  const int64_t bh = int64_t(b) * a.H + h;
+  float cmax;
+  const float lse2 = combine_row(a, b, h, false, &cmax);
+  const bool flag = cmax < a.threshold;
+  if (!flag) combine_row(a, b, h, true, nullptr);
+  if (threadIdx.x == 0) {
+    a.lse[bh] = lse2;
+    a.cmax[bh] = cmax;
+    a.flags[bh] = flag ? 1 : 0;
+    if (a.recompute) a.recompute[bh] = flag ? 1 : 0;
+    if (flag) a.queue[1 + atomicAdd(a.queue, 1)] = int(bh);
   }
 }
 
-// a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h]) for j < lc
-__global__ void __launch_bounds__(256)
-decode_importance(DecodeArgs a) {
+// Recompute queued (b, h) rows with both planes of K and V (code = 16 *
+// msb + lsb). grid (nchunk, slots); workgroup (chunk, s) takes queue
+// entries s, s + slots, ... ; thread t = (row t/2 of the chunk, 32-dim half
+// t%2 of the head). Rewrites the row's scores and chunk partials.
+__global__ void __launch_bounds__(64)
+decode_recompute(DecodeArgs a) {
+  __shared__ float ob[CH][65];
+  const int count = a.queue[0];
+  const int t = threadIdx.x, jl = t >> 1, half = t & 1;
+  const int D = a.H * a.dh;
+  const int chunk = blockIdx.x;
+  const int j = chunk * CH + jl;
+  const bool valid = j < a.lc;
+  const float sc = kLog2e / sqrtf(float(a.dh));
+  for (int slot = blockIdx.y; slot < count; slot += gridDim.y) {
+    const int e = a.queue[1 + slot];
+    const int b = e / a.H, h = e - b * a.H;
+    const int64_t bh = int64_t(b) * a.H + h;
+    const int64_t row = int64_t(b) * a.cap + (valid ? j : a.lc - 1);
+    const int64_t off = row * (D / 2) + (h * a.dh + 32 * half) / 2;
+    const u32x4 km = *reinterpret_cast<const u32x4*>(a.k_msb + off);
+    const u32x4 kl = *reinterpret_cast<const u32x4*>(a.k_lsb + off);
+    const u32x4 vm = *reinterpret_cast<const u32x4*>(a.v_msb + off);
+    const u32x4 vl = *reinterpret_cast<const u32x4*>(a.v_lsb + off);
+    const float ksc = a.k_scale[row], vsc = a.v_scale[row];
+    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) +
+                                                     int64_t(b) * D + h * a.dh + 32 * half);
+    float d = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x4 qw = qp[w];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const float qv = __uint_as_float((n & 1) ? (qw[n >> 1] & 0xffff0000u) : (qw[n >> 1] << 16));
+        const float code = 16.0f * msb_val(km[w], n) + float((kl[w] >> (4 * n)) & 15u);
+        d = fmaf(qv, code, d);
+      }
+    }
+    d += __shfl_xor(d, 1, 64);
+    const float s = valid ? d * ksc * sc : -INFINITY;
+    if (valid && half == 0) a.scores[bh * a.lc_pad + j] = s;
+    float m = s;
+#pragma unroll
+    for (int o = 32; o > 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float p = fast_exp2(s - m);
+    float l = half == 0 ? p : 0.0f;
+    l = wave_sum(l);
+    const float w = p * vsc;
+    __syncthreads();  // previous entry's column sums are done with ob
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        ob[jl][32 * half + 8 * x + n] =
+            w * (16.0f * msb_val(vm[x], n) + float((vl[x] >> (4 * n)) & 15u));
+    __syncthreads();
+    float acc = 0.0f;
+    for (int rr = 0; rr < CH; ++rr) acc += ob[rr][t];
+    a.opart[(bh * a.nchunk + chunk) * a.dh + t] = acc;
+    if (t == 0) {
+      a.mpart[bh * a.nchunk + chunk] = m;
+      a.lpart[bh * a.nchunk + chunk] = l;
+    }
+  }
+}
+
+// One workgroup per sequence, one wave per head (up to 16 waves): combine
+// the rows not combined yet (all rows, or the recomputed ones), then
+// a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h]) for j < lc.
+__global__ void __launch_bounds__(1024)
+decode_finish(DecodeArgs a, int quantized) {
   __shared__ float lse[kMaxHeads];
-  const int b = blockIdx.y, j = blockIdx.x * 256 + threadIdx.x;
-  if (threadIdx.x < a.H) lse[threadIdx.x] = a.lse[int64_t(b) * a.H + threadIdx.x];
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6, nt = blockDim.x;
+  for (int h = wave; h < a.H; h += nw) {
+    const int64_t bh = int64_t(b) * a.H + h;
+    if (!quantized || a.flags[bh]) {
+      float cmax;
+      const float l2 = combine_row(a, b, h, true, &cmax);
+      if (lane == 0) {
+        lse[h] = l2;
+        a.lse[bh] = l2;
+        if (!quantized) {
+          a.cmax[bh] = cmax;
+          if (a.recompute) a.recompute[bh] = 0;
+        }
+      }
+    } else if (lane == 0) {
+      lse[h] = a.lse[bh];
+    }
+  }
   __syncthreads();
-  if (j >= a.lc) return;
-  float acc = 0.0f;
-  for (int h = 0; h < a.H; ++h)
-    acc += fast_exp2(a.scores[(int64_t(b) * a.H + h) * a.lc_pad + j] - lse[h]);
-  a.a[int64_t(b) * a.cap + j] += acc;
+  const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
+  for (int j = threadIdx.x; j < a.lc; j += nt) {
+    float acc = 0.0f;
+    for (int h0 = 0; h0 < a.H; h0 += 8) {
+      float sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        sv[u] = h0 + u < a.H ? sp[int64_t(h0 + u) * a.lc_pad + j] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (h0 + u < a.H) acc += fast_exp2(sv[u] - lse[h0 + u]);
+    }
+    a.a[int64_t(b) * a.cap + j] += acc;
+  }
 }
 
 }  // namespace
@@ -244,26 +398,29 @@ int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream) {
   const int V = D / 8;
   int R = 256 / V;
   if (R < 1) R = 1;
-  const dim3 gp(a.nchunk, a.batch);
+  while (R > 1 && CH % R != 0) --R;
   const int threads = V * R;
-  if (threads > 256 || a.H > kMaxHeads || (V * 8 != D)) return SPATTEN_EUNSUPPORTED;
+  // the partial kernel assumes whole 8-lane head groups (dh 64), at least
+  // two full waves and at most 256 threads
+  if (a.dh != 64 || a.H > kMaxHeads || threads > 256 || threads < 128)
+    return SPATTEN_EUNSUPPORTED;
+  const dim3 gp(a.nchunk, a.batch);
   if (!quantized) {
     SPATTEN_TIMED("decode_attn", stream, decode_partial<kBf16><<<gp, threads, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
-    SPATTEN_TIMED("decode_combine", stream, decode_combine<<<a.batch * a.H, 64, 0, stream>>>(a, 0));
     SPATTEN_LAUNCH_CHECK();
   } else {
     SPATTEN_TIMED("pq_attn_msb", stream, decode_partial<kMsb><<<gp, threads, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
-    SPATTEN_TIMED("decode_combine", stream, decode_combine<<<a.batch * a.H, 64, 0, stream>>>(a, 1));
+    SPATTEN_TIMED("decode_flag", stream, decode_flag<<<a.batch * a.H, 64, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
-    SPATTEN_TIMED("pq_attn_recompute", stream, decode_partial<kFull><<<gp, threads, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
-    SPATTEN_TIMED("decode_combine", stream, decode_combine<<<a.batch * a.H, 64, 0, stream>>>(a, 2));
+    const int slots = a.batch * a.H < kRecomputeSlots ? a.batch * a.H : kRecomputeSlots;
+    const dim3 gr(a.nchunk, slots);
+    SPATTEN_TIMED("pq_attn_recompute", stream, decode_recompute<<<gr, 64, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
   }
-  const dim3 gi(unsigned(ceil_div(a.lc, 256)), a.batch);
-  SPATTEN_TIMED("decode_importance", stream, decode_importance<<<gi, 256, 0, stream>>>(a));
+  const int fw = a.H < 16 ? a.H : 16;
+  SPATTEN_TIMED("decode_finish", stream,
+                decode_finish<<<a.batch, 64 * fw, 0, stream>>>(a, quantized ? 1 : 0));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }

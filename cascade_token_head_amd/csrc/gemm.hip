@@ -430,68 +430,97 @@ gemm_tile_kernel(GemmParams p) {
 // ------------------------------------------------------------------ decode projections
 //
 // M = batch rows (at most 64): the weights are the traffic. A workgroup owns
-// 16 output columns for every row, so N/16 workgroups each stream their 16
-// weight rows once; operands go straight from global memory into 16x16x32
-// MFMA fragments (A: a row's 8 consecutive k; B: a weight row's 8
-// consecutive k). Waves take 16-row tiles; with fewer than four row tiles
-// they split K instead and add their partial sums through LDS.
+// 16 output columns for every row; its waves split K into KT 32-wide steps
+// each and issue every fragment load (a weight row's and each 16-row tile's
+// 8 consecutive k per lane) before the first 16x16x32 MFMA, so a workgroup
+// has all of its weight bytes in flight at once. Partial sums meet in LDS,
+// in wave order.
 
-template <int MODE>
-__global__ void __launch_bounds__(256)
+constexpr int kSkinnyMaxWaves = 8;
+
+template <int MODE, int KT>
+__global__ void __launch_bounds__(64 * kSkinnyMaxWaves)
 gemm_skinny_kernel(GemmParams p) {
-  __shared__ floatx4 part[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ floatx4 part[kSkinnyMaxWaves * 4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int n0 = blockIdx.x * 16;
-  const int RT = (p.M_total + 15) >> 4;            // 16-row tiles, 1..4
-  const int splits = RT == 1 ? 4 : (RT == 2 ? 2 : 1);
-  const bool active = wave < RT * splits;
-  const int rt = wave % RT, ks = wave / RT;
-  const int klen = p.K / splits, kbeg = ks * klen;
+  const int RT = (p.M_total + 15) >> 4;  // 16-row tiles, 1..4
   const int l16 = lane & 15, kq = (lane >> 4) * 8;
-
-  int row = rt * 16 + l16;
-  if (row >= p.M_total) row = p.M_total - 1;
-  const bf16_t* a_row = static_cast<const bf16_t*>(p.A) + int64_t(row) * p.lda + kq;
+  const int kbeg = wave * KT * 32 + kq;
   const int ncol = n0 + l16;
   const bf16_t* w_row = MODE == kOut
-                            ? static_cast<const bf16_t*>(p.W0) + int64_t(ncol) * p.ldw + kq
-                            : qkv_weight_row<bf16_t>(p, 0, ncol) + kq;
-  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (active) {
-    for (int k0 = kbeg; k0 < kbeg + klen; k0 += 128) {
-      u32x4 av[4], bv[4];
+                            ? static_cast<const bf16_t*>(p.W0) + int64_t(ncol) * p.ldw + kbeg
+                            : qkv_weight_row<bf16_t>(p, 0, ncol) + kbeg;
+  u32x4 bv[KT], av[4][KT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        av[u] = *reinterpret_cast<const u32x4*>(a_row + k0 + 32 * u);
-        bv[u] = *reinterpret_cast<const u32x4*>(w_row + k0 + 32 * u);
-      }
+  for (int u = 0; u < KT; ++u) bv[u] = *reinterpret_cast<const u32x4*>(w_row + 32 * u);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = mfma16x16x32(as_bf16x8(av[u]), as_bf16x8(bv[u]), acc);
+  for (int t = 0; t < 4; ++t) {
+    if (t < RT) {
+      int row = 16 * t + l16;
+      if (row >= p.M_total) row = p.M_total - 1;
+      const bf16_t* a_row = static_cast<const bf16_t*>(p.A) + int64_t(row) * p.lda + kbeg;
+#pragma unroll
+      for (int u = 0; u < KT; ++u) av[t][u] = *reinterpret_cast<const u32x4*>(a_row + 32 * u);
     }
   }
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (t < RT) {
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < KT; ++u) acc = mfma16x16x32(as_bf16x8(av[t][u]), as_bf16x8(bv[u]), acc);
+      part[wave * 4 + t][lane] = acc;
+    }
+  }
   __syncthreads();
-  if (wave >= RT) return;
-  for (int sp = 1; sp < splits; ++sp) acc += part[sp * RT + wave][lane];
-  // C fragment: lane holds rows 4*(lane/16) + i of the tile, column l16
+  for (int rt = wave; rt < RT; rt += nw) {
+    floatx4 acc = part[rt][lane];
+    for (int w = 1; w < nw; ++w) acc += part[w * 4 + rt][lane];
+    // C fragment: lane holds rows 4*(lane/16) + i of the tile, column l16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = rt * 16 + 4 * (lane >> 4) + i;
-    if (b >= p.M_total) continue;
-    const float v = acc[i];
-    if (MODE == kOut) {
-      bf16_t* x = static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D + ncol;
-      *x = f32_to_bf16(bf16_to_f32(*x) + v);
-    } else {
-      const int hd = p.h_kept * p.dh;
-      const int which = ncol / hd;
-      const int rem = ncol - which * hd;
-      bf16_t* d = which == 0 ? static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D
-                             : static_cast<bf16_t*>(which == 1 ? p.out1 : p.out2) +
-                                   int64_t(b) * p.kv_bs;
-      d[rem] = f32_to_bf16(v);
+    for (int i = 0; i < 4; ++i) {
+      const int b = rt * 16 + 4 * (lane >> 4) + i;
+      if (b >= p.M_total) continue;
+      const float v = acc[i];
+      if (MODE == kOut) {
+        bf16_t* x = static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D + ncol;
+        *x = f32_to_bf16(bf16_to_f32(*x) + v);
+      } else {
+        const int hd = p.h_kept * p.dh;
+        const int which = ncol / hd;
+        const int rem = ncol - which * hd;
+        bf16_t* d = which == 0 ? static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D
+                               : static_cast<bf16_t*>(which == 1 ? p.out1 : p.out2) +
+                                     int64_t(b) * p.kv_bs;
+        d[rem] = f32_to_bf16(v);
+      }
     }
   }
+}
+
+// Smallest K step count per wave (1, 2, 4 or 8) that splits K over at most
+// kSkinnyMaxWaves waves; 0 if none does.
+inline int skinny_kt(int K) {
+  if (K % 32 != 0) return 0;
+  const int steps = K / 32;
+  for (int kt = 1; kt <= 8; kt *= 2)
+    if (steps % kt == 0 && steps / kt <= kSkinnyMaxWaves) return kt;
+  return 0;
+}
+
+template <int MODE>
+int run_skinny(const GemmParams& p, int kt, hipStream_t stream, const char* name) {
+  const dim3 grid(unsigned(p.N / 16));
+  const int threads = 64 * (p.K / 32 / kt);
+  switch (kt) {
+    case 1: SPATTEN_TIMED(name, stream, gemm_skinny_kernel<MODE, 1><<<grid, threads, 0, stream>>>(p)); break;
+    case 2: SPATTEN_TIMED(name, stream, gemm_skinny_kernel<MODE, 2><<<grid, threads, 0, stream>>>(p)); break;
+    case 4: SPATTEN_TIMED(name, stream, gemm_skinny_kernel<MODE, 4><<<grid, threads, 0, stream>>>(p)); break;
+    default: SPATTEN_TIMED(name, stream, gemm_skinny_kernel<MODE, 8><<<grid, threads, 0, stream>>>(p)); break;
+  }
+  SPATTEN_LAUNCH_CHECK();
+  return SPATTEN_OK;
 }
 
 // ------------------------------------------------------------------ fp32 VALU
@@ -584,15 +613,10 @@ inline double tile_cost(const GemmParams& p, int bm, int bn, double rel) {
 template <int MODE>
 int run_gemm(GemmParams& p, int dtype, hipStream_t stream) {
   const char* name = MODE == kOut ? "out_gemm" : "qkv_gemm";
-  const int rt = int(ceil_div(p.M_total, 16));
-  const int splits = rt == 1 ? 4 : (rt == 2 ? 2 : 1);
+  const int kt = skinny_kt(p.K);
   if (MODE != kQkvPrefill && dtype == SPATTEN_BF16 && !p.seq_tiled && p.M_total <= 64 &&
-      p.N % 16 == 0 && p.K % (128 * splits) == 0) {
-    SPATTEN_TIMED(name, stream,
-                  gemm_skinny_kernel<MODE><<<dim3(unsigned(p.N / 16)), 256, 0, stream>>>(p));
-    SPATTEN_LAUNCH_CHECK();
-    return SPATTEN_OK;
-  }
+      p.N % 16 == 0 && kt > 0)
+    return run_skinny<MODE>(p, kt, stream, name);
   if (dtype == SPATTEN_BF16 && MODE != kQkvDecode) {
     // 128x128 tiles at two workgroups per CU hide load latency better than
     // one 256x256 workgroup per CU (measured on MI355X).

@@ -74,12 +74,14 @@ struct DecodeArgs {
   const void* q;  // [B, D] bf16
   const void* k_cache;
   const void* v_cache;  // [B, cap, D] bf16
-  const uint8_t* k_msb;
-  const uint8_t* k_lsb;
-  const float* k_scale;
-  const uint8_t* v_msb;
-  const uint8_t* v_lsb;
-  const float* v_scale;
+  uint8_t* k_msb;  // quantized planes [B, cap, D/2] and scales [B, cap]
+  uint8_t* k_lsb;
+  float* k_scale;
+  uint8_t* v_msb;
+  uint8_t* v_lsb;
+  float* v_scale;
+  const void* knew;  // quantized: this step's k and v rows [B, D] bf16, coded
+  const void* vnew;  // into plane row lc-1 by the MSB pass before it reads it
   int batch, H, dh, cap, lc, lc_pad, nchunk;
   float threshold;
   float* scores;  // [B, H, lc_pad]

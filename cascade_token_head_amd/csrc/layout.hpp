@@ -26,7 +26,7 @@ constexpr int kAttnKBlock = 256;
 // fp32 attention: query rows per workgroup.
 constexpr int kAttnF32Rows = 8;
 // Decode: cache entries per split-K chunk.
-constexpr int kDecChunk = 64;
+constexpr int kDecChunk = 32;
 
 SPATTEN_HD inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 SPATTEN_HD inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }

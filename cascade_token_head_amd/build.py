@@ -41,12 +41,19 @@ def _run(cmd):
     return r
 
 
+# Per-source extra flags. Attention never sees NaN inputs, so its max
+# reductions skip IEEE-mode NaN quieting (one v_max per element instead of
+# two); infinities (masked scores) keep their meaning.
+EXTRA_FLAGS = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])

@@ -19,6 +19,8 @@
 // permuted so each lane's 16 scores are 16 consecutive keys, which is
 // exactly the k-slot order the P V MFMA wants - P never leaves registers.
 // fp32 path: plain VALU kernels for the fp32 workload.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -32,7 +34,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // ------------------------------------------------------------------ bf16 forward
 
 template <int DH, bool CAUSAL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, DH == 64 ? 2 : 1)
 attn_fwd_bf16(AttnArgs a) {
   constexpr int KT = 64;        // keys per iteration
   constexpr int KS = DH + 8;    // LDS row stride of the K tile
@@ -126,93 +128,99 @@ attn_fwd_bf16(AttnArgs a) {
   // the C layout then gives lane group G the keys 16G .. 16G+15 in order.
   const int kperm = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
 
+  // One 32-key sub-tile (keys k0 + 32t ..) for both query halves: S^T by
+  // MFMA, online softmax in registers, then O^T += V^T P^T. MASKED is set
+  // only for sub-tiles that cross the sequence end or the causal diagonal,
+  // so interior sub-tiles carry no masking code.
+  auto subtile = [&](auto masked_tag, int buf, int k0, int t) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    floatx16 st[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[u][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) {
+      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          &Ks[buf][(32 * t + kperm) * KS + 16 * kk + 8 * G]));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) st[u] = mfma32x32x16(kf, qf[u][kk], st[u]);
+    }
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int my_q = wq0 + 32 * u + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * t + 16 * G + i;
+          const bool m = key >= n || (CAUSAL && key > my_q);
+          st[u][i] = m ? -INFINITY : st[u][i];
+        }
+      }
+    }
+    bf16x8 pb[2][2];  // [s2][u]
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float m4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m4[i] = fmaxf(fmaxf(st[u][4 * i], st[u][4 * i + 1]), fmaxf(st[u][4 * i + 2], st[u][4 * i + 3]));
+      const float tmax = xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      // move the reference only when a score would exceed it by 2^kRescale
+      const bool grow = tmax * sc > mref[u] * sc + kRescale || mref[u] == -INFINITY;
+      if (__ballot(grow)) {
+        const float m_new = grow ? fmaxf(mref[u], tmax) : mref[u];
+        const float alpha = mref[u] == -INFINITY ? 0.0f : fast_exp2((mref[u] - m_new) * sc);
+        mref[u] = m_new;
+        lsum[u] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) o[dt][u] = o[dt][u] * alpha;
+      }
+      const float msc = (mref[u] == -INFINITY ? 0.0f : mref[u]) * sc;
+      float ps[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 w;
+        float pp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(fmaf(st[u][8 * s2 + 2 * j], sc, -msc));
+          const float p1 = fast_exp2(fmaf(st[u][8 * s2 + 2 * j + 1], sc, -msc));
+          pp[j] = p0 + p1;
+          w[j] = pack_bf16x2(p0, p1);
+        }
+        ps[s2] = (pp[0] + pp[1]) + (pp[2] + pp[3]);
+        pb[s2][u] = as_bf16x8(w);
+      }
+      lsum[u] += ps[0] + ps[1];
+    }
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * s2]));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) o[dt][u] = mfma32x32x16(vf, pb[s2][u], o[dt][u]);
+      }
+  };
+
   gload(0);
   sstore(0);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1, k0 = it * KT;
     if (it + 1 < ntiles) gload(it + 1);
-    if (wave_live && k0 < wave_kend) {
-      floatx16 st[2][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st[t][u][r] = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kk = 0; kk < DH / 16; ++kk) {
-          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              &Ks[buf][(32 * t + kperm) * KS + 16 * kk + 8 * G]));
-#pragma unroll
-          for (int u = 0; u < 2; ++u) st[t][u] = mfma32x32x16(kf, qf[u][kk], st[t][u]);
-        }
-      // masks only where the tile crosses the sequence end or the diagonal
-      const bool need_mask = (k0 + KT > n) || (CAUSAL && k0 + KT - 1 > wq0);
-      if (need_mask) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int my_q = wq0 + 32 * u + col;
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * t + 16 * G + i;
-              const bool masked = key >= n || (CAUSAL && key > my_q);
-              st[t][u][i] = masked ? -INFINITY : st[t][u][i];
-            }
-        }
+    for (int t = 0; t < 2; ++t) {
+      const int ks0 = k0 + 32 * t;
+      if (wave_live && ks0 < wave_kend) {
+        const bool need_mask = (ks0 + 32 > n) || (CAUSAL && ks0 + 31 > wq0);
+        if (need_mask)
+          subtile(std::true_type{}, buf, k0, t);
+        else
+          subtile(std::false_type{}, buf, k0, t);
       }
-      bf16x8 pb[2][2][2];  // [t][s][u]
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, st[t][u][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // move the reference only when a score would exceed it by 2^kRescale
-        const bool grow = tmax * sc > mref[u] * sc + kRescale || mref[u] == -INFINITY;
-        if (__ballot(grow)) {
-          const float m_new = grow ? fmaxf(mref[u], tmax) : mref[u];
-          const float alpha = mref[u] == -INFINITY ? 0.0f : fast_exp2((mref[u] - m_new) * sc);
-          mref[u] = m_new;
-          lsum[u] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][u][r] *= alpha;
-        }
-        const float msc = (mref[u] == -INFINITY ? 0.0f : mref[u]) * sc;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            u32x4 w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float p0 = fast_exp2(fmaf(st[t][u][8 * s2 + 2 * j], sc, -msc));
-              const float p1 = fast_exp2(fmaf(st[t][u][8 * s2 + 2 * j + 1], sc, -msc));
-              lsum[u] += p0 + p1;
-              w[j] = pack_bf16x2(p0, p1);
-            }
-            pb[t][s2][u] = as_bf16x8(w);
-          }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DH / 32; ++dt)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * s2]));
-#pragma unroll
-            for (int u = 0; u < 2; ++u) o[dt][u] = mfma32x32x16(vf, pb[t][s2][u], o[dt][u]);
-          }
     }
     if (it + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();

@@ -75,6 +75,18 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Combine each lane's value with that of lane ^ 32 (v_permlane32_swap on
+// gfx950 exchanges the two 32-lane halves without a trip through LDS; the
+// two returned registers hold each half's value for every lane pair).
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // MFMA 32x32x16 bf16 -> fp32 (gfx950). Operand lane layout:
 //   A: lane l holds A[row l%32][k 8*(l/32) .. +8]
 //   B: lane l holds B[k 8*(l/32) .. +8][col l%32]

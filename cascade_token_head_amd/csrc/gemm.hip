@@ -30,6 +30,7 @@ struct GemmParams {
   int64_t ldw;
   const int32_t* head_idx;
   int batch, n, seq_tiled, mt_per_seq, M_total, N, K;
+  int tiles_y;  // M tiles of the tiled kernel (set by its launcher)
   int h_kept, dh, D, n_pad;
   void* out0;
   void* out1;
@@ -231,7 +232,15 @@ gemm_tile_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BKT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile_y = blockIdx.y, n0 = blockIdx.x * BN;
+  // Workgroup i runs on XCD i % 8. Each XCD takes one contiguous run of the
+  // column-fastest tile order, so the row blocks of A it reads stay in its
+  // own L2 while it sweeps the weight tiles, and A crosses from HBM once.
+  const int ntx = int(ceil_div(p.N, BN));
+  const int total = ntx * p.tiles_y;
+  const int per_xcd = int(ceil_div(total, 8));
+  const int t = (int(blockIdx.x) & 7) * per_xcd + (int(blockIdx.x) >> 3);
+  if (t >= total) return;
+  const int tile_y = t / ntx, n0 = (t - tile_y * ntx) * BN;
   const int b_tile = p.seq_tiled ? tile_y / p.mt_per_seq : 0;
   const int kc = tid & 7;  // 16-byte chunk along k this thread loads
 
@@ -323,25 +332,30 @@ gemm_tile_kernel(GemmParams p) {
   if (KT > 1) gload(ra0, rb0, 1);
   if (KT > 2) gload(ra1, rb1, 2);
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
+  // Pairs of steps with no exit between them, so the accumulators stay in
+  // place across the loop back-edge.
+  for (int kt = 0; kt + 1 < KT; kt += 2) {
     // even step: compute tile kt from buffer 0, stage tile kt+1 into buffer 1
-    if (kt + 1 < KT) sstore(ra0, rb0, 1);
+    sstore(ra0, rb0, 1);
     if (kt + 3 < KT) gload(ra0, rb0, kt + 3);
     compute(0);
     __syncthreads();
-    if (kt + 1 >= KT) break;
     // odd step: compute tile kt+1 from buffer 1, stage tile kt+2 into buffer 0
     if (kt + 2 < KT) sstore(ra1, rb1, 0);
     if (kt + 4 < KT) gload(ra1, rb1, kt + 4);
     compute(1);
     __syncthreads();
   }
+  if (KT & 1) compute(0);  // the last (even) tile, staged by the final odd step
 
   // ---- epilogue: each 32 x 32 MFMA block goes through a 2 KB per-wave LDS
   // stage (row-major, or transposed for V^T) and leaves as 16-byte stores.
   const int hd = p.h_kept * p.dh;
   const float inv_n = 1.0f / float(p.n);
-  bf16_t* stage = &As[0][0] + wave * 1024;
+  // stage rows are padded to 40 elements (80 bytes): the transposed writes
+  // of one store instruction then spread over 16 bank groups
+  constexpr int SS = 40;
+  bf16_t* stage = &As[0][0] + wave * (32 * SS);
   auto row_of = [&](int lr, int& b, int& m) -> bool {
     if (p.seq_tiled) {
       b = b_tile;
@@ -364,18 +378,28 @@ gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int r0 = wm + 32 * i;  // first local row of this block
+      if (trans) {
+        // registers 4q .. 4q+3 are rows 8q + 4G .. +3 of column fr: one
+        // 8-byte write each
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 8 * (r >> 2) + 4 * G + (r & 3);
-        const int idx = trans ? fr * 32 + rr : rr * 32 + fr;
-        stage[idx] = f32_to_bf16(acc[i][j][r]);
+        for (int q = 0; q < 4; ++q) {
+          const uint64_t pk = uint64_t(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1])) |
+                              (uint64_t(pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])) << 32);
+          *reinterpret_cast<uint64_t*>(&stage[fr * SS + 8 * q + 4 * G]) = pk;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 8 * (r >> 2) + 4 * G + (r & 3);
+          stage[rr * SS + fr] = f32_to_bf16(acc[i][j][r]);
+        }
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int ch = lane + 64 * q;        // 128 chunks of 8 elements
         const int a8 = ch >> 2, o8 = (ch & 3) * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[a8 * 32 + o8]);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&stage[a8 * SS + o8]);
         if (!trans) {
           // a8 = row in block, o8 = column offset
           int b, m;
@@ -595,7 +619,9 @@ int run_tile(GemmParams& p, hipStream_t stream, const char* name) {
     p.mt_per_seq = 0;
     tiles_y = int(ceil_div(p.M_total, BMt));
   }
-  const dim3 grid(unsigned(ceil_div(p.N, BNt)), unsigned(tiles_y));
+  p.tiles_y = tiles_y;
+  const int64_t total = ceil_div(p.N, BNt) * int64_t(tiles_y);
+  const dim3 grid(unsigned(8 * ceil_div(total, 8)));
   SPATTEN_TIMED(name, stream, gemm_tile_kernel<MODE, BMt, BNt><<<grid, 256, 0, stream>>>(p));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;

@@ -10,6 +10,11 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
   head_attention      torch scaled_dot_product_attention (fp64, CPU);
                       closed forms (Q = 0, n = 1, causal row 0); brute-force
                       scalar loops on tiny shapes; permutation equivariance.
+  attention_rows      rows of torch softmax attention (fp64); Q = 0 and
+                      causal row 0 closed forms.
+  column_sums         column sums of torch softmax probabilities given the
+                      exact LSE; Q = 0 harmonic closed form (causal); the
+                      columns of one head sum to the number of queries.
   prefill_layer       importance sum = heads x queries; Q = 0 closed forms
                       for the column sums (bidirectional and causal);
                       constant-V head importance; keep=1 reproduces dense

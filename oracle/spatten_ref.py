@@ -88,6 +88,44 @@ def head_attention(Q, K, V, causal: bool, row_block: int = 512):
     return O, col, lse
 
 
+def attention_rows(Q, K, V, rows, causal: bool):
+    """Selected query rows of one head, each from its own full row of scores
+    (the definition head_attention applies to every row): for query i,
+    S_i = Q_i K^T / sqrt(dh) over the keys it sees (j <= i when causal),
+    P_i = softmax(S_i), O_i = P_i V.
+
+    Returns O [len(rows), dh] and the natural-log LSE [len(rows)]. Used to
+    check long sequences on a sample of rows.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    dh = Q.shape[1]
+    S = (np.asarray(Q, np.float64)[rows] @ np.asarray(K, np.float64).T) / math.sqrt(dh)
+    if causal:
+        S = np.where(np.arange(K.shape[0])[None, :] > rows[:, None], -np.inf, S)
+    m = np.max(S, axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = np.sum(E, axis=1, keepdims=True)
+    return (E / l) @ np.asarray(V, np.float64), (m + np.log(l))[:, 0]
+
+
+def column_sums(Q, K, lse, cols, causal: bool):
+    """Column sums of one head's P at selected key columns, given every
+    row's natural-log LSE: sum over the queries i that see key j (all i, or
+    i >= j when causal) of exp(Q_i . K_j / sqrt(dh) - lse_i).
+
+    This is the token-importance contribution of the head (section II
+    "Cascade pruning": importance is the probability mass a key receives),
+    evaluated column by column so that n x n is never formed.
+    """
+    cols = np.asarray(cols, dtype=np.int64)
+    dh = Q.shape[1]
+    S = (np.asarray(Q, np.float64) @ np.asarray(K, np.float64)[cols].T) / math.sqrt(dh)
+    E = np.exp(S - np.asarray(lse, np.float64)[:, None])
+    if causal:
+        E = np.where(np.arange(Q.shape[0])[:, None] < cols[None, :], 0.0, E)
+    return E.sum(axis=0)
+
+
 # --------------------------------------------------------------------------
 # cascade token and head pruning (page: section II "Cascade pruning",
 # "B. Motivation" token pruning, "A. Cascade Token Pruning")

@@ -135,6 +135,44 @@ def test_attention_permutation_equivariance():
     np.testing.assert_allclose(col2, col[perm], atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_rows_and_column_sums_vs_torch(causal):
+    rng = np.random.default_rng(11)
+    n, dh = 97, 16
+    Q, K, V = (rng.standard_normal((n, dh)) * 2 for _ in range(3))
+    P, L = _torch_probs(Q, K, causal)
+    rows = np.array([0, 1, 31, 32, 64, 96])
+    O, lse = R.attention_rows(Q, K, V, rows, causal)
+    np.testing.assert_allclose(O, P[rows] @ V, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, L[rows], rtol=1e-12, atol=1e-12)
+    cols = np.array([0, 5, 63, 95, 96])
+    np.testing.assert_allclose(R.column_sums(Q, K, L, cols, causal), P[:, cols].sum(axis=0),
+                               rtol=1e-12, atol=1e-12)
+    # every row's probabilities sum to one, so all columns add up to n
+    assert abs(R.column_sums(Q, K, L, np.arange(n), causal).sum() - n) < 1e-9
+
+
+def test_attention_rows_and_column_sums_closed_forms():
+    rng = np.random.default_rng(12)
+    n, dh = 41, 8
+    K, V = rng.standard_normal((n, dh)), rng.standard_normal((n, dh))
+    Z = np.zeros((n, dh))
+    rows = np.array([0, 7, 40])
+    # causal, Q = 0: row i averages V over keys 0..i and has LSE log(i + 1)
+    O, lse = R.attention_rows(Z, K, V, rows, causal=True)
+    for t, i in enumerate(rows):
+        np.testing.assert_allclose(O[t], V[:i + 1].mean(axis=0), atol=1e-12)
+    np.testing.assert_allclose(lse, np.log(rows + 1.0), atol=1e-12)
+    # column j then sums 1/(i+1) over i >= j: H_n - H_j
+    cols = np.array([0, 3, 40])
+    harm = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    got = R.column_sums(Z, K, np.log(np.arange(n) + 1.0), cols, causal=True)
+    np.testing.assert_allclose(got, harm[n] - harm[cols], atol=1e-12)
+    # bidirectional, Q = 0: every column sums to exactly one
+    np.testing.assert_allclose(R.column_sums(Z, K, np.full(n, math.log(n)), cols, causal=False),
+                               1.0, atol=1e-12)
+
+
 # ----------------------------------------------------------------- layer
 
 

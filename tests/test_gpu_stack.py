@@ -207,6 +207,96 @@ def test_prefill_stack_bert_base_full_size():
     _prefill_case(BERT_BASE, [0, 13, 31], "bert_base full")
 
 
+def _sample(rng, n, k, must):
+    s = {int(v) for v in must if 0 <= v < n}
+    s.update(int(v) for v in rng.choice(n, size=min(k, n), replace=False))
+    return np.array(sorted(s))
+
+
+@pytest.mark.slow
+def test_prefill_stack_long_causal_full_size():
+    """long_causal at its full size (T = 32768, 32 heads of 128, causal) in
+    the benchmarked launch configuration. The n x n attention is too large
+    for the oracle, so it checks sampled outputs, teacher-forced on the
+    GPU's Q, K, V and row LSE: projections and attention rows at sampled
+    queries of three heads, token importance at sampled keys summed over
+    every head, the output projection at sampled rows. Properties hold at
+    any size: each layer adds heads x queries of importance in total, and
+    each head's importance is the sum of |O| over its rows. Selections and
+    compaction are checked bit for bit on the full rows."""
+    cfg = LONG_CAUSAL
+    inputs = make_prefill_inputs(cfg)
+    st = run_prefill_gpu(cfg, inputs)
+    rng = np.random.default_rng(2024)
+    B, dh = cfg.batch, cfg.head_dim
+    assert B == 1
+    for l, rec in enumerate(st.trace):
+        n, h = cfg.tokens[l], cfg.heads[l]
+        print("long_causal full size: layer %d, %d tokens, %d heads" % (l, n, h), flush=True)
+        lay = PrefillWs(B, n, h, dh, 2, True)
+        ws, npad = rec["ws"], lay.n_pad
+
+        def region(off, count):
+            return ws[off: off + count * 2].view(torch.bfloat16)
+
+        q_ws = region(lay.q, h * npad * dh).view(h, npad, dh)
+        k_ws = region(lay.k, h * npad * dh).view(h, npad, dh)
+        vt_ws = region(lay.vt, h * dh * npad).view(h, dh, npad)
+        o_ws = region(lay.o, n * h * dh).view(n, h, dh)
+        W = inputs["layers"][l]
+        heads = rec["heads"].cpu().numpy()[0]
+        lse = rec["lse"][0]
+        a_in, a_out = to_np(rec["a_in"][0]), to_np(rec["a_out"][0])
+        g_in, g_out = to_np(rec["g_in"][0]), to_np(rec["g_out"][0])
+        rows = _sample(rng, n, 40, [0, 1, 255, 256, n // 2, n - 1])
+        cols = _sample(rng, n, 24, [0, 1, 255, 256, n - 1])
+        x_rows = to_np(rec["x_in"][0, rows])
+        o_rows = to_np(o_ws[rows])
+        slots = sorted({0, h // 2, h - 1})
+        dcol = np.zeros(len(cols))
+        delta = np.zeros_like(x_rows)
+        for s, hid in enumerate(heads):
+            c = slice(hid * dh, (hid + 1) * dh)
+            Q, K = to_np(q_ws[s, :n]), to_np(k_ws[s, :n])
+            L = to_np(lse[s])
+            dcol += R.column_sums(Q, K, L, cols, True)
+            delta += o_rows[:, s] @ W["wo"][c, :].astype(np.float64)
+            if s not in slots:
+                continue
+            V = to_np(vt_ws[s, :, :n].transpose(0, 1))
+            for name, got in (("wq", Q), ("wk", K), ("wv", V)):
+                ref = R.bf16_round(x_rows @ W[name][:, c].astype(np.float64))
+                check_bf16_output(got[rows], ref, what="layer %d head %d %s" % (l, hid, name))
+            O, lr = R.attention_rows(Q, K, V, rows, True)
+            check_bf16_output(o_rows[:, s], R.bf16_round(O), what="layer %d head %d O" % (l, hid))
+            np.testing.assert_allclose(L[rows], lr, rtol=1e-5, atol=1e-4)
+        a_ref = a_in[cols] + dcol
+        err = np.max(np.abs(a_out[cols] - a_ref))
+        assert err <= 2e-5 * np.max(a_ref), ("a", l, err / np.max(a_ref))
+        total = float(np.sum(a_out - a_in))
+        assert abs(total - h * n) <= 1e-5 * h * n, ("total importance", l, total, h * n)
+        abs_o = o_ws.float().abs().sum(dim=(0, 2)).double().cpu().numpy()
+        for s, hid in enumerate(heads):
+            assert abs((g_out[hid] - g_in[hid]) - abs_o[s]) <= 2e-3 * abs_o[s], ("g", l, hid)
+        check_bf16_output(to_np(rec["x_out"][0, rows]), R.bf16_round(x_rows + delta),
+                          what="layer %d x_out" % l)
+        if l + 1 < cfg.n_layers:
+            nxt = st.trace[l + 1]
+            if "head_sel" in rec:
+                hs = rec["head_sel"].cpu().numpy()[0]
+                np.testing.assert_array_equal(
+                    hs, R.topk(g_out[heads].astype(np.float32), cfg.heads[l + 1]))
+                np.testing.assert_array_equal(nxt["heads"].cpu().numpy()[0], heads[hs])
+            ts_t = rec["tok_sel"][0]
+            ts = ts_t.cpu().numpy()
+            np.testing.assert_array_equal(
+                ts, R.topk(rec["a_out"][0].cpu().numpy(), cfg.tokens[l + 1]))
+            sel = ts_t.long()
+            assert torch.equal(nxt["x_in"][0], rec["x_out"][0].index_select(0, sel))
+            assert torch.equal(nxt["a_in"][0], rec["a_out"][0].index_select(0, sel))
+            assert torch.equal(nxt["pos"][0], rec["pos"][0].index_select(0, sel))
+
+
 # ---------------------------------------------------------------- decode
 
 

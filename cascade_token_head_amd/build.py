@@ -43,8 +43,11 @@ def _run(cmd):
 
 # Per-source extra flags. Attention never sees NaN inputs, so its max
 # reductions skip IEEE-mode NaN quieting (one v_max per element instead of
-# two); infinities (masked scores) keep their meaning.
-EXTRA_FLAGS = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# two); infinities (masked scores) keep their meaning. Its MFMA results are
+# consumed by VALU code at once, so they are kept in VGPRs rather than
+# accumulation registers that would need a copy per element.
+EXTRA_FLAGS = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
+                            "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> str:

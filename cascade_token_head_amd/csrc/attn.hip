@@ -33,25 +33,31 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // ------------------------------------------------------------------ bf16 forward
 
-template <int DH, bool CAUSAL>
-__global__ void __launch_bounds__(256, DH == 64 ? 2 : 1)
+// NU 32-query groups per wave; a workgroup covers QB queries with
+// QB / (32 NU) waves sharing each K/V tile. MINW: waves per SIMD the
+// register budget is sized for.
+template <int DH, bool CAUSAL, int NU, int MINW>
+__global__ void __launch_bounds__(2 * attn_qblock(DH) / NU, MINW)
 attn_fwd_bf16(AttnArgs a) {
+  constexpr int QB = attn_qblock(DH);
+  constexpr int NT = 2 * QB / NU;  // threads per workgroup
+  constexpr int WAVES = NT / 64;
   constexpr int KT = 64;        // keys per iteration
   constexpr int KS = DH + 8;    // LDS row stride of the K tile
   constexpr int VS = KT + 8;    // LDS row stride of the V^T tile
-  constexpr int NKC = KT * DH / 8 / 256;  // 16-byte K chunks per thread
-  constexpr int NVC = DH * KT / 8 / 256;  // 16-byte V^T chunks per thread
-  constexpr int QW = 64;                  // queries per wave (two 32-query halves)
+  constexpr int NKC = KT * DH / 8 / NT;  // 16-byte K chunks per thread
+  constexpr int NVC = DH * KT / 8 / NT;  // 16-byte V^T chunks per thread
+  constexpr int QW = 32 * NU;             // queries per wave
   constexpr float kRescale = 8.0f;        // log2 headroom before O is rescaled
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * KS];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][DH * VS];
-  __shared__ float red[4];
+  __shared__ float red[WAVES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, col = lane & 31;
   const int b = blockIdx.z, s = blockIdx.y;
   const int qb = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
-  const int q0 = qb * kAttnQBlock;
+  const int q0 = qb * QB;
   const int wq0 = q0 + QW * wave;        // first query of this wave
   const int n = a.n, n_pad = a.n_pad;
   const int64_t bs = int64_t(b) * a.h_kept + s;
@@ -61,26 +67,31 @@ attn_fwd_bf16(AttnArgs a) {
   const bool wave_live = wq0 < n;
 
   // Q operand (B of S^T = K Q^T): lane holds Q[query][16kk + 8G .. +8]
-  bf16x8 qf[2][DH / 16];
+  bf16x8 qf[NU][DH / 16];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int kk = 0; kk < DH / 16; ++kk)
       qf[u][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
           Q + int64_t(wq0 + 32 * u + col) * DH + 16 * kk + 8 * G));
 
   const float sc = kLog2e / sqrtf(float(DH));
-  float mref[2] = {-INFINITY, -INFINITY};  // max used as the exp2 reference (raw score units)
-  float lsum[2] = {0.0f, 0.0f};
-  floatx16 o[DH / 32][2];
+  float mref[NU];  // max used as the exp2 reference (raw score units)
+  float lsum[NU];
+  floatx16 o[DH / 32][NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    mref[u] = -INFINITY;
+    lsum[u] = 0.0f;
+  }
 #pragma unroll
   for (int dt = 0; dt < DH / 32; ++dt)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][u][r] = 0.0f;
 
-  const int kend = CAUSAL ? min(n, q0 + kAttnQBlock) : n;
+  const int kend = CAUSAL ? min(n, q0 + QB) : n;
   const int ntiles = int(ceil_div(kend, KT));
   const int wave_kend = CAUSAL ? min(n, wq0 + QW) : n;   // keys this wave can see
 
@@ -89,12 +100,12 @@ attn_fwd_bf16(AttnArgs a) {
     const int k0 = it * KT;
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       rk[i] = *reinterpret_cast<const u32x4*>(K + int64_t(k0) * DH + c * 8);
     }
 #pragma unroll
     for (int i = 0; i < NVC; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int row = c >> 3, k8 = (c & 7) * 8;
       rv[i] = *reinterpret_cast<const u32x4*>(VT + int64_t(row) * n_pad + k0 + k8);
       // keys past the end get exact zeros (their probabilities are 0, and
@@ -112,13 +123,13 @@ attn_fwd_bf16(AttnArgs a) {
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int row = c / (DH / 8), c8 = (c % (DH / 8)) * 8;
       *reinterpret_cast<u32x4*>(&Ks[buf][row * KS + c8]) = rk[i];
     }
 #pragma unroll
     for (int i = 0; i < NVC; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int row = c >> 3, k8 = (c & 7) * 8;
       *reinterpret_cast<u32x4*>(&Vs[buf][row * VS + k8]) = rv[i];
     }
@@ -134,9 +145,9 @@ attn_fwd_bf16(AttnArgs a) {
   // so interior sub-tiles carry no masking code.
   auto subtile = [&](auto masked_tag, int buf, int k0, int t) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    floatx16 st[2];
+    floatx16 st[NU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[u][r] = 0.0f;
 #pragma unroll
@@ -144,11 +155,11 @@ attn_fwd_bf16(AttnArgs a) {
       const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
           &Ks[buf][(32 * t + kperm) * KS + 16 * kk + 8 * G]));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) st[u] = mfma32x32x16(kf, qf[u][kk], st[u]);
+      for (int u = 0; u < NU; ++u) st[u] = mfma32x32x16(kf, qf[u][kk], st[u]);
     }
     if constexpr (MASKED) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int my_q = wq0 + 32 * u + col;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -158,9 +169,9 @@ attn_fwd_bf16(AttnArgs a) {
         }
       }
     }
-    bf16x8 pb[2][2];  // [s2][u]
+    bf16x8 pb[2][NU];  // [s2][u]
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       float m4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -201,7 +212,7 @@ attn_fwd_bf16(AttnArgs a) {
         const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
             &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * s2]));
 #pragma unroll
-        for (int u = 0; u < 2; ++u) o[dt][u] = mfma32x32x16(vf, pb[s2][u], o[dt][u]);
+        for (int u = 0; u < NU; ++u) o[dt][u] = mfma32x32x16(vf, pb[s2][u], o[dt][u]);
       }
   };
 
@@ -228,7 +239,7 @@ attn_fwd_bf16(AttnArgs a) {
 
   float gsum = 0.0f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const int my_q = wq0 + 32 * u + col;
     const float l = lsum[u] + __shfl_xor(lsum[u], 32, 64);
     const float inv = 1.0f / l;
@@ -255,7 +266,12 @@ attn_fwd_bf16(AttnArgs a) {
   gsum = wave_sum(gsum);
   if (lane == 0) red[wave] = gsum;
   __syncthreads();
-  if (tid == 0) a.gpart[bs * a.nqb + qb] = red[0] + red[1] + red[2] + red[3];
+  if (tid == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += red[w];
+    a.gpart[bs * a.nqb + qb] = t;
+  }
 }
 
 // ------------------------------------------------------------------ bf16 column sums
@@ -267,7 +283,7 @@ attn_colsum_bf16(AttnArgs a) {
   constexpr int QS = DH + 8;
   constexpr int NQC = QT * DH / 8 / 256;
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][QT * QS];
-  __shared__ float Ls[2][QT];
+  __shared__ __attribute__((aligned(16))) float Ls[2][QT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, col = lane & 31;
@@ -290,7 +306,7 @@ attn_colsum_bf16(AttnArgs a) {
       kf[t][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(K + int64_t(key) * DH + 16 * kk + 8 * G));
   }
   const float sc = kLog2e / sqrtf(float(DH));
-  float acc[2] = {0.0f, 0.0f};
+  float acc[2][4] = {};
 
   const int qstart = CAUSAL ? k0 : 0;
   const int ntiles = qstart < n ? int(ceil_div(n - qstart, QT)) : 0;
@@ -338,29 +354,34 @@ attn_colsum_bf16(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) st[t] = mfma32x32x16(qa, kf[t][kk], st[t]);
       }
-      // st[t][r]: query qt0 + 32u + 8(r/4) + 4G + r%4, key kw + 32t + col
+      // st[t][r]: query qt0 + 32u + 8(r/4) + 4G + r%4, key kw + 32t + col;
+      // register r adds into partial sum r%4 (four independent chains)
       const int qa = qt0 + 32 * u;
       const bool need_mask = (qa + 31 >= n) || (CAUSAL && qa < kw + 64);
+      float4 l4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        l4[q] = *reinterpret_cast<const float4*>(&Ls[buf][32 * u + 8 * q + 4 * G]);
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ql = 32 * u + 8 * (r >> 2) + 4 * G + (r & 3);
           const int qi = qt0 + ql;
-          const float l2 = Ls[buf][ql];
+          const float l2 = l4[r >> 2][r & 3];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int key = kw + 32 * t + col;
             const float p = fast_exp2(fmaf(st[t][r], sc, -l2));
             const bool keep = qi < n && (!CAUSAL || key <= qi);
-            acc[t] += keep ? p : 0.0f;
+            acc[t][r & 3] += keep ? p : 0.0f;
           }
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float l2 = Ls[buf][32 * u + 8 * (r >> 2) + 4 * G + (r & 3)];
+          const float l2 = l4[r >> 2][r & 3];
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] += fast_exp2(fmaf(st[t][r], sc, -l2));
+          for (int t = 0; t < 2; ++t) acc[t][r & 3] += fast_exp2(fmaf(st[t][r], sc, -l2));
         }
       }
     }
@@ -369,7 +390,7 @@ attn_colsum_bf16(AttnArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const float v = acc[t] + __shfl_xor(acc[t], 32, 64);
+    const float v = xor32_sum((acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]));
     const int key = kw + 32 * t + col;
     if (G == 0 && key < n) a.colsum[bs * n_pad + key] = v;
   }
@@ -485,8 +506,12 @@ importance_kernel(AttnArgs a) {
 
 template <int DH, bool CAUSAL>
 int run_bf16(const AttnArgs& a, hipStream_t stream) {
-  const dim3 g1(unsigned(ceil_div(a.n, kAttnQBlock)), a.h_kept, a.batch);
-  SPATTEN_TIMED("attn_fwd", stream, attn_fwd_bf16<DH, CAUSAL><<<g1, 256, 0, stream>>>(a));
+  // 32 queries per wave: more resident waves hide the MFMA -> softmax ->
+  // MFMA latency chain better than larger per-wave tiles
+  constexpr int QB = attn_qblock(DH), NU = 1, MINW = DH == 64 ? 3 : 1;
+  const dim3 g1(unsigned(ceil_div(a.n, QB)), a.h_kept, a.batch);
+  SPATTEN_TIMED("attn_fwd", stream,
+                attn_fwd_bf16<DH, CAUSAL, NU, MINW><<<g1, 2 * QB / NU, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
   const dim3 g2(unsigned(ceil_div(a.n, kAttnKBlock)), a.h_kept, a.batch);
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_bf16<DH, CAUSAL><<<g2, 256, 0, stream>>>(a));

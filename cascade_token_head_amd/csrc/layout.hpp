@@ -19,9 +19,11 @@ namespace spatten {
 // Prefill token rows of Q, K, V^T are padded per (sequence, head) to this
 // multiple so attention tiles never read past a head's slab.
 constexpr int kTokPad = 256;
-// Prefill attention: queries per workgroup in the forward (O, LSE) kernel
-// and keys per workgroup in the column-sum kernel (bf16 MFMA path).
-constexpr int kAttnQBlock = 256;
+// Prefill attention (bf16 MFMA path): queries per workgroup in the forward
+// (O, LSE) kernel - 32 per wave; 128 for head dim 64, 256 (eight waves
+// sharing each K/V tile) for larger heads - and keys per workgroup in the
+// column-sum kernel.
+SPATTEN_HD constexpr int attn_qblock(int dh) { return dh == 64 ? 128 : 256; }
 constexpr int kAttnKBlock = 256;
 // fp32 attention: query rows per workgroup.
 constexpr int kAttnF32Rows = 8;
@@ -51,7 +53,7 @@ inline PrefillWs prefill_ws(const spatten_layer_desc& d) {
   const int64_t B = d.batch, n = d.n_tokens, h = d.n_heads_kept, dh = d.head_dim;
   const size_t es = dtype_bytes(d.dtype);
   w.n_pad = round_up(n, kTokPad);
-  const int64_t rows = d.dtype == SPATTEN_BF16 ? kAttnQBlock : kAttnF32Rows;
+  const int64_t rows = d.dtype == SPATTEN_BF16 ? attn_qblock(d.head_dim) : kAttnF32Rows;
   w.nqb = ceil_div(n, rows);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };

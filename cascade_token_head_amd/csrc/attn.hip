@@ -31,6 +31,28 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Workgroup i runs on XCD i % 8. Attention grids are 1-D over (block,
+// head, sequence) with the block index fastest; each XCD takes a contiguous
+// run of that order, so the blocks of one head run on one XCD together and
+// re-read that head's K/V (forward) or Q (column sums) from its own L2.
+struct XcdItem {
+  bool valid;
+  int blk, s, b;
+};
+__device__ __forceinline__ XcdItem xcd_item(int nblk, int h, int batch) {
+  const int total = nblk * h * batch;
+  const int per = (total + 7) / 8;
+  const int t = (int(blockIdx.x) & 7) * per + (int(blockIdx.x) >> 3);
+  XcdItem it;
+  it.valid = t < total;
+  it.blk = t % nblk;
+  it.s = (t / nblk) % h;
+  it.b = t / (nblk * h);
+  return it;
+}
+
+inline unsigned xcd_grid(int64_t total) { return unsigned(8 * ((total + 7) / 8)); }
+
 // ------------------------------------------------------------------ bf16 forward
 
 // NU 32-query groups per wave; a workgroup covers QB queries with
@@ -55,8 +77,12 @@ attn_fwd_bf16(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, col = lane & 31;
-  const int b = blockIdx.z, s = blockIdx.y;
-  const int qb = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+  const int nqb_grid = int(ceil_div(a.n, QB));
+  const XcdItem item = xcd_item(nqb_grid, a.h_kept, a.batch);
+  if (!item.valid) return;
+  const int b = item.b, s = item.s;
+  // causal: the longest rows (last query blocks) first
+  const int qb = CAUSAL ? nqb_grid - 1 - item.blk : item.blk;
   const int q0 = qb * QB;
   const int wq0 = q0 + QW * wave;        // first query of this wave
   const int n = a.n, n_pad = a.n_pad;
@@ -287,8 +313,10 @@ attn_colsum_bf16(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, col = lane & 31;
-  const int b = blockIdx.z, s = blockIdx.y;
-  const int k0 = blockIdx.x * kAttnKBlock;
+  const XcdItem item = xcd_item(int(ceil_div(a.n, kAttnKBlock)), a.h_kept, a.batch);
+  if (!item.valid) return;
+  const int b = item.b, s = item.s;
+  const int k0 = item.blk * kAttnKBlock;
   const int n = a.n, n_pad = a.n_pad;
   const int64_t bs = int64_t(b) * a.h_kept + s;
   const bf16_t* Q = static_cast<const bf16_t*>(a.q) + bs * n_pad * DH;
@@ -509,11 +537,11 @@ int run_bf16(const AttnArgs& a, hipStream_t stream) {
   // 32 queries per wave: more resident waves hide the MFMA -> softmax ->
   // MFMA latency chain better than larger per-wave tiles
   constexpr int QB = attn_qblock(DH), NU = 1, MINW = DH == 64 ? 3 : 1;
-  const dim3 g1(unsigned(ceil_div(a.n, QB)), a.h_kept, a.batch);
+  const dim3 g1(xcd_grid(ceil_div(a.n, QB) * a.h_kept * a.batch));
   SPATTEN_TIMED("attn_fwd", stream,
                 attn_fwd_bf16<DH, CAUSAL, NU, MINW><<<g1, 2 * QB / NU, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
-  const dim3 g2(unsigned(ceil_div(a.n, kAttnKBlock)), a.h_kept, a.batch);
+  const dim3 g2(xcd_grid(ceil_div(a.n, kAttnKBlock) * a.h_kept * a.batch));
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_bf16<DH, CAUSAL><<<g2, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
   const dim3 g3(unsigned(ceil_div(a.n, 256)), a.batch);

@@ -232,15 +232,19 @@ gemm_tile_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BKT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Workgroup i runs on XCD i % 8. Each XCD takes one contiguous run of the
-  // column-fastest tile order, so the row blocks of A it reads stay in its
-  // own L2 while it sweeps the weight tiles, and A crosses from HBM once.
+  // Workgroup i runs on XCD i % 8, and each XCD takes one contiguous run of
+  // a grouped tile order: groups of GM row tiles, swept column by column.
+  // The ~64 tiles an XCD holds at once then span GM row blocks of A and
+  // 64 / GM weight tiles, which fit its 4 MB L2 together.
+  constexpr int GM = 8;
   const int ntx = int(ceil_div(p.N, BN));
   const int total = ntx * p.tiles_y;
   const int per_xcd = int(ceil_div(total, 8));
   const int t = (int(blockIdx.x) & 7) * per_xcd + (int(blockIdx.x) >> 3);
   if (t >= total) return;
-  const int tile_y = t / ntx, n0 = (t - tile_y * ntx) * BN;
+  const int grp = t / (GM * ntx), in_grp = t - grp * (GM * ntx);
+  const int rows_g = min(GM, p.tiles_y - grp * GM);
+  const int tile_y = grp * GM + in_grp % rows_g, n0 = (in_grp / rows_g) * BN;
   const int b_tile = p.seq_tiled ? tile_y / p.mt_per_seq : 0;
   const int kc = tid & 7;  // 16-byte chunk along k this thread loads
 

@@ -1,0 +1,137 @@
+"""HBM traffic of a kernel from rocprofv3 counter runs.
+
+    # a plain device-to-device copy of known size, for the counter scale
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o copy_fetch -- \\
+        python3 -m cascade_token_head_amd.traffic copy --mib 1024
+    # the same with WRITE_SIZE, then both counters on the benchmark command
+    python3 -m cascade_token_head_amd.traffic summarize --label qkv_gemm \\
+        --workload bert_base --kernel-regex 'gemm_tile_kernel<0,' \\
+        --fetch run_fetch.csv --write run_write.csv \\
+        --copy-fetch copy_fetch.csv --copy-write copy_write.csv \\
+        --command '...' --out profiles/
+
+FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch. Each is scaled by
+known bytes / counted bytes of the copy kernel (so a counter that reads
+high or low on this part is corrected), then averaged per launch of the
+kernel. The result, with the hash of the kernel sources it was taken on,
+goes to profiles/pmc_<label>_<workload>.json (read by bench.py) and a short
+.md summary beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "cascade_token_head_amd", "csrc")
+COPY_KERNEL = r"copyBuffer"
+
+
+def source_sha1() -> str:
+    """Hash of every kernel source file (the same hash bench.py checks)."""
+    h = hashlib.sha1()
+    for fn in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()
+
+
+def per_dispatch(path: str, counter: str, kernel_regex: str):
+    """{dispatch id: counter value} for kernels whose name matches."""
+    rx = re.compile(kernel_regex)
+    vals = defaultdict(float)
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter or not rx.search(row.get("Kernel_Name", "")):
+                continue
+            vals[row.get("Dispatch_Id") or row.get("Correlation_Id")] += float(row["Counter_Value"])
+    return dict(vals)
+
+
+def copy_main(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}))
+
+
+def summarize_main(a) -> None:
+    copy_bytes = a.copy_mib * (1 << 20)
+    cf = per_dispatch(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
+    cw = per_dispatch(a.copy_write, "WRITE_SIZE", COPY_KERNEL)
+    # the copy kernel moves copy_bytes in and out per dispatch; take the
+    # dispatches that carry the bulk (fills and small copies excluded)
+    big_f = [v for v in cf.values() if v * 1024 > 0.5 * copy_bytes]
+    big_w = [v for v in cw.values() if v * 1024 > 0.5 * copy_bytes]
+    if not big_f or not big_w:
+        sys.exit("no copy dispatch of the expected size in the calibration runs")
+    f_scale = copy_bytes / (sum(big_f) / len(big_f) * 1024)
+    w_scale = copy_bytes / (sum(big_w) / len(big_w) * 1024)
+    kf = per_dispatch(a.fetch, "FETCH_SIZE", a.kernel_regex)
+    kw = per_dispatch(a.write, "WRITE_SIZE", a.kernel_regex)
+    if not kf or not kw:
+        sys.exit("kernel %r not found in the counter runs" % a.kernel_regex)
+    fetch = sum(kf.values()) / len(kf) * 1024 * f_scale
+    write = sum(kw.values()) / len(kw) * 1024 * w_scale
+    rec = {"kernel": a.label, "workload": a.workload, "kernel_regex": a.kernel_regex,
+           "dispatches": len(kf), "fetch_bytes_per_launch": round(fetch),
+           "write_bytes_per_launch": round(write),
+           "hbm_bytes_per_launch": round(fetch + write),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "copy_bytes": copy_bytes, "source_sha1": source_sha1(), "command": a.command}
+    os.makedirs(a.out, exist_ok=True)
+    base = os.path.join(a.out, "pmc_%s_%s" % (a.label, a.workload))
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    with open(base + ".md", "w") as f:
+        f.write("# HBM traffic: %s on %s\n\n" % (a.label, a.workload))
+        f.write("Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one rocprofv3 "
+                "--pmc run each, scaled by known/counted bytes of a %d MiB device copy.\n\n"
+                % a.copy_mib)
+        f.write("| quantity | value |\n|---|---|\n")
+        for k in ("dispatches", "fetch_bytes_per_launch", "write_bytes_per_launch",
+                  "hbm_bytes_per_launch", "fetch_scale", "write_scale"):
+            f.write("| %s | %s |\n" % (k, rec[k]))
+        f.write("\nkernel symbol regex: `%s`\n\nsource sha1: `%s`\n\ncommand:\n\n```\n%s\n```\n"
+                % (a.kernel_regex, rec["source_sha1"], a.command))
+    print(json.dumps(rec))
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    s = sub.add_parser("summarize")
+    s.add_argument("--label", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--kernel-regex", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--copy-fetch", required=True)
+    s.add_argument("--copy-write", required=True)
+    s.add_argument("--copy-mib", type=int, default=1024)
+    s.add_argument("--command", default="")
+    s.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    a = ap.parse_args()
+    if a.cmd == "copy":
+        copy_main(a.mib)
+    else:
+        summarize_main(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -314,20 +314,33 @@ gemm_tile_kernel(GemmParams p) {
   const int fsw = (fr >> 1) & 7;
 
   auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 af[2][TI], bfr[2][TJ];
+    auto frag = [&](int kk, int slot) {
       const int ch = ((2 * kk + G) ^ fsw) * 8;
-      bf16x8 af[TI], bfr[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&As[buf][(wm + 32 * i + fr) * BKT + ch]));
+        af[slot][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&As[buf][(wm + 32 * i + fr) * BKT + ch]));
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Bs[buf][(wn + 32 * j + fr) * BKT + ch]));
+        bfr[slot][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Bs[buf][(wn + 32 * j + fr) * BKT + ch]));
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) frag(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = mfma32x32x16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
+    }
+    // keep that order through scheduling: reads of slice 0, then per slice
+    // the next slice's reads ahead of this slice's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, TI + TJ, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, TI + TJ, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
     }
   };
 
@@ -350,7 +363,10 @@ gemm_tile_kernel(GemmParams p) {
     compute(1);
     __syncthreads();
   }
-  if (KT & 1) compute(0);  // the last (even) tile, staged by the final odd step
+  if (KT & 1) {  // the last (even) tile, staged by the final odd step
+    compute(0);
+    __syncthreads();  // the epilogue stage reuses As
+  }
 
   // ---- epilogue: each 32 x 32 MFMA block goes through a 2 KB per-wave LDS
   // stage (row-major, or transposed for V^T) and leaves as 16-byte stores.

@@ -44,6 +44,9 @@ PREFILL_CASES = [
     ("bf16", 2, 333, 6, 6, 64, True),
     ("bf16", 1, 300, 4, 3, 128, True),
     ("bf16", 2, 257, 4, 4, 128, False),
+    # model dim 192 and 3 kept heads: odd k-tile counts in both projections
+    ("bf16", 2, 300, 3, 3, 64, False),
+    ("bf16", 1, 200, 5, 3, 64, True),
 ]
 
 

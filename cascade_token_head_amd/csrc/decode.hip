@@ -63,6 +63,19 @@ __device__ __forceinline__ float msb_val(uint32_t w, int e) {
   return float(mn >= 8 ? mn - 16 : mn);
 }
 
+// The 8 signed nibbles of a word, each offset by +8 (so 0..15): flipping a
+// nibble's top bit maps two's-complement -8..7 to 0..15, and the even and
+// odd nibbles then convert straight from bytes. u[e] = nibble e + 8.
+__device__ __forceinline__ void nibbles_plus8(uint32_t w, float* u) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u[2 * k] = float((lo >> (8 * k)) & 0xffu);
+    u[2 * k + 1] = float((hi >> (8 * k)) & 0xffu);
+  }
+}
+
 // grid (nchunk, B); block = (D/8) * R threads, R rows of the chunk at a time
 template <int KIND>
 __global__ void __launch_bounds__(256)
@@ -109,6 +122,13 @@ decode_partial(DecodeArgs a) {
     }
   }
   const float sc = kLog2e / sqrtf(float(dh));
+  // MSB dots use nibble + 8: sum q (n + 8) - 8 sum q
+  float qsum8 = 0.0f;
+  if constexpr (KIND == kMsb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qsum8 += q[e];
+    qsum8 *= 8.0f;
+  }
 
   // Rows past the cache end are read at row lc-1 (a valid address) and
   // masked: their score is -inf, so their weight in P V is exactly 0.
@@ -137,9 +157,11 @@ decode_partial(DecodeArgs a) {
           d = fmaf(q[2 * e + 1], __uint_as_float(raw[u][e] & 0xffff0000u), d);
         }
       } else {
+        float nv[8];
+        nibbles_plus8(raw[u], nv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(q[e], msb_val(raw[u], e), d);
-        d *= 16.0f;
+        for (int e = 0; e < 8; ++e) d = fmaf(q[e], nv[e], d);
+        d = (d - qsum8) * 16.0f;
       }
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
@@ -189,6 +211,7 @@ decode_partial(DecodeArgs a) {
   __syncthreads();
   // ---- P V for this thread's column group
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float wsum = 0.0f;  // MSB path: sum of weights, to remove the +8 offset
   for (int t0 = 0; t0 < kpt; t0 += KB) {
     if (t0 > 0) load_v(t0);
 #pragma unroll
@@ -203,10 +226,17 @@ decode_partial(DecodeArgs a) {
         }
       } else {
         const float w = 16.0f * p * vs[u];
+        float nv[8];
+        nibbles_plus8(vraw[u], nv);
+        wsum += w;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, msb_val(vraw[u], e), acc[e]);
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, nv[e], acc[e]);
       }
     }
+  }
+  if constexpr (KIND == kMsb) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(-8.0f, wsum, acc[e]);
   }
   // reduce the R row phases of each column group
   if (r > 0) {

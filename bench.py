@@ -114,6 +114,30 @@ def _cpu_baseline(cfg, inputs, budget_s: float):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     done, t0 = 0, time.perf_counter()
+    if cfg.kind == "prefill" and cfg.tokens[0] > 4096:
+        # A whole sequence is hours of fp64 work: time the oracle's first
+        # layer on causal prefixes of sequence 0 (rows of a causal prefix see
+        # only its own keys), doubling the prefix until the budget is spent.
+        # Later rows of the full layer see more keys, so this rate is an
+        # upper bound on the oracle's rate for the whole workload.
+        assert cfg.causal
+        W = inputs["layers"][0]
+        heads = list(range(cfg.heads[0]))
+        rows, el, S = 0, 0.0, 256
+        while S <= cfg.tokens[0]:
+            ts = time.perf_counter()
+            R.prefill_layer(inputs["x"][0, :S], W, heads, cfg.head_dim, True, True)
+            dt = time.perf_counter() - ts
+            rows, el = S, dt
+            if time.perf_counter() - t0 + 2.2 * dt > budget_s:
+                break
+            S *= 2
+        sample = ("layer 1 of sequence 0 on its first %d tokens (a causal prefix), all %d heads; "
+                  "rows of the full %d-token layer see up to %dx more keys, so this is an upper "
+                  "bound on the oracle's rate" % (rows, cfg.heads[0], cfg.tokens[0],
+                                                  cfg.tokens[0] // rows))
+        return {"value": rows / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": sample, "seconds": round(el, 2)}
     if cfg.kind == "prefill":
         per_seq = sum(cfg.tokens)
         while done < cfg.batch:

@@ -33,6 +33,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int CH = kDecChunk;  // cache entries per chunk
+// one 32-lane half-wave holds a head's chunk statistics, and the recompute
+// kernel maps its 64 threads to 32 rows x 2 halves of a head
+static_assert(CH == 32, "decode kernels are written for 32-row chunks");
 constexpr int KB = 16;         // rows per load batch
 constexpr int kMaxHeads = 32;
 constexpr int kRecomputeSlots = 128;

@@ -165,13 +165,14 @@ attn_fwd_bf16(AttnArgs a) {
   // the C layout then gives lane group G the keys 16G .. 16G+15 in order.
   const int kperm = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
 
-  // One 32-key sub-tile (keys k0 + 32t ..) for both query halves: S^T by
-  // MFMA, online softmax in registers, then O^T += V^T P^T. MASKED is set
-  // only for sub-tiles that cross the sequence end or the causal diagonal,
-  // so interior sub-tiles carry no masking code.
-  auto subtile = [&](auto masked_tag, int buf, int k0, int t) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    floatx16 st[NU];
+  // A 32-key sub-tile (keys k0 + 32t ..) runs in two parts: S^T by MFMA
+  // (qk), then online softmax in registers and O^T += V^T P^T (soft_pv).
+  // The tile loop issues both sub-tiles' qk before the first soft_pv, so
+  // the second sub-tile's MFMAs execute under the first one's softmax VALU
+  // work, and the first one's P V MFMAs under the second one's softmax.
+  // Masking is applied only to sub-tiles that cross the sequence end or the
+  // causal diagonal, so interior sub-tiles carry no masking code.
+  auto qk = [&](int buf, int t, floatx16* st) {
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -183,18 +184,20 @@ attn_fwd_bf16(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) st[u] = mfma32x32x16(kf, qf[u][kk], st[u]);
     }
-    if constexpr (MASKED) {
+  };
+  auto mask = [&](floatx16* st, int k0, int t) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int my_q = wq0 + 32 * u + col;
+    for (int u = 0; u < NU; ++u) {
+      const int my_q = wq0 + 32 * u + col;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * t + 16 * G + i;
-          const bool m = key >= n || (CAUSAL && key > my_q);
-          st[u][i] = m ? -INFINITY : st[u][i];
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * t + 16 * G + i;
+        const bool m = key >= n || (CAUSAL && key > my_q);
+        st[u][i] = m ? -INFINITY : st[u][i];
       }
     }
+  };
+  auto soft_pv = [&](floatx16* st, int buf, int t) {
     bf16x8 pb[2][NU];  // [s2][u]
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -248,16 +251,18 @@ attn_fwd_bf16(AttnArgs a) {
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1, k0 = it * KT;
     if (it + 1 < ntiles) gload(it + 1);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int ks0 = k0 + 32 * t;
-      if (wave_live && ks0 < wave_kend) {
-        const bool need_mask = (ks0 + 32 > n) || (CAUSAL && ks0 + 31 > wq0);
-        if (need_mask)
-          subtile(std::true_type{}, buf, k0, t);
-        else
-          subtile(std::false_type{}, buf, k0, t);
-      }
+    const bool live0 = wave_live && k0 < wave_kend;
+    const bool live1 = wave_live && k0 + 32 < wave_kend;
+    floatx16 st0[NU], st1[NU];
+    if (live0) qk(buf, 0, st0);
+    if (live1) qk(buf, 1, st1);
+    if (live0) {
+      if ((k0 + 32 > n) || (CAUSAL && k0 + 31 > wq0)) mask(st0, k0, 0);
+      soft_pv(st0, buf, 0);
+    }
+    if (live1) {
+      if ((k0 + 64 > n) || (CAUSAL && k0 + 63 > wq0)) mask(st1, k0, 1);
+      soft_pv(st1, buf, 1);
     }
     if (it + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();

@@ -2,7 +2,8 @@
 // k-th largest as a threshold, filter, then eliminate the dropped entries
 // while keeping input order).
 //
-// One workgroup per row. Scores map to order-preserving uint32 keys (larger
+// One workgroup per row; rows of up to 32 keys per thread are read once into
+// registers. Scores map to order-preserving uint32 keys (larger
 // value -> larger key; -0.0 below +0.0). Four MSD passes of 8 bits find the
 // exact key T of the k-th ranked element with LDS histograms; wave ballots
 // fold lanes that share a digit into one LDS atomic. A final pass in index
@@ -47,6 +48,9 @@ __device__ __forceinline__ int wave_offsets(int wave_count, int wave, int nwaves
   return off;
 }
 
+// PT > 0: the row is read once into registers (PT keys per thread, n <=
+// PT * blockDim); PT == 0: every pass re-reads the row.
+template <int PT>
 __global__ void __launch_bounds__(1024)
 topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, int k,
                   int32_t* __restrict__ out_idx, float* __restrict__ kth_out) {
@@ -59,6 +63,22 @@ topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, i
   const float* s = scores + int64_t(b) * row_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+  const int iters = (n + nthreads - 1) / nthreads;
+
+  uint32_t keys[PT > 0 ? PT : 1];
+  if constexpr (PT > 0) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + j * nthreads;
+      keys[j] = i < n ? order_key(s[i]) : 0u;
+    }
+  }
+  auto key_at = [&](int j, int i) -> uint32_t {
+    if constexpr (PT > 0)
+      return keys[j];
+    else
+      return order_key(s[i]);
+  };
 
   uint32_t prefix = 0, mask = 0;
   int krem = k;
@@ -66,12 +86,14 @@ topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, i
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < 256; i += nthreads) hist[i] = 0;
     __syncthreads();
-    for (int base = 0; base < n; base += nthreads) {
-      const int i = base + tid;
+#pragma unroll
+    for (int j = 0; j < (PT > 0 ? PT : 1 << 20); ++j) {
+      if (j >= iters) break;  // uniform
+      const int i = tid + j * nthreads;
       bool cand = false;
       uint32_t dig = 0;
       if (i < n) {
-        const uint32_t key = order_key(s[i]);
+        const uint32_t key = key_at(j, i);
         cand = (key & mask) == prefix;
         dig = (key >> shift) & 255u;
       }
@@ -128,10 +150,12 @@ topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, i
   // ordered selection: key > T, or key == T among the first krem ties
   int32_t* out = out_idx + int64_t(b) * k;
   int run_sel = 0, run_eq = 0;
-  for (int base = 0; base < n && run_sel < k; base += nthreads) {
-    const int i = base + tid;
+#pragma unroll
+  for (int j = 0; j < (PT > 0 ? PT : 1 << 20); ++j) {
+    if (j >= iters || run_sel >= k) break;  // uniform
+    const int i = tid + j * nthreads;
     uint32_t key = 0;
-    if (i < n) key = order_key(s[i]);
+    if (i < n) key = key_at(j, i);
     const bool gt = i < n && key > T;
     const bool eq = i < n && key == T;
     const uint64_t eqm = __ballot(eq);
@@ -157,9 +181,16 @@ int launch_topk(const float* scores, int batch, int n, int64_t row_stride, int k
   int threads = 256;
   if (n > 2048) threads = 512;
   if (n > 8192) threads = 1024;
-  SPATTEN_TIMED("topk", stream,
-                topk_radix_kernel<<<dim3(batch), dim3(threads), 0, stream>>>(
-                    scores, n, row_stride, k, out_idx, kth));
+  const dim3 grid(batch), block(threads);
+  if (n <= 8 * threads)
+    SPATTEN_TIMED("topk", stream, topk_radix_kernel<8><<<grid, block, 0, stream>>>(
+                                      scores, n, row_stride, k, out_idx, kth));
+  else if (n <= 32 * threads)
+    SPATTEN_TIMED("topk", stream, topk_radix_kernel<32><<<grid, block, 0, stream>>>(
+                                      scores, n, row_stride, k, out_idx, kth));
+  else
+    SPATTEN_TIMED("topk", stream, topk_radix_kernel<0><<<grid, block, 0, stream>>>(
+                                      scores, n, row_stride, k, out_idx, kth));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }

@@ -61,6 +61,9 @@ inline unsigned xcd_grid(int64_t total) { return unsigned(8 * ((total + 7) / 8))
 template <int DH, bool CAUSAL, int NU, int MINW>
 __global__ void __launch_bounds__(2 * attn_qblock(DH) / NU, MINW)
 attn_fwd_bf16(AttnArgs a) {
+  // dh 128: K/V loads run two tiles ahead (the register budget allows a
+  // second staging set); dh 64 keeps one set to stay at three waves/SIMD
+  constexpr bool DEEP = DH == 128;
   constexpr int QB = attn_qblock(DH);
   constexpr int NT = 2 * QB / NU;  // threads per workgroup
   constexpr int WAVES = NT / 64;
@@ -121,19 +124,21 @@ attn_fwd_bf16(AttnArgs a) {
   const int ntiles = int(ceil_div(kend, KT));
   const int wave_kend = CAUSAL ? min(n, wq0 + QW) : n;   // keys this wave can see
 
-  u32x4 rk[NKC], rv[NVC];
-  auto gload = [&](int it) {
+  // register staging: one set, or two when loads run two tiles ahead
+  constexpr int NSET = DEEP ? 2 : 1;
+  u32x4 rk[NSET][NKC], rv[NSET][NVC];
+  auto gload = [&](int set, int it) {
     const int k0 = it * KT;
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
       const int c = tid + NT * i;
-      rk[i] = *reinterpret_cast<const u32x4*>(K + int64_t(k0) * DH + c * 8);
+      rk[set][i] = *reinterpret_cast<const u32x4*>(K + int64_t(k0) * DH + c * 8);
     }
 #pragma unroll
     for (int i = 0; i < NVC; ++i) {
       const int c = tid + NT * i;
       const int row = c >> 3, k8 = (c & 7) * 8;
-      rv[i] = *reinterpret_cast<const u32x4*>(VT + int64_t(row) * n_pad + k0 + k8);
+      rv[set][i] = *reinterpret_cast<const u32x4*>(VT + int64_t(row) * n_pad + k0 + k8);
       // keys past the end get exact zeros (their probabilities are 0, and
       // the padding itself is never written)
       if (k0 + KT > n) {
@@ -141,23 +146,23 @@ attn_fwd_bf16(AttnArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + k8 + 2 * e;
           const uint32_t lo = key < n ? 0xffffu : 0u, hi = key + 1 < n ? 0xffff0000u : 0u;
-          rv[i][e] &= lo | hi;
+          rv[set][i][e] &= lo | hi;
         }
       }
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int set, int buf) {
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
       const int c = tid + NT * i;
       const int row = c / (DH / 8), c8 = (c % (DH / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KS + c8]) = rk[i];
+      *reinterpret_cast<u32x4*>(&Ks[buf][row * KS + c8]) = rk[set][i];
     }
 #pragma unroll
     for (int i = 0; i < NVC; ++i) {
       const int c = tid + NT * i;
       const int row = c >> 3, k8 = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&Vs[buf][row * VS + k8]) = rv[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][row * VS + k8]) = rv[set][i];
     }
   };
 
@@ -245,12 +250,7 @@ attn_fwd_bf16(AttnArgs a) {
       }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1, k0 = it * KT;
-    if (it + 1 < ntiles) gload(it + 1);
+  auto tile = [&](int buf, int k0) {
     const bool live0 = wave_live && k0 < wave_kend;
     const bool live1 = wave_live && k0 + 32 < wave_kend;
     floatx16 st0[NU], st1[NU];
@@ -264,8 +264,41 @@ attn_fwd_bf16(AttnArgs a) {
       if ((k0 + 64 > n) || (CAUSAL && k0 + 63 > wq0)) mask(st1, k0, 1);
       soft_pv(st1, buf, 1);
     }
-    if (it + 1 < ntiles) sstore(buf ^ 1);
+  };
+
+  if constexpr (!DEEP) {
+    // loads one tile ahead: fetched during tile it, stored after it
+    gload(0, 0);
+    sstore(0, 0);
     __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < ntiles) gload(0, it + 1);
+      tile(buf, it * KT);
+      if (it + 1 < ntiles) sstore(0, buf ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // loads two tiles ahead: register set s holds the tile stored at the
+    // start of the step that computes from the other LDS buffer
+    gload(0, 0);
+    sstore(0, 0);
+    if (ntiles > 1) gload(0, 1);
+    if (ntiles > 2) gload(1, 2);
+    __syncthreads();
+    auto step = [&](int it, int set) {
+      const int buf = it & 1;
+      if (it + 1 < ntiles) sstore(set, buf ^ 1);
+      if (it + 3 < ntiles) gload(set, it + 3);
+      tile(buf, it * KT);
+      __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
+      step(it, 0);
+      step(it + 1, 1);
+    }
+    if (it < ntiles) step(it, 0);
   }
 
   float gsum = 0.0f;

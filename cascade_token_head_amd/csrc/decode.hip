@@ -93,7 +93,9 @@ decode_partial(DecodeArgs a) {
   const int c = tid % V, r = tid / V;
   const int h = (8 * c) / dh;
   const int j0 = chunk * CH;
-  const int nwaves = blockDim.x >> 6;
+  // a partial last wave (e.g. 160 threads for 5 heads) takes part in the
+  // per-head statistics loop too, so it must count in the stride
+  const int nwaves = (blockDim.x + 63) >> 6;
   const int kpt = CH / R;  // rows per thread
   const int64_t rowb = int64_t(b) * a.cap;
 

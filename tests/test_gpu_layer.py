@@ -47,6 +47,11 @@ PREFILL_CASES = [
     # model dim 192 and 3 kept heads: odd k-tile counts in both projections
     ("bf16", 2, 300, 3, 3, 64, False),
     ("bf16", 1, 200, 5, 3, 64, True),
+    # degenerate shapes: one token, one kept head, tokens fewer than a tile
+    ("bf16", 1, 1, 4, 1, 64, False),
+    ("bf16", 2, 1, 4, 4, 128, True),
+    ("bf16", 3, 17, 2, 1, 64, True),
+    ("f32", 1, 1, 2, 2, 32, True),
 ]
 
 
@@ -113,7 +118,13 @@ def _decode_setup(rng, B, H, dh, L0, cap, quantized):
 
 @pytest.mark.parametrize("B,H,L0,quantized,thr", [
     (3, 12, 100, False, 0.0), (2, 12, 1024, False, 0.0), (4, 16, 300, True, 0.1),
-    (2, 16, 257, True, 0.0), (2, 16, 257, True, 1.01), (64, 12, 130, False, 0.0)])
+    (2, 16, 257, True, 0.0), (2, 16, 257, True, 1.01), (64, 12, 130, False, 0.0),
+    # empty cache before the step (the new row is the only key)
+    (1, 12, 0, False, 0.0), (2, 16, 0, True, 0.1),
+    # the most heads the decode path takes, a new row opening a 32-row chunk
+    (2, 32, 64, False, 0.0), (2, 32, 96, True, 0.1),
+    # one head; an odd head count with a partial last wave
+    (3, 1, 40, False, 0.0), (1, 5, 31, True, 0.05)])
 def test_decode_layer(S, B, H, L0, quantized, thr):
     print("decode case", B, H, L0, quantized, thr, flush=True)
     dh = 64

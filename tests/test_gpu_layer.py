@@ -124,7 +124,9 @@ def _decode_setup(rng, B, H, dh, L0, cap, quantized):
     # the most heads the decode path takes, a new row opening a 32-row chunk
     (2, 32, 64, False, 0.0), (2, 32, 96, True, 0.1),
     # one head; an odd head count with a partial last wave
-    (3, 1, 40, False, 0.0), (1, 5, 31, True, 0.05)])
+    (3, 1, 40, False, 0.0), (1, 5, 31, True, 0.05),
+    # batches past the 64-row decode projection kernel (tiled GEMM fallback)
+    (65, 12, 50, False, 0.0), (96, 16, 33, True, 0.1)])
 def test_decode_layer(S, B, H, L0, quantized, thr):
     print("decode case", B, H, L0, quantized, thr, flush=True)
     dh = 64

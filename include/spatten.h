@@ -86,7 +86,9 @@ typedef struct {
  *   in dtype. Quantized (progressive quantization, section III and
  *   "E. ... Progressive Quantization"): k_msb, k_lsb, v_msb, v_lsb are
  *   [B, cache_cap, D/2] u8 and k_scale, v_scale [B, cache_cap] fp32 as
- *   written by spatten_quantize_kv; each (b, h) row is scored with MSB-only
+ *   written by spatten_quantize_kv; this step's k and v rows are coded into
+ *   row cache_len of the planes and scales with that function's arithmetic
+ *   (bit for bit) before they are read; each (b, h) row is scored with MSB-only
  *   values (scale*16*msb) and, when its largest probability is below
  *   pq_threshold, recomputed with the full code scale*(16*msb + lsb) for
  *   both K and V. recompute (optional, [B, H] int32) receives 1 for
@@ -94,7 +96,9 @@ typedef struct {
  *   g is not used in decode and may be NULL. Decode needs head_dim 64,
  *   H <= 32, bf16 and every head kept.
  * head_idx: [B, h_kept] int32, strictly ascending head ids per sequence.
- * workspace: device scratch of *workspace_bytes bytes, 256-byte aligned.
+ * workspace: device scratch of *workspace_bytes bytes, 256-byte aligned;
+ *   its contents are overwritten by every call, so calls that share one
+ *   workspace must be ordered on one stream (or otherwise serialised).
  *   If workspace is NULL only *d is checked, the required size is stored in
  *   *workspace_bytes and SPATTEN_OK is returned without enqueuing anything
  *   (tensor pointers may then be NULL).

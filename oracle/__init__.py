@@ -27,7 +27,17 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       in tests/golden/.
   pq_head_attention   threshold 0 -> MSB-only attention; threshold > 1 ->
                       attention over the full int8 cache.
+  value_pruned_output one-hot V rows expose every kept probability (and
+                      thresholds at the m-th largest keep exactly m rows);
+                      threshold 0 -> torch attention; threshold > 1 -> 0;
+                      uniform rows at and just above 1/n.
+  prune_after_step    truth table for r = 0, 1, 3.
   run_prefill /       parity unpinned beyond the composition of the pinned
-  run_decode          parts (the pages print no worked example).
+  run_decode          parts (the pages print no worked example). Invariants
+                      checked: total importance per layer, value pruning
+                      leaves importance unchanged, every rolling cut keeps
+                      the largest entries (brute force over candidates) and
+                      never revives a pruned one, a budget that never cuts
+                      reproduces the plain run.
 """
 from . import spatten_ref, topk_engine  # noqa: F401

@@ -354,14 +354,29 @@ def run_prefill(cfg, inputs: dict, seqs=None,
     return out
 
 
+def value_pruned_output(p, V, tau: float):
+    """Local value pruning (section III, "Local Value Pruning"): once the
+    softmax has produced a head's probabilities p [Lc], the V rows whose
+    probability is below tau are dropped for this head only, so
+    o = sum over j with p_j >= tau of p_j V_j. The kept probabilities are
+    not renormalised (the softmax already normalised them) and the token
+    importance still takes every p_j. tau = 0 keeps every row. Returns
+    (o [dh], number of V rows kept)."""
+    keep = np.asarray(p) >= tau
+    return np.asarray(p)[keep] @ np.asarray(V, dtype=np.float64)[keep], int(keep.sum())
+
+
 def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: bool,
-                     threshold: float, decide: Optional[Callable] = None):
+                     threshold: float, decide: Optional[Callable] = None,
+                     v_threshold: float = 0.0):
     """Attention of one decode query q [H, dh] over every entry of a cache
     (no mask). Unquantized caches hold k, v [Lc, H, dh]; quantized ones the
-    packed planes and scales of K and V rows. Returns (o [H, dh],
-    p [H, Lc], recompute flags [H], MSB-pass max probability [H])."""
+    packed planes and scales of K and V rows. v_threshold > 0 applies local
+    value pruning to unquantized caches. Returns (o [H, dh], p [H, Lc],
+    recompute flags [H], MSB-pass max probability [H], V rows kept [H])."""
     H, dh = heads_n, head_dim
     if quantized:
+        assert v_threshold == 0.0, "value pruning is defined here for unquantized caches"
         Km = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], False).reshape(-1, H, dh)
         Kf = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], True).reshape(-1, H, dh)
         Vm = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], False).reshape(-1, H, dh)
@@ -373,6 +388,7 @@ def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: boo
     P = np.zeros((H, Lc))
     rec = np.zeros(H, dtype=bool)
     cmax = np.zeros(H)
+    kept = np.full(H, Lc, dtype=np.int64)
     for h in range(H):
         if quantized:
             dec = None if decide is None else (lambda c_, d_, h_=h: decide(h_, c_, d_))
@@ -380,16 +396,18 @@ def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: boo
                                                             Vf[:, h], threshold, dec)
         else:
             P[h] = softmax_rows((cache["k"][:, h] @ q[h]) / math.sqrt(dh))
-            O[h] = P[h] @ cache["v"][:, h]
-    return O, P, rec, cmax
+            O[h], kept[h] = value_pruned_output(P[h], cache["v"][:, h], v_threshold)
+    return O, P, rec, cmax, kept
 
 
 def decode_layer(x, w: dict, cache: dict, heads_n: int, head_dim: int, bf16: bool,
-                 quantized: bool, threshold: float, decide: Optional[Callable] = None):
+                 quantized: bool, threshold: float, decide: Optional[Callable] = None,
+                 v_threshold: float = 0.0):
     """One decode layer for one sequence. The new token's k and v are
     appended to the cache, then the query attends over every cache entry
     (no mask). Returns (x_new, p [H, Lc], recompute flags [H], MSB-pass max
-    probability [H]). decide(h, c, default) may override a PQ decision."""
+    probability [H], V rows kept [H]). decide(h, c, default) may override a
+    PQ decision."""
     H, dh = heads_n, head_dim
     x = np.asarray(x, dtype=np.float64)
     q = _store(x @ w["wq"].astype(np.float64), bf16).reshape(H, dh)
@@ -404,11 +422,20 @@ def decode_layer(x, w: dict, cache: dict, heads_n: int, head_dim: int, bf16: boo
     else:
         cache["k"] = np.concatenate([cache["k"], k.reshape(1, H, dh)], axis=0)
         cache["v"] = np.concatenate([cache["v"], v.reshape(1, H, dh)], axis=0)
-    O, P, rec, cmax = decode_attention(q, cache, H, dh, quantized, threshold, decide)
+    O, P, rec, cmax, kept = decode_attention(q, cache, H, dh, quantized, threshold, decide,
+                                             v_threshold)
     delta = np.zeros(x.shape[0])
     for h in range(H):
         delta += _store(O[h], bf16) @ w["wo"][h * dh:(h + 1) * dh, :].astype(np.float64)
-    return _store(x + delta, bf16), P, rec, cmax
+    return _store(x + delta, bf16), P, rec, cmax, kept
+
+
+def prune_after_step(cfg, s: int) -> bool:
+    """Whether the cache is pruned after 0-based step s: always after the
+    first step; with prune_every = r > 0 again after every r-th later step
+    (r = 1 re-prunes after every step, a rolling keep budget)."""
+    r = getattr(cfg, "prune_every", 0)
+    return s == 0 or (r > 0 and s % r == 0)
 
 
 def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
@@ -417,12 +444,24 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
     token per step against cached K/V. Token importance a accumulates the
     probabilities each cache entry receives, over heads, layers and steps;
     a new entry starts at 0. After every layer of step 1 has run, the cache
-    of every layer keeps topk(a over L0+1 entries, cache_keep) entries.
-    pq_adopt(b, s, l, h, c, default) may override a recompute decision."""
+    of every layer keeps topk(a over L0+1 entries, cache_keep) entries
+    (section II "Cascade pruning": a pruned token stays pruned); with
+    cfg.prune_every = r > 0 the same cut back to cache_keep entries is
+    repeated after every r-th later step, over the entries kept so far plus
+    the new ones. cfg.v_threshold > 0 adds local value pruning inside each
+    head's attention. pq_adopt(b, s, l, h, c, default) may override a
+    recompute decision.
+
+    Per sequence the result holds the step outputs, the final a, the first
+    selection (indices into the L0+1 entries), "kept_ids" after every step
+    (original entry ids, prior tokens 0..L0-1 and step s's token L0+s, in
+    cache order), "before_prune" (ids and a after each step, before its
+    cut), the recompute records and the V rows kept [step, layer, head]."""
     bf16 = cfg.dtype == "bf16"
     seqs = range(cfg.batch) if seqs is None else seqs
     steps = cfg.steps if steps is None else steps
     H, dh = cfg.n_heads, cfg.head_dim
+    vthr = getattr(cfg, "v_threshold", 0.0)
     out = {}
     for b in seqs:
         caches = []
@@ -438,30 +477,39 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
             else:
                 caches.append({"k": K0, "v": V0})
         a = np.zeros(cfg.cache_len)
-        xs, recs, sel = [], [], None
+        ids = np.arange(cfg.cache_len, dtype=np.int64)
+        xs, recs, kept, sel, kept_ids, pre = [], [], [], None, [], []
         for s in range(steps):
             x = np.asarray(inputs["x_steps"][s][b], dtype=np.float64)
             a = np.concatenate([a, [0.0]])
-            step_rec = []
+            ids = np.concatenate([ids, [cfg.cache_len + s]])
+            step_rec, step_kept = [], []
             for l in range(cfg.n_layers):
                 dec = None
                 if pq_adopt is not None:
                     dec = (lambda h_, c_, d_, b_=b, s_=s, l_=l: pq_adopt(b_, s_, l_, h_, c_, d_))
-                x, P, rec, cmax = decode_layer(x, inputs["layers"][l], caches[l], H, dh, bf16,
-                                               cfg.quantized, cfg.pq_threshold, dec)
+                x, P, rec, cmax, kv = decode_layer(x, inputs["layers"][l], caches[l], H, dh,
+                                                   bf16, cfg.quantized, cfg.pq_threshold, dec,
+                                                   vthr)
                 a = a + P.sum(axis=0)
                 step_rec.append((rec, cmax))
+                step_kept.append(kv)
             xs.append(x)
             recs.append(step_rec)
-            if s == 0:
+            kept.append(step_kept)
+            pre.append((ids.copy(), a.copy()))
+            if prune_after_step(cfg, s) and len(a) > cfg.cache_keep:
                 a32 = a.astype(np.float32)
                 idx = topk(a32, cfg.cache_keep)
                 if adopt is not None:
-                    idx = adopt("cache", b, 0, idx, a32)
-                sel = idx
+                    idx = adopt("cache", b, s, idx, a32)
+                if s == 0:
+                    sel = idx
                 for c in caches:
                     for name in c:
                         c[name] = compact(c[name], idx)
-                a = compact(a, idx)
-        out[b] = {"x_steps": np.stack(xs), "a": a, "sel": sel, "recompute": recs}
+                a, ids = compact(a, idx), compact(ids, idx)
+            kept_ids.append(ids.copy())
+        out[b] = {"x_steps": np.stack(xs), "a": a, "sel": sel, "recompute": recs,
+                  "kept_ids": kept_ids, "before_prune": pre, "v_kept": np.array(kept)}
     return out

@@ -175,7 +175,7 @@ def test_decode_layer(S, B, H, L0, quantized, thr):
         else:
             cache = {"k": K0[b].reshape(L0, H, dh).astype(np.float64),
                      "v": V0[b].reshape(L0, H, dh).astype(np.float64)}
-        xr, P, recr, cmax = R.decode_layer(x[b], w, cache, H, dh, True, quantized, thr)
+        xr, P, recr, cmax, _ = R.decode_layer(x[b], w, cache, H, dh, True, quantized, thr)
         if quantized:
             for h in range(H):
                 if abs(cmax[h] - thr) > 1e-5 * thr:

@@ -365,7 +365,7 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
                     stats["pq_in_band"] += 1
                 return g
 
-            O, P, rc, cmax = R.decode_attention(q[b], cache, H, dh, cfg.quantized,
+            O, P, rc, cmax, _ = R.decode_attention(q[b], cache, H, dh, cfg.quantized,
                                                 cfg.pq_threshold, decide)
             stats["pq_rows"] += H if cfg.quantized else 0
             stats["pq_recomputed"] += int(rc.sum())

@@ -466,3 +466,125 @@ def test_stack_amplifies_one_ulp_perturbation():
         return np.sqrt(np.mean((a - b) ** 2) / np.mean(a * a))
     assert nrmse(0) < 1e-3
     assert nrmse(5) > 100 * nrmse(0)
+
+
+# ----------------------------------------------------------------- local value pruning
+# (section III "Local Value Pruning": after the softmax, low-probability V
+# vectors are dropped for the current head only)
+
+
+def test_value_pruning_one_hot_values_expose_each_probability():
+    """With V = I (one V row per output dim) o_j is p_j when row j is kept
+    and 0 otherwise, so a wrong pairing of p with V rows, a wrong comparison
+    or renormalisation shows up entry by entry. Thresholds at the m-th
+    largest probability keep exactly m rows."""
+    rng = np.random.default_rng(31)
+    n = 24
+    q = rng.standard_normal(16) * 2
+    K = rng.standard_normal((n, 16))
+    p, _ = _torch_probs(q[None], K, False)
+    p = p[0]
+    order = np.sort(p)[::-1]
+    assert np.all(np.diff(order) < 0)
+    for m in (1, 5, 12, 24):
+        tau = order[m - 1]
+        o, kept = R.value_pruned_output(p, np.eye(n), tau)
+        assert kept == m
+        ref = np.where(p >= tau, p, 0.0)
+        np.testing.assert_array_equal(o, ref)
+        assert o.sum() <= 1.0 + 1e-15
+
+
+def test_value_pruning_threshold_extremes_and_uniform_rows():
+    rng = np.random.default_rng(32)
+    n, dh = 40, 8
+    q = rng.standard_normal(dh)
+    K, V = rng.standard_normal((n, dh)), rng.standard_normal((n, dh))
+    p, _ = _torch_probs(q[None], K, False)
+    o, kept = R.value_pruned_output(p[0], V, 0.0)
+    assert kept == n
+    np.testing.assert_allclose(o, _sdpa(q[None], K, V, False)[0], atol=1e-13)
+    o, kept = R.value_pruned_output(p[0], V, 1.01)
+    assert kept == 0 and np.all(o == 0.0)
+    # q = 0: every probability is exactly 1/8
+    p0 = R.softmax_rows(np.zeros((1, 8)))[0]
+    V8 = V[:8]
+    o, kept = R.value_pruned_output(p0, V8, 0.125)
+    assert kept == 8
+    np.testing.assert_allclose(o, V8.mean(axis=0), atol=1e-15)
+    o, kept = R.value_pruned_output(p0, V8, 0.125 * (1 + 2.0 ** -40))
+    assert kept == 0
+
+
+def test_run_decode_value_pruning_leaves_importance_whole():
+    """Token importance takes every probability, so one layer's importance
+    is the same with and without value pruning while its output is not;
+    every layer still adds H to the total importance."""
+    from workloads import GPT2_DECODE, make_decode_inputs
+    cfg = scaled(GPT2_DECODE, n_layers=1, batch=1, n_heads=3, head_dim=8, cache_len=30,
+                 cache_keep=31, steps=1)
+    inp = make_decode_inputs(cfg)
+    dense = R.run_decode(cfg, inp)[0]
+    vp = R.run_decode(scaled(cfg, v_threshold=0.02), inp)[0]
+    np.testing.assert_array_equal(vp["a"], dense["a"])
+    assert abs(vp["a"].sum() - 3) < 1e-12
+    assert np.all(dense["v_kept"] == 31)
+    assert np.all(vp["v_kept"] < 31) and np.all(vp["v_kept"] >= 1)
+    assert np.max(np.abs(vp["x_steps"] - dense["x_steps"])) > 1e-6
+    cfg3 = scaled(cfg, n_layers=3, v_threshold=0.02)
+    out = R.run_decode(cfg3, make_decode_inputs(cfg3))[0]
+    assert abs(out["a"].sum() - 3 * 3) < 1e-12
+
+
+# ----------------------------------------------------------------- repeated decode cascade
+
+
+def test_prune_schedule():
+    from workloads import GPT2_DECODE
+    once = GPT2_DECODE
+    every = scaled(GPT2_DECODE, prune_every=1)
+    third = scaled(GPT2_DECODE, prune_every=3)
+    assert [R.prune_after_step(once, s) for s in range(7)] == [True] + [False] * 6
+    assert all(R.prune_after_step(every, s) for s in range(7))
+    assert [R.prune_after_step(third, s) for s in range(7)] == [True, False, False, True,
+                                                               False, False, True]
+
+
+@pytest.mark.parametrize("every", [1, 2])
+def test_run_decode_rolling_cut_keeps_the_largest(every):
+    """After each cut the cache holds cache_keep entries: the largest by
+    importance among the entries kept so far plus the new ones (checked by
+    brute force over the candidates), each id at most once, and a pruned
+    entry never comes back."""
+    from workloads import GPT2_DECODE, make_decode_inputs
+    cfg = scaled(GPT2_DECODE, n_layers=2, batch=1, n_heads=2, head_dim=8, cache_len=20,
+                 cache_keep=9, steps=6, prune_every=every)
+    out = R.run_decode(cfg, make_decode_inputs(cfg))[0]
+    gone = set()
+    for s, (ids_pre, a_pre) in enumerate(out["before_prune"]):
+        ids = out["kept_ids"][s]
+        assert len(set(ids.tolist())) == len(ids)
+        assert not (set(ids.tolist()) & gone)
+        if R.prune_after_step(cfg, s):
+            assert len(ids) == 9
+            keep = np.isin(ids_pre, ids)
+            assert keep.sum() == 9
+            assert a_pre[keep].astype(np.float32).min() >= a_pre[~keep].astype(np.float32).max()
+            gone |= set(ids_pre[~keep].tolist())
+        else:
+            np.testing.assert_array_equal(ids, ids_pre)
+    if every == 1:
+        assert all(len(k) == 9 for k in out["kept_ids"])
+
+
+def test_run_decode_rolling_without_cuts_is_the_dense_run():
+    """A keep budget at least the final cache length never cuts, so the
+    rolling schedule reproduces the plain run that never prunes."""
+    from workloads import GPT2_DECODE, make_decode_inputs
+    cfg = scaled(GPT2_DECODE, n_layers=2, batch=1, n_heads=2, head_dim=8, cache_len=12,
+                 cache_keep=12 + 4, steps=4)
+    inp = make_decode_inputs(cfg)
+    plain = R.run_decode(cfg, inp)[0]
+    roll = R.run_decode(scaled(cfg, prune_every=1), inp)[0]
+    np.testing.assert_array_equal(roll["x_steps"], plain["x_steps"])
+    np.testing.assert_array_equal(roll["kept_ids"][-1], np.arange(16))

@@ -19,6 +19,10 @@ Five workloads are defined, each a stack of attention-only residual layers
               25% of tokens kept after layer 1, heads top-24 of 32 from
               layer 2.
 
+Two extensions of gpt2_decode: gpt2_decode_vprune (local value pruning,
+threshold 1e-4) and gpt2_decode_rolling (the cache cut back to 410 entries
+after every step).
+
 This module holds shapes and schedules only. Keep counts follow
 k = floor(f * N + 1/2) with N the original length, so fractions are absolute
 along the cascade.
@@ -55,6 +59,12 @@ class Config:
     steps: int = 0
     quantized: bool = False
     pq_threshold: float = 0.0
+    # local value pruning: V rows with probability below this are dropped
+    # for the current head (0 = off)
+    v_threshold: float = 0.0
+    # re-prune the cache back to cache_keep after every prune_every-th step
+    # following the first (0 = prune once, after step 1)
+    prune_every: int = 0
     heavy_frac: float = 0.05
     heavy_scale: float = 3.0
 
@@ -112,8 +122,15 @@ LONG_CAUSAL = Config(
     tokens=(32768,) + (keep_count(Fraction(1, 4), 32768),) * 3,
     heads=(32,) + (24,) * 3)
 
+# Extensions of the GPT-2-small decode workload: local value pruning with a
+# probability threshold of 1e-4, and a rolling cascade that cuts the cache
+# back to 410 entries after every step.
+GPT2_DECODE_VPRUNE = replace(GPT2_DECODE, name="gpt2_decode_vprune", v_threshold=1e-4)
+GPT2_DECODE_ROLLING = replace(GPT2_DECODE, name="gpt2_decode_rolling", prune_every=1)
+
 CONFIGS = [TINY, BERT_BASE, GPT2_DECODE, PQ_DECODE, LONG_CAUSAL]
-BY_NAME = {c.name: c for c in CONFIGS}
+EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING]
+BY_NAME = {c.name: c for c in CONFIGS + EXTENSIONS}
 
 
 def scaled(cfg: Config, **kw) -> Config:

@@ -34,8 +34,23 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
-def _kernel_work(cfg):
-    """Algorithmic work per kernel name for one step: (flops, bytes)."""
+def _cache_lengths(cfg):
+    """Cache entries each decode step attends over (its own entry included):
+    the cache is cut to cache_keep after step 1 and, with prune_every = r,
+    after every r-th later step."""
+    out, n = [], cfg.cache_len
+    for s in range(cfg.steps):
+        n += 1
+        out.append(n)
+        r = cfg.prune_every
+        if (s == 0 or (r > 0 and s % r == 0)) and n > cfg.cache_keep:
+            n = cfg.cache_keep
+    return out
+
+
+def _kernel_work(cfg, v_kept=None):
+    """Algorithmic work per kernel name for one step: (flops, bytes).
+    v_kept[s][l]: V rows read at step s, layer l (value pruning)."""
     B, H, dh = cfg.batch, cfg.n_heads, cfg.head_dim
     D = H * dh
     es = 2 if cfg.dtype == "bf16" else 4
@@ -54,14 +69,19 @@ def _kernel_work(cfg):
             add("attn_fwd", 4.0 * B * h * dh * pairs, es * 4 * B * h * n * dh)
             add("attn_colsum", 2.0 * B * h * dh * pairs, es * 2 * B * h * n * dh + 4 * B * h * n)
     else:
-        L0, keep, S = cfg.cache_len, cfg.cache_keep, cfg.steps
-        for s in range(S):
-            lc = L0 + 1 if s == 0 else keep + s
-            for _ in range(cfg.n_layers):
+        for s, lc in enumerate(_cache_lengths(cfg)):
+            for l in range(cfg.n_layers):
                 add("qkv_gemm", 2.0 * B * 3 * D * D, es * 3 * D * D)
                 add("out_gemm", 2.0 * B * D * D, es * D * D)
                 if cfg.quantized:
                     add("pq_attn_msb", 4.0 * B * H * dh * lc, 2 * B * lc * (D // 2 + 4))
+                elif cfg.v_threshold > 0:
+                    # K rows once; fp32 scores written, then read back with the
+                    # kept V rows (a 128-byte head slice each) and a updated
+                    add("decode_scores", 2.0 * B * H * dh * lc, B * lc * D * es + 4 * B * H * lc)
+                    kept = v_kept[s][l] if v_kept is not None else 0
+                    add("decode_vprune", 2.0 * dh * kept,
+                        kept * dh * es + 4 * B * H * lc + 8 * B * lc)
                 else:
                     add("decode_attn", 4.0 * B * H * dh * lc, 2 * B * lc * D * es)
     return w
@@ -205,7 +225,8 @@ def main():
     else:
         stack = pipeline.DecodeStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim,
                                      cfg.cache_len, cfg.cache_keep, cfg.steps, w, cfg.quantized,
-                                     cfg.pq_threshold, dtype)
+                                     cfg.pq_threshold, dtype, v_threshold=cfg.v_threshold,
+                                     prune_every=cfg.prune_every)
         k0 = [torch.from_numpy(l["k_cache"]).to(dtype).cuda() for l in inputs["layers"]]
         v0 = [torch.from_numpy(l["v_cache"]).to(dtype).cuda() for l in inputs["layers"]]
         xs = torch.from_numpy(inputs["x_steps"]).to(dtype).cuda()
@@ -245,7 +266,16 @@ def main():
     torch.cuda.synchronize()
     lib.spatten_debug_timing(0)
     ktimes = _read_kernel_times(lib)
-    work = _kernel_work(cfg)
+    v_kept, kept_frac = None, None
+    if cfg.kind == "decode" and cfg.v_threshold > 0:
+        # V rows each layer read, from one more (untimed) pass over the steps
+        stack.load(k0, v0)
+        for s in range(cfg.steps):
+            stack.step(xs[s], record=True)
+        v_kept = [[int(n) for n in t["v_kept"].sum(dim=(1, 2)).tolist()] for t in stack.trace]
+        rows = sum(cfg.batch * cfg.n_heads * lc * cfg.n_layers for lc in _cache_lengths(cfg))
+        kept_frac = round(sum(map(sum, v_kept)) / rows, 4)
+    work = _kernel_work(cfg, v_kept)
     per_kernel = {}
     for name, (ms, cnt) in ktimes.items():
         fl, by = work.get(name, (0.0, 0.0))
@@ -282,7 +312,9 @@ def main():
     else:
         conf = {"workload": cfg.name, "batch": cfg.batch, "cache_len": cfg.cache_len,
                 "cache_keep": cfg.cache_keep, "decode_steps": cfg.steps, "layers": cfg.n_layers,
-                "heads": cfg.n_heads, "head_dim": cfg.head_dim, "quantized": cfg.quantized}
+                "heads": cfg.n_heads, "head_dim": cfg.head_dim, "quantized": cfg.quantized,
+                "prune_every": cfg.prune_every, "v_threshold": cfg.v_threshold,
+                "v_rows_kept_frac": kept_frac}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "gpu_ms_per_step": round(gpu_ms / args.steps, 4),

@@ -82,8 +82,8 @@ int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const vo
 int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const void* wk,
                  const void* wv, const void* wo, const int32_t* head_idx, float* a,
                  void* k_cache, void* v_cache, uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
-                 uint8_t* v_msb, uint8_t* v_lsb, float* v_scale, int32_t* recompute, char* ws,
-                 hipStream_t st) {
+                 uint8_t* v_msb, uint8_t* v_lsb, float* v_scale, int32_t* recompute,
+                 int32_t* v_kept, char* ws, hipStream_t st) {
   const DecodeWs w = decode_ws(d);
   const int H = d.n_heads, dh = d.head_dim, D = H * dh;
   const int64_t cap = d.cache_cap, row = d.cache_len;
@@ -134,6 +134,7 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
   da.lc_pad = int(w.lc_pad);
   da.nchunk = int(w.nchunk);
   da.threshold = d.pq_threshold;
+  da.v_threshold = d.v_threshold;
   da.scores = reinterpret_cast<float*>(ws + w.scores);
   da.mpart = reinterpret_cast<float*>(ws + w.mpart);
   da.lpart = reinterpret_cast<float*>(ws + w.lpart);
@@ -142,9 +143,11 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
   da.cmax = reinterpret_cast<float*>(ws + w.cmax);
   da.flags = reinterpret_cast<int32_t*>(ws + w.flags);
   da.queue = reinterpret_cast<int32_t*>(ws + w.queue);
+  da.kcount = reinterpret_cast<int32_t*>(ws + w.kcount);
   da.o = ws + w.o;
   da.a = a;
   da.recompute = recompute;
+  da.v_kept = v_kept;
   SPATTEN_TRY(launch_decode(da, d.kv_quantized != 0, st));
   OutArgs oa{};
   oa.dtype = d.dtype;
@@ -168,7 +171,7 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x, const void* wq, 
                           const void* wv, const void* wo, const int32_t* head_idx, float* a,
                           float* g, void* k_cache, void* v_cache, uint8_t* k_msb, uint8_t* k_lsb,
                           float* k_scale, uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
-                          int32_t* recompute, float* lse, void* workspace,
+                          int32_t* recompute, int32_t* v_kept, float* lse, void* workspace,
                           size_t* workspace_bytes, void* stream) {
   const int st = check_layer(d, x, wq, wk, wv, wo, head_idx, a, g, k_cache, v_cache, k_msb, k_lsb,
                              k_scale, v_msb, v_lsb, v_scale, workspace, workspace_bytes);
@@ -182,7 +185,7 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x, const void* wq, 
   if (d->mode == SPATTEN_PREFILL)
     return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, a, g, lse, ws, as_stream(stream));
   return layer_decode(*d, x, wq, wk, wv, wo, head_idx, a, k_cache, v_cache, k_msb, k_lsb, k_scale,
-                      v_msb, v_lsb, v_scale, recompute, ws, as_stream(stream));
+                      v_msb, v_lsb, v_scale, recompute, v_kept, ws, as_stream(stream));
 }
 
 int spatten_topk(const float* scores, int32_t batch, int32_t n, int64_t row_stride, int32_t k,
@@ -201,6 +204,15 @@ int spatten_compact(int32_t n_tensors, const void* const* src, void* const* dst,
   if (st != SPATTEN_OK) return st;
   return launch_compact(n_tensors, src, dst, row_bytes, src_batch_stride, dst_batch_stride, idx,
                         batch, k, as_stream(stream));
+}
+
+int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* row_bytes,
+                            const int64_t* batch_stride, const int32_t* idx, int32_t batch,
+                            int32_t n, int32_t k, void* stream) {
+  const int st = check_compact_inplace(n_tensors, base, row_bytes, batch_stride, idx, batch, n, k);
+  if (st != SPATTEN_OK) return st;
+  return launch_compact_inplace(n_tensors, base, row_bytes, batch_stride, idx, batch, n, k,
+                                as_stream(stream));
 }
 
 int spatten_quantize_kv(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,

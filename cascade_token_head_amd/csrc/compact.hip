@@ -7,6 +7,11 @@
 // crossbar; here each destination row is a contiguous copy, split into
 // 16-byte units when the addresses allow, so consecutive lanes touch
 // consecutive bytes of the same row and HBM access stays coalesced.
+//
+// In-place form (decode caches, whose row order carries no meaning): of the
+// k selected rows, those already below k stay; the i-th selected row at or
+// above k moves into the i-th unselected row below k. A cut that drops one
+// entry from k + 1 moves at most one row per tensor instead of all k.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -74,7 +79,108 @@ int vec_shift_for(const void* s, const void* d, int64_t rb, int64_t sbs, int64_t
   return 0;
 }
 
+// moves per workgroup of the in-place form
+constexpr int kMovesPerBlock = 16;
+
+struct InplaceTensor {
+  char* base;
+  int64_t row_bytes, bs;
+  int32_t vec_shift;
+};
+
+struct InplaceParams {
+  InplaceTensor t[kCompactMax];
+  int count;
+};
+
+template <int V>
+__device__ __forceinline__ void move_units(const InplaceTensor& t, char* bbase, const int* src,
+                                           const int* dst, int nmoves) {
+  using T = typename VecT<V>::T;
+  const int64_t upr = t.row_bytes / V;
+  const int64_t total = int64_t(nmoves) * upr;
+  for (int64_t u = threadIdx.x; u < total; u += blockDim.x) {
+    const int m = int(u / upr);
+    const int64_t part = u - int64_t(m) * upr;
+    const T* s = reinterpret_cast<const T*>(bbase + int64_t(src[m]) * t.row_bytes) + part;
+    T* d = reinterpret_cast<T*>(bbase + int64_t(dst[m]) * t.row_bytes) + part;
+    *d = *s;
+  }
+}
+
+// grid (ceil(max moves / kMovesPerBlock), batch). Sequence b's selection
+// idx[b, 0:k] is ascending; c = number of selected rows below k, and the
+// k - c selected rows at or above k are idx[c..k-1]. With d_j = idx[j] - j
+// (non-decreasing for j < c), the i-th unselected row below k is
+// i + #{j < c : d_j <= i}.
+__global__ void __launch_bounds__(256)
+compact_inplace_kernel(InplaceParams p, const int32_t* __restrict__ idx, int k) {
+  __shared__ int sel[kInplaceMaxK];
+  __shared__ int src[kMovesPerBlock], dst[kMovesPerBlock];
+  __shared__ int nbelow;
+  const int b = blockIdx.y;
+  const int32_t* ib = idx + int64_t(b) * k;
+  for (int j = threadIdx.x; j < k; j += blockDim.x) sel[j] = ib[j];
+  if (threadIdx.x == 0) nbelow = 0;
+  __syncthreads();
+  // c: selected rows below k (ascending, so a count is a boundary)
+  int cnt = 0;
+  for (int j = threadIdx.x; j < k; j += blockDim.x) cnt += sel[j] < k ? 1 : 0;
+  if (cnt) atomicAdd(&nbelow, cnt);
+  __syncthreads();
+  const int c = nbelow, moves = k - c;
+  const int m0 = blockIdx.x * kMovesPerBlock;
+  if (m0 >= moves) return;
+  const int nm = moves - m0 < kMovesPerBlock ? moves - m0 : kMovesPerBlock;
+  if (threadIdx.x < nm) {
+    const int i = m0 + threadIdx.x;
+    int lo = 0, hi = c;  // first j in [0, c) with idx[j] - j > i
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sel[mid] - mid <= i) lo = mid + 1; else hi = mid;
+    }
+    dst[threadIdx.x] = i + lo;
+    src[threadIdx.x] = sel[c + i];
+  }
+  __syncthreads();
+  for (int ti = 0; ti < p.count; ++ti) {
+    const InplaceTensor& t = p.t[ti];
+    char* bbase = t.base + int64_t(b) * t.bs;
+    switch (t.vec_shift) {
+      case 4: move_units<16>(t, bbase, src, dst, nm); break;
+      case 3: move_units<8>(t, bbase, src, dst, nm); break;
+      case 2: move_units<4>(t, bbase, src, dst, nm); break;
+      case 1: move_units<2>(t, bbase, src, dst, nm); break;
+      default: move_units<1>(t, bbase, src, dst, nm); break;
+    }
+  }
+}
+
 }  // namespace
+
+int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_bytes,
+                           const int64_t* bs, const int32_t* idx, int batch, int n, int k,
+                           hipStream_t stream) {
+  if (n_tensors == 0 || batch == 0 || k == n) return SPATTEN_OK;
+  const int max_moves = k < n - k ? k : n - k;
+  const unsigned blocks = unsigned(ceil_div(max_moves, kMovesPerBlock));
+  for (int t0 = 0; t0 < n_tensors; t0 += kCompactMax) {
+    InplaceParams p{};
+    p.count = n_tensors - t0 < kCompactMax ? n_tensors - t0 : kCompactMax;
+    for (int i = 0; i < p.count; ++i) {
+      const int t = t0 + i;
+      p.t[i].base = static_cast<char*>(base[t]);
+      p.t[i].row_bytes = row_bytes[t];
+      p.t[i].bs = bs[t];
+      p.t[i].vec_shift = vec_shift_for(base[t], base[t], row_bytes[t], bs[t], bs[t]);
+    }
+    SPATTEN_TIMED("compact_inplace", stream,
+                  compact_inplace_kernel<<<dim3(blocks, unsigned(batch)), dim3(256), 0,
+                                           stream>>>(p, idx, k));
+    SPATTEN_LAUNCH_CHECK();
+  }
+  return SPATTEN_OK;
+}
 
 int launch_compact(int n_tensors, const void* const* src, void* const* dst,
                    const int64_t* row_bytes, const int64_t* sbs, const int64_t* dbs,

@@ -24,6 +24,15 @@
 // row, chunk) over both planes of that head only. decode_finish combines
 // what is left, writes O and adds the probabilities that produced O to the
 // token importance.
+//
+// Local value pruning (section III "Local Value Pruning": after the softmax
+// a head drops its low-probability V vectors): the scores pass reads K only
+// and leaves per-chunk statistics; decode_vprune, with every chunk's
+// statistics of a row in hand, forms the exact probabilities of its chunk,
+// adds them to the token importance and reads only the V rows whose
+// probability reaches the threshold for that head (a 128-byte head slice of
+// the cache row is fetched or skipped whole); decode_vsum adds the chunks'
+// normalised partial outputs.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -79,8 +88,9 @@ __device__ __forceinline__ void nibbles_plus8(uint32_t w, float* u) {
   }
 }
 
-// grid (nchunk, B); block = (D/8) * R threads, R rows of the chunk at a time
-template <int KIND>
+// grid (nchunk, B); block = (D/8) * R threads, R rows of the chunk at a time.
+// WITH_V = false stops after the scores and chunk statistics.
+template <int KIND, bool WITH_V = true>
 __global__ void __launch_bounds__(256)
 decode_partial(DecodeArgs a) {
   using Raw = typename RawRow<KIND>::T;
@@ -192,7 +202,7 @@ decode_partial(DecodeArgs a) {
       if constexpr (KIND == kMsb) vs[u] = a.v_scale[row];
     }
   };
-  load_v(0);
+  if constexpr (WITH_V) load_v(0);
   __syncthreads();
   // ---- per-head chunk statistics, two heads per wave (32 lanes each);
   // S becomes exp2(S - m)
@@ -213,6 +223,7 @@ decode_partial(DecodeArgs a) {
       a.lpart[i] = l;
     }
   }
+  if constexpr (!WITH_V) return;
   __syncthreads();
   // ---- P V for this thread's column group
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -257,6 +268,128 @@ decode_partial(DecodeArgs a) {
     float* op = a.opart + ((int64_t(b) * H + h) * a.nchunk + chunk) * dh + d0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) op[e] = acc[e];
+  }
+}
+
+// Local value pruning, after the K-only scores pass. grid (nchunk, B), the
+// thread layout of decode_partial. Each half-wave combines one head's chunk
+// statistics into its log2-sum-exp, forms the chunk's 32 probabilities and
+// counts the kept rows; the workgroup then adds the chunk's importance
+// (it owns those a entries) and accumulates p V over the kept rows only.
+__global__ void __launch_bounds__(256)
+decode_vprune(DecodeArgs a) {
+  __shared__ float P[kMaxHeads][CH];
+  __shared__ float obuf[256 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, b = blockIdx.y;
+  const int H = a.H, dh = a.dh, D = H * dh;
+  const int V = D / 8, R = blockDim.x / V;
+  const int c = tid % V, r = tid / V;
+  const int h = (8 * c) / dh;
+  const int j0 = chunk * CH;
+  const int nwaves = (blockDim.x + 63) >> 6;
+  const int kpt = CH / R;
+  const int64_t rowb = int64_t(b) * a.cap;
+  const float tau = a.v_threshold;
+
+  for (int hh = 2 * wave + (lane >> 5); hh < H; hh += 2 * nwaves) {
+    const int l32 = lane & 31;
+    const int64_t bh = int64_t(b) * H + hh;
+    const float* mp = a.mpart + bh * a.nchunk;
+    const float* lp = a.lpart + bh * a.nchunk;
+    float M = -INFINITY;
+    for (int ci = l32; ci < a.nchunk; ci += 32) M = fmaxf(M, mp[ci]);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = 0.0f;
+    for (int ci = l32; ci < a.nchunk; ci += 32) L += lp[ci] * fast_exp2(mp[ci] - M);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    const float lse2 = M + log2f(L);
+    const int j = j0 + l32;
+    const bool valid = j < a.lc;
+    const float p = valid ? fast_exp2(a.scores[bh * a.lc_pad + j] - lse2) : 0.0f;
+    P[hh][l32] = p;
+    const uint64_t kept = __ballot(valid && p >= tau);
+    if (l32 == 0) {
+      a.kcount[bh * a.nchunk + chunk] = __popcll(kept >> (lane & 32) & 0xffffffffull);
+      if (chunk == 0) {
+        a.lse[bh] = lse2;
+        a.cmax[bh] = 1.0f / L;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < CH && j0 + tid < a.lc) {
+    float s = 0.0f;
+    for (int hh = 0; hh < H; ++hh) s += P[hh][tid];
+    a.a[rowb + j0 + tid] += s;
+  }
+  // P V over this head's kept rows; a dropped row is not read
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t0 = 0; t0 < kpt; t0 += KB) {
+    u32x4 vraw[KB];
+    float pw[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int jl = r + R * (t0 + u);
+      const bool in = t0 + u < kpt;
+      pw[u] = in ? P[h][jl] : 0.0f;
+      if (in && j0 + jl < a.lc && pw[u] >= tau) {
+        vraw[u] = load_row<kBf16>(a.v_cache, nullptr, rowb + j0 + jl, c, D);
+      } else {
+        vraw[u] = u32x4{0u, 0u, 0u, 0u};
+        pw[u] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(pw[u], __uint_as_float(vraw[u][e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(pw[u], __uint_as_float(vraw[u][e] & 0xffff0000u), acc[2 * e + 1]);
+      }
+    }
+  }
+  if (r > 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) obuf[((r - 1) * V + c) * 8 + e] = acc[e];
+  }
+  __syncthreads();
+  if (r == 0) {
+    for (int rr = 1; rr < R; ++rr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += obuf[((rr - 1) * V + c) * 8 + e];
+    const int d0 = 8 * c - h * dh;
+    float* op = a.opart + ((int64_t(b) * H + h) * a.nchunk + chunk) * dh + d0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) op[e] = acc[e];
+  }
+}
+
+// Value pruning, last step: one wave per (b, h), lane = output dim (dh 64).
+// The chunk partials are already normalised, so O is their plain sum.
+__global__ void __launch_bounds__(64)
+decode_vsum(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const float* op = a.opart + bh * a.nchunk * a.dh + lane;
+  float acc = 0.0f;
+  for (int k = 0; k < a.nchunk; k += 8) {
+    float ov[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ov[u] = k + u < a.nchunk ? op[int64_t(k + u) * a.dh] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += ov[u];
+  }
+  static_cast<bf16_t*>(a.o)[bh * a.dh + lane] = f32_to_bf16(acc);
+  int cnt = 0;
+  for (int ci = lane; ci < a.nchunk; ci += 64) cnt += a.kcount[bh * a.nchunk + ci];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) {
+    if (a.v_kept) a.v_kept[bh] = cnt;
+    if (a.recompute) a.recompute[bh] = 0;
   }
 }
 
@@ -408,6 +541,7 @@ decode_finish(DecodeArgs a, int quantized) {
     } else if (lane == 0) {
       lse[h] = a.lse[bh];
     }
+    if (lane == 0 && a.v_kept) a.v_kept[bh] = a.lc;
   }
   __syncthreads();
   const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
@@ -440,6 +574,16 @@ int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream) {
   if (a.dh != 64 || a.H > kMaxHeads || threads > 256 || threads < 128)
     return SPATTEN_EUNSUPPORTED;
   const dim3 gp(a.nchunk, a.batch);
+  if (!quantized && a.v_threshold > 0.0f) {
+    SPATTEN_TIMED("decode_scores", stream,
+                  (decode_partial<kBf16, false><<<gp, threads, 0, stream>>>(a)));
+    SPATTEN_LAUNCH_CHECK();
+    SPATTEN_TIMED("decode_vprune", stream, decode_vprune<<<gp, threads, 0, stream>>>(a));
+    SPATTEN_LAUNCH_CHECK();
+    SPATTEN_TIMED("decode_vsum", stream, decode_vsum<<<a.batch * a.H, 64, 0, stream>>>(a));
+    SPATTEN_LAUNCH_CHECK();
+    return SPATTEN_OK;
+  }
   if (!quantized) {
     SPATTEN_TIMED("decode_attn", stream, decode_partial<kBf16><<<gp, threads, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();

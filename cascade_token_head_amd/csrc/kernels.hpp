@@ -17,6 +17,10 @@ int launch_compact(int n_tensors, const void* const* src, void* const* dst,
                    const int64_t* row_bytes, const int64_t* sbs, const int64_t* dbs,
                    const int32_t* idx, int batch, int k, hipStream_t stream);
 
+int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_bytes,
+                           const int64_t* bs, const int32_t* idx, int batch, int n, int k,
+                           hipStream_t stream);
+
 int launch_quantize(const void* kv, int dtype, int batch, int n, int dim, int64_t kv_bs,
                     uint8_t* msb, uint8_t* lsb, float* scale, int64_t pbs, hipStream_t stream);
 
@@ -84,6 +88,7 @@ struct DecodeArgs {
   const void* vnew;  // into plane row lc-1 by the MSB pass before it reads it
   int batch, H, dh, cap, lc, lc_pad, nchunk;
   float threshold;
+  float v_threshold;  // local value pruning (unquantized; 0 = off)
   float* scores;  // [B, H, lc_pad]
   float* mpart;
   float* lpart;   // [B, H, nchunk]
@@ -92,9 +97,11 @@ struct DecodeArgs {
   float* cmax;    // [B, H]
   int32_t* flags; // [B, H]
   int32_t* queue; // [0] = count, then entries b*H + h
+  int32_t* kcount;  // [B, H, nchunk] V rows kept per chunk (value pruning)
   void* o;        // [B, D] bf16
   float* a;       // [B, cap]
   int32_t* recompute;  // optional [B, H]
+  int32_t* v_kept;     // optional [B, H]
 };
 int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream);
 

@@ -29,6 +29,9 @@ constexpr int kAttnKBlock = 256;
 constexpr int kAttnF32Rows = 8;
 // Decode: cache entries per split-K chunk.
 constexpr int kDecChunk = 32;
+// In-place compaction: most rows one call may keep per sequence (the
+// selection is staged in LDS).
+constexpr int kInplaceMaxK = 8192;
 
 SPATTEN_HD inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 SPATTEN_HD inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
@@ -43,7 +46,7 @@ struct PrefillWs {
 
 struct DecodeWs {
   int64_t lc, lc_pad, nchunk;
-  size_t q, knew, vnew, scores, mpart, lpart, opart, lse, cmax, flags, queue, o, total;
+  size_t q, knew, vnew, scores, mpart, lpart, opart, lse, cmax, flags, queue, kcount, o, total;
 };
 
 inline size_t dtype_bytes(int dt) { return dt == SPATTEN_BF16 ? 2 : 4; }
@@ -88,6 +91,7 @@ inline DecodeWs decode_ws(const spatten_layer_desc& d) {
   w.cmax = take(B * H * 4);
   w.flags = take(B * H * 4);
   w.queue = take((B * H + 1) * 4);
+  w.kcount = take(B * H * w.nchunk * 4);
   w.o = take(B * D * 2);
   w.total = off;
   return w;

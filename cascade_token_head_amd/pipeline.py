@@ -1,4 +1,4 @@
-"""Cascade drivers: sequences the four C-ABI calls over a stack of layers.
+"""Cascade drivers: sequences the C-ABI calls over a stack of layers.
 
 All device memory is allocated up front (constructors), so `run()` /
 `step()` only enqueue library calls and can be captured in a HIP graph.
@@ -12,7 +12,9 @@ cumulative head importance.
 
 Decode (section II, generation): one token per step against per-layer K/V
 caches; after every layer of step 1 the caches of all layers are pruned to
-the top cache_keep entries by cumulative importance.
+the top cache_keep entries by cumulative importance, and with prune_every
+= r > 0 cut back to cache_keep again after every r-th later step. Local
+value pruning (section III) is a per-layer option of the attention call.
 """
 from __future__ import annotations
 
@@ -126,15 +128,21 @@ class PrefillStack:
 class DecodeStack:
     def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, cache_len: int,
                  cache_keep: int, steps: int, weights: List[dict], quantized: bool = False,
-                 threshold: float = 0.0, dtype: torch.dtype = torch.bfloat16, device="cuda"):
+                 threshold: float = 0.0, dtype: torch.dtype = torch.bfloat16, device="cuda",
+                 v_threshold: float = 0.0, prune_every: int = 0):
         self.L, self.B, self.H, self.dh = n_layers, batch, n_heads, head_dim
         self.D = D = n_heads * head_dim
         self.L0, self.keep, self.steps = cache_len, cache_keep, steps
         self.cap = cap = cache_len + steps
         self.quantized, self.threshold, self.w, self.dtype = quantized, threshold, weights, dtype
+        self.v_threshold, self.prune_every = v_threshold, prune_every
+        # repeated cuts run in place on one copy of the caches; a single cut
+        # gathers the survivors, in order, into the second copy
+        self.inplace = prune_every > 0
+        sides = 1 if self.inplace else 2
         B, dev = batch, device
-        self.caches = [[], []]
-        for side in range(2):
+        self.caches = [[] for _ in range(sides)]
+        for side in range(sides):
             for _ in range(n_layers):
                 if quantized:
                     c = {"k_msb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
@@ -147,14 +155,15 @@ class DecodeStack:
                     c = {"k_cache": torch.empty(B, cap, D, dtype=dtype, device=dev),
                          "v_cache": torch.empty(B, cap, D, dtype=dtype, device=dev)}
                 self.caches[side].append(c)
-        self.abuf = [torch.zeros(B, cap, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.abuf = [torch.zeros(B, cap, dtype=torch.float32, device=dev) for _ in range(sides)]
         self.x = torch.empty(B, 1, D, dtype=dtype, device=dev)
         self.head_idx = torch.arange(n_heads, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
         self.g = torch.zeros(B, n_heads, dtype=torch.float32, device=dev)
         self.recompute = torch.zeros(n_layers, B, n_heads, dtype=torch.int32, device=dev)
+        self.v_kept = torch.zeros(n_layers, B, n_heads, dtype=torch.int32, device=dev)
         self.cache_sel = torch.empty(B, cache_keep, dtype=torch.int32, device=dev)
         dmax = S.make_desc(S.DECODE, S.dtype_code(dtype), False, B, 1, n_heads, n_heads, head_dim,
-                           cap - 1, cap, quantized, threshold)
+                           cap - 1, cap, quantized, threshold, v_threshold)
         self.ws = torch.empty(max(S.workspace_bytes(dmax), 256), dtype=torch.uint8, device=dev)
         self.side, self.len, self.s = 0, cache_len, 0
         self.trace = []
@@ -183,32 +192,57 @@ class DecodeStack:
         B, H = self.B, self.H
         self.x.view(B, self.D).copy_(x)
         desc = S.make_desc(S.DECODE, S.dtype_code(self.dtype), False, B, 1, H, H, self.dh,
-                           self.len, self.cap, self.quantized, self.threshold)
+                           self.len, self.cap, self.quantized, self.threshold, self.v_threshold)
         a = self.abuf[self.side]
         for l in range(self.L):
             w, c = self.w[l], self.caches[self.side][l]
             if hook is not None:
                 hook("pre", l)
             S.layer_forward(desc, self.x, w["wq"], w["wk"], w["wv"], w["wo"], self.head_idx, a,
-                            self.g, self.ws, recompute=self.recompute[l], **c)
+                            self.g, self.ws, recompute=self.recompute[l], v_kept=self.v_kept[l],
+                            **c)
             if hook is not None:
                 hook("post", l)
         self.len += 1
         if record:
-            self.trace.append({"recompute": self.recompute.clone()})
-        if self.s == 0:
+            self.trace.append({"recompute": self.recompute.clone(),
+                               "v_kept": self.v_kept.clone()})
+        if self.cut_due():
+            if record:
+                self.trace[-1]["a_before_cut"] = self.abuf[self.side][:, :self.len].clone()
             self.prune()
             if record:
                 self.trace[-1]["cache_sel"] = self.cache_sel.clone()
         self.s += 1
         return self.x.view(B, self.D)
 
+    def cut_due(self) -> bool:
+        """After the first step, and after every prune_every-th later one,
+        when the cache holds more than `keep` entries."""
+        r = self.prune_every
+        return (self.s == 0 or (r > 0 and self.s % r == 0)) and self.len > self.keep
+
     def prune(self):
         """Keep the top `keep` cache entries (by cumulative importance) in
-        every layer, in one multi-tensor compaction."""
+        every layer: a gather into the second copy of the caches, in order,
+        or for repeated cuts an in-place move of the survivors that sit past
+        the kept range into the dropped rows."""
         B, cap, k = self.B, self.cap, self.keep
-        a, a2 = self.abuf[self.side], self.abuf[self.side ^ 1]
+        a = self.abuf[self.side]
         S.topk(a, k, n=self.len, out=self.cache_sel)
+        if self.inplace:
+            tensors = [(a, 4, cap * 4)]
+            for c in self.caches[0]:
+                for t in c.values():
+                    rb = t.stride(1) * t.element_size() if t.dim() == 3 else t.element_size()
+                    tensors.append((t, rb, t.stride(0) * t.element_size()))
+            S.compact_inplace(tensors, self.cache_sel, self.len, k)
+            # rows past the kept range take the next entries, whose
+            # importance starts at 0
+            a[:, k:self.len].zero_()
+            self.len = k
+            return
+        a2 = self.abuf[self.side ^ 1]
         pairs = [(a, a2, 4, cap * 4, cap * 4)]
         for l in range(self.L):
             src, dst = self.caches[self.side][l], self.caches[self.side ^ 1][l]

@@ -21,8 +21,8 @@ PREFILL, DECODE = 0, 1
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
-EXPORTED = ("spatten_layer_forward", "spatten_topk", "spatten_compact", "spatten_quantize_kv",
-            "spatten_status_string")
+EXPORTED = ("spatten_layer_forward", "spatten_topk", "spatten_compact", "spatten_compact_inplace",
+            "spatten_quantize_kv", "spatten_status_string")
 
 
 class SpattenError(RuntimeError):
@@ -39,6 +39,7 @@ class LayerDesc(ctypes.Structure):
         ("n_heads_kept", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("cache_len", ctypes.c_int32), ("cache_cap", ctypes.c_int32),
         ("kv_quantized", ctypes.c_int32), ("pq_threshold", ctypes.c_float),
+        ("v_threshold", ctypes.c_float),
     ]
 
 
@@ -53,7 +54,7 @@ def _lib():
         lib = ctypes.CDLL(LIB_PATH)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         lib.spatten_layer_forward.restype = ctypes.c_int
-        lib.spatten_layer_forward.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 19 + \
+        lib.spatten_layer_forward.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 20 + \
             [ctypes.POINTER(ctypes.c_size_t), vp]
         lib.spatten_topk.restype = ctypes.c_int
         lib.spatten_topk.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp]
@@ -61,6 +62,9 @@ def _lib():
         lib.spatten_compact.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(i64), ctypes.POINTER(i64),
                                         ctypes.POINTER(i64), vp, i32, i32, vp]
+        lib.spatten_compact_inplace.restype = ctypes.c_int
+        lib.spatten_compact_inplace.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                                ctypes.POINTER(i64), vp, i32, i32, i32, vp]
         lib.spatten_quantize_kv.restype = ctypes.c_int
         lib.spatten_quantize_kv.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, i64, vp]
         lib.spatten_status_string.restype = ctypes.c_char_p
@@ -102,28 +106,30 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def make_desc(mode=PREFILL, dtype=BF16, causal=False, batch=1, n_tokens=1, n_heads=1,
               n_heads_kept=None, head_dim=64, cache_len=0, cache_cap=0, kv_quantized=False,
-              pq_threshold=0.0) -> LayerDesc:
+              pq_threshold=0.0, v_threshold=0.0) -> LayerDesc:
     return LayerDesc(mode, dtype, int(causal), batch, n_tokens, n_heads,
                      n_heads if n_heads_kept is None else n_heads_kept, head_dim, cache_len,
-                     cache_cap, int(kv_quantized), float(pq_threshold))
+                     cache_cap, int(kv_quantized), float(pq_threshold), float(v_threshold))
 
 
 def workspace_bytes(desc: LayerDesc) -> int:
     """Workspace size the library needs for `desc` (query mode)."""
     nb = ctypes.c_size_t(0)
-    st = _lib().spatten_layer_forward(ctypes.byref(desc), *([None] * 19), ctypes.byref(nb), None)
+    st = _lib().spatten_layer_forward(ctypes.byref(desc), *([None] * 20), ctypes.byref(nb), None)
     _check("spatten_layer_forward(query)", st)
     return nb.value
 
 
 def layer_forward(desc: LayerDesc, x, wq, wk, wv, wo, head_idx, a, g, workspace,
                   k_cache=None, v_cache=None, k_msb=None, k_lsb=None, k_scale=None,
-                  v_msb=None, v_lsb=None, v_scale=None, recompute=None, lse=None, stream=None):
+                  v_msb=None, v_lsb=None, v_scale=None, recompute=None, v_kept=None, lse=None,
+                  stream=None):
     nb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     st = _lib().spatten_layer_forward(
         ctypes.byref(desc), _p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(head_idx), _p(a), _p(g),
         _p(k_cache), _p(v_cache), _p(k_msb), _p(k_lsb), _p(k_scale), _p(v_msb), _p(v_lsb),
-        _p(v_scale), _p(recompute), _p(lse), _p(workspace), ctypes.byref(nb), _stream(stream))
+        _p(v_scale), _p(recompute), _p(v_kept), _p(lse), _p(workspace), ctypes.byref(nb),
+        _stream(stream))
     _check("spatten_layer_forward", st)
 
 
@@ -168,3 +174,20 @@ def quantize_kv(kv: torch.Tensor, msb: torch.Tensor, lsb: torch.Tensor, scale: t
     st = _lib().spatten_quantize_kv(_p(kv), dtype_code(kv.dtype), B, n, D, kv.stride(0), _p(msb),
                                     _p(lsb), _p(scale), scale.stride(0), _stream(stream))
     _check("spatten_quantize_kv", st)
+
+
+def compact_inplace(tensors: Sequence, idx: torch.Tensor, n: int, k: int, stream=None):
+    """In-place cut of rows whose order carries no meaning.
+
+    tensors: (base, row_bytes, batch_stride_bytes) per tensor.
+    idx:     int32 [B, k] ascending selected rows, each below n.
+    """
+    m = len(tensors)
+    VP = ctypes.c_void_p * max(m, 1)
+    I64 = ctypes.c_int64 * max(m, 1)
+    base = VP(*[t[0].data_ptr() for t in tensors])
+    rb = I64(*[t[1] for t in tensors])
+    bs = I64(*[t[2] for t in tensors])
+    B = idx.shape[0]
+    st = _lib().spatten_compact_inplace(m, base, rb, bs, _p(idx), B, n, k, _stream(stream))
+    _check("spatten_compact_inplace", st)

@@ -60,6 +60,7 @@ typedef struct {
   int32_t cache_cap;     /* decode: cache rows allocated per sequence */
   int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
   float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
+  float v_threshold;     /* decode, unquantized: local value pruning threshold (0 = off) */
 } spatten_layer_desc;
 
 /*
@@ -93,6 +94,13 @@ typedef struct {
  *   pq_threshold, recomputed with the full code scale*(16*msb + lsb) for
  *   both K and V. recompute (optional, [B, H] int32) receives 1 for
  *   recomputed rows. a accumulates the probabilities that produced O.
+ *   Local value pruning (section III "Local Value Pruning"; unquantized
+ *   caches, v_threshold > 0): after the softmax, V row j of head h enters
+ *   O_h only when P_h[j] >= v_threshold, O_h = sum over those j of
+ *   P_h[j] V_h[j] (no renormalisation); the other V rows are never read.
+ *   a still takes every probability. v_kept (optional, [B, H] int32)
+ *   receives the number of V rows that entered O_h (cache_len + 1 without
+ *   value pruning).
  *   g is not used in decode and may be NULL. Decode needs head_dim 64,
  *   H <= 32, bf16 and every head kept.
  * head_idx: [B, h_kept] int32, strictly ascending head ids per sequence.
@@ -103,7 +111,9 @@ typedef struct {
  *   *workspace_bytes and SPATTEN_OK is returned without enqueuing anything
  *   (tensor pointers may then be NULL).
  * Supported: prefill bf16 with head_dim 64 or 128, prefill fp32 with
- *   n_tokens <= 1024; other shapes return SPATTEN_EUNSUPPORTED.
+ *   n_tokens <= 1024; other shapes return SPATTEN_EUNSUPPORTED, as does a
+ *   non-zero v_threshold in prefill or with a quantized cache. A NaN or
+ *   negative v_threshold is SPATTEN_EINVAL.
  */
 int spatten_layer_forward(const spatten_layer_desc* d, void* x,
                           const void* wq, const void* wk, const void* wv, const void* wo,
@@ -111,7 +121,7 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x,
                           void* k_cache, void* v_cache,
                           uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
                           uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
-                          int32_t* recompute, float* lse,
+                          int32_t* recompute, int32_t* v_kept, float* lse,
                           void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
@@ -142,6 +152,28 @@ int spatten_compact(int32_t n_tensors, const void* const* src, void* const* dst,
                     const int64_t* row_bytes, const int64_t* src_batch_stride,
                     const int64_t* dst_batch_stride, const int32_t* idx,
                     int32_t batch, int32_t k, void* stream);
+
+/*
+ * spatten_compact_inplace - the same cut done in place, for tensors whose
+ * row order carries no meaning (decode caches: the query attends to every
+ * kept entry without a mask), so that a cascade can cut the cache again at
+ * every step (section II "Cascade pruning": pruned tokens stay pruned).
+ * For each sequence b, idx[b*k + 0 .. k-1] lists k strictly ascending rows
+ * below n (as spatten_topk returns them). Afterwards rows 0 .. k-1 hold
+ * exactly the selected rows, as a set: a selected row below k stays where
+ * it is, and the i-th selected row at or above k (in ascending order) moves
+ * into the i-th unselected row below k (in ascending order). No other row
+ * is read or written, so a cut from k + 1 rows to k moves at most one row.
+ * Row r of sequence b of tensor t is base[t] + b*batch_stride[t] +
+ * r*row_bytes[t]; base, row_bytes and batch_stride are HOST arrays of
+ * n_tensors entries. Requires 1 <= k <= n and k <= 8192 (larger k returns
+ * SPATTEN_EUNSUPPORTED); each idx entry must lie in [0, n) - the caller
+ * guarantees this. Sequences must not overlap (batch_stride >= n*row_bytes
+ * when batch > 1).
+ */
+int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* row_bytes,
+                            const int64_t* batch_stride, const int32_t* idx, int32_t batch,
+                            int32_t n, int32_t k, void* stream);
 
 /*
  * spatten_quantize_kv - K/V rows to separately fetchable MSB and LSB

@@ -67,6 +67,21 @@ int main() {
   d.cache_cap = 2048;
   EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_EINVAL);
+  // local value pruning: unquantized decode only; NaN and negative rejected
+  d.cache_cap = 2049;
+  d.v_threshold = 1e-4f;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+                     P, &got), SPATTEN_EUNSUPPORTED);
+  d.kv_quantized = 0;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, P, &got), SPATTEN_OK);
+  d.v_threshold = -1e-4f;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, P, &got), SPATTEN_EINVAL);
+  d.v_threshold = __builtin_nanf("");
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, P, &got), SPATTEN_EINVAL);
+  d.v_threshold = 0.0f;
   // top-k
   EXPECT(check_topk(fp, 4, 100, 100, 100, hi), SPATTEN_OK);
   EXPECT(check_topk(fp, 4, 100, 100, 101, hi), SPATTEN_EINVAL);
@@ -82,6 +97,16 @@ int main() {
   db[1] = 40;
   dst[0] = P + 800;
   EXPECT(check_compact(2, src, dst, rb, sb, db, hi, 2, 10), SPATTEN_EINVAL);
+  // in-place compaction
+  void* base[1] = {P};
+  int64_t irb[1] = {16}, ibs[1] = {1600};
+  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 100, 10), SPATTEN_OK);
+  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 100, 101), SPATTEN_EINVAL);
+  ibs[0] = 1599;
+  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 100, 10), SPATTEN_EINVAL);
+  ibs[0] = int64_t(16) << 20;
+  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 1 << 16, 8193), SPATTEN_EUNSUPPORTED);
+  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 1 << 16, 8192), SPATTEN_OK);
   // quantize
   EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 5 * 1024, u8, u8, fp, 5), SPATTEN_OK);
   EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1023, 5 * 1023, u8, u8, fp, 5), SPATTEN_EINVAL);

@@ -69,7 +69,7 @@ FAKE = 1 << 20   # 256-aligned fake address: the validator never dereferences
 def _call_layer(S, desc, ws_bytes, **kw):
     vp = ctypes.c_void_p
     names = ["x", "wq", "wk", "wv", "wo", "head_idx", "a", "g", "k_cache", "v_cache", "k_msb",
-             "k_lsb", "k_scale", "v_msb", "v_lsb", "v_scale", "recompute", "lse"]
+             "k_lsb", "k_scale", "v_msb", "v_lsb", "v_scale", "recompute", "v_kept", "lse"]
     args = [vp(kw[n]) if kw.get(n) else None for n in names]
     nb = ctypes.c_size_t(ws_bytes)
     return S.load().spatten_layer_forward(ctypes.byref(desc), *args, vp(kw.get("ws", FAKE)),
@@ -111,9 +111,6 @@ def test_decode_rejections(S):
                 n_heads_kept=12, head_dim=64, cache_len=10, cache_cap=11)
     p = _prefill_ptrs()
     p.update(k_cache=FAKE, v_cache=FAKE)
-    d = S.make_desc(**base)
-    need = S.workspace_bytes(d)
-    assert _call_layer(S, d, need, **p) == S.OK or True  # valid args would launch; not called
     d = S.make_desc(**{**base, "cache_cap": 10})
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(**{**base, "n_heads_kept": 10})
@@ -122,6 +119,15 @@ def test_decode_rejections(S):
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(**{**base, "kv_quantized": True})
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL     # planes missing, caches given
+    # local value pruning: a threshold must be a non-negative number, and is
+    # taken by unquantized decode only
+    for bad in (-1e-3, float("nan")):
+        d = S.make_desc(**{**base, "v_threshold": bad})
+        assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
+    d = S.make_desc(**{**base, "v_threshold": 1e-3, "kv_quantized": True, "pq_threshold": 0.1})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
+    d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, v_threshold=1e-3)
+    assert _call_layer(S, d, 1 << 40, **_prefill_ptrs()) == S.EUNSUPPORTED
 
 
 def test_topk_compact_quantize_rejections(S):
@@ -144,6 +150,24 @@ def test_topk_compact_quantize_rejections(S):
     assert lib.spatten_quantize_kv(vp(FAKE), 3, 2, 3, 8, 24, vp(FAKE), vp(FAKE), vp(FAKE), 3,
                                    None) == S.EINVAL       # bad dtype
     assert lib.spatten_quantize_kv(None, 1, 0, 3, 8, 24, None, None, None, 3, None) == S.OK
+
+
+def test_compact_inplace_rejections(S):
+    lib = S.load()
+    vp = ctypes.c_void_p
+    VP, I64 = vp * 1, ctypes.c_int64 * 1
+    f = lib.spatten_compact_inplace
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 101, None) == S.EINVAL  # k > n
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 0, None) == S.EINVAL
+    assert f(1, VP(FAKE), I64(16), I64(1599), vp(FAKE * 2), 2, 100, 10, None) == S.EINVAL
+    assert f(1, VP(FAKE), I64(0), I64(1600), vp(FAKE * 2), 2, 100, 10, None) == S.EINVAL
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2 + 2), 2, 100, 10, None) == S.EINVAL
+    assert f(1, VP(0), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 10, None) == S.EINVAL
+    # the selection is staged on chip: at most 8192 kept rows per sequence
+    assert f(1, VP(FAKE), I64(16), I64(16 * 9000), vp(FAKE * 2), 1, 9000, 8193,
+             None) == S.EUNSUPPORTED
+    assert f(0, None, None, None, None, 2, 100, 10, None) == S.OK
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 0, 100, 10, None) == S.OK
 
 
 def test_validator_standalone_with_sanitizers(tmp_path):

@@ -113,6 +113,71 @@ def test_compact_rejects_overlap(S):
         S.compact([(t, t, 16, 160, 160)], idx, 3)
 
 
+def inplace_expected(t, idx, k):
+    """The in-place cut as spatten.h states it: selected rows below k stay;
+    the i-th selected row at or above k goes to the i-th unselected row
+    below k; nothing else changes."""
+    out = t.copy()
+    below = set(int(j) for j in idx if j < k)
+    above = [int(j) for j in idx if j >= k]
+    holes = [r for r in range(k) if r not in below]
+    assert len(holes) == len(above)
+    for h, src in zip(holes, above):
+        out[h] = t[src]
+    return out
+
+
+def _inplace_case(S, B, n, k, idx, tensors):
+    dev = [torch.from_numpy(t.copy()).cuda() for t in tensors]
+    spec = [(d, d[0, 0].numel() * d.element_size(), d.stride(0) * d.element_size()) for d in dev]
+    S.compact_inplace(spec, torch.from_numpy(idx).cuda(), n, k)
+    for t, d in zip(tensors, dev):
+        got = d.cpu().numpy()
+        for b in range(B):
+            np.testing.assert_array_equal(got[b], inplace_expected(t[b], idx[b], k))
+            # as a set, the kept rows are the gathered ones
+            kept = got[b, :k].reshape(k, -1)
+            ref = R.compact(t[b], idx[b]).reshape(k, -1)
+            assert sorted(map(bytes, kept)) == sorted(map(bytes, ref))
+
+
+@pytest.mark.parametrize("B,n,k,pattern", [
+    (3, 97, 41, "random"), (4, 411, 410, "random"), (2, 411, 410, "drop_first"),
+    (2, 411, 410, "drop_last"), (3, 1025, 410, "random"), (2, 60, 20, "tail"),
+    (2, 60, 20, "head"), (1, 9000, 8192, "random"), (5, 7, 7, "random"), (2, 2, 1, "random")])
+def test_compact_inplace_bit_exact(S, B, n, k, pattern):
+    print("inplace case", B, n, k, pattern, flush=True)
+    rng = np.random.default_rng(n * 7 + k)
+    if pattern == "random":
+        idx = [np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]
+    elif pattern == "drop_first":
+        idx = [np.arange(1, n) for _ in range(B)]
+    elif pattern == "drop_last":
+        idx = [np.arange(0, n - 1) for _ in range(B)]
+    elif pattern == "tail":
+        idx = [np.arange(n - k, n) for _ in range(B)]
+    else:
+        idx = [np.arange(k) for _ in range(B)]
+    idx = np.stack(idx).astype(np.int32)
+    tensors = [
+        rng.standard_normal((B, n, 384)).astype(np.float32),           # 16-byte units
+        rng.integers(0, 255, (B, n, 6), dtype=np.uint8),               # 2-byte units
+        rng.integers(0, 255, (B, n, 3), dtype=np.uint8),               # byte units
+        rng.standard_normal((B, n)).astype(np.float32),                 # 4-byte rows
+        rng.integers(0, 1 << 30, (B, n, 2), dtype=np.int32),           # 8-byte units
+    ]
+    _inplace_case(S, B, n, k, idx, tensors)
+
+
+def test_compact_inplace_many_tensors(S):
+    """More tensors than one launch takes: the call splits them."""
+    rng = np.random.default_rng(5)
+    B, n, k = 2, 50, 30
+    idx = np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    tensors = [rng.integers(0, 1 << 20, (B, n, i % 5 + 1), dtype=np.int32) for i in range(60)]
+    _inplace_case(S, B, n, k, idx, tensors)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("B,n,D", [(1, 1, 2), (2, 5, 8), (3, 17, 768), (2, 33, 1024), (1, 4, 1026)])
 def test_quantize_bit_exact(S, dtype, B, n, D):

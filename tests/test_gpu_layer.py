@@ -116,7 +116,7 @@ def _decode_setup(rng, B, H, dh, L0, cap, quantized):
     return K0.astype(np.float32), V0.astype(np.float32)
 
 
-@pytest.mark.parametrize("B,H,L0,quantized,thr", [
+DECODE_LAYER_CASES = [
     (3, 12, 100, False, 0.0), (2, 12, 1024, False, 0.0), (4, 16, 300, True, 0.1),
     (2, 16, 257, True, 0.0), (2, 16, 257, True, 1.01), (64, 12, 130, False, 0.0),
     # empty cache before the step (the new row is the only key)
@@ -126,9 +126,20 @@ def _decode_setup(rng, B, H, dh, L0, cap, quantized):
     # one head; an odd head count with a partial last wave
     (3, 1, 40, False, 0.0), (1, 5, 31, True, 0.05),
     # batches past the 64-row decode projection kernel (tiled GEMM fallback)
-    (65, 12, 50, False, 0.0), (96, 16, 33, True, 0.1)])
-def test_decode_layer(S, B, H, L0, quantized, thr):
-    print("decode case", B, H, L0, quantized, thr, flush=True)
+    (65, 12, 50, False, 0.0), (96, 16, 33, True, 0.1)]
+# local value pruning: (B, H, L0, v_threshold). Threshold 0.5 keeps at most
+# one V row per head, 1.01 keeps none (O = 0), and an empty cache's only row
+# (p = 1) is kept.
+VPRUNE_CASES = [(3, 12, 100, 1e-3), (2, 12, 1024, 1e-4), (64, 12, 130, 1e-2),
+                (2, 32, 64, 2e-2), (3, 1, 40, 3e-2), (1, 5, 31, 5e-2), (65, 12, 50, 1e-2),
+                (2, 12, 100, 0.5), (2, 12, 100, 1.01), (1, 12, 0, 0.5)]
+
+
+@pytest.mark.parametrize("B,H,L0,quantized,thr,vthr",
+                         [c + (0.0,) for c in DECODE_LAYER_CASES] +
+                         [(B, H, L0, False, 0.0, v) for B, H, L0, v in VPRUNE_CASES])
+def test_decode_layer(S, B, H, L0, quantized, thr, vthr):
+    print("decode case", B, H, L0, quantized, thr, vthr, flush=True)
     dh = 64
     D = H * dh
     rng = np.random.default_rng(B * 10 + L0)
@@ -138,7 +149,7 @@ def test_decode_layer(S, B, H, L0, quantized, thr):
     x = R.bf16_round(rng.standard_normal((B, D))).astype(np.float32)
     a0 = np.zeros((B, cap), np.float32)
     a0[:, :L0] = rng.random((B, L0)) * 5
-    desc = S.make_desc(S.DECODE, S.BF16, False, B, 1, H, H, dh, L0, cap, quantized, thr)
+    desc = S.make_desc(S.DECODE, S.BF16, False, B, 1, H, H, dh, L0, cap, quantized, thr, vthr)
     ws = torch.zeros(S.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     wd = _dev_w(w, torch.bfloat16)
     xd = to_dev(x.reshape(B, 1, D), torch.bfloat16)
@@ -146,6 +157,7 @@ def test_decode_layer(S, B, H, L0, quantized, thr):
     gd = torch.zeros(B, H, device="cuda")
     hidx = torch.arange(H, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
     rec = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
+    vk = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     kw = {}
     if quantized:
         for name, arr in (("k", K0), ("v", V0)):
@@ -161,9 +173,10 @@ def test_decode_layer(S, B, H, L0, quantized, thr):
         vc[:, :L0] = to_dev(V0, torch.bfloat16)
         kw.update({"k_cache": kc, "v_cache": vc})
     S.layer_forward(desc, xd, wd["wq"], wd["wk"], wd["wv"], wd["wo"], hidx, ad, gd, ws,
-                    recompute=rec, **kw)
+                    recompute=rec, v_kept=vk, **kw)
     torch.cuda.synchronize()
     xo, ao, rc = to_np(xd).reshape(B, D), to_np(ad), rec.cpu().numpy()
+    vkept = vk.cpu().numpy()
     assert float(gd.abs().sum()) == 0.0
     n_rec = 0
     for b in range(B):
@@ -175,7 +188,13 @@ def test_decode_layer(S, B, H, L0, quantized, thr):
         else:
             cache = {"k": K0[b].reshape(L0, H, dh).astype(np.float64),
                      "v": V0[b].reshape(L0, H, dh).astype(np.float64)}
-        xr, P, recr, cmax, _ = R.decode_layer(x[b], w, cache, H, dh, True, quantized, thr)
+        xr, P, recr, cmax, kr = R.decode_layer(x[b], w, cache, H, dh, True, quantized, thr,
+                                               v_threshold=vthr)
+        # V rows kept: equal to the oracle's count but for probabilities
+        # within 2% of the threshold, where the bf16 rounding of q and k on
+        # the two sides may put a row on either side
+        band = np.sum(np.abs(P - vthr) <= 2e-2 * vthr, axis=1) if vthr > 0 else 0
+        assert np.all(np.abs(vkept[b] - kr) <= band), (b, vkept[b], kr)
         if quantized:
             for h in range(H):
                 if abs(cmax[h] - thr) > 1e-5 * thr:

@@ -28,10 +28,15 @@ from gpu_util import PrefillWs, check_bf16_output, check_selection, to_np
 from oracle import spatten_ref as R
 from workloads import (BERT_BASE, GPT2_DECODE, LONG_CAUSAL, PQ_DECODE, TINY, make_decode_inputs,
                        make_prefill_inputs, scaled)
+from workloads.configs import GPT2_DECODE_ROLLING, GPT2_DECODE_VPRUNE
 
 pytestmark = pytest.mark.gpu
 
 BAND = 1e-5
+# value-pruning decisions compare fp32 probabilities of deep layers, whose
+# scores reach hundreds (log2 units): exp2(s - lse) carries up to ~1e-4
+# relative error there
+VBAND = 1e-3
 
 
 def _dtype(cfg):
@@ -307,21 +312,62 @@ def _cache_np(c, b, rows, quantized, H, dh):
             "v": to_np(c["v_cache"][b, :rows]).reshape(rows, H, dh)}
 
 
+def _rows_np(t, b, n):
+    """Rows 0..n-1 of sequence b of a cache tensor, exact (bf16 as fp32)."""
+    v = t[b, :n]
+    return (v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy()
+
+
+def cut_slots(slots, sel, k, inplace):
+    """Slot contents after a cut, as the pipeline states it: a gather in
+    order, or the in-place move (selected rows below k stay, the i-th
+    selected row at or above k fills the i-th unselected row below k)."""
+    slots = list(slots)
+    if not inplace:
+        return [slots[j] for j in sel]
+    below = set(int(j) for j in sel if j < k)
+    above = [int(j) for j in sel if j >= k]
+    holes = [r for r in range(k) if r not in below]
+    out = slots[:k]
+    for h, j in zip(holes, above):
+        out[h] = slots[j]
+    return out
+
+
 def run_decode_checked(cfg, inputs, seqs, steps=None):
     """Run the decode stack on the GPU; at every layer of every step check
-    the sampled sequences against the oracle on the GPU's own inputs."""
+    the sampled sequences against the oracle on the GPU's own inputs, and
+    check that every cache row holds the entry the cuts say it holds."""
     dt = _dtype(cfg)
     H, dh, D, B = cfg.n_heads, cfg.head_dim, cfg.model_dim, cfg.batch
     w = pipeline.weights_to_device(inputs["layers"], dt)
     st = pipeline.DecodeStack(cfg.n_layers, B, H, dh, cfg.cache_len, cfg.cache_keep, cfg.steps,
-                              w, cfg.quantized, cfg.pq_threshold, dt)
+                              w, cfg.quantized, cfg.pq_threshold, dt,
+                              v_threshold=cfg.v_threshold, prune_every=cfg.prune_every)
     k0 = [torch.from_numpy(l["k_cache"]).to(dt).cuda() for l in inputs["layers"]]
     v0 = [torch.from_numpy(l["v_cache"]).to(dt).cuda() for l in inputs["layers"]]
     st.load(k0, v0)
-    stats = {"pq_rows": 0, "pq_recomputed": 0, "pq_in_band": 0, "sel_diff": 0,
-             "x_nrmse": 0.0, "q_nrmse": 0.0}
+    stats = {"pq_rows": 0, "pq_recomputed": 0, "pq_in_band": 0, "sel_diff": 0, "cuts": 0,
+             "x_nrmse": 0.0, "q_nrmse": 0.0, "v_rows": 0, "v_kept": 0}
     snap = {}
-    a_ora = {b: np.zeros(cfg.cache_len + 1) for b in seqs}   # oracle importance, step 1
+    cap = cfg.cache_cap
+    # oracle importance (fp64) and the entry id of every cache slot, per sequence
+    a_ora = {b: np.zeros(cap) for b in seqs}
+    ids = {b: list(range(cfg.cache_len)) for b in seqs}
+    # cache rows by entry id (ids are 0 .. L0 + steps - 1), per layer,
+    # sequence and tensor: the loaded rows, then each step's appended row
+    # (itself checked against the oracle)
+    rows = []
+    for l in range(cfg.n_layers):
+        c = st.caches[st.side][l]
+        per_b = {}
+        for b in seqs:
+            per_b[b] = {}
+            for name, t in c.items():
+                store = np.zeros((cap,) + tuple(t.shape[2:]), dtype=_rows_np(t, b, 1).dtype)
+                store[:cfg.cache_len] = _rows_np(t, b, cfg.cache_len)
+                per_b[b][name] = store
+        rows.append(per_b)
 
     def hook(phase, l):
         torch.cuda.synchronize()
@@ -334,6 +380,7 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
         q = to_np(st.ws[: B * D * 2].view(torch.bfloat16)).reshape(B, H, dh)
         a_out = to_np(st.abuf[st.side])
         rec = st.recompute[l].cpu().numpy()
+        vk = st.v_kept[l].cpu().numpy()
         W = inputs["layers"][l]
         c = st.caches[st.side][l]
         for b in seqs:
@@ -342,6 +389,13 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
             stats["q_nrmse"] = max(stats["q_nrmse"],
                                    check_bf16_output(q[b], qref, what="q l%d b%d" % (l, b))[0])
             cache = _cache_np(c, b, lc, cfg.quantized, H, dh)
+            # every row but the appended one holds the entry the cuts put there
+            new_id = cfg.cache_len + st.s
+            for name, t in c.items():
+                arr = _rows_np(t, b, lc)
+                np.testing.assert_array_equal(arr[:lc - 1], rows[l][b][name][ids[b]],
+                                              err_msg="%s l%d b%d" % (name, l, b))
+                rows[l][b][name][new_id] = arr[lc - 1]
             # the appended entry holds this token's k and v
             for name, wname in (("k", "wk"), ("v", "wv")):
                 ref = R.bf16_round(xi @ W[wname].astype(np.float64))
@@ -365,8 +419,14 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
                     stats["pq_in_band"] += 1
                 return g
 
-            O, P, rc, cmax, _ = R.decode_attention(q[b], cache, H, dh, cfg.quantized,
-                                                cfg.pq_threshold, decide)
+            O, P, rc, cmax, kr = R.decode_attention(q[b], cache, H, dh, cfg.quantized,
+                                                    cfg.pq_threshold, decide, cfg.v_threshold)
+            # same q and cache on both sides: a kept-row count may differ only
+            # by rows whose probability is within the tie band of the threshold
+            vb = np.sum(np.abs(P - cfg.v_threshold) <= VBAND * cfg.v_threshold, axis=1)
+            assert np.all(np.abs(vk[b] - kr) <= vb), (l, b, vk[b], kr)
+            stats["v_rows"] += H * lc
+            stats["v_kept"] += int(vk[b].sum())
             stats["pq_rows"] += H if cfg.quantized else 0
             stats["pq_recomputed"] += int(rc.sum())
             xr = R.bf16_round(xi + sum(R.bf16_round(O[h]) @ W["wo"][h * dh:(h + 1) * dh, :]
@@ -378,20 +438,35 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
             # deep layers carry large scores (hundreds in log2 units); fp32
             # exp(s - lse) then has ~1e-5..1e-4 relative error per entry
             assert np.max(np.abs(da - ps)) <= 2e-6 * H + 1e-4 * np.max(ps), (l, b)
-            if st.s == 0:
-                a_ora[b] += ps
+            a_ora[b][:lc] += ps
 
     outs = []
+    keep = cfg.cache_keep
     for s in range(cfg.steps if steps is None else steps):
         x = torch.from_numpy(inputs["x_steps"][s]).to(dt).cuda()
         outs.append(to_np(st.step(x, record=True, hook=hook)))
-        if s == 0:
-            sel = st.trace[0]["cache_sel"].cpu().numpy()
-            a_gpu = to_np(st.abuf[st.side ^ 1])
-            for b in seqs:
-                np.testing.assert_array_equal(
-                    sel[b], R.topk(a_gpu[b, :cfg.cache_len + 1].astype(np.float32), cfg.cache_keep))
-                stats["sel_diff"] += check_selection(sel[b], a_ora[b], cfg.cache_keep, BAND)
+        for b in seqs:
+            ids[b].append(cfg.cache_len + s)
+        tr = st.trace[-1]
+        assert ("cache_sel" in tr) == (R.prune_after_step(cfg, s) and len(ids[seqs[0]]) > keep)
+        if "cache_sel" not in tr:
+            continue
+        stats["cuts"] += 1
+        sel = tr["cache_sel"].cpu().numpy()
+        a_pre = tr["a_before_cut"].cpu().numpy()
+        a_now = to_np(st.abuf[st.side])
+        n = a_pre.shape[1]
+        for b in seqs:
+            np.testing.assert_array_equal(sel[b], R.topk(a_pre[b].astype(np.float32), keep))
+            stats["sel_diff"] += check_selection(sel[b], a_ora[b][:n], keep, BAND)
+            # the cut moves a with the caches; entries past the kept range
+            # start again from 0
+            moved = np.array(cut_slots(a_pre[b], sel[b], keep, st.inplace))
+            np.testing.assert_array_equal(a_now[b, :keep], moved)
+            assert np.all(a_now[b, keep:] == 0)
+            a_ora[b] = np.concatenate([cut_slots(a_ora[b][:n], sel[b], keep, st.inplace),
+                                       np.zeros(cap - keep)])
+            ids[b] = cut_slots(ids[b], sel[b], keep, st.inplace)
     return st, np.stack(outs), stats
 
 
@@ -402,6 +477,16 @@ DECODE_CFGS = {
                              steps=3, pq_threshold=0.0), [0, 1]),
     "pq_small_all": (scaled(PQ_DECODE, batch=2, n_layers=3, cache_len=200, cache_keep=100,
                             steps=3, pq_threshold=1.01), [1]),
+    "gpt2_vprune": (scaled(GPT2_DECODE_VPRUNE, batch=4, cache_len=256, cache_keep=102, steps=4),
+                    [0, 3]),
+    "gpt2_vprune_coarse": (scaled(GPT2_DECODE_VPRUNE, batch=3, n_layers=4, cache_len=300,
+                                  cache_keep=120, steps=3, v_threshold=1e-2), [1]),
+    "gpt2_rolling": (scaled(GPT2_DECODE_ROLLING, batch=4, n_layers=4, cache_len=256,
+                            cache_keep=102, steps=6), [0, 3]),
+    "gpt2_rolling_every3": (scaled(GPT2_DECODE_ROLLING, batch=3, n_layers=3, cache_len=200,
+                                   cache_keep=80, steps=8, prune_every=3), [2]),
+    "pq_rolling": (scaled(PQ_DECODE, batch=2, n_layers=3, cache_len=300, cache_keep=150,
+                          steps=5, prune_every=1), [1]),
 }
 
 
@@ -416,10 +501,18 @@ def test_decode_stack(name):
         assert stats["pq_recomputed"] == 0
     if cfg.quantized and cfg.pq_threshold > 1.0:
         assert stats["pq_recomputed"] == stats["pq_rows"]
+    if cfg.v_threshold > 0:
+        assert 0 < stats["v_kept"] < stats["v_rows"]
+    else:
+        assert stats["v_kept"] == stats["v_rows"]
+    steps = cfg.steps
+    assert stats["cuts"] == sum(R.prune_after_step(cfg, s) for s in range(steps))
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("cfg", [GPT2_DECODE, PQ_DECODE], ids=["gpt2_decode", "pq_decode"])
+@pytest.mark.parametrize("cfg", [GPT2_DECODE, PQ_DECODE, GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING],
+                         ids=["gpt2_decode", "pq_decode", "gpt2_decode_vprune",
+                              "gpt2_decode_rolling"])
 def test_decode_stack_full_size(cfg):
     """Full batch, cache and layer count; per-layer checks on 1 sequence
     for the first 3 steps (the cache pruning happens after step 1)."""

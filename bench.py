@@ -76,12 +76,18 @@ def _kernel_work(cfg, v_kept=None):
                 if cfg.quantized:
                     add("pq_attn_msb", 4.0 * B * H * dh * lc, 2 * B * lc * (D // 2 + 4))
                 elif cfg.v_threshold > 0:
-                    # K rows once; fp32 scores written, then read back with the
-                    # kept V rows (a 128-byte head slice each) and a updated
-                    add("decode_scores", 2.0 * B * H * dh * lc, B * lc * D * es + 4 * B * H * lc)
+                    # K rows once, the kept V rows (a 128-byte head slice
+                    # each) and the fp32 scores the importance pass reads
                     kept = v_kept[s][l] if v_kept is not None else 0
-                    add("decode_vprune", 2.0 * dh * kept,
-                        kept * dh * es + 4 * B * H * lc + 8 * B * lc)
+                    fl = 2.0 * B * H * dh * lc + 2.0 * dh * kept
+                    by = B * lc * D * es + kept * dh * es + 4 * B * H * lc
+                    if -(-lc // 32) * 32 <= 4096:
+                        add("decode_vrow", fl, by)
+                    else:
+                        add("decode_scores", 2.0 * B * H * dh * lc,
+                            B * lc * D * es + 4 * B * H * lc)
+                        add("decode_vprune", 2.0 * dh * kept,
+                            kept * dh * es + 4 * B * H * lc + 8 * B * lc)
                 else:
                     add("decode_attn", 4.0 * B * H * dh * lc, 2 * B * lc * D * es)
     return w

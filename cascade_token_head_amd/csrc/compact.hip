@@ -90,7 +90,6 @@ struct InplaceTensor {
 
 struct InplaceParams {
   InplaceTensor t[kCompactMax];
-  int count;
 };
 
 template <int V>
@@ -108,7 +107,8 @@ __device__ __forceinline__ void move_units(const InplaceTensor& t, char* bbase, 
   }
 }
 
-// grid (ceil(max moves / kMovesPerBlock), batch). Sequence b's selection
+// grid (ceil(max moves / kMovesPerBlock), batch, tensors): each workgroup
+// moves its share of one tensor's rows of one sequence. Sequence b's selection
 // idx[b, 0:k] is ascending; c = number of selected rows below k, and the
 // k - c selected rows at or above k are idx[c..k-1]. With d_j = idx[j] - j
 // (non-decreasing for j < c), the i-th unselected row below k is
@@ -143,16 +143,14 @@ compact_inplace_kernel(InplaceParams p, const int32_t* __restrict__ idx, int k) 
     src[threadIdx.x] = sel[c + i];
   }
   __syncthreads();
-  for (int ti = 0; ti < p.count; ++ti) {
-    const InplaceTensor& t = p.t[ti];
-    char* bbase = t.base + int64_t(b) * t.bs;
-    switch (t.vec_shift) {
-      case 4: move_units<16>(t, bbase, src, dst, nm); break;
-      case 3: move_units<8>(t, bbase, src, dst, nm); break;
-      case 2: move_units<4>(t, bbase, src, dst, nm); break;
-      case 1: move_units<2>(t, bbase, src, dst, nm); break;
-      default: move_units<1>(t, bbase, src, dst, nm); break;
-    }
+  const InplaceTensor& t = p.t[blockIdx.z];
+  char* bbase = t.base + int64_t(b) * t.bs;
+  switch (t.vec_shift) {
+    case 4: move_units<16>(t, bbase, src, dst, nm); break;
+    case 3: move_units<8>(t, bbase, src, dst, nm); break;
+    case 2: move_units<4>(t, bbase, src, dst, nm); break;
+    case 1: move_units<2>(t, bbase, src, dst, nm); break;
+    default: move_units<1>(t, bbase, src, dst, nm); break;
   }
 }
 
@@ -166,8 +164,8 @@ int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_
   const unsigned blocks = unsigned(ceil_div(max_moves, kMovesPerBlock));
   for (int t0 = 0; t0 < n_tensors; t0 += kCompactMax) {
     InplaceParams p{};
-    p.count = n_tensors - t0 < kCompactMax ? n_tensors - t0 : kCompactMax;
-    for (int i = 0; i < p.count; ++i) {
+    const int cnt = n_tensors - t0 < kCompactMax ? n_tensors - t0 : kCompactMax;
+    for (int i = 0; i < cnt; ++i) {
       const int t = t0 + i;
       p.t[i].base = static_cast<char*>(base[t]);
       p.t[i].row_bytes = row_bytes[t];
@@ -175,8 +173,8 @@ int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_
       p.t[i].vec_shift = vec_shift_for(base[t], base[t], row_bytes[t], bs[t], bs[t]);
     }
     SPATTEN_TIMED("compact_inplace", stream,
-                  compact_inplace_kernel<<<dim3(blocks, unsigned(batch)), dim3(256), 0,
-                                           stream>>>(p, idx, k));
+                  compact_inplace_kernel<<<dim3(blocks, unsigned(batch), unsigned(cnt)),
+                                           dim3(256), 0, stream>>>(p, idx, k));
     SPATTEN_LAUNCH_CHECK();
   }
   return SPATTEN_OK;

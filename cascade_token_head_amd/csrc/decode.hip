@@ -26,13 +26,15 @@
 // token importance.
 //
 // Local value pruning (section III "Local Value Pruning": after the softmax
-// a head drops its low-probability V vectors): the scores pass reads K only
-// and leaves per-chunk statistics; decode_vprune, with every chunk's
-// statistics of a row in hand, forms the exact probabilities of its chunk,
-// adds them to the token importance and reads only the V rows whose
-// probability reaches the threshold for that head (a 128-byte head slice of
-// the cache row is fetched or skipped whole); decode_vsum adds the chunks'
-// normalised partial outputs.
+// a head drops its low-probability V vectors). A V row can only be skipped
+// once the row's exact probabilities are known, i.e. after the softmax over
+// the whole cache. decode_vrow gives each (sequence, head) row one
+// workgroup that keeps all of the row's scores in LDS, so it reads K, forms
+// the probabilities and then fetches only the V head slices (128 bytes of a
+// cache row) that reach the threshold; decode_finish adds the importance.
+// Caches too long for LDS take a split path: a K-only scores pass with
+// per-chunk statistics, decode_vprune (exact probabilities per chunk,
+// importance, kept V rows) and decode_vsum (sum of the chunk outputs).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
@@ -268,6 +270,130 @@ decode_partial(DecodeArgs a) {
     float* op = a.opart + ((int64_t(b) * H + h) * a.nchunk + chunk) * dh + d0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) op[e] = acc[e];
+  }
+}
+
+// Cache rows one decode_vrow workgroup keeps scores for in LDS.
+constexpr int kVrowMaxRows = 4096;
+
+// Local value pruning, one workgroup per (sequence, head) row, grid B * H,
+// 256 threads = 32 row groups x 8 lanes; lane c8 of row group g owns the
+// 16-byte slice c8 (dims 8 c8 .. 8 c8 + 7) of rows g, g + 32, ... of the
+// head. Needs lc_pad <= kVrowMaxRows and dh 64.
+__global__ void __launch_bounds__(256)
+decode_vrow(DecodeArgs a) {
+  __shared__ float S[kVrowMaxRows];
+  __shared__ float ob[32][65];
+  __shared__ float red[8];
+  __shared__ int kred[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = t >> 3, c8 = t & 7;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int D = a.H * 64;
+  const int64_t rowb = int64_t(b) * a.cap;
+  const int col = h * 64 + 8 * c8;
+  const int lc = a.lc;
+  const int nit = (lc + 31) >> 5;  // rows per row group
+  const float tau = a.v_threshold;
+  float q[8];
+  {
+    const u32x4 w =
+        *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + int64_t(b) * D + col);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[2 * e] = __uint_as_float(w[e] << 16);
+      q[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  const float sc = kLog2e / 8.0f;  // log2(e) / sqrt(64)
+  const bf16_t* kc = static_cast<const bf16_t*>(a.k_cache) + col;
+  const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache) + col;
+  // ---- scores of the whole row (rows past the end read row lc-1, unused)
+  for (int i0 = 0; i0 < nit; i0 += KB) {
+    u32x4 raw[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = g + 32 * (i0 + u);
+      raw[u] = *reinterpret_cast<const u32x4*>(kc + (rowb + (j < lc ? j : lc - 1)) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(q[2 * e], __uint_as_float(raw[u][e] << 16), d);
+        d = fmaf(q[2 * e + 1], __uint_as_float(raw[u][e] & 0xffff0000u), d);
+      }
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 4, 64);
+      const int j = g + 32 * (i0 + u);
+      if (c8 == 0 && j < lc) {
+        S[j] = d * sc;
+        a.scores[int64_t(bh) * a.lc_pad + j] = d * sc;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- row log2-sum-exp
+  float m = -INFINITY;
+  for (int j = t; j < lc; j += 256) m = fmaxf(m, S[j]);
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float l = 0.0f;
+  for (int j = t; j < lc; j += 256) l += fast_exp2(S[j] - M);
+  l = wave_sum(l);
+  if (lane == 0) red[4 + wave] = l;
+  __syncthreads();
+  const float L = (red[4] + red[5]) + (red[6] + red[7]);
+  const float lse2 = M + log2f(L);
+  // ---- P V over the rows that reach the threshold; the others are not read
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int kept = 0;
+  for (int i0 = 0; i0 < nit; i0 += KB) {
+    u32x4 vr[KB];
+    float pw[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = g + 32 * (i0 + u);
+      const float p = j < lc ? fast_exp2(S[j] - lse2) : 0.0f;
+      if (j < lc && p >= tau) {
+        vr[u] = *reinterpret_cast<const u32x4*>(vc + (rowb + j) * D);
+        pw[u] = p;
+        kept += c8 == 0 ? 1 : 0;
+      } else {
+        vr[u] = u32x4{0u, 0u, 0u, 0u};
+        pw[u] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(pw[u], __uint_as_float(vr[u][e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(pw[u], __uint_as_float(vr[u][e] & 0xffff0000u), acc[2 * e + 1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ob[g][8 * c8 + e] = acc[e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kept += __shfl_xor(kept, o, 64);
+  if (lane == 0) kred[wave] = kept;
+  __syncthreads();
+  if (t < 64) {
+    float o = 0.0f;
+    for (int r = 0; r < 32; ++r) o += ob[r][t];
+    static_cast<bf16_t*>(a.o)[int64_t(b) * D + h * 64 + t] = f32_to_bf16(o);
+  }
+  if (t == 0) {
+    a.lse[bh] = lse2;
+    a.cmax[bh] = 1.0f / L;
+    if (a.v_kept) a.v_kept[bh] = (kred[0] + kred[1]) + (kred[2] + kred[3]);
+    if (a.recompute) a.recompute[bh] = 0;
   }
 }
 
@@ -518,16 +644,19 @@ decode_recompute(DecodeArgs a) {
 }
 
 // One workgroup per sequence, one wave per head (up to 16 waves): combine
-// the rows not combined yet (all rows, or the recomputed ones), then
+// the rows not combined yet (mode 0: every row; 1, quantized: the
+// recomputed ones; 2: none, every row's lse is written), then
 // a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h]) for j < lc.
+enum { kFinishAll = 0, kFinishQuantized = 1, kFinishLseReady = 2 };
 __global__ void __launch_bounds__(1024)
-decode_finish(DecodeArgs a, int quantized) {
+decode_finish(DecodeArgs a, int mode) {
+  const bool quantized = mode == kFinishQuantized;
   __shared__ float lse[kMaxHeads];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6, nt = blockDim.x;
   for (int h = wave; h < a.H; h += nw) {
     const int64_t bh = int64_t(b) * a.H + h;
-    if (!quantized || a.flags[bh]) {
+    if (mode == kFinishAll || (quantized && a.flags[bh])) {
       float cmax;
       const float l2 = combine_row(a, b, h, true, &cmax);
       if (lane == 0) {
@@ -541,7 +670,7 @@ decode_finish(DecodeArgs a, int quantized) {
     } else if (lane == 0) {
       lse[h] = a.lse[bh];
     }
-    if (lane == 0 && a.v_kept) a.v_kept[bh] = a.lc;
+    if (lane == 0 && a.v_kept && mode != kFinishLseReady) a.v_kept[bh] = a.lc;
   }
   __syncthreads();
   const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
@@ -574,6 +703,16 @@ int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream) {
   if (a.dh != 64 || a.H > kMaxHeads || threads > 256 || threads < 128)
     return SPATTEN_EUNSUPPORTED;
   const dim3 gp(a.nchunk, a.batch);
+  const int fw = a.H < 16 ? a.H : 16;
+  if (!quantized && a.v_threshold > 0.0f && a.lc_pad <= kVrowMaxRows) {
+    SPATTEN_TIMED("decode_vrow", stream,
+                  decode_vrow<<<a.batch * a.H, 256, 0, stream>>>(a));
+    SPATTEN_LAUNCH_CHECK();
+    SPATTEN_TIMED("decode_finish", stream,
+                  decode_finish<<<a.batch, 64 * fw, 0, stream>>>(a, kFinishLseReady));
+    SPATTEN_LAUNCH_CHECK();
+    return SPATTEN_OK;
+  }
   if (!quantized && a.v_threshold > 0.0f) {
     SPATTEN_TIMED("decode_scores", stream,
                   (decode_partial<kBf16, false><<<gp, threads, 0, stream>>>(a)));
@@ -597,9 +736,9 @@ int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream) {
     SPATTEN_TIMED("pq_attn_recompute", stream, decode_recompute<<<gr, 64, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
   }
-  const int fw = a.H < 16 ? a.H : 16;
   SPATTEN_TIMED("decode_finish", stream,
-                decode_finish<<<a.batch, 64 * fw, 0, stream>>>(a, quantized ? 1 : 0));
+                decode_finish<<<a.batch, 64 * fw, 0, stream>>>(
+                    a, quantized ? kFinishQuantized : kFinishAll));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }

@@ -132,7 +132,9 @@ DECODE_LAYER_CASES = [
 # (p = 1) is kept.
 VPRUNE_CASES = [(3, 12, 100, 1e-3), (2, 12, 1024, 1e-4), (64, 12, 130, 1e-2),
                 (2, 32, 64, 2e-2), (3, 1, 40, 3e-2), (1, 5, 31, 5e-2), (65, 12, 50, 1e-2),
-                (2, 12, 100, 0.5), (2, 12, 100, 1.01), (1, 12, 0, 0.5)]
+                (2, 12, 100, 0.5), (2, 12, 100, 1.01), (1, 12, 0, 0.5),
+                # past the 4096 rows one workgroup holds: the split path
+                (2, 12, 4200, 1e-4), (3, 5, 5000, 1e-3)]
 
 
 @pytest.mark.parametrize("B,H,L0,quantized,thr,vthr",

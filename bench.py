@@ -20,7 +20,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -117,18 +116,10 @@ def _traffic(kernel, workload, launches):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha1") != _source_hash():
+    from cascade_token_head_amd.traffic import source_sha1
+    if rec.get("source_sha1") != source_sha1(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
-
-
-def _source_hash():
-    h = hashlib.sha1()
-    csrc = os.path.join(ROOT, "cascade_token_head_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode() + f.read())
-    return h.hexdigest()
 
 
 def _cpu_baseline(cfg, inputs, budget_s: float):

@@ -96,37 +96,54 @@ template <int V>
 __device__ __forceinline__ void move_units(const InplaceTensor& t, char* bbase, const int* src,
                                            const int* dst, int nmoves) {
   using T = typename VecT<V>::T;
-  const int64_t upr = t.row_bytes / V;
-  const int64_t total = int64_t(nmoves) * upr;
-  for (int64_t u = threadIdx.x; u < total; u += blockDim.x) {
-    const int m = int(u / upr);
-    const int64_t part = u - int64_t(m) * upr;
-    const T* s = reinterpret_cast<const T*>(bbase + int64_t(src[m]) * t.row_bytes) + part;
-    T* d = reinterpret_cast<T*>(bbase + int64_t(dst[m]) * t.row_bytes) + part;
-    *d = *s;
+  constexpr int U = 8;  // loads in flight per thread before their stores
+  const int upr = int(t.row_bytes / V);
+  const int total = nmoves * upr;
+  for (int u0 = threadIdx.x; u0 < total; u0 += U * blockDim.x) {
+    T buf[U];
+#pragma unroll
+    for (int w = 0; w < U; ++w) {
+      const int u = u0 + w * blockDim.x;
+      if (u < total) {
+        const int m = u / upr, part = u - m * upr;
+        buf[w] = reinterpret_cast<const T*>(bbase + int64_t(src[m]) * t.row_bytes)[part];
+      }
+    }
+    // sources sit at or above k, destinations below it: no overlap
+#pragma unroll
+    for (int w = 0; w < U; ++w) {
+      const int u = u0 + w * blockDim.x;
+      if (u < total) {
+        const int m = u / upr, part = u - m * upr;
+        reinterpret_cast<T*>(bbase + int64_t(dst[m]) * t.row_bytes)[part] = buf[w];
+      }
+    }
   }
 }
 
 // grid (ceil(max moves / kMovesPerBlock), batch, tensors): each workgroup
-// moves its share of one tensor's rows of one sequence. Sequence b's selection
-// idx[b, 0:k] is ascending; c = number of selected rows below k, and the
-// k - c selected rows at or above k are idx[c..k-1]. With d_j = idx[j] - j
-// (non-decreasing for j < c), the i-th unselected row below k is
-// i + #{j < c : d_j <= i}.
-__global__ void __launch_bounds__(256)
+// moves its share of one tensor's rows of one sequence. Sequence b's
+// selection idx[b, 0:k] is ascending and staged in LDS (k ints); c = number
+// of selected rows below k, and the k - c selected rows at or above k are
+// idx[c..k-1]. With d_j = idx[j] - j (non-decreasing for j < c), the i-th
+// unselected row below k is i + #{j < c : d_j <= i}.
+__global__ void __launch_bounds__(128)
 compact_inplace_kernel(InplaceParams p, const int32_t* __restrict__ idx, int k) {
-  __shared__ int sel[kInplaceMaxK];
+  extern __shared__ int sel[];
   __shared__ int src[kMovesPerBlock], dst[kMovesPerBlock];
   __shared__ int nbelow;
   const int b = blockIdx.y;
   const int32_t* ib = idx + int64_t(b) * k;
   for (int j = threadIdx.x; j < k; j += blockDim.x) sel[j] = ib[j];
-  if (threadIdx.x == 0) nbelow = 0;
   __syncthreads();
-  // c: selected rows below k (ascending, so a count is a boundary)
-  int cnt = 0;
-  for (int j = threadIdx.x; j < k; j += blockDim.x) cnt += sel[j] < k ? 1 : 0;
-  if (cnt) atomicAdd(&nbelow, cnt);
+  if (threadIdx.x == 0) {
+    int lo = 0, hi = k;  // first j with idx[j] >= k
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sel[mid] < k) lo = mid + 1; else hi = mid;
+    }
+    nbelow = lo;
+  }
   __syncthreads();
   const int c = nbelow, moves = k - c;
   const int m0 = blockIdx.x * kMovesPerBlock;
@@ -174,7 +191,8 @@ int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_
     }
     SPATTEN_TIMED("compact_inplace", stream,
                   compact_inplace_kernel<<<dim3(blocks, unsigned(batch), unsigned(cnt)),
-                                           dim3(256), 0, stream>>>(p, idx, k));
+                                           dim3(128), size_t(k) * sizeof(int), stream>>>(p, idx,
+                                                                                        k));
     SPATTEN_LAUNCH_CHECK();
   }
   return SPATTEN_OK;

@@ -30,8 +30,10 @@ constexpr int kAttnF32Rows = 8;
 // Decode: cache entries per split-K chunk.
 constexpr int kDecChunk = 32;
 // In-place compaction: most rows one call may keep per sequence (the
-// selection is staged in LDS).
+// selection is staged in LDS), and the longest row it moves (row units are
+// counted in 32-bit integers).
 constexpr int kInplaceMaxK = 8192;
+constexpr int64_t kInplaceMaxRowBytes = int64_t(1) << 26;
 
 SPATTEN_HD inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 SPATTEN_HD inline int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }

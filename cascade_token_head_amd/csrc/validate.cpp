@@ -121,6 +121,7 @@ int check_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* r
   if (!aligned(idx, 4)) return SPATTEN_EINVAL;
   for (int32_t t = 0; t < n_tensors; ++t) {
     if (!base[t] || row_bytes[t] <= 0 || batch_stride[t] < 0) return SPATTEN_EINVAL;
+    if (row_bytes[t] > kInplaceMaxRowBytes) return SPATTEN_EUNSUPPORTED;
     // the n rows of one sequence must not run into the next sequence's
     if (batch > 1 && batch_stride[t] < int64_t(n) * row_bytes[t]) return SPATTEN_EINVAL;
   }

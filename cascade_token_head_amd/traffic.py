@@ -13,9 +13,10 @@
 FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch. Each is scaled by
 known bytes / counted bytes of the copy kernel (so a counter that reads
 high or low on this part is corrected), then averaged per launch of the
-kernel. The result, with the hash of the kernel sources it was taken on,
-goes to profiles/pmc_<label>_<workload>.json (read by bench.py) and a short
-.md summary beside it.
+kernel. The result, with the hash of the sources that kernel is built from
+(its .hip file and the shared headers), goes to
+profiles/pmc_<label>_<workload>.json (read by bench.py) and a short .md
+summary beside it.
 """
 from __future__ import annotations
 
@@ -32,11 +33,28 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "cascade_token_head_amd", "csrc")
 COPY_KERNEL = r"copyBuffer"
 
+# The source file each timed kernel is built from; every kernel also
+# depends on the shared headers.
+KERNEL_SOURCE = {
+    "qkv_gemm": "gemm.hip", "out_gemm": "gemm.hip",
+    "attn_fwd": "attn.hip", "attn_colsum": "attn.hip", "importance": "attn.hip",
+    "decode_attn": "decode.hip", "decode_finish": "decode.hip", "pq_attn_msb": "decode.hip",
+    "decode_flag": "decode.hip", "pq_attn_recompute": "decode.hip", "decode_vrow": "decode.hip",
+    "decode_scores": "decode.hip", "decode_vprune": "decode.hip", "decode_vsum": "decode.hip",
+    "topk": "topk.hip", "compact": "compact.hip", "compact_inplace": "compact.hip",
+    "quantize": "quant.hip",
+}
+SHARED_HEADERS = ("common.hpp", "kernels.hpp", "layout.hpp", "timing.hpp")
 
-def source_sha1() -> str:
-    """Hash of every kernel source file (the same hash bench.py checks)."""
+
+def source_sha1(kernel: str) -> str:
+    """Hash of the sources a kernel is built from: its .hip file and the
+    shared headers (bench.py checks the same hash before it reports a
+    counter summary). Unknown kernels hash every source file."""
+    files = ([KERNEL_SOURCE[kernel]] + list(SHARED_HEADERS) if kernel in KERNEL_SOURCE
+             else sorted(os.listdir(CSRC)))
     h = hashlib.sha1()
-    for fn in sorted(os.listdir(CSRC)):
+    for fn in files:
         with open(os.path.join(CSRC, fn), "rb") as f:
             h.update(fn.encode() + f.read())
     return h.hexdigest()
@@ -90,7 +108,7 @@ def summarize_main(a) -> None:
            "write_bytes_per_launch": round(write),
            "hbm_bytes_per_launch": round(fetch + write),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-           "copy_bytes": copy_bytes, "source_sha1": source_sha1(), "command": a.command}
+           "copy_bytes": copy_bytes, "source_sha1": source_sha1(a.label), "command": a.command}
     os.makedirs(a.out, exist_ok=True)
     base = os.path.join(a.out, "pmc_%s_%s" % (a.label, a.workload))
     with open(base + ".json", "w") as f:

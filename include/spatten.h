@@ -166,8 +166,8 @@ int spatten_compact(int32_t n_tensors, const void* const* src, void* const* dst,
  * is read or written, so a cut from k + 1 rows to k moves at most one row.
  * Row r of sequence b of tensor t is base[t] + b*batch_stride[t] +
  * r*row_bytes[t]; base, row_bytes and batch_stride are HOST arrays of
- * n_tensors entries. Requires 1 <= k <= n and k <= 8192 (larger k returns
- * SPATTEN_EUNSUPPORTED); each idx entry must lie in [0, n) - the caller
+ * n_tensors entries. Requires 1 <= k <= n; k > 8192 or a row longer than
+ * 64 MiB returns SPATTEN_EUNSUPPORTED. Each idx entry must lie in [0, n) - the caller
  * guarantees this. Sequences must not overlap (batch_stride >= n*row_bytes
  * when batch > 1).
  */

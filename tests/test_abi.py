@@ -166,6 +166,8 @@ def test_compact_inplace_rejections(S):
     # the selection is staged on chip: at most 8192 kept rows per sequence
     assert f(1, VP(FAKE), I64(16), I64(16 * 9000), vp(FAKE * 2), 1, 9000, 8193,
              None) == S.EUNSUPPORTED
+    assert f(1, VP(FAKE), I64((1 << 26) + 16), I64(1 << 40), vp(FAKE * 2), 2, 100, 10,
+             None) == S.EUNSUPPORTED
     assert f(0, None, None, None, None, 2, 100, 10, None) == S.OK
     assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 0, 100, 10, None) == S.OK
 

@@ -2,9 +2,10 @@
 // "Attention mechanism": inputs split into per-head Q, K, V; head outputs
 // concatenated; "Cascade pruning": a pruned head's Q/K/V chunks are gone).
 //
-// bf16 path: 128x128x64 workgroup tiles on gfx950 MFMA 32x32x16 (fp32
-// accumulate), four waves of 64x64, operands staged through padded LDS
-// rows with double buffering. Head pruning is a gather: each output
+// bf16 path: 128x128x64 workgroup tiles of four 64x64 waves, or for large
+// projections 256x256x64 tiles of eight 128x64 waves, on gfx950 MFMA
+// 32x32x16 (fp32 accumulate), operands staged through swizzled LDS rows
+// with double buffering. Head pruning is a gather: each output
 // column block (QKV) or K block (output projection) reads the weight rows
 // or columns of the head kept in that slot, per sequence. When every head
 // is kept all sequences share the weights and M tiles run across sequence
@@ -222,12 +223,15 @@ gemm_bf16_kernel(GemmParams p) {
 // stages of a 256 x 256 tile fit in 128 KB. Epilogue index math is hoisted:
 // column terms once per MFMA column tile, row terms advanced incrementally.
 
-template <int MODE, int BM, int BN>
-__global__ void __launch_bounds__(256, (BM * BN <= 128 * 128) ? 2 : 1)
+template <int MODE, int BM, int BN, int NW>
+__global__ void __launch_bounds__(64 * NW, (BM * BN <= 128 * 128) ? 2 : 1)
 gemm_tile_kernel(GemmParams p) {
   constexpr int BKT = 64;
-  constexpr int WM = BM / 2, WN = BN / 2, TI = WM / 32, TJ = WN / 32;
-  constexpr int NA = BM * 8 / 256, NB = BN * 8 / 256;  // 16-byte chunks per thread
+  constexpr int NT = 64 * NW;                 // threads
+  constexpr int WGN = NW == 8 ? 4 : 2;        // waves across N (2 or 4) x 2 across M
+  constexpr int WM = BM / 2, WN = BN / WGN, TI = WM / 32, TJ = WN / 32;
+  constexpr int NA = BM * 8 / NT, NB = BN * 8 / NT;  // 16-byte chunks per thread
+  constexpr int RS = NT / 8;                  // rows between a thread's chunks
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BKT];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BKT];
 
@@ -252,14 +256,14 @@ gemm_tile_kernel(GemmParams p) {
   const bf16_t* w_src[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = (tid >> 3) + RS * i;
     RowMap rm = map_row(p, tile_y, r, BM);
     if (!rm.valid) rm = p.seq_tiled ? RowMap{true, rm.b, p.n - 1} : RowMap{true, p.batch - 1, p.n - 1};
     a_src[i] = static_cast<const bf16_t*>(p.A) + (int64_t(rm.b) * p.n + rm.m) * p.lda + kc * 8;
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = (tid >> 3) + RS * i;
     int ncol = n0 + r;
     if (ncol >= p.N) ncol = p.N - 1;
     if (MODE == kOut)
@@ -277,7 +281,7 @@ gemm_tile_kernel(GemmParams p) {
   const int KT = p.K / BKT;
   // two register staging sets: the tile stored into LDS at the start of
   // iteration kt was requested two iterations earlier
-  u32x4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
+  u32x4 ra0[NA], rb0[NB], ra1[NW == 4 ? NA : 1], rb1[NW == 4 ? NB : 1];
   auto gload = [&](u32x4* ra, u32x4* rb, int kt) {
     const int k0 = kt * BKT;
     int wk = k0;
@@ -291,13 +295,13 @@ gemm_tile_kernel(GemmParams p) {
     for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(w_src[i] + wk);
   };
   auto sstore = [&](const u32x4* ra, const u32x4* rb, int buf) {
-    // rows tid/8 + 32 i keep the same (row >> 1) & 7, so one swizzled offset serves all i
+    // rows tid/8 + RS i keep the same (row >> 1) & 7, so one swizzled offset serves all i
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][st_off + 32 * i * BKT]) = ra[i];
+      *reinterpret_cast<u32x4*>(&As[buf][st_off + RS * i * BKT]) = ra[i];
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      *reinterpret_cast<u32x4*>(&Bs[buf][st_off + 32 * i * BKT]) = rb[i];
+      *reinterpret_cast<u32x4*>(&Bs[buf][st_off + RS * i * BKT]) = rb[i];
   };
 
   floatx16 acc[TI][TJ];
@@ -308,7 +312,7 @@ gemm_tile_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  const int wm = (wave / WGN) * WM, wn = (wave % WGN) * WN;
   const int fr = lane & 31, G = lane >> 5;
   // fragment rows wm + 32 i + fr all share (row >> 1) & 7 == (fr >> 1) & 7
   const int fsw = (fr >> 1) & 7;
@@ -347,21 +351,36 @@ gemm_tile_kernel(GemmParams p) {
   gload(ra0, rb0, 0);
   sstore(ra0, rb0, 0);
   if (KT > 1) gload(ra0, rb0, 1);
-  if (KT > 2) gload(ra1, rb1, 2);
+  if constexpr (NW == 4) {
+    if (KT > 2) gload(ra1, rb1, 2);
+  }
   __syncthreads();
   // Pairs of steps with no exit between them, so the accumulators stay in
-  // place across the loop back-edge.
+  // place across the loop back-edge. Four waves keep two register staging
+  // sets (loads two tiles ahead); eight waves, with twice the accumulators
+  // per wave, keep one (one tile ahead).
   for (int kt = 0; kt + 1 < KT; kt += 2) {
-    // even step: compute tile kt from buffer 0, stage tile kt+1 into buffer 1
-    sstore(ra0, rb0, 1);
-    if (kt + 3 < KT) gload(ra0, rb0, kt + 3);
-    compute(0);
-    __syncthreads();
-    // odd step: compute tile kt+1 from buffer 1, stage tile kt+2 into buffer 0
-    if (kt + 2 < KT) sstore(ra1, rb1, 0);
-    if (kt + 4 < KT) gload(ra1, rb1, kt + 4);
-    compute(1);
-    __syncthreads();
+    if constexpr (NW == 4) {
+      // even step: compute tile kt from buffer 0, stage tile kt+1 into buffer 1
+      sstore(ra0, rb0, 1);
+      if (kt + 3 < KT) gload(ra0, rb0, kt + 3);
+      compute(0);
+      __syncthreads();
+      // odd step: compute tile kt+1 from buffer 1, stage tile kt+2 into buffer 0
+      if (kt + 2 < KT) sstore(ra1, rb1, 0);
+      if (kt + 4 < KT) gload(ra1, rb1, kt + 4);
+      compute(1);
+      __syncthreads();
+    } else {
+      sstore(ra0, rb0, 1);
+      if (kt + 2 < KT) gload(ra0, rb0, kt + 2);
+      compute(0);
+      __syncthreads();
+      if (kt + 2 < KT) sstore(ra0, rb0, 0);
+      if (kt + 3 < KT) gload(ra0, rb0, kt + 3);
+      compute(1);
+      __syncthreads();
+    }
   }
   if (KT & 1) {  // the last (even) tile, staged by the final odd step
     compute(0);
@@ -628,7 +647,7 @@ gemm_f32_kernel(GemmParams p) {
   }
 }
 
-template <int MODE, int BMt, int BNt>
+template <int MODE, int BMt, int BNt, int NW = 4>
 int run_tile(GemmParams& p, hipStream_t stream, const char* name) {
   if (!p.seq_tiled && p.M_total >= (1 << 24)) p.seq_tiled = 1;
   int tiles_y;
@@ -642,18 +661,19 @@ int run_tile(GemmParams& p, hipStream_t stream, const char* name) {
   p.tiles_y = tiles_y;
   const int64_t total = ceil_div(p.N, BNt) * int64_t(tiles_y);
   const dim3 grid(unsigned(8 * ceil_div(total, 8)));
-  SPATTEN_TIMED(name, stream, gemm_tile_kernel<MODE, BMt, BNt><<<grid, 256, 0, stream>>>(p));
+  SPATTEN_TIMED(name, stream,
+                (gemm_tile_kernel<MODE, BMt, BNt, NW><<<grid, 64 * NW, 0, stream>>>(p)));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }
 
-// Work estimate (tile-rows x tile-cols x relative cost) for picking a tile.
-inline double tile_cost(const GemmParams& p, int bm, int bn, double rel) {
+// Rounds of workgroups over the 256 CUs for a tile shape: tiles / (CUs x
+// workgroups per CU), rounded up, since the last partial round costs a
+// whole one.
+inline double tile_rounds(const GemmParams& p, int bm, int bn, int per_cu) {
   const double my = p.seq_tiled ? double(ceil_div(p.n, bm)) * p.batch : double(ceil_div(p.M_total, bm));
-  const double nx = double(ceil_div(p.N, bn));
-  const double tiles = my * nx;
-  const double waves = std::ceil(tiles / 256.0);  // rounds of workgroups over 256 CUs
-  return waves * bm * bn * rel;
+  const double tiles = my * double(ceil_div(p.N, bn));
+  return std::ceil(tiles / (256.0 * per_cu));
 }
 
 template <int MODE>
@@ -664,8 +684,13 @@ int run_gemm(GemmParams& p, int dtype, hipStream_t stream) {
       p.N % 16 == 0 && kt > 0)
     return run_skinny<MODE>(p, kt, stream, name);
   if (dtype == SPATTEN_BF16 && MODE != kQkvDecode) {
-    // 128x128 tiles at two workgroups per CU hide load latency better than
-    // one 256x256 workgroup per CU (measured on MI355X).
+    // 128x128 tiles of four 64x64 waves run two workgroups per CU; 256x256
+    // tiles of eight 128x64 waves run one, read a quarter fewer LDS bytes
+    // per MFMA and finish a round in ~1.67x the time of a 128x128 round
+    // (measured on MI355X: ~20% faster on 4096-deep projections). The
+    // larger tile wins when its coarser rounds do not waste more than that.
+    const double r128 = tile_rounds(p, 128, 128, 2), r256 = tile_rounds(p, 256, 256, 1);
+    if (p.K >= 256 && 1.67 * r256 < 0.97 * r128) return run_tile<MODE, 256, 256, 8>(p, stream, name);
     return run_tile<MODE, 128, 128>(p, stream, name);
   }
   const int tm = dtype == SPATTEN_BF16 ? BM : FT;

@@ -725,7 +725,11 @@ int launch_qkv(const QkvArgs& a, hipStream_t stream) {
   p.head_idx = a.head_idx;
   p.batch = a.batch;
   p.n = a.n;
-  p.seq_tiled = a.h_kept != a.D / a.dh;
+  // Tiles stay inside one sequence when heads differ per sequence, and for
+  // prefill when n is not a multiple of 8: the V^T epilogue stores 8
+  // consecutive rows of one sequence as one 16-byte chunk, which a tile
+  // that starts mid-sequence would leave misaligned.
+  p.seq_tiled = a.h_kept != a.D / a.dh || (a.mode == SPATTEN_PREFILL && a.n % 8 != 0);
   p.M_total = a.batch * a.n;
   p.N = 3 * a.h_kept * a.dh;
   p.K = a.D;

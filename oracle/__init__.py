@@ -38,6 +38,8 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       leaves importance unchanged, every rolling cut keeps
                       the largest entries (brute force over candidates) and
                       never revives a pruned one, a budget that never cuts
-                      reproduces the plain run.
+                      reproduces the plain run; per-head pruning reduces to
+                      the shared cut for one head and for identical heads,
+                      and each head's cut keeps that head's largest entries.
 """
 from . import spatten_ref, topk_engine  # noqa: F401

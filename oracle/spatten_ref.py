@@ -449,8 +449,12 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
     cfg.prune_every = r > 0 the same cut back to cache_keep entries is
     repeated after every r-th later step, over the entries kept so far plus
     the new ones. cfg.v_threshold > 0 adds local value pruning inside each
-    head's attention. pq_adopt(b, s, l, h, c, default) may override a
-    recompute decision.
+    head's attention. With cfg.per_head (per-head token pruning, page
+    section VI "Token Pruning" names it) each head h keeps its own entries:
+    a_h[j] accumulates only head h's probabilities and every cut keeps
+    topk(a_h, cache_keep) for that head in every layer's K and V. All heads
+    keep the same count, so slot r of head h holds head h's r-th entry.
+    pq_adopt(b, s, l, h, c, default) may override a recompute decision.
 
     Per sequence the result holds the step outputs, the final a, the first
     selection (indices into the L0+1 entries), "kept_ids" after every step
@@ -462,6 +466,8 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
     steps = cfg.steps if steps is None else steps
     H, dh = cfg.n_heads, cfg.head_dim
     vthr = getattr(cfg, "v_threshold", 0.0)
+    per_head = getattr(cfg, "per_head", False)
+    assert not (per_head and cfg.quantized), "per-token scales are shared by all heads"
     out = {}
     for b in seqs:
         caches = []
@@ -476,13 +482,14 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
                                "v_msb": vm, "v_lsb": vl, "v_scale": vs})
             else:
                 caches.append({"k": K0, "v": V0})
-        a = np.zeros(cfg.cache_len)
-        ids = np.arange(cfg.cache_len, dtype=np.int64)
+        shape = (H, cfg.cache_len) if per_head else (cfg.cache_len,)
+        a = np.zeros(shape)
+        ids = np.broadcast_to(np.arange(cfg.cache_len, dtype=np.int64), shape).copy()
         xs, recs, kept, sel, kept_ids, pre = [], [], [], None, [], []
         for s in range(steps):
             x = np.asarray(inputs["x_steps"][s][b], dtype=np.float64)
-            a = np.concatenate([a, [0.0]])
-            ids = np.concatenate([ids, [cfg.cache_len + s]])
+            a = np.concatenate([a, np.zeros(shape[:-1] + (1,))], axis=-1)
+            ids = np.concatenate([ids, np.full(shape[:-1] + (1,), cfg.cache_len + s)], axis=-1)
             step_rec, step_kept = [], []
             for l in range(cfg.n_layers):
                 dec = None
@@ -491,24 +498,36 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
                 x, P, rec, cmax, kv = decode_layer(x, inputs["layers"][l], caches[l], H, dh,
                                                    bf16, cfg.quantized, cfg.pq_threshold, dec,
                                                    vthr)
-                a = a + P.sum(axis=0)
+                a = a + (P if per_head else P.sum(axis=0))
                 step_rec.append((rec, cmax))
                 step_kept.append(kv)
             xs.append(x)
             recs.append(step_rec)
             kept.append(step_kept)
             pre.append((ids.copy(), a.copy()))
-            if prune_after_step(cfg, s) and len(a) > cfg.cache_keep:
-                a32 = a.astype(np.float32)
-                idx = topk(a32, cfg.cache_keep)
-                if adopt is not None:
-                    idx = adopt("cache", b, s, idx, a32)
+            if prune_after_step(cfg, s) and a.shape[-1] > cfg.cache_keep:
+                if per_head:
+                    idx = np.stack([topk(a[h].astype(np.float32), cfg.cache_keep)
+                                    for h in range(H)])
+                    if adopt is not None:
+                        idx = np.stack([adopt("cache_head", b, s, idx[h], a[h].astype(np.float32))
+                                        for h in range(H)])
+                    for c in caches:
+                        for name in c:
+                            c[name] = np.stack([c[name][idx[h], h] for h in range(H)], axis=1)
+                    a = np.stack([a[h][idx[h]] for h in range(H)])
+                    ids = np.stack([ids[h][idx[h]] for h in range(H)])
+                else:
+                    a32 = a.astype(np.float32)
+                    idx = topk(a32, cfg.cache_keep)
+                    if adopt is not None:
+                        idx = adopt("cache", b, s, idx, a32)
+                    for c in caches:
+                        for name in c:
+                            c[name] = compact(c[name], idx)
+                    a, ids = compact(a, idx), compact(ids, idx)
                 if s == 0:
                     sel = idx
-                for c in caches:
-                    for name in c:
-                        c[name] = compact(c[name], idx)
-                a, ids = compact(a, idx), compact(ids, idx)
             kept_ids.append(ids.copy())
         out[b] = {"x_steps": np.stack(xs), "a": a, "sel": sel, "recompute": recs,
                   "kept_ids": kept_ids, "before_prune": pre, "v_kept": np.array(kept)}

@@ -588,3 +588,71 @@ def test_run_decode_rolling_without_cuts_is_the_dense_run():
     roll = R.run_decode(scaled(cfg, prune_every=1), inp)[0]
     np.testing.assert_array_equal(roll["x_steps"], plain["x_steps"])
     np.testing.assert_array_equal(roll["kept_ids"][-1], np.arange(16))
+
+
+# ----------------------------------------------------------------- per-head token pruning
+# (page section VI "Token Pruning": per-head token pruning; reading: in
+# decode each head keeps its own cache entries by its own importance)
+
+
+def _small_decode(**kw):
+    from workloads import GPT2_DECODE
+    base = dict(n_layers=2, batch=1, n_heads=2, head_dim=8, cache_len=20, cache_keep=9, steps=4)
+    base.update(kw)
+    return scaled(GPT2_DECODE, **base)
+
+
+def test_per_head_with_one_head_is_the_shared_cut():
+    from workloads import make_decode_inputs
+    cfg = _small_decode(n_heads=1, head_dim=16, prune_every=1)
+    inp = make_decode_inputs(cfg)
+    shared = R.run_decode(cfg, inp)[0]
+    ph = R.run_decode(scaled(cfg, per_head=True), inp)[0]
+    np.testing.assert_array_equal(ph["x_steps"], shared["x_steps"])
+    np.testing.assert_array_equal(ph["a"][0], shared["a"])
+    for k1, k2 in zip(ph["kept_ids"], shared["kept_ids"]):
+        np.testing.assert_array_equal(k1[0], k2)
+
+
+def test_per_head_with_identical_heads_is_the_shared_cut():
+    """Two heads with identical weights and caches see identical
+    probabilities: each head's importance is half the shared one (exact in
+    binary), so every head keeps the shared selection and the outputs
+    match."""
+    from workloads import make_decode_inputs
+    cfg = _small_decode(n_heads=2, head_dim=8, prune_every=2)
+    inp = make_decode_inputs(cfg)
+    dh = 8
+    for L in inp["layers"]:
+        for name in ("wq", "wk", "wv"):
+            L[name][:, dh:] = L[name][:, :dh]
+        L["wo"][dh:, :] = L["wo"][:dh, :]
+        for name in ("k_cache", "v_cache"):
+            L[name][:, :, 1] = L[name][:, :, 0]
+    shared = R.run_decode(cfg, inp)[0]
+    ph = R.run_decode(scaled(cfg, per_head=True), inp)[0]
+    np.testing.assert_array_equal(ph["x_steps"], shared["x_steps"])
+    for k1, k2 in zip(ph["kept_ids"], shared["kept_ids"]):
+        np.testing.assert_array_equal(k1[0], k2)
+        np.testing.assert_array_equal(k1[1], k2)
+
+
+def test_per_head_cut_keeps_each_heads_largest():
+    from workloads import make_decode_inputs
+    cfg = _small_decode(n_heads=3, head_dim=8, prune_every=1, steps=5, per_head=True)
+    out = R.run_decode(cfg, make_decode_inputs(cfg))[0]
+    differ = False
+    for s, (ids_pre, a_pre) in enumerate(out["before_prune"]):
+        assert ids_pre.shape[0] == 3
+        if s == 0:
+            # before the first cut every head holds L0 + 1 entries whose
+            # importance adds up to one per layer
+            np.testing.assert_allclose(a_pre.sum(axis=1), [2.0] * 3, atol=1e-12)
+        ids = out["kept_ids"][s]
+        for h in range(3):
+            keep = np.isin(ids_pre[h], ids[h])
+            assert keep.sum() == 9 and len(set(ids[h].tolist())) == 9
+            assert (a_pre[h][keep].astype(np.float32).min()
+                    >= a_pre[h][~keep].astype(np.float32).max())
+        differ |= not (np.array_equal(ids[0], ids[1]) and np.array_equal(ids[1], ids[2]))
+    assert differ, "heads never chose different entries"

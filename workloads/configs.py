@@ -19,9 +19,10 @@ Five workloads are defined, each a stack of attention-only residual layers
               25% of tokens kept after layer 1, heads top-24 of 32 from
               layer 2.
 
-Two extensions of gpt2_decode: gpt2_decode_vprune (local value pruning,
-threshold 1e-4) and gpt2_decode_rolling (the cache cut back to 410 entries
-after every step).
+Three extensions of gpt2_decode: gpt2_decode_vprune (local value pruning,
+threshold 1e-4), gpt2_decode_rolling (the cache cut back to 410 entries
+after every step) and gpt2_decode_perhead (each head keeps its own 410
+entries by its own importance).
 
 This module holds shapes and schedules only. Keep counts follow
 k = floor(f * N + 1/2) with N the original length, so fractions are absolute
@@ -65,6 +66,9 @@ class Config:
     # re-prune the cache back to cache_keep after every prune_every-th step
     # following the first (0 = prune once, after step 1)
     prune_every: int = 0
+    # per-head token pruning: each head keeps its own cache entries by its
+    # own cumulative importance (unquantized decode)
+    per_head: bool = False
     heavy_frac: float = 0.05
     heavy_scale: float = 3.0
 
@@ -123,13 +127,14 @@ LONG_CAUSAL = Config(
     heads=(32,) + (24,) * 3)
 
 # Extensions of the GPT-2-small decode workload: local value pruning with a
-# probability threshold of 1e-4, and a rolling cascade that cuts the cache
-# back to 410 entries after every step.
+# probability threshold of 1e-4, a rolling cascade that cuts the cache back
+# to 410 entries after every step, and per-head cache pruning.
 GPT2_DECODE_VPRUNE = replace(GPT2_DECODE, name="gpt2_decode_vprune", v_threshold=1e-4)
 GPT2_DECODE_ROLLING = replace(GPT2_DECODE, name="gpt2_decode_rolling", prune_every=1)
+GPT2_DECODE_PERHEAD = replace(GPT2_DECODE, name="gpt2_decode_perhead", per_head=True)
 
 CONFIGS = [TINY, BERT_BASE, GPT2_DECODE, PQ_DECODE, LONG_CAUSAL]
-EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING]
+EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD]
 BY_NAME = {c.name: c for c in CONFIGS + EXTENSIONS}
 
 

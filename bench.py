@@ -223,7 +223,7 @@ def main():
         stack = pipeline.DecodeStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim,
                                      cfg.cache_len, cfg.cache_keep, cfg.steps, w, cfg.quantized,
                                      cfg.pq_threshold, dtype, v_threshold=cfg.v_threshold,
-                                     prune_every=cfg.prune_every)
+                                     prune_every=cfg.prune_every, per_head=cfg.per_head)
         k0 = [torch.from_numpy(l["k_cache"]).to(dtype).cuda() for l in inputs["layers"]]
         v0 = [torch.from_numpy(l["v_cache"]).to(dtype).cuda() for l in inputs["layers"]]
         xs = torch.from_numpy(inputs["x_steps"]).to(dtype).cuda()
@@ -311,6 +311,7 @@ def main():
                 "cache_keep": cfg.cache_keep, "decode_steps": cfg.steps, "layers": cfg.n_layers,
                 "heads": cfg.n_heads, "head_dim": cfg.head_dim, "quantized": cfg.quantized,
                 "prune_every": cfg.prune_every, "v_threshold": cfg.v_threshold,
+                "per_head": cfg.per_head,
                 "v_rows_kept_frac": kept_frac}
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),

@@ -135,6 +135,7 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
   da.nchunk = int(w.nchunk);
   da.threshold = d.pq_threshold;
   da.v_threshold = d.v_threshold;
+  da.per_head = d.per_head;
   da.scores = reinterpret_cast<float*>(ws + w.scores);
   da.mpart = reinterpret_cast<float*>(ws + w.mpart);
   da.lpart = reinterpret_cast<float*>(ws + w.lpart);
@@ -207,12 +208,14 @@ int spatten_compact(int32_t n_tensors, const void* const* src, void* const* dst,
 }
 
 int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* row_bytes,
-                            const int64_t* batch_stride, const int32_t* idx, int32_t batch,
-                            int32_t n, int32_t k, void* stream) {
-  const int st = check_compact_inplace(n_tensors, base, row_bytes, batch_stride, idx, batch, n, k);
+                            const int64_t* row_pitch, const int64_t* batch_stride,
+                            const int32_t* idx, int32_t batch, int32_t n, int32_t k,
+                            void* stream) {
+  const int st = check_compact_inplace(n_tensors, base, row_bytes, row_pitch, batch_stride, idx,
+                                       batch, n, k);
   if (st != SPATTEN_OK) return st;
-  return launch_compact_inplace(n_tensors, base, row_bytes, batch_stride, idx, batch, n, k,
-                                as_stream(stream));
+  return launch_compact_inplace(n_tensors, base, row_bytes, row_pitch, batch_stride, idx, batch,
+                                n, k, as_stream(stream));
 }
 
 int spatten_quantize_kv(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,

@@ -84,7 +84,7 @@ constexpr int kMovesPerBlock = 16;
 
 struct InplaceTensor {
   char* base;
-  int64_t row_bytes, bs;
+  int64_t row_bytes, pitch, bs;
   int32_t vec_shift;
 };
 
@@ -106,7 +106,7 @@ __device__ __forceinline__ void move_units(const InplaceTensor& t, char* bbase, 
       const int u = u0 + w * blockDim.x;
       if (u < total) {
         const int m = u / upr, part = u - m * upr;
-        buf[w] = reinterpret_cast<const T*>(bbase + int64_t(src[m]) * t.row_bytes)[part];
+        buf[w] = reinterpret_cast<const T*>(bbase + int64_t(src[m]) * t.pitch)[part];
       }
     }
     // sources sit at or above k, destinations below it: no overlap
@@ -115,7 +115,7 @@ __device__ __forceinline__ void move_units(const InplaceTensor& t, char* bbase, 
       const int u = u0 + w * blockDim.x;
       if (u < total) {
         const int m = u / upr, part = u - m * upr;
-        reinterpret_cast<T*>(bbase + int64_t(dst[m]) * t.row_bytes)[part] = buf[w];
+        reinterpret_cast<T*>(bbase + int64_t(dst[m]) * t.pitch)[part] = buf[w];
       }
     }
   }
@@ -174,8 +174,8 @@ compact_inplace_kernel(InplaceParams p, const int32_t* __restrict__ idx, int k) 
 }  // namespace
 
 int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_bytes,
-                           const int64_t* bs, const int32_t* idx, int batch, int n, int k,
-                           hipStream_t stream) {
+                           const int64_t* row_pitch, const int64_t* bs, const int32_t* idx,
+                           int batch, int n, int k, hipStream_t stream) {
   if (n_tensors == 0 || batch == 0 || k == n) return SPATTEN_OK;
   const int max_moves = k < n - k ? k : n - k;
   const unsigned blocks = unsigned(ceil_div(max_moves, kMovesPerBlock));
@@ -186,8 +186,9 @@ int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_
       const int t = t0 + i;
       p.t[i].base = static_cast<char*>(base[t]);
       p.t[i].row_bytes = row_bytes[t];
+      p.t[i].pitch = row_pitch ? row_pitch[t] : row_bytes[t];
       p.t[i].bs = bs[t];
-      p.t[i].vec_shift = vec_shift_for(base[t], base[t], row_bytes[t], bs[t], bs[t]);
+      p.t[i].vec_shift = vec_shift_for(base[t], base[t], row_bytes[t], p.t[i].pitch, bs[t]);
     }
     SPATTEN_TIMED("compact_inplace", stream,
                   compact_inplace_kernel<<<dim3(blocks, unsigned(batch), unsigned(cnt)),

@@ -447,9 +447,13 @@ decode_vprune(DecodeArgs a) {
   }
   __syncthreads();
   if (tid < CH && j0 + tid < a.lc) {
-    float s = 0.0f;
-    for (int hh = 0; hh < H; ++hh) s += P[hh][tid];
-    a.a[rowb + j0 + tid] += s;
+    if (a.per_head) {
+      for (int hh = 0; hh < H; ++hh) a.a[(int64_t(b) * H + hh) * a.cap + j0 + tid] += P[hh][tid];
+    } else {
+      float s = 0.0f;
+      for (int hh = 0; hh < H; ++hh) s += P[hh][tid];
+      a.a[rowb + j0 + tid] += s;
+    }
   }
   // P V over this head's kept rows; a dropped row is not read
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -646,7 +650,8 @@ decode_recompute(DecodeArgs a) {
 // One workgroup per sequence, one wave per head (up to 16 waves): combine
 // the rows not combined yet (mode 0: every row; 1, quantized: the
 // recomputed ones; 2: none, every row's lse is written), then
-// a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h]) for j < lc.
+// a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h]) for j < lc (with
+// per_head, a[b, h, j] += exp2(score[b, h, j] - lse2[b, h])).
 enum { kFinishAll = 0, kFinishQuantized = 1, kFinishLseReady = 2 };
 __global__ void __launch_bounds__(1024)
 decode_finish(DecodeArgs a, int mode) {
@@ -674,6 +679,30 @@ decode_finish(DecodeArgs a, int mode) {
   }
   __syncthreads();
   const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
+  if (a.per_head) {
+    // a[b, h, j] += exp2(score[b, h, j] - lse2[b, h]) over the H * lc
+    // (head, entry) pairs, eight pairs' loads in flight per thread
+    const int total = a.H * a.lc;
+    float* ab = a.a + int64_t(b) * a.H * a.cap;
+    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * nt) {
+      float sv[8], av[8];
+      int ai[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * nt;
+        if (i < total) {
+          const int h = i / a.lc, j = i - h * a.lc;
+          ai[u] = h * a.cap + j;
+          sv[u] = sp[int64_t(h) * a.lc_pad + j] - lse[h];
+          av[u] = ab[ai[u]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * nt < total) ab[ai[u]] = av[u] + fast_exp2(sv[u]);
+    }
+    return;
+  }
   for (int j = threadIdx.x; j < a.lc; j += nt) {
     float acc = 0.0f;
     for (int h0 = 0; h0 < a.H; h0 += 8) {

@@ -18,8 +18,8 @@ int launch_compact(int n_tensors, const void* const* src, void* const* dst,
                    const int32_t* idx, int batch, int k, hipStream_t stream);
 
 int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_bytes,
-                           const int64_t* bs, const int32_t* idx, int batch, int n, int k,
-                           hipStream_t stream);
+                           const int64_t* row_pitch, const int64_t* bs, const int32_t* idx,
+                           int batch, int n, int k, hipStream_t stream);
 
 int launch_quantize(const void* kv, int dtype, int batch, int n, int dim, int64_t kv_bs,
                     uint8_t* msb, uint8_t* lsb, float* scale, int64_t pbs, hipStream_t stream);
@@ -89,6 +89,7 @@ struct DecodeArgs {
   int batch, H, dh, cap, lc, lc_pad, nchunk;
   float threshold;
   float v_threshold;  // local value pruning (unquantized; 0 = off)
+  int per_head;       // 1: a is [B, H, cap] and takes each head's probabilities apart
   float* scores;  // [B, H, lc_pad]
   float* mpart;
   float* lpart;   // [B, H, nchunk]
@@ -99,7 +100,7 @@ struct DecodeArgs {
   int32_t* queue; // [0] = count, then entries b*H + h
   int32_t* kcount;  // [B, H, nchunk] V rows kept per chunk (value pruning)
   void* o;        // [B, D] bf16
-  float* a;       // [B, cap]
+  float* a;       // [B, cap], or [B, H, cap] with per_head
   int32_t* recompute;  // optional [B, H]
   int32_t* v_kept;     // optional [B, H]
 };

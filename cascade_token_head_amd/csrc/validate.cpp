@@ -41,6 +41,8 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
   if (d->n_heads_kept < 1 || d->n_heads_kept > d->n_heads) return SPATTEN_EINVAL;
   if (int64_t(d->n_heads) * d->head_dim > (1 << 20)) return SPATTEN_EINVAL;
   if (!(d->v_threshold >= 0.0f)) return SPATTEN_EINVAL;  // negative or NaN
+  if (d->per_head != 0 && d->per_head != 1) return SPATTEN_EINVAL;
+  if (d->per_head && (d->mode != SPATTEN_DECODE || d->kv_quantized)) return SPATTEN_EUNSUPPORTED;
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return SPATTEN_EUNSUPPORTED;
   if (d->v_threshold > 0.0f && (d->mode != SPATTEN_DECODE || d->kv_quantized))
     return SPATTEN_EUNSUPPORTED;
@@ -112,8 +114,8 @@ int check_compact(int32_t n_tensors, const void* const* src, void* const* dst,
 }
 
 int check_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* row_bytes,
-                          const int64_t* batch_stride, const int32_t* idx, int32_t batch,
-                          int32_t n, int32_t k) {
+                          const int64_t* row_pitch, const int64_t* batch_stride,
+                          const int32_t* idx, int32_t batch, int32_t n, int32_t k) {
   if (n_tensors < 0 || batch < 0 || n < 1 || k < 1 || k > n) return SPATTEN_EINVAL;
   if (k > kInplaceMaxK) return SPATTEN_EUNSUPPORTED;
   if (n_tensors == 0 || batch == 0) return SPATTEN_OK;
@@ -122,8 +124,10 @@ int check_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* r
   for (int32_t t = 0; t < n_tensors; ++t) {
     if (!base[t] || row_bytes[t] <= 0 || batch_stride[t] < 0) return SPATTEN_EINVAL;
     if (row_bytes[t] > kInplaceMaxRowBytes) return SPATTEN_EUNSUPPORTED;
+    const int64_t pitch = row_pitch ? row_pitch[t] : row_bytes[t];
+    if (pitch < row_bytes[t]) return SPATTEN_EINVAL;
     // the n rows of one sequence must not run into the next sequence's
-    if (batch > 1 && batch_stride[t] < int64_t(n) * row_bytes[t]) return SPATTEN_EINVAL;
+    if (batch > 1 && batch_stride[t] < int64_t(n - 1) * pitch + row_bytes[t]) return SPATTEN_EINVAL;
   }
   return SPATTEN_OK;
 }

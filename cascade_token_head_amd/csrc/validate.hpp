@@ -28,8 +28,8 @@ int check_compact(int32_t n_tensors, const void* const* src, void* const* dst,
                   const int64_t* dst_batch_stride, const int32_t* idx, int32_t batch, int32_t k);
 
 int check_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* row_bytes,
-                          const int64_t* batch_stride, const int32_t* idx, int32_t batch,
-                          int32_t n, int32_t k);
+                          const int64_t* row_pitch, const int64_t* batch_stride,
+                          const int32_t* idx, int32_t batch, int32_t n, int32_t k);
 
 int check_quantize(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,
                    int64_t kv_batch_stride, const uint8_t* msb, const uint8_t* lsb,

@@ -129,16 +129,17 @@ class DecodeStack:
     def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, cache_len: int,
                  cache_keep: int, steps: int, weights: List[dict], quantized: bool = False,
                  threshold: float = 0.0, dtype: torch.dtype = torch.bfloat16, device="cuda",
-                 v_threshold: float = 0.0, prune_every: int = 0):
+                 v_threshold: float = 0.0, prune_every: int = 0, per_head: bool = False):
         self.L, self.B, self.H, self.dh = n_layers, batch, n_heads, head_dim
         self.D = D = n_heads * head_dim
         self.L0, self.keep, self.steps = cache_len, cache_keep, steps
         self.cap = cap = cache_len + steps
         self.quantized, self.threshold, self.w, self.dtype = quantized, threshold, weights, dtype
-        self.v_threshold, self.prune_every = v_threshold, prune_every
-        # repeated cuts run in place on one copy of the caches; a single cut
-        # gathers the survivors, in order, into the second copy
-        self.inplace = prune_every > 0
+        self.v_threshold, self.prune_every, self.per_head = v_threshold, prune_every, per_head
+        # repeated and per-head cuts run in place on one copy of the caches;
+        # a single shared cut gathers the survivors, in order, into the
+        # second copy
+        self.inplace = prune_every > 0 or per_head
         sides = 1 if self.inplace else 2
         B, dev = batch, device
         self.caches = [[] for _ in range(sides)]
@@ -155,15 +156,17 @@ class DecodeStack:
                     c = {"k_cache": torch.empty(B, cap, D, dtype=dtype, device=dev),
                          "v_cache": torch.empty(B, cap, D, dtype=dtype, device=dev)}
                 self.caches[side].append(c)
-        self.abuf = [torch.zeros(B, cap, dtype=torch.float32, device=dev) for _ in range(sides)]
+        ashape = (B, n_heads, cap) if per_head else (B, cap)
+        self.abuf = [torch.zeros(ashape, dtype=torch.float32, device=dev) for _ in range(sides)]
         self.x = torch.empty(B, 1, D, dtype=dtype, device=dev)
         self.head_idx = torch.arange(n_heads, dtype=torch.int32, device=dev).repeat(B, 1).contiguous()
         self.g = torch.zeros(B, n_heads, dtype=torch.float32, device=dev)
         self.recompute = torch.zeros(n_layers, B, n_heads, dtype=torch.int32, device=dev)
         self.v_kept = torch.zeros(n_layers, B, n_heads, dtype=torch.int32, device=dev)
-        self.cache_sel = torch.empty(B, cache_keep, dtype=torch.int32, device=dev)
+        self.cache_sel = torch.empty((n_heads, B, cache_keep) if per_head else (B, cache_keep),
+                                     dtype=torch.int32, device=dev)
         dmax = S.make_desc(S.DECODE, S.dtype_code(dtype), False, B, 1, n_heads, n_heads, head_dim,
-                           cap - 1, cap, quantized, threshold, v_threshold)
+                           cap - 1, cap, quantized, threshold, v_threshold, per_head)
         self.ws = torch.empty(max(S.workspace_bytes(dmax), 256), dtype=torch.uint8, device=dev)
         self.side, self.len, self.s = 0, cache_len, 0
         self.trace = []
@@ -192,7 +195,8 @@ class DecodeStack:
         B, H = self.B, self.H
         self.x.view(B, self.D).copy_(x)
         desc = S.make_desc(S.DECODE, S.dtype_code(self.dtype), False, B, 1, H, H, self.dh,
-                           self.len, self.cap, self.quantized, self.threshold, self.v_threshold)
+                           self.len, self.cap, self.quantized, self.threshold, self.v_threshold,
+                           self.per_head)
         a = self.abuf[self.side]
         for l in range(self.L):
             w, c = self.w[l], self.caches[self.side][l]
@@ -209,7 +213,7 @@ class DecodeStack:
                                "v_kept": self.v_kept.clone()})
         if self.cut_due():
             if record:
-                self.trace[-1]["a_before_cut"] = self.abuf[self.side][:, :self.len].clone()
+                self.trace[-1]["a_before_cut"] = self.abuf[self.side][..., :self.len].clone()
             self.prune()
             if record:
                 self.trace[-1]["cache_sel"] = self.cache_sel.clone()
@@ -229,6 +233,23 @@ class DecodeStack:
         the kept range into the dropped rows."""
         B, cap, k = self.B, self.cap, self.keep
         a = self.abuf[self.side]
+        if self.per_head:
+            # each head: its own top-k, then an in-place cut of its 128-byte
+            # slice of every layer's cache rows and of its importance row
+            H, dh, D = self.H, self.dh, self.D
+            for h in range(H):
+                sel = self.cache_sel[h]
+                S.topk(a[:, h, :], k, n=self.len, out=sel)
+                tensors = [(a[:, h, :], 4, H * cap * 4)]
+                for c in self.caches[0]:
+                    for t in c.values():
+                        es = t.element_size()
+                        tensors.append((t[:, :, h * dh:(h + 1) * dh], dh * es, cap * D * es,
+                                        D * es))
+                S.compact_inplace(tensors, sel, self.len, k)
+            a[:, :, k:self.len].zero_()
+            self.len = k
+            return
         S.topk(a, k, n=self.len, out=self.cache_sel)
         if self.inplace:
             tensors = [(a, 4, cap * 4)]

@@ -39,7 +39,7 @@ class LayerDesc(ctypes.Structure):
         ("n_heads_kept", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("cache_len", ctypes.c_int32), ("cache_cap", ctypes.c_int32),
         ("kv_quantized", ctypes.c_int32), ("pq_threshold", ctypes.c_float),
-        ("v_threshold", ctypes.c_float),
+        ("v_threshold", ctypes.c_float), ("per_head", ctypes.c_int32),
     ]
 
 
@@ -64,7 +64,8 @@ def _lib():
                                         ctypes.POINTER(i64), vp, i32, i32, vp]
         lib.spatten_compact_inplace.restype = ctypes.c_int
         lib.spatten_compact_inplace.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(i64),
-                                                ctypes.POINTER(i64), vp, i32, i32, i32, vp]
+                                                ctypes.POINTER(i64), ctypes.POINTER(i64), vp,
+                                                i32, i32, i32, vp]
         lib.spatten_quantize_kv.restype = ctypes.c_int
         lib.spatten_quantize_kv.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, i64, vp]
         lib.spatten_status_string.restype = ctypes.c_char_p
@@ -106,10 +107,11 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def make_desc(mode=PREFILL, dtype=BF16, causal=False, batch=1, n_tokens=1, n_heads=1,
               n_heads_kept=None, head_dim=64, cache_len=0, cache_cap=0, kv_quantized=False,
-              pq_threshold=0.0, v_threshold=0.0) -> LayerDesc:
+              pq_threshold=0.0, v_threshold=0.0, per_head=False) -> LayerDesc:
     return LayerDesc(mode, dtype, int(causal), batch, n_tokens, n_heads,
                      n_heads if n_heads_kept is None else n_heads_kept, head_dim, cache_len,
-                     cache_cap, int(kv_quantized), float(pq_threshold), float(v_threshold))
+                     cache_cap, int(kv_quantized), float(pq_threshold), float(v_threshold),
+                     int(per_head))
 
 
 def workspace_bytes(desc: LayerDesc) -> int:
@@ -179,7 +181,8 @@ def quantize_kv(kv: torch.Tensor, msb: torch.Tensor, lsb: torch.Tensor, scale: t
 def compact_inplace(tensors: Sequence, idx: torch.Tensor, n: int, k: int, stream=None):
     """In-place cut of rows whose order carries no meaning.
 
-    tensors: (base, row_bytes, batch_stride_bytes) per tensor.
+    tensors: (base, row_bytes, batch_stride_bytes[, row_pitch_bytes]) per
+             tensor; base may be a view (its data_ptr is the first row).
     idx:     int32 [B, k] ascending selected rows, each below n.
     """
     m = len(tensors)
@@ -188,6 +191,7 @@ def compact_inplace(tensors: Sequence, idx: torch.Tensor, n: int, k: int, stream
     base = VP(*[t[0].data_ptr() for t in tensors])
     rb = I64(*[t[1] for t in tensors])
     bs = I64(*[t[2] for t in tensors])
+    rp = I64(*[t[3] if len(t) > 3 else t[1] for t in tensors])
     B = idx.shape[0]
-    st = _lib().spatten_compact_inplace(m, base, rb, bs, _p(idx), B, n, k, _stream(stream))
+    st = _lib().spatten_compact_inplace(m, base, rb, rp, bs, _p(idx), B, n, k, _stream(stream))
     _check("spatten_compact_inplace", st)

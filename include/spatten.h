@@ -61,6 +61,7 @@ typedef struct {
   int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
   float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
   float v_threshold;     /* decode, unquantized: local value pruning threshold (0 = off) */
+  int32_t per_head;      /* decode, unquantized: 1 = per-head importance, a is [B, H, cache_cap] */
 } spatten_layer_desc;
 
 /*
@@ -101,6 +102,10 @@ typedef struct {
  *   a still takes every probability. v_kept (optional, [B, H] int32)
  *   receives the number of V rows that entered O_h (cache_len + 1 without
  *   value pruning).
+ *   Per-head token pruning (section VI "Token Pruning"; per_head = 1,
+ *   unquantized): a is [B, H, cache_cap] and a[b, h, j] takes head h's
+ *   probabilities only, so each head can keep its own cache entries (cut
+ *   with spatten_compact_inplace on the head's 128-byte slice of each row).
  *   g is not used in decode and may be NULL. Decode needs head_dim 64,
  *   H <= 32, bf16 and every head kept.
  * head_idx: [B, h_kept] int32, strictly ascending head ids per sequence.
@@ -113,7 +118,8 @@ typedef struct {
  * Supported: prefill bf16 with head_dim 64 or 128, prefill fp32 with
  *   n_tokens <= 1024; other shapes return SPATTEN_EUNSUPPORTED, as does a
  *   non-zero v_threshold in prefill or with a quantized cache. A NaN or
- *   negative v_threshold is SPATTEN_EINVAL.
+ *   negative v_threshold is SPATTEN_EINVAL; per_head is 0 or 1 and, when 1,
+ *   needs an unquantized decode (else SPATTEN_EUNSUPPORTED).
  */
 int spatten_layer_forward(const spatten_layer_desc* d, void* x,
                           const void* wq, const void* wk, const void* wv, const void* wo,
@@ -164,16 +170,20 @@ int spatten_compact(int32_t n_tensors, const void* const* src, void* const* dst,
  * it is, and the i-th selected row at or above k (in ascending order) moves
  * into the i-th unselected row below k (in ascending order). No other row
  * is read or written, so a cut from k + 1 rows to k moves at most one row.
- * Row r of sequence b of tensor t is base[t] + b*batch_stride[t] +
- * r*row_bytes[t]; base, row_bytes and batch_stride are HOST arrays of
- * n_tensors entries. Requires 1 <= k <= n; k > 8192 or a row longer than
+ * Row r of sequence b of tensor t is the row_bytes[t] bytes at base[t] +
+ * b*batch_stride[t] + r*row_pitch[t] (row_pitch NULL: rows are packed,
+ * pitch = row_bytes; a pitch larger than the row moves one slice of each
+ * row, e.g. one head of a token-major cache); base, row_bytes, row_pitch
+ * and batch_stride are HOST arrays of n_tensors entries. Requires 1 <= k <= n; k > 8192 or a row longer than
  * 64 MiB returns SPATTEN_EUNSUPPORTED. Each idx entry must lie in [0, n) - the caller
- * guarantees this. Sequences must not overlap (batch_stride >= n*row_bytes
- * when batch > 1).
+ * guarantees this. row_pitch must be at least row_bytes, and sequences
+ * must not overlap (batch_stride >= (n-1)*row_pitch + row_bytes when
+ * batch > 1).
  */
 int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* row_bytes,
-                            const int64_t* batch_stride, const int32_t* idx, int32_t batch,
-                            int32_t n, int32_t k, void* stream);
+                            const int64_t* row_pitch, const int64_t* batch_stride,
+                            const int32_t* idx, int32_t batch, int32_t n, int32_t k,
+                            void* stream);
 
 /*
  * spatten_quantize_kv - K/V rows to separately fetchable MSB and LSB

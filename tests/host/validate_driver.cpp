@@ -100,13 +100,22 @@ int main() {
   // in-place compaction
   void* base[1] = {P};
   int64_t irb[1] = {16}, ibs[1] = {1600};
-  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 100, 10), SPATTEN_OK);
-  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 100, 101), SPATTEN_EINVAL);
+  EXPECT(check_compact_inplace(1, base, irb, nullptr, ibs, hi, 2, 100, 10), SPATTEN_OK);
+  EXPECT(check_compact_inplace(1, base, irb, nullptr, ibs, hi, 2, 100, 101), SPATTEN_EINVAL);
   ibs[0] = 1599;
-  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 100, 10), SPATTEN_EINVAL);
+  EXPECT(check_compact_inplace(1, base, irb, nullptr, ibs, hi, 2, 100, 10), SPATTEN_EINVAL);
   ibs[0] = int64_t(16) << 20;
-  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 1 << 16, 8193), SPATTEN_EUNSUPPORTED);
-  EXPECT(check_compact_inplace(1, base, irb, ibs, hi, 2, 1 << 16, 8192), SPATTEN_OK);
+  EXPECT(check_compact_inplace(1, base, irb, nullptr, ibs, hi, 2, 1 << 16, 8193),
+         SPATTEN_EUNSUPPORTED);
+  EXPECT(check_compact_inplace(1, base, irb, nullptr, ibs, hi, 2, 1 << 16, 8192), SPATTEN_OK);
+  // one 128-byte head slice of 1536-byte rows
+  int64_t hrb[1] = {128}, hpitch[1] = {1536}, hbs[1] = {99 * 1536 + 128};
+  EXPECT(check_compact_inplace(1, base, hrb, hpitch, hbs, hi, 2, 100, 10), SPATTEN_OK);
+  hbs[0] = 99 * 1536 + 127;
+  EXPECT(check_compact_inplace(1, base, hrb, hpitch, hbs, hi, 2, 100, 10), SPATTEN_EINVAL);
+  hpitch[0] = 127;
+  hbs[0] = 1 << 20;
+  EXPECT(check_compact_inplace(1, base, hrb, hpitch, hbs, hi, 2, 100, 10), SPATTEN_EINVAL);
   // quantize
   EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 5 * 1024, u8, u8, fp, 5), SPATTEN_OK);
   EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1023, 5 * 1023, u8, u8, fp, 5), SPATTEN_EINVAL);

@@ -128,6 +128,14 @@ def test_decode_rejections(S):
     assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, v_threshold=1e-3)
     assert _call_layer(S, d, 1 << 40, **_prefill_ptrs()) == S.EUNSUPPORTED
+    # per-head importance: a flag, for unquantized decode only
+    d = S.make_desc(**base)
+    d.per_head = 2
+    assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
+    d = S.make_desc(**{**base, "per_head": True, "kv_quantized": True, "pq_threshold": 0.1})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
+    d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, per_head=True)
+    assert _call_layer(S, d, 1 << 40, **_prefill_ptrs()) == S.EUNSUPPORTED
 
 
 def test_topk_compact_quantize_rejections(S):
@@ -156,20 +164,25 @@ def test_compact_inplace_rejections(S):
     lib = S.load()
     vp = ctypes.c_void_p
     VP, I64 = vp * 1, ctypes.c_int64 * 1
-    f = lib.spatten_compact_inplace
-    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 101, None) == S.EINVAL  # k > n
-    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 0, None) == S.EINVAL
-    assert f(1, VP(FAKE), I64(16), I64(1599), vp(FAKE * 2), 2, 100, 10, None) == S.EINVAL
-    assert f(1, VP(FAKE), I64(0), I64(1600), vp(FAKE * 2), 2, 100, 10, None) == S.EINVAL
-    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2 + 2), 2, 100, 10, None) == S.EINVAL
-    assert f(1, VP(0), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 10, None) == S.EINVAL
+
+    def f(nt, base, rb, bs, idx, batch, n, k, pitch=None):
+        return lib.spatten_compact_inplace(nt, base, rb, pitch, bs, idx, batch, n, k, None)
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 101) == S.EINVAL  # k > n
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 0) == S.EINVAL
+    assert f(1, VP(FAKE), I64(16), I64(1599), vp(FAKE * 2), 2, 100, 10) == S.EINVAL
+    assert f(1, VP(FAKE), I64(0), I64(1600), vp(FAKE * 2), 2, 100, 10) == S.EINVAL
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2 + 2), 2, 100, 10) == S.EINVAL
+    assert f(1, VP(0), I64(16), I64(1600), vp(FAKE * 2), 2, 100, 10) == S.EINVAL
+    # a pitch below the row, and sequences that would overlap at the pitch
+    assert f(1, VP(FAKE), I64(16), I64(1 << 20), vp(FAKE * 2), 2, 100, 10, I64(8)) == S.EINVAL
+    assert f(1, VP(FAKE), I64(128), I64(99 * 1536), vp(FAKE * 2), 2, 100, 10,
+             I64(1536)) == S.EINVAL
     # the selection is staged on chip: at most 8192 kept rows per sequence
-    assert f(1, VP(FAKE), I64(16), I64(16 * 9000), vp(FAKE * 2), 1, 9000, 8193,
-             None) == S.EUNSUPPORTED
-    assert f(1, VP(FAKE), I64((1 << 26) + 16), I64(1 << 40), vp(FAKE * 2), 2, 100, 10,
-             None) == S.EUNSUPPORTED
-    assert f(0, None, None, None, None, 2, 100, 10, None) == S.OK
-    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 0, 100, 10, None) == S.OK
+    assert f(1, VP(FAKE), I64(16), I64(16 * 9000), vp(FAKE * 2), 1, 9000, 8193) == S.EUNSUPPORTED
+    assert f(1, VP(FAKE), I64((1 << 26) + 16), I64(1 << 40), vp(FAKE * 2), 2, 100,
+             10) == S.EUNSUPPORTED
+    assert f(0, None, None, None, None, 2, 100, 10) == S.OK
+    assert f(1, VP(FAKE), I64(16), I64(1600), vp(FAKE * 2), 0, 100, 10) == S.OK
 
 
 def test_validator_standalone_with_sanitizers(tmp_path):

@@ -178,6 +178,34 @@ def test_compact_inplace_many_tensors(S):
     _inplace_case(S, B, n, k, idx, tensors)
 
 
+@pytest.mark.parametrize("B,n,k,H,dh", [(3, 97, 41, 4, 64), (2, 411, 410, 12, 64),
+                                         (2, 1025, 410, 12, 64), (1, 50, 7, 3, 128)])
+def test_compact_inplace_head_slices(S, B, n, k, H, dh):
+    """Each head cut separately on its slice of token-major rows (row pitch
+    = the whole row): every head follows its own selection, and no call
+    touches another head's bytes."""
+    print("inplace heads", B, n, k, H, dh, flush=True)
+    rng = np.random.default_rng(n + 31 * H)
+    D = H * dh
+    t = rng.integers(0, 1 << 15, (B, n, D), dtype=np.int32).astype(np.int16)
+    a = rng.standard_normal((B, H, n)).astype(np.float32)
+    idx = np.stack([np.stack([np.sort(rng.choice(n, k, replace=False)) for _ in range(B)])
+                    for _ in range(H)]).astype(np.int32)          # [H, B, k]
+    td = torch.from_numpy(t.copy()).cuda()
+    ad = torch.from_numpy(a.copy()).cuda()
+    idd = torch.from_numpy(idx).cuda()
+    for h in range(H):
+        S.compact_inplace([(td[:, :, h * dh:(h + 1) * dh], dh * 2, n * D * 2, D * 2),
+                           (ad[:, h, :], 4, H * n * 4)], idd[h], n, k)
+    got, ga = td.cpu().numpy(), ad.cpu().numpy()
+    for h in range(H):
+        for b in range(B):
+            np.testing.assert_array_equal(got[b, :, h * dh:(h + 1) * dh],
+                                          inplace_expected(t[b, :, h * dh:(h + 1) * dh],
+                                                           idx[h, b], k))
+            np.testing.assert_array_equal(ga[b, h], inplace_expected(a[b, h], idx[h, b], k))
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("B,n,D", [(1, 1, 2), (2, 5, 8), (3, 17, 768), (2, 33, 1024), (1, 4, 1026)])
 def test_quantize_bit_exact(S, dtype, B, n, D):

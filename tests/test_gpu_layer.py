@@ -158,11 +158,17 @@ VPRUNE_CASES = [(3, 12, 100, 1e-3), (2, 12, 1024, 1e-4), (64, 12, 130, 1e-2),
                 (2, 12, 4200, 1e-4), (3, 5, 5000, 1e-3)]
 
 
-@pytest.mark.parametrize("B,H,L0,quantized,thr,vthr",
-                         [c + (0.0,) for c in DECODE_LAYER_CASES] +
-                         [(B, H, L0, False, 0.0, v) for B, H, L0, v in VPRUNE_CASES])
-def test_decode_layer(S, B, H, L0, quantized, thr, vthr):
-    print("decode case", B, H, L0, quantized, thr, vthr, flush=True)
+# per-head importance (a is [B, H, cap]): (B, H, L0, v_threshold)
+PERHEAD_CASES = [(3, 12, 100, 0.0), (2, 16, 257, 0.0), (64, 12, 130, 0.0), (1, 5, 31, 0.0),
+                 (2, 12, 300, 1e-3), (2, 12, 4200, 1e-4)]
+
+
+@pytest.mark.parametrize("B,H,L0,quantized,thr,vthr,per_head",
+                         [c + (0.0, False) for c in DECODE_LAYER_CASES] +
+                         [(B, H, L0, False, 0.0, v, False) for B, H, L0, v in VPRUNE_CASES] +
+                         [(B, H, L0, False, 0.0, v, True) for B, H, L0, v in PERHEAD_CASES])
+def test_decode_layer(S, B, H, L0, quantized, thr, vthr, per_head):
+    print("decode case", B, H, L0, quantized, thr, vthr, per_head, flush=True)
     dh = 64
     D = H * dh
     rng = np.random.default_rng(B * 10 + L0)
@@ -170,9 +176,10 @@ def test_decode_layer(S, B, H, L0, quantized, thr, vthr):
     K0, V0 = _decode_setup(rng, B, H, dh, L0, cap, quantized)
     w = _weights(rng, D, True)
     x = R.bf16_round(rng.standard_normal((B, D))).astype(np.float32)
-    a0 = np.zeros((B, cap), np.float32)
-    a0[:, :L0] = rng.random((B, L0)) * 5
-    desc = S.make_desc(S.DECODE, S.BF16, False, B, 1, H, H, dh, L0, cap, quantized, thr, vthr)
+    a0 = np.zeros((B, H, cap) if per_head else (B, cap), np.float32)
+    a0[..., :L0] = rng.random(a0[..., :L0].shape) * 5
+    desc = S.make_desc(S.DECODE, S.BF16, False, B, 1, H, H, dh, L0, cap, quantized, thr, vthr,
+                       per_head)
     ws = torch.zeros(S.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     wd = _dev_w(w, torch.bfloat16)
     xd = to_dev(x.reshape(B, 1, D), torch.bfloat16)
@@ -228,10 +235,18 @@ def test_decode_layer(S, B, H, L0, quantized, thr, vthr):
         else:
             assert np.all(rc[b] == 0)
         check_bf16_output(xo[b], xr, what="decode x_out b=%d" % b)
-        da = ao[b, :L0 + 1] - a0[b, :L0 + 1]
-        np.testing.assert_allclose(da, P.sum(axis=0), atol=2e-3 * H / (L0 + 1) + 1e-6, rtol=2e-2)
-        assert abs(da.sum() - H) <= 1e-4 * H
-        assert np.all(ao[b, L0 + 1:] == 0)
+        if per_head:
+            # each head's row of a takes that head's probabilities only
+            da = ao[b, :, :L0 + 1] - a0[b, :, :L0 + 1]
+            np.testing.assert_allclose(da, P, atol=2e-3 / (L0 + 1) + 1e-6, rtol=2e-2)
+            np.testing.assert_allclose(da.sum(axis=1), 1.0, atol=1e-4)
+            assert np.all(ao[b, :, L0 + 1:] == 0)
+        else:
+            da = ao[b, :L0 + 1] - a0[b, :L0 + 1]
+            np.testing.assert_allclose(da, P.sum(axis=0), atol=2e-3 * H / (L0 + 1) + 1e-6,
+                                       rtol=2e-2)
+            assert abs(da.sum() - H) <= 1e-4 * H
+            assert np.all(ao[b, L0 + 1:] == 0)
     if quantized and thr == 0.0:
         assert n_rec == 0
     if quantized and thr > 1:

@@ -28,7 +28,7 @@ from gpu_util import PrefillWs, check_bf16_output, check_selection, to_np
 from oracle import spatten_ref as R
 from workloads import (BERT_BASE, GPT2_DECODE, LONG_CAUSAL, PQ_DECODE, TINY, make_decode_inputs,
                        make_prefill_inputs, scaled)
-from workloads.configs import GPT2_DECODE_ROLLING, GPT2_DECODE_VPRUNE
+from workloads.configs import GPT2_DECODE_PERHEAD, GPT2_DECODE_ROLLING, GPT2_DECODE_VPRUNE
 
 pytestmark = pytest.mark.gpu
 
@@ -343,7 +343,8 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
     w = pipeline.weights_to_device(inputs["layers"], dt)
     st = pipeline.DecodeStack(cfg.n_layers, B, H, dh, cfg.cache_len, cfg.cache_keep, cfg.steps,
                               w, cfg.quantized, cfg.pq_threshold, dt,
-                              v_threshold=cfg.v_threshold, prune_every=cfg.prune_every)
+                              v_threshold=cfg.v_threshold, prune_every=cfg.prune_every,
+                              per_head=cfg.per_head)
     k0 = [torch.from_numpy(l["k_cache"]).to(dt).cuda() for l in inputs["layers"]]
     v0 = [torch.from_numpy(l["v_cache"]).to(dt).cuda() for l in inputs["layers"]]
     st.load(k0, v0)
@@ -351,9 +352,15 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
              "x_nrmse": 0.0, "q_nrmse": 0.0, "v_rows": 0, "v_kept": 0}
     snap = {}
     cap = cfg.cache_cap
-    # oracle importance (fp64) and the entry id of every cache slot, per sequence
-    a_ora = {b: np.zeros(cap) for b in seqs}
-    ids = {b: list(range(cfg.cache_len)) for b in seqs}
+    # importance groups: one shared row, or one row per head (per-head
+    # pruning); oracle importance (fp64) and the entry id of every cache
+    # slot, per sequence and group
+    G = H if cfg.per_head else 1
+    a_ora = {b: np.zeros((G, cap)) for b in seqs}
+    ids = {b: [list(range(cfg.cache_len)) for _ in range(G)] for b in seqs}
+
+    def grp(arr):  # importance of one sequence as [G, cap]
+        return arr.reshape(G, -1)
     # cache rows by entry id (ids are 0 .. L0 + steps - 1), per layer,
     # sequence and tensor: the loaded rows, then each step's appended row
     # (itself checked against the oracle)
@@ -393,8 +400,14 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
             new_id = cfg.cache_len + st.s
             for name, t in c.items():
                 arr = _rows_np(t, b, lc)
-                np.testing.assert_array_equal(arr[:lc - 1], rows[l][b][name][ids[b]],
-                                              err_msg="%s l%d b%d" % (name, l, b))
+                for g in range(G):
+                    want = rows[l][b][name][ids[b][g]]
+                    got = arr[:lc - 1]
+                    if cfg.per_head:   # head g's slice of every row
+                        want = want.reshape(lc - 1, H, dh)[:, g]
+                        got = got.reshape(lc - 1, H, dh)[:, g]
+                    np.testing.assert_array_equal(got, want,
+                                                  err_msg="%s l%d b%d g%d" % (name, l, b, g))
                 rows[l][b][name][new_id] = arr[lc - 1]
             # the appended entry holds this token's k and v
             for name, wname in (("k", "wk"), ("v", "wv")):
@@ -433,12 +446,12 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
                                        for h in range(H)))
             stats["x_nrmse"] = max(stats["x_nrmse"],
                                    check_bf16_output(x_out[b], xr, what="x l%d b%d" % (l, b))[0])
-            da = a_out[b, :lc] - snap["a_in"][b, :lc]
-            ps = P.sum(axis=0)
+            da = grp(a_out[b])[:, :lc] - grp(snap["a_in"][b])[:, :lc]
+            ps = P if cfg.per_head else P.sum(axis=0)[None]
             # deep layers carry large scores (hundreds in log2 units); fp32
             # exp(s - lse) then has ~1e-5..1e-4 relative error per entry
             assert np.max(np.abs(da - ps)) <= 2e-6 * H + 1e-4 * np.max(ps), (l, b)
-            a_ora[b][:lc] += ps
+            a_ora[b][:, :lc] += ps
 
     outs = []
     keep = cfg.cache_keep
@@ -446,27 +459,32 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
         x = torch.from_numpy(inputs["x_steps"][s]).to(dt).cuda()
         outs.append(to_np(st.step(x, record=True, hook=hook)))
         for b in seqs:
-            ids[b].append(cfg.cache_len + s)
+            for g in range(G):
+                ids[b][g].append(cfg.cache_len + s)
         tr = st.trace[-1]
-        assert ("cache_sel" in tr) == (R.prune_after_step(cfg, s) and len(ids[seqs[0]]) > keep)
+        assert ("cache_sel" in tr) == (R.prune_after_step(cfg, s) and
+                                       len(ids[seqs[0]][0]) > keep)
         if "cache_sel" not in tr:
             continue
         stats["cuts"] += 1
-        sel = tr["cache_sel"].cpu().numpy()
+        sel = tr["cache_sel"].cpu().numpy().reshape(G, B, keep)
         a_pre = tr["a_before_cut"].cpu().numpy()
         a_now = to_np(st.abuf[st.side])
-        n = a_pre.shape[1]
+        n = a_pre.shape[-1]
         for b in seqs:
-            np.testing.assert_array_equal(sel[b], R.topk(a_pre[b].astype(np.float32), keep))
-            stats["sel_diff"] += check_selection(sel[b], a_ora[b][:n], keep, BAND)
-            # the cut moves a with the caches; entries past the kept range
-            # start again from 0
-            moved = np.array(cut_slots(a_pre[b], sel[b], keep, st.inplace))
-            np.testing.assert_array_equal(a_now[b, :keep], moved)
-            assert np.all(a_now[b, keep:] == 0)
-            a_ora[b] = np.concatenate([cut_slots(a_ora[b][:n], sel[b], keep, st.inplace),
-                                       np.zeros(cap - keep)])
-            ids[b] = cut_slots(ids[b], sel[b], keep, st.inplace)
+            ap, an = grp(a_pre[b]), grp(a_now[b])
+            for g in range(G):
+                sg = sel[g, b]
+                np.testing.assert_array_equal(sg, R.topk(ap[g].astype(np.float32), keep))
+                stats["sel_diff"] += check_selection(sg, a_ora[b][g, :n], keep, BAND)
+                # the cut moves a with the caches; entries past the kept range
+                # start again from 0
+                moved = np.array(cut_slots(ap[g], sg, keep, st.inplace))
+                np.testing.assert_array_equal(an[g, :keep], moved)
+                assert np.all(an[g, keep:] == 0)
+                a_ora[b][g] = np.concatenate([cut_slots(a_ora[b][g, :n], sg, keep, st.inplace),
+                                              np.zeros(cap - keep)])
+                ids[b][g] = cut_slots(ids[b][g], sg, keep, st.inplace)
     return st, np.stack(outs), stats
 
 
@@ -487,6 +505,11 @@ DECODE_CFGS = {
                                    cache_keep=80, steps=8, prune_every=3), [2]),
     "pq_rolling": (scaled(PQ_DECODE, batch=2, n_layers=3, cache_len=300, cache_keep=150,
                           steps=5, prune_every=1), [1]),
+    "gpt2_perhead": (scaled(GPT2_DECODE_PERHEAD, batch=4, n_layers=4, cache_len=256,
+                            cache_keep=102, steps=4), [0, 3]),
+    "gpt2_perhead_rolling_vprune": (scaled(GPT2_DECODE_PERHEAD, batch=3, n_layers=3,
+                                           cache_len=200, cache_keep=80, steps=5, prune_every=1,
+                                           v_threshold=1e-3), [2]),
 }
 
 
@@ -510,9 +533,10 @@ def test_decode_stack(name):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("cfg", [GPT2_DECODE, PQ_DECODE, GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING],
+@pytest.mark.parametrize("cfg", [GPT2_DECODE, PQ_DECODE, GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING,
+                                 GPT2_DECODE_PERHEAD],
                          ids=["gpt2_decode", "pq_decode", "gpt2_decode_vprune",
-                              "gpt2_decode_rolling"])
+                              "gpt2_decode_rolling", "gpt2_decode_perhead"])
 def test_decode_stack_full_size(cfg):
     """Full batch, cache and layer count; per-layer checks on 1 sequence
     for the first 3 steps (the cache pruning happens after step 1)."""

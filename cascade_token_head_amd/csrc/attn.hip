@@ -177,17 +177,32 @@ attn_fwd_bf16(AttnArgs a) {
   // work, and the first one's P V MFMAs under the second one's softmax.
   // Masking is applied only to sub-tiles that cross the sequence end or the
   // causal diagonal, so interior sub-tiles carry no masking code.
+  // K fragments go through a ring of RING registers: RING reads in flight,
+  // one new read issued per MFMA, so LDS latency hides under the MFMAs
+  constexpr int NKK = DH / 16, RING = NKK < 4 ? NKK : 4;
   auto qk = [&](int buf, int t, floatx16* st) {
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[u][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < DH / 16; ++kk) {
-      const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+    bf16x8 kf[RING];
+    auto kread = [&](int kk) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(
           &Ks[buf][(32 * t + kperm) * KS + 16 * kk + 8 * G]));
+    };
 #pragma unroll
-      for (int u = 0; u < NU; ++u) st[u] = mfma32x32x16(kf, qf[u][kk], st[u]);
+    for (int p = 0; p < RING; ++p) kf[p] = kread(p);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) st[u] = mfma32x32x16(kf[kk % RING], qf[u][kk], st[u]);
+      if (kk + RING < NKK) kf[kk % RING] = kread(kk + RING);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NU, 0);
+      if (kk + RING < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
   auto mask = [&](floatx16* st, int k0, int t) {
@@ -239,15 +254,21 @@ attn_fwd_bf16(AttnArgs a) {
       }
       lsum[u] += ps[0] + ps[1];
     }
+    // V fragments through the same kind of ring (DH / 16 of them)
+    bf16x8 vf[RING];
+    auto vread = [&](int i) {
+      const int dt = i >> 1, s2 = i & 1;
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(
+          &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * s2]));
+    };
 #pragma unroll
-    for (int dt = 0; dt < DH / 32; ++dt)
+    for (int p = 0; p < RING; ++p) vf[p] = vread(p);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &Vs[buf][(32 * dt + col) * VS + 32 * t + 16 * G + 8 * s2]));
+    for (int i = 0; i < NKK; ++i) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) o[dt][u] = mfma32x32x16(vf, pb[s2][u], o[dt][u]);
-      }
+      for (int u = 0; u < NU; ++u) o[i >> 1][u] = mfma32x32x16(vf[i % RING], pb[i & 1][u], o[i >> 1][u]);
+      if (i + RING < NKK) vf[i % RING] = vread(i + RING);
+    }
   };
 
   auto tile = [&](int buf, int k0) {

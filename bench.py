@@ -14,7 +14,12 @@ kernel with the largest share of GPU time, timed with HIP events on its own
 stream in a second, instrumented pass over the same steps. `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+With --graph the timed steps replay one pass captured into a HIP graph (the
+stacks allocate nothing and only enqueue kernels; replays match the eager
+pass bit for bit). On MI355X both time the same: the host already keeps the
+kernels back to back. The per-kernel pass is always eager.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--graph]
 """
 from __future__ import annotations
 
@@ -187,6 +192,9 @@ def main():
     ap.add_argument("--config", default="bert_base")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one pass captured into a HIP graph instead of "
+                         "launching every kernel from the host")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -211,13 +219,20 @@ def main():
                                       cfg.tokens, cfg.heads, dtype, cfg.causal, w)
         x0 = torch.from_numpy(inputs["x"]).to(dtype).cuda()
 
-        def run_pass():
+        def reset():
             stack.load(x0)
+
+        def body():
             stack.run()
+
+        def run_pass():
+            reset()
+            body()
 
         def timed_pass(ev0, ev1):
             ev0.record()
-            run_pass()
+            reset()
+            replay_or(body)
             ev1.record()
     else:
         stack = pipeline.DecodeStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim,
@@ -228,21 +243,49 @@ def main():
         v0 = [torch.from_numpy(l["v_cache"]).to(dtype).cuda() for l in inputs["layers"]]
         xs = torch.from_numpy(inputs["x_steps"]).to(dtype).cuda()
 
-        def run_pass():
+        def reset():
             stack.load(k0, v0)
+
+        def body():
             for s in range(cfg.steps):
                 stack.step(xs[s])
 
+        def run_pass():
+            reset()
+            body()
+
         def timed_pass(ev0, ev1):
-            stack.load(k0, v0)     # cache reset is not part of the decode work
+            reset()                # cache reset is not part of the decode work
             ev0.record()
-            for s in range(cfg.steps):
-                stack.step(xs[s])
+            replay_or(body)
             ev1.record()
 
     for _ in range(args.warmup):
         run_pass()
     torch.cuda.synchronize()
+    # With --graph, one pass is captured into a HIP graph (the stacks allocate
+    # nothing and only enqueue kernels once constructed) and each timed step
+    # replays it from a freshly loaded state.
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_pass()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        reset()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            body()
+        torch.cuda.synchronize()
+
+    def replay_or(fn):
+        if graph is not None:
+            graph.replay()
+        else:
+            fn()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -318,7 +361,8 @@ def main():
            "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic (seeded)",
-           "config": conf, "roofline": roof, "kernels": per_kernel, "cpu_baseline": cpu}
+           "config": conf, "launch": "hip_graph" if args.graph else "eager",
+           "roofline": roof, "kernels": per_kernel, "cpu_baseline": cpu}
     print(json.dumps(out))
 
 

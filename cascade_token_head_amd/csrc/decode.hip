@@ -526,39 +526,58 @@ decode_vsum(DecodeArgs a) {
 // One wave combines the chunk statistics of row (b, h) into its log2-sum-exp
 // (returned) and 1 / sum (the largest probability, exp2(M - lse2)); with
 // write_o it also writes the normalised bf16 output row (lane = dim, dh 64).
-// Lane i holds chunk i's rescale factor; the output pass broadcasts it with
-// readlane and keeps eight chunk loads in flight.
+// The loads are issued up front as one round: lane i's chunk statistics
+// (chunks i, i + 64, ...) and, for the output, the first kPre chunks'
+// partials of dim `lane`. Lane i's first chunk weight is broadcast with
+// readlane; chunks past kPre follow in batches of eight loads.
+constexpr int kPre = 16;
 __device__ float combine_row(const DecodeArgs& a, int b, int h, bool write_o, float* cmax) {
   const int lane = threadIdx.x & 63;
   const int64_t bh = int64_t(b) * a.H + h;
   const float* mp = a.mpart + bh * a.nchunk;
   const float* lp = a.lpart + bh * a.nchunk;
-  float M = -INFINITY;
-  for (int ci = lane; ci < a.nchunk; ci += 64) M = fmaxf(M, mp[ci]);
-  M = wave_max(M);
-  float L = 0.0f;
-  for (int ci = lane; ci < a.nchunk; ci += 64) L += lp[ci] * fast_exp2(mp[ci] - M);
-  L = wave_sum(L);
+  const float* op = a.opart + bh * a.nchunk * a.dh + lane;
+  float ov[kPre];
+  if (write_o) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) ov[u] = u < a.nchunk ? op[int64_t(u) * a.dh] : 0.0f;
+  }
+  const bool has = lane < a.nchunk;
+  const float m0 = has ? mp[lane] : -INFINITY;
+  const float l0 = has ? lp[lane] : 0.0f;
+  // this lane's running (max, sum) over its chunks
+  float M = m0, Ls = l0;
+  for (int ci = lane + 64; ci < a.nchunk; ci += 64) {
+    const float m = mp[ci], l = lp[ci];
+    const float mn = fmaxf(M, m);
+    Ls = Ls * fast_exp2(M - mn) + l * fast_exp2(m - mn);
+    M = mn;
+  }
+  const float Mw = wave_max(M);
+  const float L = wave_sum(M == -INFINITY ? 0.0f : Ls * fast_exp2(M - Mw));
   const float inv = 1.0f / L;
   if (cmax) *cmax = inv;
   if (write_o) {
-    const float* op = a.opart + bh * a.nchunk * a.dh + lane;
+    const float w0 = has ? fast_exp2(m0 - Mw) : 0.0f;
     float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+      acc += ov[u] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), u));
     for (int g0 = 0; g0 < a.nchunk; g0 += 64) {
       const int cnt = a.nchunk - g0 < 64 ? a.nchunk - g0 : 64;
-      const float wl = lane < cnt ? fast_exp2(mp[g0 + lane] - M) : 0.0f;
-      for (int k = 0; k < cnt; k += 8) {
-        float ov[8];
+      const float wl = g0 == 0 ? w0 : (lane < cnt ? fast_exp2(mp[g0 + lane] - Mw) : 0.0f);
+      for (int k = g0 == 0 ? kPre : 0; k < cnt; k += 8) {
+        float ovb[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = k + u < cnt ? op[int64_t(g0 + k + u) * a.dh] : 0.0f;
+        for (int u = 0; u < 8; ++u) ovb[u] = k + u < cnt ? op[int64_t(g0 + k + u) * a.dh] : 0.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          acc += ov[u] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k + u));
+          acc += ovb[u] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k + u));
       }
     }
     static_cast<bf16_t*>(a.o)[int64_t(b) * a.H * a.dh + h * a.dh + lane] = f32_to_bf16(acc * inv);
   }
-  return M + log2f(L);
+  return Mw + log2f(L);
 }
 
 // Quantized caches, after the MSB pass: one wave per (b, h). A row whose
@@ -659,6 +678,34 @@ decode_finish(DecodeArgs a, int mode) {
   __shared__ float lse[kMaxHeads];
   const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6, nt = blockDim.x;
+  const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
+  // The importance operands of this thread's first entry (per head: its
+  // first eight (head, entry) pairs) are requested before the heads are
+  // combined, so their latency overlaps the combine.
+  const int total = a.per_head ? a.H * a.lc : a.lc;
+  float* ab = a.a + int64_t(b) * (a.per_head ? a.H : 1) * a.cap;
+  float sv0[kMaxHeads], av0 = 0.0f;
+  float pv[8], pa[8];
+  int pi[8], ph[8];
+  if (a.per_head) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = threadIdx.x + u * nt;
+      ph[u] = 0;
+      if (i < total) {
+        const int h = i / a.lc, j = i - h * a.lc;
+        ph[u] = h;
+        pi[u] = h * a.cap + j;
+        pv[u] = sp[int64_t(h) * a.lc_pad + j];
+        pa[u] = ab[pi[u]];
+      }
+    }
+  } else if (int(threadIdx.x) < a.lc) {
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h)
+      sv0[h] = h < a.H ? sp[int64_t(h) * a.lc_pad + threadIdx.x] : 0.0f;
+    av0 = ab[threadIdx.x];
+  }
   for (int h = wave; h < a.H; h += nw) {
     const int64_t bh = int64_t(b) * a.H + h;
     if (mode == kFinishAll || (quantized && a.flags[bh])) {
@@ -678,13 +725,13 @@ decode_finish(DecodeArgs a, int mode) {
     if (lane == 0 && a.v_kept && mode != kFinishLseReady) a.v_kept[bh] = a.lc;
   }
   __syncthreads();
-  const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
   if (a.per_head) {
     // a[b, h, j] += exp2(score[b, h, j] - lse2[b, h]) over the H * lc
     // (head, entry) pairs, eight pairs' loads in flight per thread
-    const int total = a.H * a.lc;
-    float* ab = a.a + int64_t(b) * a.H * a.cap;
-    for (int i0 = threadIdx.x; i0 < total; i0 += 8 * nt) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (int(threadIdx.x) + u * nt < total) ab[pi[u]] = pa[u] + fast_exp2(pv[u] - lse[ph[u]]);
+    for (int i0 = threadIdx.x + 8 * nt; i0 < total; i0 += 8 * nt) {
       float sv[8], av[8];
       int ai[8];
 #pragma unroll
@@ -703,7 +750,15 @@ decode_finish(DecodeArgs a, int mode) {
     }
     return;
   }
-  for (int j = threadIdx.x; j < a.lc; j += nt) {
+  // a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h])
+  if (int(threadIdx.x) < a.lc) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h)
+      if (h < a.H) acc += fast_exp2(sv0[h] - lse[h]);
+    ab[threadIdx.x] = av0 + acc;
+  }
+  for (int j = threadIdx.x + nt; j < a.lc; j += nt) {
     float acc = 0.0f;
     for (int h0 = 0; h0 < a.H; h0 += 8) {
       float sv[8];
@@ -714,7 +769,7 @@ decode_finish(DecodeArgs a, int mode) {
       for (int u = 0; u < 8; ++u)
         if (h0 + u < a.H) acc += fast_exp2(sv[u] - lse[h0 + u]);
     }
-    a.a[int64_t(b) * a.cap + j] += acc;
+    ab[j] += acc;
   }
 }
 

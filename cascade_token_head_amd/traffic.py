@@ -1,4 +1,4 @@
-"""HBM traffic of a kernel from rocprofv3 counter runs.
+"""HBM traffic and executed MFMA work of a kernel from rocprofv3 counter runs.
 
     # a plain device-to-device copy of known size, for the counter scale
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o copy_fetch -- \\
@@ -9,6 +9,12 @@
         --fetch run_fetch.csv --write run_write.csv \\
         --copy-fetch copy_fetch.csv --copy-write copy_write.csv \\
         --command '...' --out profiles/
+
+The mfma subcommand reads SQ_INSTS_MFMA (wave-level MFMA instructions per
+dispatch; every prefill MFMA here is a 32x32x16 bf16 one, 32768 flops) and
+the kernel's average duration from a kernel-trace statistics file of the
+same command, and writes profiles/mfma_<label>_<workload>.{json,md} with the
+executed flops per launch and their rate against the bf16 dense peak.
 
 FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch. Each is scaled by
 known bytes / counted bytes of the copy kernel (so a counter that reads
@@ -128,6 +134,52 @@ def summarize_main(a) -> None:
     print(json.dumps(rec))
 
 
+MFMA_FLOPS = {"32x32x16": 2 * 32 * 32 * 16}
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def mfma_main(a) -> None:
+    counts = per_dispatch(a.counters, "SQ_INSTS_MFMA", a.kernel_regex)
+    if not counts:
+        sys.exit("kernel %r not found in the counter run" % a.kernel_regex)
+    rx = re.compile(a.kernel_regex)
+    durs = []
+    with open(a.stats, newline="") as f:
+        for row in csv.DictReader(f):
+            if rx.search(row["Name"]):
+                durs.append((int(row["Calls"]), float(row["TotalDurationNs"])))
+    if not durs:
+        sys.exit("kernel %r not found in the trace statistics" % a.kernel_regex)
+    avg_ns = sum(t for _, t in durs) / sum(c for c, _ in durs)
+    insts = sum(counts.values()) / len(counts)
+    flops = insts * MFMA_FLOPS[a.shape]
+    rate = flops / (avg_ns * 1e-9) / 1e12
+    rec = {"kernel": a.label, "workload": a.workload, "kernel_regex": a.kernel_regex,
+           "dispatches": len(counts), "mfma_insts_per_launch": round(insts),
+           "mfma_shape": a.shape, "executed_flops_per_launch": flops,
+           "avg_duration_us": round(avg_ns / 1e3, 3), "executed_tflops": round(rate, 1),
+           "peak_tflops": PEAK_BF16_TFLOPS, "executed_frac": round(rate / PEAK_BF16_TFLOPS, 4),
+           "source_sha1": source_sha1(a.label), "command": a.command}
+    os.makedirs(a.out, exist_ok=True)
+    base = os.path.join(a.out, "mfma_%s_%s" % (a.label, a.workload))
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    with open(base + ".md", "w") as f:
+        f.write("# Executed MFMA work: %s on %s\n\n" % (a.label, a.workload))
+        f.write("SQ_INSTS_MFMA per dispatch (one rocprofv3 --pmc run) times %d flops per "
+                "v_mfma_f32_%s_bf16, over the kernel's average duration from a "
+                "rocprofv3 --kernel-trace --stats run of the same command.\n\n"
+                % (MFMA_FLOPS[a.shape], a.shape))
+        f.write("| quantity | value |\n|---|---|\n")
+        for k in ("dispatches", "mfma_insts_per_launch", "executed_flops_per_launch",
+                  "avg_duration_us", "executed_tflops", "peak_tflops", "executed_frac"):
+            f.write("| %s | %s |\n" % (k, rec[k]))
+        f.write("\nkernel symbol regex: `%s`\n\nsource sha1: `%s`\n\ncommand:\n\n```\n%s\n```\n"
+                % (a.kernel_regex, rec["source_sha1"], a.command))
+    print(json.dumps(rec))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -144,9 +196,20 @@ def main() -> None:
     s.add_argument("--copy-mib", type=int, default=1024)
     s.add_argument("--command", default="")
     s.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    m = sub.add_parser("mfma")
+    m.add_argument("--label", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--kernel-regex", required=True)
+    m.add_argument("--counters", required=True)
+    m.add_argument("--stats", required=True)
+    m.add_argument("--shape", default="32x32x16", choices=sorted(MFMA_FLOPS))
+    m.add_argument("--command", default="")
+    m.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
     if a.cmd == "copy":
         copy_main(a.mib)
+    elif a.cmd == "mfma":
+        mfma_main(a)
     else:
         summarize_main(a)
 

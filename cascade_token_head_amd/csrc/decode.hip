@@ -1,7 +1,7 @@
 // Decode attention: one new query per sequence against the kept K/V cache,
 // with cumulative token importance (SpAtten, section II "Attention-based NLP
 // models": generation handles one new token per step against cached K and
-// V) and progressive quantization (section III "Progressive Quantization";
+// V) and progressive quantization ("A. Cascade Token Pruning", bullet "Progressive Quantization";
 // "E. ... Progressive Quantization": MSBs first, LSBs fetched and the row
 // recomputed when its largest probability is below a threshold).
 //
@@ -25,7 +25,7 @@
 // what is left, writes O and adds the probabilities that produced O to the
 // token importance.
 //
-// Local value pruning (section III "Local Value Pruning": after the softmax
+// Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning": after the softmax
 // a head drops its low-probability V vectors). A V row can only be skipped
 // once the row's exact probabilities are known, i.e. after the softmax over
 // the whole cache. decode_vrow gives each (sequence, head) row one

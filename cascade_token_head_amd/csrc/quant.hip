@@ -1,6 +1,7 @@
 // Per-token symmetric int8 quantization of K/V rows, split into
-// separately fetchable 4-bit MSB and LSB planes (SpAtten, section III
-// "Progressive Quantization"; IV "Quantization Support": the bitwidth
+// separately fetchable 4-bit MSB and LSB planes (SpAtten, "A. Cascade
+// Token Pruning", bullet "Progressive Quantization"; section IV, bullet
+// "Quantization Support": the bitwidth
 // converter splits fetched bits and joins MSBs with LSBs).
 //
 // One wave per row. Arithmetic is fp32 with IEEE division and

@@ -14,7 +14,7 @@ Decode (section II, generation): one token per step against per-layer K/V
 caches; after every layer of step 1 the caches of all layers are pruned to
 the top cache_keep entries by cumulative importance, and with prune_every
 = r > 0 cut back to cache_keep again after every r-th later step. Local
-value pruning (section III) is a per-layer option of the attention call.
+value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning") is a per-layer option of the attention call.
 """
 from __future__ import annotations
 

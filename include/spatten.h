@@ -85,8 +85,8 @@ typedef struct {
  *   appended at cache row cache_len, then the query attends over rows
  *   0..cache_len (no mask) and a[b, j] (a is [B, cache_cap]) accumulates
  *   for those rows. Unquantized: k_cache, v_cache are [B, cache_cap, D]
- *   in dtype. Quantized (progressive quantization, section III and
- *   "E. ... Progressive Quantization"): k_msb, k_lsb, v_msb, v_lsb are
+ *   in dtype. Quantized (progressive quantization, "A. Cascade
+ *   Token Pruning" and "E. ... Progressive Quantization"): k_msb, k_lsb, v_msb, v_lsb are
  *   [B, cache_cap, D/2] u8 and k_scale, v_scale [B, cache_cap] fp32 as
  *   written by spatten_quantize_kv; this step's k and v rows are coded into
  *   row cache_len of the planes and scales with that function's arithmetic
@@ -95,14 +95,14 @@ typedef struct {
  *   pq_threshold, recomputed with the full code scale*(16*msb + lsb) for
  *   both K and V. recompute (optional, [B, H] int32) receives 1 for
  *   recomputed rows. a accumulates the probabilities that produced O.
- *   Local value pruning (section III "Local Value Pruning"; unquantized
+ *   Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning"; unquantized
  *   caches, v_threshold > 0): after the softmax, V row j of head h enters
  *   O_h only when P_h[j] >= v_threshold, O_h = sum over those j of
  *   P_h[j] V_h[j] (no renormalisation); the other V rows are never read.
  *   a still takes every probability. v_kept (optional, [B, H] int32)
  *   receives the number of V rows that entered O_h (cache_len + 1 without
  *   value pruning).
- *   Per-head token pruning (section VI "Token Pruning"; per_head = 1,
+ *   Per-head token pruning (section "A. Neural Networks Pruning and Quantization", bullet "Token Pruning"; per_head = 1,
  *   unquantized): a is [B, H, cache_cap] and a[b, h, j] takes head h's
  *   probabilities only, so each head can keep its own cache entries (cut
  *   with spatten_compact_inplace on the head's 128-byte slice of each row).
@@ -187,8 +187,8 @@ int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t*
 
 /*
  * spatten_quantize_kv - K/V rows to separately fetchable MSB and LSB
- * planes (section III "Progressive Quantization"; IV "Quantization
- * Support"). For each row of `dim` values, in fp32:
+ * planes ("A. Cascade Token Pruning", bullet "Progressive Quantization"; section IV, bullet
+ * "Quantization Support"). For each row of `dim` values, in fp32:
  *   s = max|x| / 127;  q = clamp(round_half_even(x / s), -127, 127)
  *   (s = 0 and q = 0 for an all-zero row)
  *   msb = q >> 4 (arithmetic, -8..7), lsb = q & 15 (0..15)

@@ -26,7 +26,18 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       bound |x - s q| <= s/2, amax -> +-127, hand-worked rows
                       in tests/golden/.
   pq_head_attention   threshold 0 -> MSB-only attention; threshold > 1 ->
-                      attention over the full int8 cache.
+                      attention over the full int8 cache; a uniform row whose
+                      max p equals the threshold exactly keeps its MSB result
+                      (strict test); at a middle threshold the flat head
+                      returns p and o of torch's softmax over the full codes
+                      and the confident head those over the MSB-only codes.
+  decode_attention /  one new token = the last row of causal torch SDPA
+  decode_layer        (fp64) over [cache; new k/v], with the new key and
+                      value appended in that order; q = 0 gives p = 1/Lc and
+                      o = mean of V; two keys whose scores differ by
+                      sqrt(dh) ln 3 give p = (3/4, 1/4) (the 1/sqrt(dh)
+                      scale); under progressive quantization the stack's
+                      importance sums the recomputed probabilities.
   value_pruned_output one-hot V rows expose every kept probability (and
                       thresholds at the m-th largest keep exactly m rows);
                       threshold 0 -> torch attention; threshold > 1 -> 0;

@@ -207,7 +207,7 @@ def compact(arr, idx) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# progressive quantization (page: section III "Progressive Quantization",
+# progressive quantization (page: "A. Cascade Token Pruning", bullet "Progressive Quantization",
 # IV "Quantization Support", E "Progressive Quantization")
 # --------------------------------------------------------------------------
 
@@ -355,7 +355,7 @@ def run_prefill(cfg, inputs: dict, seqs=None,
 
 
 def value_pruned_output(p, V, tau: float):
-    """Local value pruning (section III, "Local Value Pruning"): once the
+    """Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning"): once the
     softmax has produced a head's probabilities p [Lc], the V rows whose
     probability is below tau are dropped for this head only, so
     o = sum over j with p_j >= tau of p_j V_j. The kept probabilities are
@@ -450,7 +450,7 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
     repeated after every r-th later step, over the entries kept so far plus
     the new ones. cfg.v_threshold > 0 adds local value pruning inside each
     head's attention. With cfg.per_head (per-head token pruning, page
-    section VI "Token Pruning" names it) each head h keeps its own entries:
+    section "A. Neural Networks Pruning and Quantization", bullet "Token Pruning" names it) each head h keeps its own entries:
     a_h[j] accumulates only head h's probabilities and every cut keeps
     topk(a_h, cache_keep) for that head in every layer's K and V. All heads
     keep the same count, so slot r of head h holds head h's r-th entry.

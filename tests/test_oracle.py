@@ -5,8 +5,8 @@ Cited definitions (SpAtten, paperlayer.ai summary of arXiv 2012.09852):
 attention = section II "Attention mechanism"; token importance = column
 sums of probabilities ("B. Motivation", "A. Cascade Token Pruning"); head
 importance = cumulative |attention output| (section II "Cascade pruning");
-top-k = "B. Top-k Engine"; MSB/LSB planes = section III "Progressive
-Quantization" and IV "Quantization Support".
+top-k = "B. Top-k Engine"; MSB/LSB planes = "A. Cascade Token Pruning", bullet
+"Progressive Quantization", and section IV, bullet "Quantization Support".
 """
 import itertools
 import json
@@ -469,7 +469,7 @@ def test_stack_amplifies_one_ulp_perturbation():
 
 
 # ----------------------------------------------------------------- local value pruning
-# (section III "Local Value Pruning": after the softmax, low-probability V
+# ("A. Cascade Token Pruning", bullet "Local Value Pruning": after the softmax, low-probability V
 # vectors are dropped for the current head only)
 
 
@@ -591,7 +591,7 @@ def test_run_decode_rolling_without_cuts_is_the_dense_run():
 
 
 # ----------------------------------------------------------------- per-head token pruning
-# (page section VI "Token Pruning": per-head token pruning; reading: in
+# (page section "A. Neural Networks Pruning and Quantization", bullet "Token Pruning": per-head token pruning; reading: in
 # decode each head keeps its own cache entries by its own importance)
 
 
@@ -656,3 +656,189 @@ def test_per_head_cut_keeps_each_heads_largest():
                     >= a_pre[h][~keep].astype(np.float32).max())
         differ |= not (np.array_equal(ids[0], ids[1]) and np.array_equal(ids[1], ids[2]))
     assert differ, "heads never chose different entries"
+
+
+# ----------------------------------------------------------------- generation-mode attention
+# (SpAtten page, section II "Attention-based NLP models": generation takes one
+# new token per iteration and combines it with the cached keys and values;
+# "E. Query-Key Multiplication Module", bullet "Progressive Quantization":
+# LSBs are fetched and the probabilities recomputed when the largest
+# probability is below the threshold)
+
+
+def _decode_case(seed, H=3, dh=8, L0=11):
+    rng = np.random.default_rng(seed)
+    D = H * dh
+    w = _tiny_weights(D, rng)
+    x = rng.standard_normal(D) * 1.5
+    K0 = rng.standard_normal((L0, H, dh))
+    V0 = rng.standard_normal((L0, H, dh))
+    return w, x, K0, V0
+
+
+def _torch_decode_reference(w, x, K0, V0, H, dh):
+    """The new token's query is the last row of causal attention over the
+    old cache followed by the new token itself: torch SDPA in fp64 on
+    [cache; new] keys and values, written from the definition with torch's
+    own projections (nothing from the oracle)."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    xt = t(x)
+    q = (xt @ t(w["wq"])).reshape(H, dh)
+    k = (xt @ t(w["wk"])).reshape(1, H, dh)
+    v = (xt @ t(w["wv"])).reshape(1, H, dh)
+    Kc = torch.cat([t(K0), k], 0)           # [L0+1, H, dh]
+    Vc = torch.cat([t(V0), v], 0)
+    L = Kc.shape[0]
+    # the new token sits at position L-1 of a causal sequence: as the last
+    # query it sees every key, so SDPA's causal mask on a full query block
+    # gives its row exactly; the other queries are placeholders
+    Qfull = torch.zeros(H, L, dh, dtype=torch.float64)
+    Qfull[:, L - 1] = q
+    o = torch.nn.functional.scaled_dot_product_attention(
+        Qfull[None], Kc.permute(1, 0, 2)[None], Vc.permute(1, 0, 2)[None], is_causal=True)[0]
+    o = o[:, L - 1]                          # [H, dh]
+    p = torch.softmax((Kc.permute(1, 0, 2) @ q[:, :, None])[:, :, 0] / math.sqrt(dh), dim=-1)
+    x_new = xt + o.reshape(-1) @ t(w["wo"])
+    return x_new.numpy(), p.numpy(), k.numpy(), v.numpy()
+
+
+def test_decode_layer_is_the_last_row_of_causal_attention_over_cache_and_new_token():
+    H, dh = 3, 8
+    w, x, K0, V0 = _decode_case(31, H, dh)
+    cache = {"k": K0.copy(), "v": V0.copy()}
+    x_new, P, rec, _, kept = R.decode_layer(x, w, cache, H, dh, bf16=False, quantized=False,
+                                            threshold=0.0)
+    x_ref, p_ref, k_ref, v_ref = _torch_decode_reference(w, x, K0, V0, H, dh)
+    np.testing.assert_allclose(x_new, x_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(P, p_ref, rtol=1e-12, atol=1e-14)
+    # the appended entry is the new token's own key and value, in that order
+    assert cache["k"].shape == (K0.shape[0] + 1, H, dh)
+    np.testing.assert_allclose(cache["k"][-1], k_ref[0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(cache["v"][-1], v_ref[0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(cache["k"][:-1], K0)
+    np.testing.assert_array_equal(cache["v"][:-1], V0)
+    assert not rec.any() and np.all(kept == K0.shape[0] + 1)
+
+
+def test_decode_attention_zero_query_is_uniform_over_the_cache():
+    """q = 0: every score is 0, so p = 1/Lc exactly and o is the mean of
+    the cached values (closed form, independent of the score scale)."""
+    rng = np.random.default_rng(32)
+    H, dh, Lc = 2, 4, 13
+    cache = {"k": rng.standard_normal((Lc, H, dh)), "v": rng.standard_normal((Lc, H, dh))}
+    O, P, _, _, _ = R.decode_attention(np.zeros((H, dh)), cache, H, dh, False, 0.0)
+    np.testing.assert_allclose(P, 1.0 / Lc, rtol=0, atol=1e-16)
+    np.testing.assert_allclose(O, cache["v"].mean(axis=0), atol=1e-14)
+
+
+def test_decode_attention_scale_is_inverse_sqrt_head_dim():
+    """Two cached keys whose scores differ by exactly sqrt(dh) * ln 3 under
+    q . k: with the 1/sqrt(dh) scale the probabilities are 3/4 and 1/4
+    (closed form)."""
+    H, dh = 1, 16
+    q = np.zeros((H, dh))
+    q[0, 0] = 1.0
+    K = np.zeros((2, H, dh))
+    K[0, 0, 0] = math.sqrt(dh) * math.log(3.0)
+    V = np.array([[[1.0] + [0.0] * (dh - 1)], [[0.0] * (dh - 1) + [1.0]]])
+    O, P, _, _, _ = R.decode_attention(q, {"k": K, "v": V}, H, dh, False, 0.0)
+    np.testing.assert_allclose(P[0], [0.75, 0.25], atol=1e-15)
+    np.testing.assert_allclose(O[0, 0], 0.75, atol=1e-15)
+    np.testing.assert_allclose(O[0, -1], 0.25, atol=1e-15)
+
+
+def _quantized_cache(K, V):
+    km, kl, ks = R.quantize_kv(K.reshape(K.shape[0], -1).astype(np.float32))
+    vm, vl, vs = R.quantize_kv(V.reshape(V.shape[0], -1).astype(np.float32))
+    return {"k_msb": km, "k_lsb": kl, "k_scale": ks, "v_msb": vm, "v_lsb": vl, "v_scale": vs}
+
+
+def test_pq_confidence_exactly_at_threshold_is_not_recomputed():
+    """Ten cached keys with identical codes give a uniform MSB-pass row:
+    max p = 1/10, which is the double nearest 0.1, the workload's
+    threshold. The test is strict (recompute only when max p < threshold),
+    so that row keeps its MSB result; just above the threshold it is
+    recomputed."""
+    rng = np.random.default_rng(33)
+    H, dh, Lc = 2, 8, 10
+    # integer-valued rows with amax 127 have scale 1 and exact codes, and an
+    # integer query makes every score exact in any summation order
+    row = rng.integers(-127, 128, H * dh).astype(np.float32)
+    row[0] = 127.0
+    K = np.tile(row, (Lc, 1)).reshape(Lc, H, dh)
+    V = rng.standard_normal((Lc, H, dh)).astype(np.float32)
+    cache = _quantized_cache(K, V)
+    assert np.all(cache["k_scale"] == 1.0)
+    q = rng.integers(-3, 4, (H, dh)).astype(np.float64)
+    O, P, rec, cmax, _ = R.decode_attention(q, cache, H, dh, True, 0.1)
+    assert np.all(cmax == 0.1), cmax
+    assert not rec.any()
+    _, _, rec2, _, _ = R.decode_attention(q, cache, H, dh, True, np.nextafter(0.1, 1.0))
+    assert rec2.all()
+
+
+def test_pq_importance_takes_the_probabilities_that_produced_the_output():
+    """At a middle threshold one head is confident and one is flat. The flat
+    head's returned p and o must be the full-code softmax (both planes),
+    the confident head's the MSB-only one; each is checked against torch's
+    softmax over values dequantised from the int8 codes directly."""
+    rng = np.random.default_rng(34)
+    H, dh, Lc = 2, 16, 40
+    K = rng.standard_normal((Lc, H, dh)).astype(np.float32)
+    V = rng.standard_normal((Lc, H, dh)).astype(np.float32)
+    # head 0 sharp (its query aligned with one key), head 1 flat
+    q = np.zeros((H, dh))
+    q[0] = K[7, 0] * 3.0
+    q[1] = rng.standard_normal(dh) * 0.05
+    cache = _quantized_cache(K, V)
+    q8k, sk = R.quantize_rows(K.reshape(Lc, -1))
+    q8v, sv = R.quantize_rows(V.reshape(Lc, -1))
+    kf = (q8k.astype(np.float64) * sk[:, None]).reshape(Lc, H, dh)
+    vf = (q8v.astype(np.float64) * sv[:, None]).reshape(Lc, H, dh)
+    # MSB-only values: the code with its low four bits cleared
+    km = ((q8k.astype(np.int16) >> 4) * 16 * sk[:, None].astype(np.float64)).reshape(Lc, H, dh)
+    vm = ((q8v.astype(np.int16) >> 4) * 16 * sv[:, None].astype(np.float64)).reshape(Lc, H, dh)
+
+    def tsoft(Kh, qh):
+        s = torch.from_numpy(Kh @ qh / math.sqrt(dh))
+        return torch.softmax(s, dim=0).numpy()
+
+    p_msb = [tsoft(km[:, h], q[h]) for h in range(H)]
+    p_full = [tsoft(kf[:, h], q[h]) for h in range(H)]
+    assert p_msb[0].max() > 0.5 and p_msb[1].max() < 0.1
+    # the two planes must disagree on the flat head, or the pin is empty
+    assert np.max(np.abs(p_full[1] - p_msb[1])) > 1e-4
+    O, P, rec, cmax, _ = R.decode_attention(q, cache, H, dh, True, 0.1)
+    np.testing.assert_array_equal(rec, [False, True])
+    np.testing.assert_allclose(cmax, [p_msb[0].max(), p_msb[1].max()], rtol=1e-12)
+    np.testing.assert_allclose(P[0], p_msb[0], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(P[1], p_full[1], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(O[0], p_msb[0] @ vm[:, 0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(O[1], p_full[1] @ vf[:, 1], rtol=1e-12, atol=1e-14)
+
+
+def test_run_decode_pq_importance_accumulates_recomputed_probabilities():
+    """Through the stack: the importance after step 1 (before the cut) is
+    the sum over layers and heads of the probabilities that produced each
+    head's output; with threshold 1.01 every row is recomputed, so it must
+    equal the sum of full-code softmaxes, which differ from MSB-only ones."""
+    from workloads import PQ_DECODE, make_decode_inputs
+    cfg = scaled(PQ_DECODE, n_layers=1, batch=1, n_heads=2, head_dim=8, cache_len=24,
+                 cache_keep=12, steps=1, pq_threshold=1.01)
+    inp = make_decode_inputs(cfg)
+    out = R.run_decode(cfg, inp)[0]
+    _, a_pre = out["before_prune"][0]
+    L = inp["layers"][0]
+    H, dh = 2, 8
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    x = t(inp["x_steps"][0][0].astype(np.float64))
+    q = R.bf16_round((x @ t(L["wq"])).numpy()).reshape(H, dh)
+    k = R.bf16_round((x @ t(L["wk"])).numpy())
+    Kc = np.concatenate([np.asarray(L["k_cache"][0], np.float64).reshape(24, -1), k[None]], 0)
+    q8, s = R.quantize_rows(Kc.astype(np.float32))
+    kf = (q8.astype(np.float64) * s[:, None]).reshape(25, H, dh)
+    km = ((q8.astype(np.int16) >> 4) * 16 * s[:, None].astype(np.float64)).reshape(25, H, dh)
+    want = sum(torch.softmax(t(kf[:, h] @ q[h] / math.sqrt(dh)), 0).numpy() for h in range(H))
+    msb = sum(torch.softmax(t(km[:, h] @ q[h] / math.sqrt(dh)), 0).numpy() for h in range(H))
+    assert np.max(np.abs(want - msb)) > 1e-4
+    np.testing.assert_allclose(a_pre, want, rtol=1e-10, atol=1e-14)

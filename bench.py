@@ -1,23 +1,31 @@
 #!/usr/bin/env python3
 """Pruned-attention throughput on one MI355X.
 
-A step is one pass of the whole cascade over one batch of synthetic input:
-for the default workload (bert_base: 12 attention-only layers, batch 32,
-T=512, H=12, dh=64, bf16, token keep 1.0 -> 0.5, heads 12 -> 10 from layer
-4) that is QKV projection, attention with fused token/head importance,
-output projection + residual, head and token top-k and compaction, for
-every layer. Inputs are resident on the GPU before timing starts.
+A step is one pass of the whole cascade over one batch of synthetic input.
+The headline workload is long_causal (4 attention-only layers, batch 1,
+T = 32768, H = 32, dh = 128, D = 4096, bf16, causal; 25% of tokens kept
+after layer 1, heads top-24 of 32 from layer 2), the largest configuration
+that fits one GPU: per layer a QKV projection, a row log-sum-exp pass with
+the attention output, a column-sum pass for token importance, the output
+projection + residual, then head and token top-k and compaction. Inputs are
+resident on the GPU before timing starts.
 
 Prints one JSON line. `value` is token-layers per second (sum over layers
 of B * n_l per step, divided by the step time). `roofline` describes the
-kernel with the largest share of GPU time, timed with HIP events on its own
-stream in a second, instrumented pass over the same steps. `cpu_baseline`
+kernel with the largest share of GPU time, timed with HIP events on the
+library's stream in a second, instrumented pass over the same steps;
+`roofline.attention` adds the attention kernels' combined rate (prefill:
+algorithmic and executed MFMA work; decode: attention bytes) and
+`roofline.step` the whole step against the same roof. `per_layer` gives each
+layer's tokens/s including its selection and compaction. `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
+Without --config the line also carries `workloads`: the same measurements
+(no CPU baseline) for bert_base, gpt2_decode and pq_decode, the last with
+the fraction of rows the progressive quantization recomputed.
 
 With --graph the timed steps replay one pass captured into a HIP graph (the
 stacks allocate nothing and only enqueue kernels; replays match the eager
-pass bit for bit). On MI355X both time the same: the host already keeps the
-kernels back to back. The per-kernel pass is always eager.
+pass bit for bit). The per-kernel pass is always eager.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--graph]
 """
@@ -52,9 +60,11 @@ def _cache_lengths(cfg):
     return out
 
 
-def _kernel_work(cfg, v_kept=None):
+def _kernel_work(cfg, v_kept=None, recompute_frac=None):
     """Algorithmic work per kernel name for one step: (flops, bytes).
-    v_kept[s][l]: V rows read at step s, layer l (value pruning)."""
+    v_kept[s][l]: V rows read at step s, layer l (value pruning);
+    recompute_frac: fraction of (step, layer, sequence, head) rows that
+    progressive quantization recomputed with both planes."""
     B, H, dh = cfg.batch, cfg.n_heads, cfg.head_dim
     D = H * dh
     es = 2 if cfg.dtype == "bf16" else 4
@@ -77,8 +87,15 @@ def _kernel_work(cfg, v_kept=None):
             for l in range(cfg.n_layers):
                 add("qkv_gemm", 2.0 * B * 3 * D * D, es * 3 * D * D)
                 add("out_gemm", 2.0 * B * D * D, es * D * D)
+                # importance: a[b, j] read and written once per layer
+                add("decode_finish", 0.0, 8.0 * B * lc)
                 if cfg.quantized:
                     add("pq_attn_msb", 4.0 * B * H * dh * lc, 2 * B * lc * (D // 2 + 4))
+                    # a recomputed (sequence, head) row reads both planes of
+                    # its head slice of K and V, and the two scales
+                    r = recompute_frac or 0.0
+                    add("pq_attn_recompute", 4.0 * r * B * H * dh * lc,
+                        r * B * H * lc * (2 * dh + 8))
                 elif cfg.v_threshold > 0:
                     # K rows once, the kept V rows (a 128-byte head slice
                     # each) and the fp32 scores the importance pass reads
@@ -184,32 +201,61 @@ def _cpu_baseline(cfg, inputs, budget_s: float):
             "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="bert_base")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of one pass captured into a HIP graph instead of "
-                         "launching every kernel from the host")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sequences are independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
+ATTN_KERNELS = {
+    "prefill": ("attn_fwd", "attn_colsum", "importance"),
+    "decode": ("decode_attn", "pq_attn_msb", "decode_flag", "pq_attn_recompute", "decode_finish",
+               "decode_vrow", "decode_scores", "decode_vprune", "decode_vsum"),
+}
 
+
+def _attention_roof(cfg, ktimes, work, steps):
+    """Combined rate of the attention kernels of one step."""
+    names = [n for n in ATTN_KERNELS[cfg.kind] if n in ktimes]
+    ms = sum(ktimes[n][0] for n in names) / steps
+    if ms <= 0:
+        return None
+    if cfg.kind == "prefill":
+        B, dh = cfg.batch, cfg.head_dim
+        alg = 0.0
+        for l in range(cfg.n_layers):
+            n, h = cfg.tokens[l], cfg.heads[l]
+            pairs = n * (n + 1) / 2 if cfg.causal else float(n) * n
+            alg += 4.0 * B * h * dh * pairs
+        # the column-sum pass recomputes Q K^T: 6 instead of 4 flops per
+        # (pair, dim)
+        executed = 1.5 * alg
+        a = alg / (ms / 1e3) / 1e12
+        e = executed / (ms / 1e3) / 1e12
+        return {"kernels": names, "ms_per_step": round(ms, 4), "bound": "mfma", "unit": "TFLOP/s",
+                "achieved_alg": round(a, 2), "frac_alg": round(a / PEAK_BF16_TFLOPS, 4),
+                "achieved_executed": round(e, 2),
+                "frac_executed": round(e / PEAK_BF16_TFLOPS, 4)}
+    by = sum(work.get(n, (0.0, 0.0))[1] for n in names)
+    a = by / (ms / 1e3) / 1e9
+    return {"kernels": names, "ms_per_step": round(ms, 4), "bound": "hbm", "unit": "GB/s",
+            "achieved": round(a, 1), "frac": round(a / PEAK_HBM_GBS, 4)}
+
+
+def _step_roof(cfg, work, ms_per_step):
+    """The whole step's algorithmic work against the config's roof."""
+    fl = sum(v[0] for v in work.values())
+    by = sum(v[1] for v in work.values())
+    sec = ms_per_step / 1e3
+    if cfg.kind == "prefill":
+        a = fl / sec / 1e12
+        return {"bound": "mfma", "unit": "TFLOP/s", "alg_tflop": round(fl / 1e12, 4),
+                "achieved": round(a, 2), "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    a = by / sec / 1e9
+    return {"bound": "hbm", "unit": "GB/s", "alg_gb": round(by / 1e9, 3),
+            "achieved": round(a, 1), "frac": round(a / PEAK_HBM_GBS, 4)}
+
+
+def measure(cfg, args, lib, with_cpu: bool) -> dict:
     import torch
 
     from cascade_token_head_amd import pipeline
-    from cascade_token_head_amd import spatten as S
-    from workloads import BY_NAME, make_inputs
+    from workloads import make_inputs
 
-    cfg = BY_NAME[args.config]
-    lib = S.load()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     inputs = make_inputs(cfg)
     w = pipeline.weights_to_device(inputs["layers"], dtype)
@@ -222,8 +268,8 @@ def main():
         def reset():
             stack.load(x0)
 
-        def body():
-            stack.run()
+        def body(layer_hook=None):
+            stack.run(layer_hook=layer_hook)
 
         def run_pass():
             reset()
@@ -246,9 +292,9 @@ def main():
         def reset():
             stack.load(k0, v0)
 
-        def body():
+        def body(hook=None, record=False):
             for s in range(cfg.steps):
-                stack.step(xs[s])
+                stack.step(xs[s], hook=hook, record=record)
 
         def run_pass():
             reset()
@@ -288,6 +334,7 @@ def main():
             fn()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e0, e1 in evs:
         timed_pass(e0, e1)
@@ -298,6 +345,44 @@ def main():
     tokens = cfg.token_layers()
     value = tokens / (ms_per_step / 1e3)
 
+    # per-layer pass: events at layer boundaries (decode: around each layer
+    # call of every step; the cache cut after a step is timed on its own)
+    per_layer = []
+    if cfg.kind == "prefill":
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(cfg.n_layers + 1)]
+        reset()
+        marks[0].record()
+        body(layer_hook=lambda l: marks[l + 1].record())
+        torch.cuda.synchronize()
+        for l in range(cfg.n_layers):
+            us = marks[l].elapsed_time(marks[l + 1]) * 1e3
+            n = cfg.batch * cfg.tokens[l]
+            per_layer.append({"layer": l + 1, "tokens": n, "heads": cfg.heads[l],
+                              "us": round(us, 2), "tokens_per_s": round(n / (us / 1e6), 1)})
+    else:
+        ev = {}
+
+        def hook(phase, l):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev[(stack.s, l, phase)] = e
+        reset()
+        cut_us = []
+        for s in range(cfg.steps):
+            stack.step(xs[s], hook=hook)
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev[(s, "end")] = e
+        torch.cuda.synchronize()
+        for s in range(cfg.steps):
+            cut_us.append(ev[(s, cfg.n_layers - 1, "post")].elapsed_time(ev[(s, "end")]) * 1e3)
+        for l in range(cfg.n_layers):
+            us = sum(ev[(s, l, "pre")].elapsed_time(ev[(s, l, "post")])
+                     for s in range(cfg.steps)) * 1e3 / cfg.steps
+            per_layer.append({"layer": l + 1, "tokens": cfg.batch, "us": round(us, 2),
+                              "tokens_per_s": round(cfg.batch / (us / 1e6), 1)})
+        per_layer.append({"cache_cuts_us_per_step": round(sum(cut_us) / cfg.steps, 2)})
+
     # instrumented pass: per-kernel HIP-event durations over the same steps
     _read_kernel_times(lib)
     lib.spatten_debug_timing(1)
@@ -306,16 +391,21 @@ def main():
     torch.cuda.synchronize()
     lib.spatten_debug_timing(0)
     ktimes = _read_kernel_times(lib)
-    v_kept, kept_frac = None, None
-    if cfg.kind == "decode" and cfg.v_threshold > 0:
-        # V rows each layer read, from one more (untimed) pass over the steps
-        stack.load(k0, v0)
-        for s in range(cfg.steps):
-            stack.step(xs[s], record=True)
-        v_kept = [[int(n) for n in t["v_kept"].sum(dim=(1, 2)).tolist()] for t in stack.trace]
-        rows = sum(cfg.batch * cfg.n_heads * lc * cfg.n_layers for lc in _cache_lengths(cfg))
-        kept_frac = round(sum(map(sum, v_kept)) / rows, 4)
-    work = _kernel_work(cfg, v_kept)
+    v_kept, kept_frac, recompute_frac = None, None, None
+    if cfg.kind == "decode" and (cfg.v_threshold > 0 or cfg.quantized):
+        # V rows each layer read and rows recomputed, from one more (untimed)
+        # pass over the steps
+        reset()
+        body(record=True)
+        if cfg.v_threshold > 0:
+            v_kept = [[int(n) for n in t["v_kept"].sum(dim=(1, 2)).tolist()]
+                      for t in stack.trace]
+            rows = sum(cfg.batch * cfg.n_heads * lc * cfg.n_layers for lc in _cache_lengths(cfg))
+            kept_frac = round(sum(map(sum, v_kept)) / rows, 4)
+        if cfg.quantized:
+            rc = sum(int(t["recompute"].sum()) for t in stack.trace)
+            recompute_frac = round(rc / (cfg.steps * cfg.n_layers * cfg.batch * cfg.n_heads), 5)
+    work = _kernel_work(cfg, v_kept, recompute_frac)
     per_kernel = {}
     for name, (ms, cnt) in ktimes.items():
         fl, by = work.get(name, (0.0, 0.0))
@@ -338,11 +428,11 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof.update({"kernel": dom, "avg_us": round(dms * 1e3 / max(dcnt, 1), 3),
                  "launches_per_step": dcnt // args.steps,
-                 "traffic": _traffic(dom, cfg.name, dcnt // args.steps)})
+                 "traffic": _traffic(dom, cfg.name, dcnt // args.steps),
+                 "attention": _attention_roof(cfg, ktimes, work, args.steps),
+                 "step": _step_roof(cfg, work, ms_per_step)})
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = _cpu_baseline(cfg, inputs, args.cpu_seconds)
+    cpu = _cpu_baseline(cfg, inputs, args.cpu_seconds) if with_cpu else None
 
     if cfg.kind == "prefill":
         conf = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.tokens[0],
@@ -353,16 +443,67 @@ def main():
         conf = {"workload": cfg.name, "batch": cfg.batch, "cache_len": cfg.cache_len,
                 "cache_keep": cfg.cache_keep, "decode_steps": cfg.steps, "layers": cfg.n_layers,
                 "heads": cfg.n_heads, "head_dim": cfg.head_dim, "quantized": cfg.quantized,
-                "prune_every": cfg.prune_every, "v_threshold": cfg.v_threshold,
-                "per_head": cfg.per_head,
-                "v_rows_kept_frac": kept_frac}
-    out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-           "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+                "pq_threshold": cfg.pq_threshold, "prune_every": cfg.prune_every,
+                "v_threshold": cfg.v_threshold, "per_head": cfg.per_head,
+                "v_rows_kept_frac": kept_frac, "pq_recompute_frac": recompute_frac}
+    del stack, w, inputs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
+            "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+            "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "config": conf,
+            "roofline": roof, "per_layer": per_layer, "kernels": per_kernel,
+            "cpu_baseline": cpu}
+
+
+HEADLINE = "long_causal"
+OTHERS = ("bert_base", "gpt2_decode", "pq_decode")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=None,
+                    help="measure only this workload (default: long_causal as the headline, "
+                         "plus bert_base, gpt2_decode and pq_decode)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one pass captured into a HIP graph instead of "
+                         "launching every kernel from the host")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sequences are independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from cascade_token_head_amd import spatten as S
+    from workloads import BY_NAME
+
+    lib = S.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    head = args.config or HEADLINE
+    print("measuring %s" % head, file=sys.stderr, flush=True)
+    r = measure(BY_NAME[head], args, lib, with_cpu=not args.no_cpu)
+    out = {"metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+           "gpu_ms_per_step": r["gpu_ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic (seeded)",
-           "config": conf, "launch": "hip_graph" if args.graph else "eager",
-           "roofline": roof, "kernels": per_kernel, "cpu_baseline": cpu}
+           "dtype": r["dtype"], "data": "synthetic (seeded)",
+           "config": r["config"], "launch": "hip_graph" if args.graph else "eager",
+           "roofline": r["roofline"], "per_layer": r["per_layer"], "kernels": r["kernels"],
+           "cpu_baseline": r["cpu_baseline"]}
+    if args.config is None:
+        out["workloads"] = {}
+        for name in OTHERS:
+            print("measuring %s" % name, file=sys.stderr, flush=True)
+            o = measure(BY_NAME[name], args, lib, with_cpu=False)
+            o.pop("cpu_baseline")
+            out["workloads"][name] = o
     print(json.dumps(out))
 
 

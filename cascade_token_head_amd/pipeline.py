@@ -70,8 +70,11 @@ class PrefillStack:
         self.pbuf[0].copy_(torch.arange(T, dtype=torch.int32, device=self.g.device).repeat(B))
         self.hbuf[0].copy_(torch.arange(H, dtype=torch.int32, device=self.g.device).repeat(B))
 
-    def run(self, record: bool = False):
-        """Run all layers; returns (x [B, n_L, D], pos [B, n_L], heads [B, h_L])."""
+    def run(self, record: bool = False, layer_hook=None):
+        """Run all layers; returns (x [B, n_L, D], pos [B, n_L], heads [B, h_L]).
+        layer_hook(l), if given, is called after layer l's calls (its
+        forward, and the head and token selection and compaction that
+        follow it) have been enqueued."""
         B, D, es = self.B, self.D, self.es
         cur_t, cur_h = 0, 0
         self.trace = [] if record else None
@@ -117,6 +120,8 @@ class PrefillStack:
                     rec["tok_sel"] = idx.clone()
             if record:
                 self.trace.append(rec)
+            if layer_hook is not None:
+                layer_hook(l)
         nL, hL = self.tokens[-1], self.heads[-1]
         self.final = (self.xbuf[cur_t][: B * nL * D].view(B, nL, D),
                       self.pbuf[cur_t][: B * nL].view(B, nL),

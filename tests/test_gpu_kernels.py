@@ -25,6 +25,9 @@ TOPK_CASES = [
     (5, 300, 150, "signed_zero"), (4, 1025, 410, "normal"), (16, 2049, 1024, "normal"),
     (3, 4097, 2000, "ties"), (1, 32768, 8192, "normal"), (2, 32768, 1, "uniform"),
     (1, 32768, 32768, "ties"), (2, 12, 10, "normal"), (2, 32, 24, "uniform"),
+    # rows longer than 32 keys per thread: every radix pass re-reads the row
+    (1, 40000, 12345, "ties"), (2, 40000, 40000, "normal"), (1, 100000, 1, "uniform"),
+    (2, 65537, 30000, "signed_zero"),
 ]
 
 

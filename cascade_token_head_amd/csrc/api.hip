@@ -1,6 +1,10 @@
 // C ABI entry points of libspatten.so (declared in include/spatten.h).
 // Each call validates on the host (validate.cpp), then enqueues kernels on
-// the caller's stream. Nothing here allocates, synchronises or keeps state.
+// the caller's stream. Nothing here allocates or synchronises; the only
+// state is the per-device address of the fixed scratch array that the
+// allocation-free layer entry point runs in.
+#include <mutex>
+
 #include "../../include/spatten.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -164,6 +168,35 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
   return launch_out(oa, st);
 }
 
+// Scratch of spatten_layer_forward_noalloc: device memory beyond the
+// caller's tensors (projected Q/K/V, partial results, the recompute queue)
+// for callers that cannot allocate. Each device that loads the library
+// holds its own copy until the process ends. In host code `scratch` names
+// a host-side stand-in; kernels get the per-device address from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) char scratch[SPATTEN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char* scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPATTEN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SPATTEN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SPATTEN_EHIP;
+    }
+    scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return SPATTEN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,6 +216,32 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x, const void* wq, 
   }
   if (d->batch == 0) return SPATTEN_OK;
   char* ws = static_cast<char*>(workspace);
+  if (d->mode == SPATTEN_PREFILL)
+    return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, a, g, lse, ws, as_stream(stream));
+  return layer_decode(*d, x, wq, wk, wv, wo, head_idx, a, k_cache, v_cache, k_msb, k_lsb, k_scale,
+                      v_msb, v_lsb, v_scale, recompute, v_kept, ws, as_stream(stream));
+}
+
+int spatten_layer_forward_noalloc(const spatten_layer_desc* d, void* x, const void* wq,
+                                  const void* wk, const void* wv, const void* wo,
+                                  const int32_t* head_idx, float* a, float* g, void* k_cache,
+                                  void* v_cache, uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
+                                  uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
+                                  int32_t* recompute, int32_t* v_kept, float* lse,
+                                  void* stream) {
+  size_t bytes = SPATTEN_NOALLOC_SCRATCH_BYTES;
+  // descriptor first (no workspace: only *d is checked), then the size
+  int st = check_layer(d, x, wq, wk, wv, wo, head_idx, a, g, k_cache, v_cache, k_msb, k_lsb,
+                       k_scale, v_msb, v_lsb, v_scale, nullptr, &bytes);
+  if (st != SPATTEN_OK) return st;
+  if (layer_workspace_bytes(*d) > SPATTEN_NOALLOC_SCRATCH_BYTES) return SPATTEN_EWORKSPACE;
+  if (d->batch == 0) return SPATTEN_OK;
+  char* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != SPATTEN_OK) return st;
+  st = check_layer(d, x, wq, wk, wv, wo, head_idx, a, g, k_cache, v_cache, k_msb, k_lsb, k_scale,
+                   v_msb, v_lsb, v_scale, ws, &bytes);
+  if (st != SPATTEN_OK) return st;
   if (d->mode == SPATTEN_PREFILL)
     return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, a, g, lse, ws, as_stream(stream));
   return layer_decode(*d, x, wq, wk, wv, wo, head_idx, a, k_cache, v_cache, k_msb, k_lsb, k_scale,

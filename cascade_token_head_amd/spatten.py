@@ -21,7 +21,7 @@ PREFILL, DECODE = 0, 1
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
-EXPORTED = ("spatten_layer_forward", "spatten_topk", "spatten_compact", "spatten_compact_inplace",
+EXPORTED = ("spatten_layer_forward", "spatten_layer_forward_noalloc", "spatten_topk", "spatten_compact", "spatten_compact_inplace",
             "spatten_quantize_kv", "spatten_status_string")
 
 
@@ -56,6 +56,8 @@ def _lib():
         lib.spatten_layer_forward.restype = ctypes.c_int
         lib.spatten_layer_forward.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 20 + \
             [ctypes.POINTER(ctypes.c_size_t), vp]
+        lib.spatten_layer_forward_noalloc.restype = ctypes.c_int
+        lib.spatten_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 20
         lib.spatten_topk.restype = ctypes.c_int
         lib.spatten_topk.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp]
         lib.spatten_compact.restype = ctypes.c_int
@@ -133,6 +135,21 @@ def layer_forward(desc: LayerDesc, x, wq, wk, wv, wo, head_idx, a, g, workspace,
         _p(v_scale), _p(recompute), _p(v_kept), _p(lse), _p(workspace), ctypes.byref(nb),
         _stream(stream))
     _check("spatten_layer_forward", st)
+
+
+def layer_forward_noalloc(desc: LayerDesc, x, wq, wk, wv, wo, head_idx, a, g,
+                          k_cache=None, v_cache=None, k_msb=None, k_lsb=None, k_scale=None,
+                          v_msb=None, v_lsb=None, v_scale=None, recompute=None, v_kept=None,
+                          lse=None, stream=None):
+    """layer_forward in the library's fixed per-device scratch (no workspace)."""
+    st = _lib().spatten_layer_forward_noalloc(
+        ctypes.byref(desc), _p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(head_idx), _p(a), _p(g),
+        _p(k_cache), _p(v_cache), _p(k_msb), _p(k_lsb), _p(k_scale), _p(v_msb), _p(v_lsb),
+        _p(v_scale), _p(recompute), _p(v_kept), _p(lse), _stream(stream))
+    _check("spatten_layer_forward_noalloc", st)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def topk(scores: torch.Tensor, k: int, n: Optional[int] = None, out: Optional[torch.Tensor] = None,

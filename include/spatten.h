@@ -131,6 +131,30 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x,
                           void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * spatten_layer_forward_noalloc - spatten_layer_forward without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * arguments and results are those of spatten_layer_forward; the scratch it
+ * needs lives in a fixed device array of SPATTEN_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends (its
+ * address is taken once per device, on the first call with that device
+ * current). It calls no allocating routine. A descriptor whose workspace
+ * (as spatten_layer_forward reports it) exceeds the array returns
+ * SPATTEN_EWORKSPACE before anything is enqueued. Nothing in the array
+ * needs to start at zero: every call writes what it reads. All calls on one
+ * device share the array, so calls that may overlap on one device (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+#define SPATTEN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int spatten_layer_forward_noalloc(const spatten_layer_desc* d, void* x,
+                                  const void* wq, const void* wk, const void* wv, const void* wo,
+                                  const int32_t* head_idx, float* a, float* g,
+                                  void* k_cache, void* v_cache,
+                                  uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
+                                  uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
+                                  int32_t* recompute, int32_t* v_kept, float* lse, void* stream);
+
+/*
  * spatten_topk - on-the-fly top-k ("B. Top-k Engine"): for each row b the
  * k largest of scores[b*row_stride + 0 .. n-1], ranked by fp32 value with
  * -0.0 below +0.0 and equal values broken towards the lower index

@@ -199,3 +199,21 @@ def test_validator_standalone_with_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all validator cases passed" in r.stdout
+
+
+def test_noalloc_rejects_oversized_and_malformed_calls_on_the_host(S):
+    """The allocation-free entry point checks the descriptor, then its fixed
+    scratch size, before it touches a device: a bert_base-sized prefill
+    layer needs more than the scratch holds."""
+    lib = S.load()
+    big = S.make_desc(S.PREFILL, S.BF16, False, 32, 512, 12, 12, 64)
+    assert S.workspace_bytes(big) > S.NOALLOC_SCRATCH_BYTES
+    args = [ctypes.byref(big)] + [None] * 20
+    assert lib.spatten_layer_forward_noalloc(*args) == S.EWORKSPACE
+    bad = S.make_desc(S.PREFILL, S.BF16, False, 2, 64, 12, 13, 64)   # more kept heads than H
+    assert lib.spatten_layer_forward_noalloc(ctypes.byref(bad), *([None] * 20)) == S.EINVAL
+    dec = S.make_desc(S.DECODE, S.BF16, False, 64, 1, 12, 12, 64, 1024, 1056)
+    assert S.workspace_bytes(dec) <= S.NOALLOC_SCRATCH_BYTES
+    with open(HEADER) as f:
+        assert "#define SPATTEN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in f.read()
+    assert S.NOALLOC_SCRATCH_BYTES == 64 << 20

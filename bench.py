@@ -86,16 +86,16 @@ def _kernel_work(cfg, v_kept=None, recompute_frac=None):
         for s, lc in enumerate(_cache_lengths(cfg)):
             for l in range(cfg.n_layers):
                 add("qkv_gemm", 2.0 * B * 3 * D * D, es * 3 * D * D)
-                add("out_gemm", 2.0 * B * D * D, es * D * D)
-                # importance: a[b, j] read and written once per layer
-                add("decode_finish", 0.0, 8.0 * B * lc)
+                # the output projection's launch also runs the importance
+                # pass: a[b, j] read and written once per layer
+                add("out_gemm", 2.0 * B * D * D, es * D * D + 8.0 * B * lc)
                 if cfg.quantized:
-                    add("pq_attn_msb", 4.0 * B * H * dh * lc, 2 * B * lc * (D // 2 + 4))
-                    # a recomputed (sequence, head) row reads both planes of
-                    # its head slice of K and V, and the two scales
+                    # MSB planes and scales of K and V; a recomputed
+                    # (sequence, head) row also reads both planes of its head
+                    # slice of K and V, and the two scales
                     r = recompute_frac or 0.0
-                    add("pq_attn_recompute", 4.0 * r * B * H * dh * lc,
-                        r * B * H * lc * (2 * dh + 8))
+                    add("pq_attn", 4.0 * B * H * dh * lc * (1 + r),
+                        2 * B * lc * (D // 2 + 4) + r * B * H * lc * (2 * dh + 8))
                 elif cfg.v_threshold > 0:
                     # K rows once, the kept V rows (a 128-byte head slice
                     # each) and the fp32 scores the importance pass reads
@@ -203,8 +203,8 @@ def _cpu_baseline(cfg, inputs, budget_s: float):
 
 ATTN_KERNELS = {
     "prefill": ("attn_fwd", "attn_colsum", "importance"),
-    "decode": ("decode_attn", "pq_attn_msb", "decode_flag", "pq_attn_recompute", "decode_finish",
-               "decode_vrow", "decode_scores", "decode_vprune", "decode_vsum"),
+    "decode": ("decode_attn", "pq_attn", "decode_vrow", "decode_scores", "decode_vprune",
+               "decode_vsum", "decode_importance"),
 }
 
 

@@ -146,15 +146,15 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
   da.opart = reinterpret_cast<float*>(ws + w.opart);
   da.lse = reinterpret_cast<float*>(ws + w.lse);
   da.cmax = reinterpret_cast<float*>(ws + w.cmax);
-  da.flags = reinterpret_cast<int32_t*>(ws + w.flags);
-  da.queue = reinterpret_cast<int32_t*>(ws + w.queue);
   da.kcount = reinterpret_cast<int32_t*>(ws + w.kcount);
   da.o = ws + w.o;
   da.a = a;
   da.recompute = recompute;
   da.v_kept = v_kept;
-  SPATTEN_TRY(launch_decode(da, d.kv_quantized != 0, st));
+  ImpArgs imp{};
+  SPATTEN_TRY(launch_decode(da, d.kv_quantized != 0, &imp, st));
   OutArgs oa{};
+  oa.imp = &imp;
   oa.dtype = d.dtype;
   oa.o = ws + w.o;
   oa.wo = wo;
@@ -169,7 +169,7 @@ int layer_decode(const spatten_layer_desc& d, void* x, const void* wq, const voi
 }
 
 // Scratch of spatten_layer_forward_noalloc: device memory beyond the
-// caller's tensors (projected Q/K/V, partial results, the recompute queue)
+// caller's tensors (projected Q/K/V, scores, partial results)
 // for callers that cannot allocate. Each device that loads the library
 // holds its own copy until the process ends. In host code `scratch` names
 // a host-side stand-in; kernels get the per-device address from

@@ -36,6 +36,7 @@
 // per-chunk statistics, decode_vprune (exact probabilities per chunk,
 // importance, kept V rows) and decode_vsum (sum of the chunk outputs).
 #include "common.hpp"
+#include "importance.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
@@ -49,29 +50,15 @@ constexpr int CH = kDecChunk;  // cache entries per chunk
 static_assert(CH == 32, "decode kernels are written for 32-row chunks");
 constexpr int KB = 16;         // rows per load batch
 constexpr int kMaxHeads = 32;
-constexpr int kRecomputeSlots = 128;
 
 enum { kBf16 = 0, kMsb = 1 };
 
 template <int KIND>
-struct RawRow {
-  using T = u32x4;  // 8 bf16 values
-};
-template <>
-struct RawRow<kMsb> {
-  using T = uint32_t;  // 8 MSB nibbles
-};
-
-template <int KIND>
-__device__ __forceinline__ typename RawRow<KIND>::T load_row(const void* bf, const uint8_t* msb,
-                                                             int64_t row, int c, int D) {
-  if constexpr (KIND == kBf16)
-    return *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(bf) + row * D + 8 * c);
-  else
-    return *reinterpret_cast<const uint32_t*>(msb + row * (D / 2) + 4 * c);
+__device__ __forceinline__ u32x4 load_row(const void* bf, int64_t row, int c, int D) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(bf) + row * D + 8 * c);
 }
 
-// signed MSB nibble e of an 8-nibble word
+// signed nibble e of an 8-nibble word
 __device__ __forceinline__ float msb_val(uint32_t w, int e) {
   const int mn = int((w >> (4 * e)) & 15u);
   return float(mn >= 8 ? mn - 16 : mn);
@@ -90,14 +77,29 @@ __device__ __forceinline__ void nibbles_plus8(uint32_t w, float* u) {
   }
 }
 
-// grid (nchunk, B); block = (D/8) * R threads, R rows of the chunk at a time.
-// WITH_V = false stops after the scores and chunk statistics.
-template <int KIND, bool WITH_V = true>
+// The 8 full int8 codes 16 * msb + lsb of a word pair, each offset by +128
+// (so 0..255): the offset MSB nibble becomes the high half of a byte whose
+// low half is the LSB nibble. u[e] = code e + 128.
+__device__ __forceinline__ void codes_plus128(uint32_t wm, uint32_t wl, float* u) {
+  const uint32_t x = wm ^ 0x88888888u;
+  const uint32_t ev = ((x & 0x0F0F0F0Fu) << 4) | (wl & 0x0F0F0F0Fu);
+  const uint32_t od = (x & 0xF0F0F0F0u) | ((wl >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u[2 * k] = float((ev >> (8 * k)) & 0xffu);
+    u[2 * k + 1] = float((od >> (8 * k)) & 0xffu);
+  }
+}
+
+// Scores and per-chunk statistics only (the split value-pruning path, for
+// caches whose scores do not fit one workgroup's LDS): grid (nchunk, B);
+// block = (D/8) * R threads, R rows of the chunk at a time. A thread owns
+// one 8-dim column group (one head's slice) of every R-th row of the chunk
+// and issues all of its row loads before using them; partial dots reduce
+// over the 8 lanes of a head.
 __global__ void __launch_bounds__(256)
-decode_partial(DecodeArgs a) {
-  using Raw = typename RawRow<KIND>::T;
+decode_scores(DecodeArgs a) {
   __shared__ float S[kMaxHeads][CH];
-  __shared__ float obuf[256 * 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, b = blockIdx.y;
   const int H = a.H, dh = a.dh, D = H * dh;
@@ -110,80 +112,30 @@ decode_partial(DecodeArgs a) {
   const int nwaves = (blockDim.x + 63) >> 6;
   const int kpt = CH / R;  // rows per thread
   const int64_t rowb = int64_t(b) * a.cap;
-
-  if constexpr (KIND == kMsb) {
-    if (chunk == 0 && b == 0 && tid == 0) a.queue[0] = 0;
-    if (a.knew && chunk == (a.lc - 1) / CH) {
-      // this workgroup owns the new row: code it before reading it (waves 0
-      // and 1 are always full, since the block has at least 128 threads)
-      const int64_t nr = rowb + a.lc - 1;
-      if (wave == 0)
-        quantize_row_wave<bf16_t>(static_cast<const bf16_t*>(a.knew) + int64_t(b) * D, D,
-                                  a.k_msb + nr * (D / 2), a.k_lsb + nr * (D / 2), a.k_scale + nr);
-      else if (wave == 1)
-        quantize_row_wave<bf16_t>(static_cast<const bf16_t*>(a.vnew) + int64_t(b) * D, D,
-                                  a.v_msb + nr * (D / 2), a.v_lsb + nr * (D / 2), a.v_scale + nr);
-      __threadfence_block();
-      __syncthreads();
-    }
-  }
-
   float q[8];
-  {
-    const u32x4 w =
-        *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + int64_t(b) * D + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      q[2 * e] = __uint_as_float(w[e] << 16);
-      q[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-    }
-  }
+  load8_f32(static_cast<const bf16_t*>(a.q) + int64_t(b) * D + 8 * c, q);
   const float sc = kLog2e / sqrtf(float(dh));
-  // MSB dots use nibble + 8: sum q (n + 8) - 8 sum q
-  float qsum8 = 0.0f;
-  if constexpr (KIND == kMsb) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qsum8 += q[e];
-    qsum8 *= 8.0f;
-  }
-
   // Rows past the cache end are read at row lc-1 (a valid address) and
-  // masked: their score is -inf, so their weight in P V is exactly 0.
+  // masked with a -inf score.
   auto row_of = [&](int tt) {
     const int j = j0 + r + R * tt;
     return rowb + (j < a.lc ? j : a.lc - 1);
   };
-
-  // ---- scores
   for (int t0 = 0; t0 < kpt; t0 += KB) {
-    Raw raw[KB];
-    float ks[KB];
+    u32x4 raw[KB];
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int64_t row = row_of(t0 + u < kpt ? t0 + u : t0);
-      raw[u] = load_row<KIND>(a.k_cache, a.k_msb, row, c, D);
-      if constexpr (KIND == kMsb) ks[u] = a.k_scale[row];
-    }
+    for (int u = 0; u < KB; ++u) raw[u] = load_row<kBf16>(a.k_cache, row_of(t0 + u < kpt ? t0 + u : t0), c, D);
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       float d = 0.0f;
-      if constexpr (KIND == kBf16) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d = fmaf(q[2 * e], __uint_as_float(raw[u][e] << 16), d);
-          d = fmaf(q[2 * e + 1], __uint_as_float(raw[u][e] & 0xffff0000u), d);
-        }
-      } else {
-        float nv[8];
-        nibbles_plus8(raw[u], nv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(q[e], nv[e], d);
-        d = (d - qsum8) * 16.0f;
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(q[2 * e], __uint_as_float(raw[u][e] << 16), d);
+        d = fmaf(q[2 * e + 1], __uint_as_float(raw[u][e] & 0xffff0000u), d);
       }
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
       d += __shfl_xor(d, 4, 64);
-      if constexpr (KIND == kMsb) d *= ks[u];
       const int jl = r + R * (t0 + u), j = j0 + jl;
       if (t0 + u < kpt && (c & 7) == 0) {
         const float sv = j < a.lc ? d * sc : -INFINITY;
@@ -192,22 +144,8 @@ decode_partial(DecodeArgs a) {
       }
     }
   }
-
-  // V rows of the first batch are in flight across the softmax barrier
-  Raw vraw[KB];
-  float vs[KB];
-  auto load_v = [&](int t0) {
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int64_t row = row_of(t0 + u < kpt ? t0 + u : t0);
-      vraw[u] = load_row<KIND>(a.v_cache, a.v_msb, row, c, D);
-      if constexpr (KIND == kMsb) vs[u] = a.v_scale[row];
-    }
-  };
-  if constexpr (WITH_V) load_v(0);
   __syncthreads();
-  // ---- per-head chunk statistics, two heads per wave (32 lanes each);
-  // S becomes exp2(S - m)
+  // per-head chunk statistics, two heads per wave (32 lanes each)
   for (int hh = 2 * wave + (lane >> 5); hh < H; hh += 2 * nwaves) {
     const int l32 = lane & 31;
     const float v = S[hh][l32];
@@ -218,63 +156,14 @@ decode_partial(DecodeArgs a) {
     float l = e;
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    S[hh][l32] = e;
     if (l32 == 0) {
       const int64_t i = (int64_t(b) * H + hh) * a.nchunk + chunk;
       a.mpart[i] = m;
       a.lpart[i] = l;
     }
   }
-  if constexpr (!WITH_V) return;
-  __syncthreads();
-  // ---- P V for this thread's column group
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float wsum = 0.0f;  // MSB path: sum of weights, to remove the +8 offset
-  for (int t0 = 0; t0 < kpt; t0 += KB) {
-    if (t0 > 0) load_v(t0);
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      if (t0 + u >= kpt) break;
-      const float p = S[h][r + R * (t0 + u)];
-      if constexpr (KIND == kBf16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] = fmaf(p, __uint_as_float(vraw[u][e] << 16), acc[2 * e]);
-          acc[2 * e + 1] = fmaf(p, __uint_as_float(vraw[u][e] & 0xffff0000u), acc[2 * e + 1]);
-        }
-      } else {
-        const float w = 16.0f * p * vs[u];
-        float nv[8];
-        nibbles_plus8(vraw[u], nv);
-        wsum += w;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, nv[e], acc[e]);
-      }
-    }
-  }
-  if constexpr (KIND == kMsb) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(-8.0f, wsum, acc[e]);
-  }
-  // reduce the R row phases of each column group
-  if (r > 0) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) obuf[((r - 1) * V + c) * 8 + e] = acc[e];
-  }
-  __syncthreads();
-  if (r == 0) {
-    for (int rr = 1; rr < R; ++rr)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += obuf[((rr - 1) * V + c) * 8 + e];
-    const int d0 = 8 * c - h * dh;
-    float* op = a.opart + ((int64_t(b) * H + h) * a.nchunk + chunk) * dh + d0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) op[e] = acc[e];
-  }
 }
 
-// Cache rows one decode_vrow workgroup keeps scores for in LDS.
-constexpr int kVrowMaxRows = 4096;
 
 // Local value pruning, one workgroup per (sequence, head) row, grid B * H,
 // 256 threads = 32 row groups x 8 lanes; lane c8 of row group g owns the
@@ -466,7 +355,7 @@ decode_vprune(DecodeArgs a) {
       const bool in = t0 + u < kpt;
       pw[u] = in ? P[h][jl] : 0.0f;
       if (in && j0 + jl < a.lc && pw[u] >= tau) {
-        vraw[u] = load_row<kBf16>(a.v_cache, nullptr, rowb + j0 + jl, c, D);
+        vraw[u] = load_row<kBf16>(a.v_cache, rowb + j0 + jl, c, D);
       } else {
         vraw[u] = u32x4{0u, 0u, 0u, 0u};
         pw[u] = 0.0f;
@@ -523,306 +412,486 @@ decode_vsum(DecodeArgs a) {
   }
 }
 
-// One wave combines the chunk statistics of row (b, h) into its log2-sum-exp
-// (returned) and 1 / sum (the largest probability, exp2(M - lse2)); with
-// write_o it also writes the normalised bf16 output row (lane = dim, dh 64).
-// The loads are issued up front as one round: lane i's chunk statistics
-// (chunks i, i + 64, ...) and, for the output, the first kPre chunks'
-// partials of dim `lane`. Lane i's first chunk weight is broadcast with
-// readlane; chunks past kPre follow in batches of eight loads.
-constexpr int kPre = 16;
-__device__ float combine_row(const DecodeArgs& a, int b, int h, bool write_o, float* cmax) {
-  const int lane = threadIdx.x & 63;
-  const int64_t bh = int64_t(b) * a.H + h;
-  const float* mp = a.mpart + bh * a.nchunk;
-  const float* lp = a.lpart + bh * a.nchunk;
-  const float* op = a.opart + bh * a.nchunk * a.dh + lane;
-  float ov[kPre];
-  if (write_o) {
+// ------------------------------------------------ one workgroup per (sequence, head)
+//
+// Dense and progressive-quantization decode: the workgroup streams its
+// head's slice of every cache row (bf16: 128 bytes of K and of V;
+// quantized: 32 bytes of each plane it reads plus the row scales), with K
+// and V of a row requested together, and keeps an online softmax per row
+// group: each load batch raises the group's reference maximum once and
+// rescales its running sum and output. The groups then meet in LDS, so the
+// workgroup ends with the row's exact log2-sum-exp and normalised output
+// and no cross-workgroup combine is needed. Scores go to the stash for the
+// importance pass (a = sum over heads of exp2(s - lse)). Workgroups are
+// mapped so that the heads of one sequence, which read neighbouring slices
+// of the same cache lines, run on one XCD and share its L2.
+//
+// Quantized caches: this step's k and v rows are coded into the planes by
+// every head's workgroup for its own slice (each computes the same
+// per-token scale from the whole row), kept in LDS and entered last. When
+// the row's largest MSB-pass probability (1 / sum) is below the threshold,
+// the workgroup recomputes the whole row at once with both planes of K and
+// V. A quantized row has 512 threads (128 row groups of 4 lanes): the rows
+// of a batch (B * H) are few, so each takes more of a CU.
+
+template <int KIND>
+struct BhCfg;
+template <>
+struct BhCfg<kBf16> {
+  static constexpr int NT = 256;  // threads
+  static constexpr int LPR = 8;   // lanes per cache row, 16 bytes (8 dims) of K and of V each
+  static constexpr int DPL = 8;   // head dims per lane
+  static constexpr int KB = 8;    // rows per lane per load batch
+  static constexpr int WAVES = 4; // waves per SIMD it is built for
+};
+template <>
+struct BhCfg<kMsb> {
+  static constexpr int NT = 512;
+  static constexpr int LPR = 4;   // lanes per cache row, 8 bytes (16 nibbles) of each plane
+  static constexpr int DPL = 16;
+  static constexpr int KB = 9;    // MSB pass; the recompute reads four planes, KBF rows a batch
+  static constexpr int KBF = 4;
+  static constexpr int WAVES = 2;
+};
+
+template <int DPL>
+struct BhState {
+  float m;      // reference maximum of the row group's scores (log2 units)
+  float l;      // sum of exp2(s - m) over the group's rows
+  float wsum;   // quantized: sum of the V weights, to remove the code offset
+  float acc[DPL];
+};
+
+template <int DPL>
+__device__ __forceinline__ void bh_reset(BhState<DPL>& st) {
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.wsum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) ov[u] = u < a.nchunk ? op[int64_t(u) * a.dh] : 0.0f;
-  }
-  const bool has = lane < a.nchunk;
-  const float m0 = has ? mp[lane] : -INFINITY;
-  const float l0 = has ? lp[lane] : 0.0f;
-  // this lane's running (max, sum) over its chunks
-  float M = m0, Ls = l0;
-  for (int ci = lane + 64; ci < a.nchunk; ci += 64) {
-    const float m = mp[ci], l = lp[ci];
-    const float mn = fmaxf(M, m);
-    Ls = Ls * fast_exp2(M - mn) + l * fast_exp2(m - mn);
-    M = mn;
-  }
-  const float Mw = wave_max(M);
-  const float L = wave_sum(M == -INFINITY ? 0.0f : Ls * fast_exp2(M - Mw));
-  const float inv = 1.0f / L;
-  if (cmax) *cmax = inv;
-  if (write_o) {
-    const float w0 = has ? fast_exp2(m0 - Mw) : 0.0f;
-    float acc = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kPre; ++u)
-      acc += ov[u] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), u));
-    for (int g0 = 0; g0 < a.nchunk; g0 += 64) {
-      const int cnt = a.nchunk - g0 < 64 ? a.nchunk - g0 : 64;
-      const float wl = g0 == 0 ? w0 : (lane < cnt ? fast_exp2(mp[g0 + lane] - Mw) : 0.0f);
-      for (int k = g0 == 0 ? kPre : 0; k < cnt; k += 8) {
-        float ovb[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ovb[u] = k + u < cnt ? op[int64_t(g0 + k + u) * a.dh] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          acc += ovb[u] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k + u));
-      }
-    }
-    static_cast<bf16_t*>(a.o)[int64_t(b) * a.H * a.dh + h * a.dh + lane] = f32_to_bf16(acc * inv);
-  }
-  return Mw + log2f(L);
+  for (int e = 0; e < DPL; ++e) st.acc[e] = 0.0f;
 }
 
-// Quantized caches, after the MSB pass: one wave per (b, h). A row whose
-// largest MSB-pass probability is below the threshold is flagged and queued
-// for recompute; the others write O now.
-__global__ void __launch_bounds__(64)
-decode_flag(DecodeArgs a) {
-  const int b = blockIdx.x / a.H, h = blockIdx.x - b * a.H;
-  const int64_t bh = int64_t(b) * a.H + h;
-  float cmax;
-  const float lse2 = combine_row(a, b, h, false, &cmax);
-  const bool flag = cmax < a.threshold;
-  if (!flag) combine_row(a, b, h, true, nullptr);
-  if (threadIdx.x == 0) {
-    a.lse[bh] = lse2;
-    a.cmax[bh] = cmax;
-    a.flags[bh] = flag ? 1 : 0;
-    if (a.recompute) a.recompute[bh] = flag ? 1 : 0;
-    if (flag) a.queue[1 + atomicAdd(a.queue, 1)] = int(bh);
+// Raise the reference maximum to bm (if larger) and rescale what was summed.
+template <int DPL>
+__device__ __forceinline__ void bh_raise(BhState<DPL>& st, float bm) {
+  if (bm > st.m) {
+    const float r = fast_exp2(st.m - bm);  // 0 while nothing was summed
+    st.l *= r;
+    st.wsum *= r;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) st.acc[e] *= r;
+    st.m = bm;
   }
 }
 
-// Recompute queued (b, h) rows with both planes of K and V (code = 16 *
-// msb + lsb). grid (nchunk, slots); workgroup (chunk, s) takes queue
-// entries s, s + slots, ... ; thread t = (row t/2 of the chunk, 32-dim half
-// t%2 of the head). Rewrites the row's scores and chunk partials.
-__global__ void __launch_bounds__(64)
-decode_recompute(DecodeArgs a) {
-  __shared__ float ob[CH][65];
-  const int count = a.queue[0];
-  const int t = threadIdx.x, jl = t >> 1, half = t & 1;
-  const int D = a.H * a.dh;
-  const int chunk = blockIdx.x;
-  const int j = chunk * CH + jl;
-  const bool valid = j < a.lc;
-  const float sc = kLog2e / sqrtf(float(a.dh));
-  for (int slot = blockIdx.y; slot < count; slot += gridDim.y) {
-    const int e = a.queue[1 + slot];
-    const int b = e / a.H, h = e - b * a.H;
-    const int64_t bh = int64_t(b) * a.H + h;
-    const int64_t row = int64_t(b) * a.cap + (valid ? j : a.lc - 1);
-    const int64_t off = row * (D / 2) + (h * a.dh + 32 * half) / 2;
-    const u32x4 km = *reinterpret_cast<const u32x4*>(a.k_msb + off);
-    const u32x4 kl = *reinterpret_cast<const u32x4*>(a.k_lsb + off);
-    const u32x4 vm = *reinterpret_cast<const u32x4*>(a.v_msb + off);
-    const u32x4 vl = *reinterpret_cast<const u32x4*>(a.v_lsb + off);
-    const float ksc = a.k_scale[row], vsc = a.v_scale[row];
-    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) +
-                                                     int64_t(b) * D + h * a.dh + 32 * half);
-    float d = 0.0f;
+// bf16 cache: rows r0..r1-1 of head h; row r0 + g + 32 i belongs to row group g.
+__device__ __forceinline__ void bh_pass_bf16(const DecodeArgs& a, int b, int h, int g, int cl,
+                                             int r0, int r1, const float* q, BhState<8>& st) {
+  constexpr int LPR = BhCfg<kBf16>::LPR, NG = BhCfg<kBf16>::NT / LPR, KBb = BhCfg<kBf16>::KB;
+  const int D = a.H * 64;
+  const int64_t rowb = int64_t(b) * a.cap;
+  const bf16_t* kc = static_cast<const bf16_t*>(a.k_cache) + h * 64 + 8 * cl;
+  const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache) + h * 64 + 8 * cl;
+  float* srow = a.scores + (int64_t(b) * a.H + h) * a.lc_pad;
+  const float sc = kLog2e * 0.125f;  // log2(e) / sqrt(64)
+  const int nit = (r1 - r0 + NG - 1) / NG;
+  for (int i0 = 0; i0 < nit; i0 += KBb) {
+    u32x4 kr[KBb], vr[KBb];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32x4 qw = qp[w];
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const float qv = __uint_as_float((n & 1) ? (qw[n >> 1] & 0xffff0000u) : (qw[n >> 1] << 16));
-        const float code = 16.0f * msb_val(km[w], n) + float((kl[w] >> (4 * n)) & 15u);
-        d = fmaf(qv, code, d);
-      }
+    for (int u = 0; u < KBb; ++u) {
+      const int j = r0 + g + NG * (i0 + u);
+      const int64_t row = rowb + (j < r1 ? j : r0);  // past the range: a valid row, masked
+      kr[u] = *reinterpret_cast<const u32x4*>(kc + row * D);
+      vr[u] = *reinterpret_cast<const u32x4*>(vc + row * D);
     }
-    d += __shfl_xor(d, 1, 64);
-    const float s = valid ? d * ksc * sc : -INFINITY;
-    if (valid && half == 0) a.scores[bh * a.lc_pad + j] = s;
-    float m = s;
+    float s[KBb];
+    float bm = -INFINITY;
 #pragma unroll
-    for (int o = 32; o > 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float p = fast_exp2(s - m);
-    float l = half == 0 ? p : 0.0f;
-    l = wave_sum(l);
-    const float w = p * vsc;
-    __syncthreads();  // previous entry's column sums are done with ob
+    for (int u = 0; u < KBb; ++u) {
+      float d = 0.0f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(q[2 * e], __uint_as_float(kr[u][e] << 16), d);
+        d = fmaf(q[2 * e + 1], __uint_as_float(kr[u][e] & 0xffff0000u), d);
+      }
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 4, 64);
+      const int j = r0 + g + NG * (i0 + u);
+      s[u] = j < r1 ? d * sc : -INFINITY;
+      if (cl == 0 && j < r1) srow[j] = s[u];
+      bm = fmaxf(bm, s[u]);
+    }
+    bh_raise(st, bm);
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
-        ob[jl][32 * half + 8 * x + n] =
-            w * (16.0f * msb_val(vm[x], n) + float((vl[x] >> (4 * n)) & 15u));
-    __syncthreads();
-    float acc = 0.0f;
-    for (int rr = 0; rr < CH; ++rr) acc += ob[rr][t];
-    a.opart[(bh * a.nchunk + chunk) * a.dh + t] = acc;
-    if (t == 0) {
-      a.mpart[bh * a.nchunk + chunk] = m;
-      a.lpart[bh * a.nchunk + chunk] = l;
+    for (int u = 0; u < KBb; ++u) {
+      const int j = r0 + g + NG * (i0 + u);
+      const float p = j < r1 ? fast_exp2(s[u] - st.m) : 0.0f;
+      st.l += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st.acc[2 * e] = fmaf(p, __uint_as_float(vr[u][e] << 16), st.acc[2 * e]);
+        st.acc[2 * e + 1] = fmaf(p, __uint_as_float(vr[u][e] & 0xffff0000u), st.acc[2 * e + 1]);
+      }
     }
   }
 }
 
-// One workgroup per sequence, one wave per head (up to 16 waves): combine
-// the rows not combined yet (mode 0: every row; 1, quantized: the
-// recomputed ones; 2: none, every row's lse is written), then
-// a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h]) for j < lc (with
-// per_head, a[b, h, j] += exp2(score[b, h, j] - lse2[b, h])).
-enum { kFinishAll = 0, kFinishQuantized = 1, kFinishLseReady = 2 };
-__global__ void __launch_bounds__(1024)
-decode_finish(DecodeArgs a, int mode) {
-  const bool quantized = mode == kFinishQuantized;
-  __shared__ float lse[kMaxHeads];
-  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6, nt = blockDim.x;
-  const float* sp = a.scores + int64_t(b) * a.H * a.lc_pad;
-  // The importance operands of this thread's first entry (per head: its
-  // first eight (head, entry) pairs) are requested before the heads are
-  // combined, so their latency overlaps the combine.
-  const int total = a.per_head ? a.H * a.lc : a.lc;
-  float* ab = a.a + int64_t(b) * (a.per_head ? a.H : 1) * a.cap;
-  float sv0[kMaxHeads], av0 = 0.0f;
-  float pv[8], pa[8];
-  int pi[8], ph[8];
-  if (a.per_head) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = threadIdx.x + u * nt;
-      ph[u] = 0;
-      if (i < total) {
-        const int h = i / a.lc, j = i - h * a.lc;
-        ph[u] = h;
-        pi[u] = h * a.cap + j;
-        pv[u] = sp[int64_t(h) * a.lc_pad + j];
-        pa[u] = ab[pi[u]];
-      }
-    }
-  } else if (int(threadIdx.x) < a.lc) {
-#pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h)
-      sv0[h] = h < a.H ? sp[int64_t(h) * a.lc_pad + threadIdx.x] : 0.0f;
-    av0 = ab[threadIdx.x];
+// Offset codes of one lane's 16 dims of a row: MSB only (nibble + 8, the
+// value being 16 * nibble) or both planes (code + 128).
+template <bool FULL>
+__device__ __forceinline__ void bh_codes(uint2 m, uint2 l, float* u) {
+  if constexpr (FULL) {
+    codes_plus128(m.x, l.x, u);
+    codes_plus128(m.y, l.y, u + 8);
+  } else {
+    nibbles_plus8(m.x, u);
+    nibbles_plus8(m.y, u + 8);
   }
-  for (int h = wave; h < a.H; h += nw) {
-    const int64_t bh = int64_t(b) * a.H + h;
-    if (mode == kFinishAll || (quantized && a.flags[bh])) {
-      float cmax;
-      const float l2 = combine_row(a, b, h, true, &cmax);
-      if (lane == 0) {
-        lse[h] = l2;
-        a.lse[bh] = l2;
-        if (!quantized) {
-          a.cmax[bh] = cmax;
-          if (a.recompute) a.recompute[bh] = 0;
-        }
+}
+
+// One row's score and its entry into the state: codes cu of K (offset),
+// the K and V row scales, and the V codes cv.
+template <bool FULL>
+__device__ __forceinline__ float bh_q_dot(const float* q, float qsum, const float* cu, float ks) {
+  const float kmul = FULL ? 1.0f : 16.0f;  // value = scale * kmul * code
+  const float qoff = (FULL ? 128.0f : 8.0f) * qsum;
+  float d = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) d = fmaf(q[e], cu[e], d);
+  d = (d - qoff) * kmul;
+  d += __shfl_xor(d, 1, 64);
+  d += __shfl_xor(d, 2, 64);
+  return d * ks * (kLog2e * 0.125f);
+}
+
+// Quantized cache: rows r0..r1-1 of head h read from the planes (row r0 +
+// g + 128 i belongs to row group g), MSB only or (FULL) both planes.
+template <bool FULL>
+__device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int g, int cl,
+                                          int r0, int r1, const float* q, float qsum,
+                                          BhState<16>& st) {
+  constexpr int LPR = BhCfg<kMsb>::LPR, NG = BhCfg<kMsb>::NT / LPR;
+  constexpr int KBq = FULL ? BhCfg<kMsb>::KBF : BhCfg<kMsb>::KB;
+  const int D = a.H * 64;
+  const int64_t rowb = int64_t(b) * a.cap;
+  const int64_t off = h * 32 + 8 * cl;  // byte offset of this lane's 16 nibbles in a row
+  float* srow = a.scores + (int64_t(b) * a.H + h) * a.lc_pad;
+  const float kmul = FULL ? 1.0f : 16.0f;
+  const int nit = (r1 - r0 + NG - 1) / NG;
+  for (int i0 = 0; i0 < nit; i0 += KBq) {
+    uint2 km[KBq], vm[KBq], kl[KBq], vl[KBq];
+    float ks[KBq], vs[KBq];
+#pragma unroll
+    for (int u = 0; u < KBq; ++u) {
+      const int j = r0 + g + NG * (i0 + u);
+      const int64_t row = rowb + (j < r1 ? j : r0);  // past the range: a valid row, masked
+      km[u] = *reinterpret_cast<const uint2*>(a.k_msb + row * (D / 2) + off);
+      vm[u] = *reinterpret_cast<const uint2*>(a.v_msb + row * (D / 2) + off);
+      if constexpr (FULL) {
+        kl[u] = *reinterpret_cast<const uint2*>(a.k_lsb + row * (D / 2) + off);
+        vl[u] = *reinterpret_cast<const uint2*>(a.v_lsb + row * (D / 2) + off);
+      } else {
+        kl[u] = vl[u] = uint2{0u, 0u};
       }
-    } else if (lane == 0) {
-      lse[h] = a.lse[bh];
+      ks[u] = a.k_scale[row];
+      vs[u] = a.v_scale[row];
     }
-    if (lane == 0 && a.v_kept && mode != kFinishLseReady) a.v_kept[bh] = a.lc;
+    float s[KBq];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < KBq; ++u) {
+      float cu[16];
+      bh_codes<FULL>(km[u], kl[u], cu);
+      const float sv = bh_q_dot<FULL>(q, qsum, cu, ks[u]);
+      const int j = r0 + g + NG * (i0 + u);
+      s[u] = j < r1 ? sv : -INFINITY;
+      if (cl == 0 && j < r1) srow[j] = s[u];
+      bm = fmaxf(bm, s[u]);
+    }
+    bh_raise(st, bm);
+#pragma unroll
+    for (int u = 0; u < KBq; ++u) {
+      const int j = r0 + g + NG * (i0 + u);
+      const float w = j < r1 ? fast_exp2(s[u] - st.m) : 0.0f;
+      st.l += w;
+      const float wv = w * vs[u] * kmul;
+      st.wsum += wv;
+      float cu[16];
+      bh_codes<FULL>(vm[u], vl[u], cu);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(wv, cu[e], st.acc[e]);
+    }
   }
+}
+
+// The new row (index lc-1) from its codes in LDS (MSB words, and LSB words
+// for the recompute): enters the state of row group 0.
+template <bool FULL>
+__device__ __forceinline__ void bh_new_row_q(const DecodeArgs& a, int b, int h, int g, int cl,
+                                             const float* q, float qsum, BhState<16>& st,
+                                             const uint32_t (*nw)[8], const uint32_t (*nlw)[8],
+                                             const float* nscale) {
+  if (g != 0) return;
+  const int j = a.lc - 1;
+  const float kmul = FULL ? 1.0f : 16.0f;
+  const uint2 km = {nw[0][2 * cl], nw[0][2 * cl + 1]};
+  const uint2 kl = {nlw[0][2 * cl], nlw[0][2 * cl + 1]};
+  const uint2 vm = {nw[1][2 * cl], nw[1][2 * cl + 1]};
+  const uint2 vl = {nlw[1][2 * cl], nlw[1][2 * cl + 1]};
+  float cu[16];
+  bh_codes<FULL>(km, kl, cu);
+  const float s = bh_q_dot<FULL>(q, qsum, cu, nscale[0]);
+  if (cl == 0) a.scores[(int64_t(b) * a.H + h) * a.lc_pad + j] = s;
+  bh_raise(st, s);
+  const float w = fast_exp2(s - st.m);
+  st.l += w;
+  const float wv = w * nscale[1] * kmul;
+  st.wsum += wv;
+  bh_codes<FULL>(vm, vl, cu);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(wv, cu[e], st.acc[e]);
+}
+
+// The row groups of the workgroup meet: M = largest reference maximum, L =
+// sum of every group's sum at M, and (threads 0..63) o = dim t of the
+// unnormalised output at M.
+template <int NT, int NG, int DPL>
+__device__ __forceinline__ void bh_combine(const BhState<DPL>& st, int g, int cl,
+                                           float (*red)[65], float* wred, float* M, float* L,
+                                           float* o) {
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float wm = wave_max(st.m);
+  __syncthreads();  // red and wred may still be read by an earlier combine
+  if (lane == 0) wred[wave] = wm;
   __syncthreads();
-  if (a.per_head) {
-    // a[b, h, j] += exp2(score[b, h, j] - lse2[b, h]) over the H * lc
-    // (head, entry) pairs, eight pairs' loads in flight per thread
+  float Mb = wred[0];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (int(threadIdx.x) + u * nt < total) ab[pi[u]] = pa[u] + fast_exp2(pv[u] - lse[ph[u]]);
-    for (int i0 = threadIdx.x + 8 * nt; i0 < total; i0 += 8 * nt) {
-      float sv[8], av[8];
-      int ai[8];
+  for (int w = 1; w < NW; ++w) Mb = fmaxf(Mb, wred[w]);
+  const float f = st.m > -INFINITY ? fast_exp2(st.m - Mb) : 0.0f;
+  const float lw = wave_sum(cl == 0 ? st.l * f : 0.0f);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * nt;
-        if (i < total) {
-          const int h = i / a.lc, j = i - h * a.lc;
-          ai[u] = h * a.cap + j;
-          sv[u] = sp[int64_t(h) * a.lc_pad + j] - lse[h];
-          av[u] = ab[ai[u]];
-        }
+  for (int e = 0; e < DPL; ++e) red[g][DPL * cl + e] = st.acc[e] * f;
+  if (lane == 0) wred[NW + wave] = lw;
+  __syncthreads();
+  *M = Mb;
+  float Ls = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) Ls += wred[NW + w];
+  *L = Ls;
+  // every wave sums NG / NW of the row groups for all 64 dims, then wave 0
+  // adds the NW partial rows (red rows 0..NW-1 are rewritten only after
+  // every wave has read its own rows)
+  constexpr int RPW = NG / NW;
+  float part = 0.0f;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) part += red[wave * RPW + r][lane];
+  __syncthreads();
+  red[wave][lane] = part;
+  __syncthreads();
+  float acc = 0.0f;
+  if (t < 64) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += red[w][t];
+  }
+  *o = acc;
+}
+
+// grid B * H workgroups of BhCfg<KIND>::NT threads; head_dim 64, H <= 32.
+template <int KIND>
+__global__ void __launch_bounds__(BhCfg<KIND>::NT, BhCfg<KIND>::WAVES)
+decode_bh(DecodeArgs a) {
+  constexpr int NT = BhCfg<KIND>::NT, LPR = BhCfg<KIND>::LPR, NG = NT / LPR;
+  constexpr int DPL = BhCfg<KIND>::DPL, NW = NT / 64;
+  __shared__ float red[NG][65];
+  __shared__ float wred[2 * NW];
+  __shared__ uint32_t nw[2][8];   // new row of this head: [k, v] MSB words
+  __shared__ uint32_t nlw[2][8];  // and LSB words
+  __shared__ float nscale[2];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = t / LPR, cl = t - g * LPR;
+  // Workgroups go to the 8 XCDs round-robin; map each XCD's share to a
+  // contiguous range of (b, h) rows, so the heads of one sequence - which
+  // read neighbouring slices of the same cache lines - share one L2.
+  const int nb = int(gridDim.x);
+  const int bh = (nb & 7) == 0 ? (int(blockIdx.x) & 7) * (nb >> 3) + (int(blockIdx.x) >> 3)
+                               : int(blockIdx.x);
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int D = a.H * 64;
+  const bf16_t* qp = static_cast<const bf16_t*>(a.q) + int64_t(b) * D + h * 64 + DPL * cl;
+  float q[DPL];
+  load8_f32(qp, q);
+  if constexpr (DPL == 16) load8_f32(qp + 8, q + 8);
+  float qsum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) qsum += q[e];
+  BhState<DPL> st;
+  bh_reset(st);
+  float M, L, o;
+  float cm;
+  bool flag = false;
+  if constexpr (KIND == kBf16) {
+    bh_pass_bf16(a, b, h, g, cl, 0, a.lc, q, st);
+    bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M, &L, &o);
+    cm = 1.0f / L;
+  } else {
+    // this step's k and v rows: requested now, used after the old rows
+    float xk[8], xv[8];
+    const bool hasx = t < D / 8;
+    if (hasx) {
+      load8_f32(static_cast<const bf16_t*>(a.knew) + int64_t(b) * D + 8 * t, xk);
+      load8_f32(static_cast<const bf16_t*>(a.vnew) + int64_t(b) * D + 8 * t, xv);
+    }
+    bh_pass_q<false>(a, b, h, g, cl, 0, a.lc - 1, q, qsum, st);
+    // code the new row: per-token scale from the whole row, then this
+    // head's 64 dims into the planes (the arithmetic of spatten_quantize_kv,
+    // so every head's workgroup finds the same scale)
+    float amk = 0.0f, amv = 0.0f;
+    if (hasx) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        amk = fmaxf(amk, fabsf(xk[e]));
+        amv = fmaxf(amv, fabsf(xv[e]));
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i0 + u * nt < total) ab[ai[u]] = av[u] + fast_exp2(sv[u]);
     }
-    return;
-  }
-  // a[b, j] += sum_h exp2(score[b, h, j] - lse2[b, h])
-  if (int(threadIdx.x) < a.lc) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h)
-      if (h < a.H) acc += fast_exp2(sv0[h] - lse[h]);
-    ab[threadIdx.x] = av0 + acc;
-  }
-  for (int j = threadIdx.x + nt; j < a.lc; j += nt) {
-    float acc = 0.0f;
-    for (int h0 = 0; h0 < a.H; h0 += 8) {
-      float sv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        sv[u] = h0 + u < a.H ? sp[int64_t(h0 + u) * a.lc_pad + j] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (h0 + u < a.H) acc += fast_exp2(sv[u] - lse[h0 + u]);
+    amk = wave_max(amk);
+    amv = wave_max(amv);
+    if (lane == 0) {
+      wred[wave] = amk;
+      wred[NW + wave] = amv;
     }
-    ab[j] += acc;
+    __syncthreads();
+    float mk = wred[0], mv = wred[NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      mk = fmaxf(mk, wred[w]);
+      mv = fmaxf(mv, wred[NW + w]);
+    }
+    const float sk = mk / 127.0f, sv = mv / 127.0f;
+    const int64_t nrow = int64_t(b) * a.cap + a.lc - 1;
+    if (wave < 2) {
+      const bf16_t* src = static_cast<const bf16_t*>(wave == 0 ? a.knew : a.vnew) +
+                          int64_t(b) * D + h * 64;
+      const int qc = quant_code(bf16_to_f32(src[lane]), wave == 0 ? sk : sv);
+      uint32_t mn = uint32_t((qc >> 4) & 15) << (4 * (lane & 7));
+      uint32_t ln = uint32_t(qc & 15) << (4 * (lane & 7));
+#pragma unroll
+      for (int o2 = 1; o2 < 8; o2 <<= 1) {
+        mn |= __shfl_xor(mn, o2, 64);
+        ln |= __shfl_xor(ln, o2, 64);
+      }
+      if ((lane & 7) == 0) {
+        const int w = lane >> 3;
+        nw[wave][w] = mn;
+        nlw[wave][w] = ln;
+        uint8_t* mp = (wave == 0 ? a.k_msb : a.v_msb) + nrow * (D / 2) + h * 32 + 4 * w;
+        uint8_t* lp = (wave == 0 ? a.k_lsb : a.v_lsb) + nrow * (D / 2) + h * 32 + 4 * w;
+        *reinterpret_cast<uint32_t*>(mp) = mn;
+        *reinterpret_cast<uint32_t*>(lp) = ln;
+      }
+    }
+    if (t == 0) {
+      nscale[0] = sk;
+      nscale[1] = sv;
+      if (h == 0) {
+        a.k_scale[nrow] = sk;
+        a.v_scale[nrow] = sv;
+      }
+    }
+    __syncthreads();
+    bh_new_row_q<false>(a, b, h, g, cl, q, qsum, st, nw, nlw, nscale);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(-8.0f, st.wsum, st.acc[e]);
+    bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M, &L, &o);
+    cm = 1.0f / L;
+    flag = cm < a.threshold;  // uniform: every thread read the same L
+    if (flag) {
+      // flat row: the old rows again with both planes, then the new row
+      // from its codes in LDS (this workgroup wrote its planes; the scale
+      // may come from another head's workgroup, so it is not read back)
+      bh_reset(st);
+      bh_pass_q<true>(a, b, h, g, cl, 0, a.lc - 1, q, qsum, st);
+      bh_new_row_q<true>(a, b, h, g, cl, q, qsum, st, nw, nlw, nscale);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(-128.0f, st.wsum, st.acc[e]);
+      bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M, &L, &o);
+    }
   }
+  if (t < 64) static_cast<bf16_t*>(a.o)[int64_t(b) * D + h * 64 + t] = f32_to_bf16(o / L);
+  if (t == 0) {
+    a.lse[bh] = M + log2f(L);
+    a.cmax[bh] = cm;
+    if (a.recompute) a.recompute[bh] = flag ? 1 : 0;
+    if (a.v_kept) a.v_kept[bh] = a.lc;
+  }
+}
+
+// Importance of the entries a workgroup of the output projection (or of
+// decode_importance) owns, after the attention has written every score
+// and row log2-sum-exp.
+__global__ void __launch_bounds__(256)
+decode_importance(ImpArgs p) {
+  importance_block(p, blockIdx.x);
 }
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream) {
-  const int D = a.H * a.dh;
-  const int V = D / 8;
-  int R = 256 / V;
-  if (R < 1) R = 1;
-  while (R > 1 && CH % R != 0) --R;
-  const int threads = V * R;
-  // the partial kernel assumes whole 8-lane head groups (dh 64), at least
-  // two full waves and at most 256 threads
-  if (a.dh != 64 || a.H > kMaxHeads || threads > 256 || threads < 128)
-    return SPATTEN_EUNSUPPORTED;
-  const dim3 gp(a.nchunk, a.batch);
-  const int fw = a.H < 16 ? a.H : 16;
+int launch_decode(const DecodeArgs& a, bool quantized, ImpArgs* imp, hipStream_t stream) {
+  if (a.dh != 64 || a.H > kMaxHeads) return SPATTEN_EUNSUPPORTED;
+  // the importance pass that follows reads the stash and the row LSE
+  imp->scores = a.scores;
+  imp->lse = a.lse;
+  imp->a = a.a;
+  imp->batch = a.batch;
+  imp->H = a.H;
+  imp->lc = a.lc;
+  imp->lc_pad = a.lc_pad;
+  imp->cap = a.cap;
+  imp->per_head = a.per_head;
+  imp->span = kImpSpan;
+  imp->pieces = int(ceil_div(int64_t(a.per_head ? a.H : 1) * a.lc, kImpSpan));
+  imp->pending = 1;
   if (!quantized && a.v_threshold > 0.0f && a.lc_pad <= kVrowMaxRows) {
-    SPATTEN_TIMED("decode_vrow", stream,
-                  decode_vrow<<<a.batch * a.H, 256, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
-    SPATTEN_TIMED("decode_finish", stream,
-                  decode_finish<<<a.batch, 64 * fw, 0, stream>>>(a, kFinishLseReady));
+    SPATTEN_TIMED("decode_vrow", stream, decode_vrow<<<a.batch * a.H, 256, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
     return SPATTEN_OK;
   }
   if (!quantized && a.v_threshold > 0.0f) {
-    SPATTEN_TIMED("decode_scores", stream,
-                  (decode_partial<kBf16, false><<<gp, threads, 0, stream>>>(a)));
+    // split path: scores and chunk statistics, then exact probabilities per
+    // chunk (importance included) with the kept V rows, then the sum
+    const int D = a.H * a.dh;
+    const int V = D / 8;
+    int R = 256 / V;
+    if (R < 1) R = 1;
+    while (R > 1 && CH % R != 0) --R;
+    const int threads = V * R;
+    if (threads > 256 || threads < 128) return SPATTEN_EUNSUPPORTED;
+    const dim3 gp(a.nchunk, a.batch);
+    SPATTEN_TIMED("decode_scores", stream, (decode_scores<<<gp, threads, 0, stream>>>(a)));
     SPATTEN_LAUNCH_CHECK();
     SPATTEN_TIMED("decode_vprune", stream, decode_vprune<<<gp, threads, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
     SPATTEN_TIMED("decode_vsum", stream, decode_vsum<<<a.batch * a.H, 64, 0, stream>>>(a));
     SPATTEN_LAUNCH_CHECK();
+    imp->pending = 0;
     return SPATTEN_OK;
   }
+  const int blocks = a.batch * a.H;
   if (!quantized) {
-    SPATTEN_TIMED("decode_attn", stream, decode_partial<kBf16><<<gp, threads, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
+    SPATTEN_TIMED("decode_attn", stream,
+                  decode_bh<kBf16><<<blocks, BhCfg<kBf16>::NT, 0, stream>>>(a));
   } else {
-    SPATTEN_TIMED("pq_attn_msb", stream, decode_partial<kMsb><<<gp, threads, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
-    SPATTEN_TIMED("decode_flag", stream, decode_flag<<<a.batch * a.H, 64, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
-    const int slots = a.batch * a.H < kRecomputeSlots ? a.batch * a.H : kRecomputeSlots;
-    const dim3 gr(a.nchunk, slots);
-    SPATTEN_TIMED("pq_attn_recompute", stream, decode_recompute<<<gr, 64, 0, stream>>>(a));
-    SPATTEN_LAUNCH_CHECK();
+    SPATTEN_TIMED("pq_attn", stream, decode_bh<kMsb><<<blocks, BhCfg<kMsb>::NT, 0, stream>>>(a));
   }
-  SPATTEN_TIMED("decode_finish", stream,
-                decode_finish<<<a.batch, 64 * fw, 0, stream>>>(
-                    a, quantized ? kFinishQuantized : kFinishAll));
+  SPATTEN_LAUNCH_CHECK();
+  return SPATTEN_OK;
+}
+
+int launch_importance(const ImpArgs& p, hipStream_t stream) {
+  if (!p.pending || p.batch == 0) return SPATTEN_OK;
+  SPATTEN_TIMED("decode_importance", stream,
+                decode_importance<<<p.batch * p.pieces, 256, 0, stream>>>(p));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }

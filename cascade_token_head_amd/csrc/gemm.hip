@@ -12,6 +12,7 @@
 // boundaries; otherwise M tiles stay inside one sequence.
 // fp32 path: a plain 64x64 VALU tile for the fp32 workload.
 #include "common.hpp"
+#include "importance.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
@@ -37,6 +38,10 @@ struct GemmParams {
   void* out1;
   void* out2;
   int64_t kv_bs;
+  // skinny path: workgroups [0, gemm_blocks) project; the rest run the
+  // decode importance pass (imp.pending)
+  int gemm_blocks;
+  ImpArgs imp;
 };
 
 // Row of M tile `mt_flat`, local row r -> (valid, sequence, row in sequence)
@@ -493,71 +498,72 @@ gemm_tile_kernel(GemmParams p) {
 // ------------------------------------------------------------------ decode projections
 //
 // M = batch rows (at most 64): the weights are the traffic. A workgroup owns
-// 16 output columns for every row; its waves split K into KT 32-wide steps
-// each and issue every fragment load (a weight row's and each 16-row tile's
-// 8 consecutive k per lane) before the first 16x16x32 MFMA, so a workgroup
-// has all of its weight bytes in flight at once. Partial sums meet in LDS,
-// in wave order.
+// 16 output columns of one 16-row tile (the tiles of one column block read
+// the same weights, from one XCD's L2 when the column-block count is a
+// multiple of 8); its waves split K into KT 32-wide steps each and issue
+// every fragment load (a weight row's and the tile's 8 consecutive k per
+// lane) before the first 16x16x32 MFMA. Partial sums meet in LDS, in wave
+// order. The output projection's residual is requested at the start.
 
 constexpr int kSkinnyMaxWaves = 8;
 
 template <int MODE, int KT>
 __global__ void __launch_bounds__(64 * kSkinnyMaxWaves)
 gemm_skinny_kernel(GemmParams p) {
-  __shared__ floatx4 part[kSkinnyMaxWaves * 4][64];
+  if (int(blockIdx.x) >= p.gemm_blocks) {
+    importance_block(p.imp, int(blockIdx.x) - p.gemm_blocks);
+    return;
+  }
+  __shared__ floatx4 part[kSkinnyMaxWaves][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int RT = (p.M_total + 15) >> 4;  // 16-row tiles, 1..4
+  const int ntiles = p.N >> 4;
+  const int rt = int(blockIdx.x) / ntiles, n0 = (int(blockIdx.x) - rt * ntiles) * 16;
   const int l16 = lane & 15, kq = (lane >> 4) * 8;
   const int kbeg = wave * KT * 32 + kq;
   const int ncol = n0 + l16;
-  const bf16_t* w_row = MODE == kOut
-                            ? static_cast<const bf16_t*>(p.W0) + int64_t(ncol) * p.ldw + kbeg
-                            : qkv_weight_row<bf16_t>(p, 0, ncol) + kbeg;
-  u32x4 bv[KT], av[4][KT];
-#pragma unroll
-  for (int u = 0; u < KT; ++u) bv[u] = *reinterpret_cast<const u32x4*>(w_row + 32 * u);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t < RT) {
-      int row = 16 * t + l16;
-      if (row >= p.M_total) row = p.M_total - 1;
-      const bf16_t* a_row = static_cast<const bf16_t*>(p.A) + int64_t(row) * p.lda + kbeg;
-#pragma unroll
-      for (int u = 0; u < KT; ++u) av[t][u] = *reinterpret_cast<const u32x4*>(a_row + 32 * u);
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (t < RT) {
-      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int u = 0; u < KT; ++u) acc = mfma16x16x32(as_bf16x8(av[t][u]), as_bf16x8(bv[u]), acc);
-      part[wave * 4 + t][lane] = acc;
-    }
-  }
-  __syncthreads();
-  for (int rt = wave; rt < RT; rt += nw) {
-    floatx4 acc = part[rt][lane];
-    for (int w = 1; w < nw; ++w) acc += part[w * 4 + rt][lane];
-    // C fragment: lane holds rows 4*(lane/16) + i of the tile, column l16
+  // residual rows of this lane in the epilogue (wave 0)
+  float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (MODE == kOut && wave == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = rt * 16 + 4 * (lane >> 4) + i;
-      if (b >= p.M_total) continue;
-      const float v = acc[i];
-      if (MODE == kOut) {
-        bf16_t* x = static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D + ncol;
-        *x = f32_to_bf16(bf16_to_f32(*x) + v);
-      } else {
-        const int hd = p.h_kept * p.dh;
-        const int which = ncol / hd;
-        const int rem = ncol - which * hd;
-        bf16_t* d = which == 0 ? static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D
-                               : static_cast<bf16_t*>(which == 1 ? p.out1 : p.out2) +
-                                     int64_t(b) * p.kv_bs;
-        d[rem] = f32_to_bf16(v);
-      }
+      if (b < p.M_total) res[i] = bf16_to_f32(static_cast<const bf16_t*>(p.out0)[int64_t(b) * p.D + ncol]);
+    }
+  }
+  const bf16_t* w_row = MODE == kOut
+                            ? static_cast<const bf16_t*>(p.W0) + int64_t(ncol) * p.ldw + kbeg
+                            : qkv_weight_row<bf16_t>(p, 0, ncol) + kbeg;
+  int row = 16 * rt + l16;
+  if (row >= p.M_total) row = p.M_total - 1;
+  const bf16_t* a_row = static_cast<const bf16_t*>(p.A) + int64_t(row) * p.lda + kbeg;
+  u32x4 bv[KT], av[KT];
+#pragma unroll
+  for (int u = 0; u < KT; ++u) bv[u] = *reinterpret_cast<const u32x4*>(w_row + 32 * u);
+#pragma unroll
+  for (int u = 0; u < KT; ++u) av[u] = *reinterpret_cast<const u32x4*>(a_row + 32 * u);
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < KT; ++u) acc = mfma16x16x32(as_bf16x8(av[u]), as_bf16x8(bv[u]), acc);
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  for (int w = 1; w < nw; ++w) acc += part[w][lane];
+  // C fragment: lane holds rows 4*(lane/16) + i of the tile, column l16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = rt * 16 + 4 * (lane >> 4) + i;
+    if (b >= p.M_total) continue;
+    const float v = acc[i];
+    if (MODE == kOut) {
+      static_cast<bf16_t*>(p.out0)[int64_t(b) * p.D + ncol] = f32_to_bf16(res[i] + v);
+    } else {
+      const int hd = p.h_kept * p.dh;
+      const int which = ncol / hd;
+      const int rem = ncol - which * hd;
+      bf16_t* d = which == 0 ? static_cast<bf16_t*>(p.out0) + int64_t(b) * p.D
+                             : static_cast<bf16_t*>(which == 1 ? p.out1 : p.out2) +
+                                   int64_t(b) * p.kv_bs;
+      d[rem] = f32_to_bf16(v);
     }
   }
 }
@@ -573,8 +579,10 @@ inline int skinny_kt(int K) {
 }
 
 template <int MODE>
-int run_skinny(const GemmParams& p, int kt, hipStream_t stream, const char* name) {
-  const dim3 grid(unsigned(p.N / 16));
+int run_skinny(GemmParams& p, int kt, hipStream_t stream, const char* name) {
+  p.gemm_blocks = (p.N / 16) * int((p.M_total + 15) / 16);
+  const int imp_blocks = p.imp.pending ? p.imp.batch * p.imp.pieces : 0;
+  const dim3 grid(unsigned(p.gemm_blocks + imp_blocks));
   const int threads = 64 * (p.K / 32 / kt);
   switch (kt) {
     case 1: SPATTEN_TIMED(name, stream, gemm_skinny_kernel<MODE, 1><<<grid, threads, 0, stream>>>(p)); break;
@@ -683,6 +691,11 @@ int run_gemm(GemmParams& p, int dtype, hipStream_t stream) {
   if (MODE != kQkvPrefill && dtype == SPATTEN_BF16 && !p.seq_tiled && p.M_total <= 64 &&
       p.N % 16 == 0 && kt > 0)
     return run_skinny<MODE>(p, kt, stream, name);
+  if (p.imp.pending) {
+    // the projection takes a tiled path: the importance pass runs alone
+    const int st = launch_importance(p.imp, stream);
+    if (st != SPATTEN_OK) return st;
+  }
   if (dtype == SPATTEN_BF16 && MODE != kQkvDecode) {
     // 128x128 tiles of four 64x64 waves run two workgroups per CU; 256x256
     // tiles of eight 128x64 waves run one, read a quarter fewer LDS bytes
@@ -762,6 +775,7 @@ int launch_out(const OutArgs& a, hipStream_t stream) {
   p.dh = a.dh;
   p.D = a.D;
   p.out0 = a.x;
+  if (a.imp) p.imp = *a.imp;
   return run_gemm<kOut>(p, a.dtype, stream);
 }
 

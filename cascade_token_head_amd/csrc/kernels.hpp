@@ -41,7 +41,22 @@ struct QkvArgs {
 };
 int launch_qkv(const QkvArgs& a, hipStream_t stream);
 
-// Output projection with residual: x[b, m, :] += O[b, m, :] wo[:, gathered]^T
+// Decode token importance from the score stash and row LSE of one layer
+// (see importance.hpp): blocks = batch * pieces, `span` entries each.
+constexpr int kImpSpan = 512;
+struct ImpArgs {
+  const float* scores;  // [B, H, lc_pad] log2 units
+  const float* lse;     // [B, H] log2-sum-exp
+  float* a;             // [B, cap], or [B, H, cap] with per_head
+  int batch, H, lc, lc_pad, cap, per_head;
+  int span, pieces;
+  int pending;          // 0: the attention kernels already added it
+};
+int launch_importance(const ImpArgs& p, hipStream_t stream);
+
+// Output projection with residual: x[b, m, :] += O[b, m, :] wo[:, gathered]^T.
+// imp (decode, optional): the layer's importance pass, run by extra
+// workgroups of the projection when it takes the skinny path, else alone.
 struct OutArgs {
   int dtype;
   const void* o;  // [B, n, h_kept*dh]
@@ -49,6 +64,7 @@ struct OutArgs {
   const int32_t* head_idx;
   int batch, n, h_kept, dh, D;
   void* x;
+  const ImpArgs* imp;
 };
 int launch_out(const OutArgs& a, hipStream_t stream);
 
@@ -73,7 +89,9 @@ struct AttnArgs {
 };
 int launch_attention(const AttnArgs& a, hipStream_t stream);
 
-// Decode attention over cache rows 0..lc-1 for every (b, h).
+// Decode attention over cache rows 0..lc-1 for every (b, h). Quantized
+// caches: knew/vnew hold this step's k and v rows [B, D] bf16, which the
+// attention codes into plane row lc-1.
 struct DecodeArgs {
   const void* q;  // [B, D] bf16
   const void* k_cache;
@@ -84,26 +102,25 @@ struct DecodeArgs {
   uint8_t* v_msb;
   uint8_t* v_lsb;
   float* v_scale;
-  const void* knew;  // quantized: this step's k and v rows [B, D] bf16, coded
-  const void* vnew;  // into plane row lc-1 by the MSB pass before it reads it
+  const void* knew;
+  const void* vnew;
   int batch, H, dh, cap, lc, lc_pad, nchunk;
   float threshold;
   float v_threshold;  // local value pruning (unquantized; 0 = off)
   int per_head;       // 1: a is [B, H, cap] and takes each head's probabilities apart
-  float* scores;  // [B, H, lc_pad]
+  float* scores;  // [B, H, lc_pad] log2-unit scores (the importance pass reads them)
   float* mpart;
-  float* lpart;   // [B, H, nchunk]
+  float* lpart;   // [B, H, nchunk] chunk statistics (split value-pruning path)
   float* opart;   // [B, H, nchunk, dh]
-  float* lse;     // [B, H]
-  float* cmax;    // [B, H]
-  int32_t* flags; // [B, H]
-  int32_t* queue; // [0] = count, then entries b*H + h
+  float* lse;     // [B, H] row log2-sum-exp
+  float* cmax;    // [B, H] largest probability (MSB pass when quantized)
   int32_t* kcount;  // [B, H, nchunk] V rows kept per chunk (value pruning)
   void* o;        // [B, D] bf16
   float* a;       // [B, cap], or [B, H, cap] with per_head
   int32_t* recompute;  // optional [B, H]
   int32_t* v_kept;     // optional [B, H]
 };
-int launch_decode(const DecodeArgs& a, bool quantized, hipStream_t stream);
+// Fills *imp with the importance pass the layer still needs (imp->pending).
+int launch_decode(const DecodeArgs& a, bool quantized, ImpArgs* imp, hipStream_t stream);
 
 }  // namespace spatten

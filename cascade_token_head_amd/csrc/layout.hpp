@@ -27,8 +27,11 @@ SPATTEN_HD constexpr int attn_qblock(int dh) { return dh == 64 ? 128 : 256; }
 constexpr int kAttnKBlock = 256;
 // fp32 attention: query rows per workgroup.
 constexpr int kAttnF32Rows = 8;
-// Decode: cache entries per split-K chunk.
+// Decode: cache entries per chunk of the split value-pruning path, and the
+// most cache rows whose scores one value-pruning workgroup keeps in LDS
+// (longer caches take the split path).
 constexpr int kDecChunk = 32;
+constexpr int kVrowMaxRows = 4096;
 // In-place compaction: most rows one call may keep per sequence (the
 // selection is staged in LDS), and the longest row it moves (row units are
 // counted in 32-bit integers).
@@ -48,7 +51,7 @@ struct PrefillWs {
 
 struct DecodeWs {
   int64_t lc, lc_pad, nchunk;
-  size_t q, knew, vnew, scores, mpart, lpart, opart, lse, cmax, flags, queue, kcount, o, total;
+  size_t q, knew, vnew, scores, mpart, lpart, opart, lse, cmax, kcount, o, total;
 };
 
 inline size_t dtype_bytes(int dt) { return dt == SPATTEN_BF16 ? 2 : 4; }
@@ -86,14 +89,16 @@ inline DecodeWs decode_ws(const spatten_layer_desc& d) {
   w.knew = take(B * D * 2);
   w.vnew = take(B * D * 2);
   w.scores = take(B * H * w.lc_pad * 4);
-  w.mpart = take(B * H * w.nchunk * 4);
-  w.lpart = take(B * H * w.nchunk * 4);
-  w.opart = take(B * H * w.nchunk * dh * 4);
+  // chunk statistics and partial outputs: only the split value-pruning
+  // path uses them
+  const bool split = d.v_threshold > 0.0f && w.lc_pad > kVrowMaxRows;
+  w.mpart = take(split ? B * H * w.nchunk * 4 : 0);
+  w.lpart = take(split ? B * H * w.nchunk * 4 : 0);
+  w.opart = take(split ? B * H * w.nchunk * dh * 4 : 0);
   w.lse = take(B * H * 4);
   w.cmax = take(B * H * 4);
-  w.flags = take(B * H * 4);
-  w.queue = take((B * H + 1) * 4);
-  w.kcount = take(B * H * w.nchunk * 4);
+  w.kcount = take(split ? B * H * w.nchunk * 4 : 0);
+
   w.o = take(B * D * 2);
   w.total = off;
   return w;

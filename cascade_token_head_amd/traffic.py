@@ -44,13 +44,13 @@ COPY_KERNEL = r"copyBuffer"
 KERNEL_SOURCE = {
     "qkv_gemm": "gemm.hip", "out_gemm": "gemm.hip",
     "attn_fwd": "attn.hip", "attn_colsum": "attn.hip", "importance": "attn.hip",
-    "decode_attn": "decode.hip", "decode_finish": "decode.hip", "pq_attn_msb": "decode.hip",
-    "decode_flag": "decode.hip", "pq_attn_recompute": "decode.hip", "decode_vrow": "decode.hip",
+    "decode_attn": "decode.hip", "pq_attn": "decode.hip", "decode_vrow": "decode.hip",
     "decode_scores": "decode.hip", "decode_vprune": "decode.hip", "decode_vsum": "decode.hip",
+    "decode_importance": "decode.hip",
     "topk": "topk.hip", "compact": "compact.hip", "compact_inplace": "compact.hip",
     "quantize": "quant.hip",
 }
-SHARED_HEADERS = ("common.hpp", "kernels.hpp", "layout.hpp", "timing.hpp")
+SHARED_HEADERS = ("common.hpp", "importance.hpp", "kernels.hpp", "layout.hpp", "timing.hpp")
 
 
 def source_sha1(kernel: str) -> str:

@@ -347,8 +347,9 @@ def importance_error_bound(q, cache, P, cfg, a_out):
     Score s2 = q.k * log2(e) / sqrt(dh) in fp32: a dot product of dh
     products carries at most gamma = dh * u relative to sum |q_i k_i| (u =
     2^-24), plus a few roundings of the scaling; for quantized caches the
-    codes enter as scale * 16 * (nibble + 8) - 8 * sum q or as scale *
-    (16 msb + lsb), whose terms are bounded by scale * 368 * |q_i|. The
+    codes enter with an offset, as scale * 16 * ((nibble + 8) - 8) or as
+    scale * ((code + 128) - 128), whose terms are bounded by scale * 368 *
+    |q_i| and scale * 383 * |q_i|. The
     row's log2-sum-exp is a smooth maximum, so its error is at most the
     largest score error plus the relative error of the fp32 sums of lc
     exponentials ((lc + 64) u). p = exp2(s2 - lse2) then has relative
@@ -360,7 +361,7 @@ def importance_error_bound(q, cache, P, cfg, a_out):
     sc2 = math.log2(math.e) / math.sqrt(dh)
     qa = np.abs(np.asarray(q, np.float64)).reshape(H, dh)
     if cfg.quantized:
-        E = 368.0 * np.asarray(cache["k_scale"], np.float64)[None, :] * qa.sum(axis=1)[:, None]
+        E = 383.0 * np.asarray(cache["k_scale"], np.float64)[None, :] * qa.sum(axis=1)[:, None]
     else:
         E = np.einsum("hd,jhd->hj", qa, np.abs(cache["k"]))
     lc = P.shape[1]

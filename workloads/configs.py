@@ -138,6 +138,41 @@ EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD]
 BY_NAME = {c.name: c for c in CONFIGS + EXTENSIONS}
 
 
+@dataclass(frozen=True)
+class AdaConfig:
+    """Cascade representative-token selection over a stack of per-layer
+    activations (page 5): T tokens of dimension d per sequence and layer,
+    threshold tau on the Gram (cosine) product.
+
+    Synthetic activations: a token is a cluster centre (round(clusters_frac
+    * T) centres, N(0, I)) plus spread * N(0, I); every later layer adds
+    drift * N(0, I) to the previous layer's activations (a residual stream
+    whose near-duplicates slowly come apart)."""
+    name: str
+    batch: int
+    seq_len: int
+    dim: int
+    n_layers: int
+    tau: float = 0.30
+    clusters_frac: float = 0.25
+    spread: float = 0.2
+    drift: float = 0.07
+    kind: str = "ada"
+
+    def token_layers(self) -> int:
+        return self.batch * self.seq_len * self.n_layers
+
+
+# the page's measured setting (T = 512, tau = 0.30) on GPT-2-small-shaped
+# activations (d = 768, 12 layers), and its projected long sequence (T =
+# 8192) at d = 4096; a small case for oracle pins and parity tests
+ADA_GPT2 = AdaConfig(name="ada_gpt2", batch=16, seq_len=512, dim=768, n_layers=12)
+ADA_LONG = AdaConfig(name="ada_long", batch=1, seq_len=8192, dim=4096, n_layers=4)
+ADA_SMALL = AdaConfig(name="ada_small", batch=2, seq_len=96, dim=32, n_layers=4)
+ADA_CONFIGS = [ADA_GPT2, ADA_LONG]
+BY_NAME.update({c.name: c for c in ADA_CONFIGS})
+
+
 def scaled(cfg: Config, **kw) -> Config:
     """A smaller variant of a workload for parity tests (same structure)."""
     return replace(cfg, **kw)

@@ -23,7 +23,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .configs import Config
+from .configs import AdaConfig, Config
 
 
 def _cast(a64: np.ndarray, dtype: str) -> np.ndarray:
@@ -105,3 +105,27 @@ def random_scores(shape, seed: int = 0, kind: str = "normal") -> np.ndarray:
     if kind == "uniform":
         return rng.random(shape).astype(np.float32)
     raise ValueError(kind)
+
+
+def ada_layers(cfg: AdaConfig, seq: int, seed: int = 0):
+    """Per-layer activations [T, d] (float32) of sequence `seq`, one layer
+    at a time: layer 0 = cluster centre + spread noise, layer l = layer l-1
+    + drift noise. Each sequence has its own generator (PCG64 seeded with
+    (seed, seq)), so sequences can be generated independently."""
+    rng = np.random.Generator(np.random.PCG64([seed, seq]))
+    T, d = cfg.seq_len, cfg.dim
+    K = max(1, int(np.floor(cfg.clusters_frac * T + 0.5)))
+    centres = rng.standard_normal((K, d))
+    x = centres[rng.integers(0, K, T)] + cfg.spread * rng.standard_normal((T, d))
+    del centres
+    for l in range(cfg.n_layers):
+        if l > 0:
+            x += cfg.drift * rng.standard_normal((T, d))
+        yield x.astype(np.float32)
+
+
+def ada_batch_layers(cfg: AdaConfig, seed: int = 0):
+    """Per-layer activations [B, T, d] (float32) of every sequence."""
+    gens = [ada_layers(cfg, b, seed) for b in range(cfg.batch)]
+    for _ in range(cfg.n_layers):
+        yield np.stack([next(g) for g in gens])

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libspatten.so")
 
 HIP_SOURCES = ["api.hip", "gemm.hip", "attn.hip", "decode.hip", "topk.hip", "compact.hip",
-               "quant.hip", "timing.hip"]
+               "quant.hip", "ada.hip", "timing.hip"]
 CXX_SOURCES = ["validate.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -248,6 +248,38 @@ int spatten_layer_forward_noalloc(const spatten_layer_desc* d, void* x, const vo
                       v_msb, v_lsb, v_scale, recompute, v_kept, ws, as_stream(stream));
 }
 
+int spatten_ada_select(const float* x, int32_t batch, int32_t T, int32_t d, float tau,
+                       const int32_t* prev, int32_t* flags, float* maxcos, int32_t* counts,
+                       void* workspace, size_t* workspace_bytes, void* stream) {
+  const int st = check_ada(x, batch, T, d, tau, flags, workspace, workspace_bytes);
+  if (st != SPATTEN_OK) return st;
+  const AdaWs w = ada_ws(batch, T);
+  if (!workspace) {
+    *workspace_bytes = w.total;
+    return SPATTEN_OK;
+  }
+  if (batch == 0) return SPATTEN_OK;
+  char* ws = static_cast<char*>(workspace);
+  AdaArgs a{};
+  a.x = x;
+  a.batch = batch;
+  a.T = T;
+  a.d = d;
+  a.tau = tau;
+  a.prev = prev;
+  a.flags = flags;
+  a.maxcos = maxcos;
+  a.counts = counts;
+  a.inv = reinterpret_cast<float*>(ws + w.inv);
+  a.listR = reinterpret_cast<int32_t*>(ws + w.listR);
+  a.listN = reinterpret_cast<int32_t*>(ws + w.listN);
+  a.listV = reinterpret_cast<int32_t*>(ws + w.listV);
+  a.cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+  a.rc = reinterpret_cast<float*>(ws + w.rc);
+  a.ac = reinterpret_cast<float*>(ws + w.ac);
+  return launch_ada_select(a, as_stream(stream));
+}
+
 int spatten_topk(const float* scores, int32_t batch, int32_t n, int64_t row_stride, int32_t k,
                  int32_t* out_idx, float* kth_value, void* stream) {
   const int st = check_topk(scores, batch, n, row_stride, k, out_idx);

@@ -123,4 +123,25 @@ struct DecodeArgs {
 // Fills *imp with the importance pass the layer still needs (imp->pending).
 int launch_decode(const DecodeArgs& a, bool quantized, ImpArgs* imp, hipStream_t stream);
 
+// Representative-token selection for one layer (see ada.hip): prev null =
+// full-Gram selection, else a cascade step from the flags in prev.
+struct AdaArgs {
+  const float* x;        // [B, T, d] activations
+  int batch, T, d;
+  float tau;
+  const int32_t* prev;   // [B, T] flags of the inherited set, or null
+  int32_t* flags;        // [B, T] out
+  float* maxcos;         // [B, T] out (optional): the cosine each decision took
+  int32_t* counts;       // [B, 4] out (optional): size, removed, added, Gram pairs
+  // workspace
+  float* inv;            // [B, T]
+  int32_t* listR;        // [B, T] each
+  int32_t* listN;
+  int32_t* listV;
+  int32_t* cnt;          // [B, 4]
+  float* rc;             // [B, T] removal (full: selection) cosines, by R position
+  float* ac;             // [B, T] addition cosines, by N position
+};
+int launch_ada_select(const AdaArgs& a, hipStream_t stream);
+
 }  // namespace spatten

@@ -56,6 +56,26 @@ struct DecodeWs {
 
 inline size_t dtype_bytes(int dt) { return dt == SPATTEN_BF16 ? 2 : 4; }
 
+// Workspace of spatten_ada_select.
+struct AdaWs {
+  size_t inv, listR, listN, listV, cnt, rc, ac, total;
+};
+inline AdaWs ada_ws(int64_t batch, int64_t T) {
+  AdaWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  const size_t n = size_t(batch) * size_t(T);
+  w.inv = take(n * 4);
+  w.listR = take(n * 4);
+  w.listN = take(n * 4);
+  w.listV = take(n * 4);
+  w.cnt = take(size_t(batch) * 16);
+  w.rc = take(n * 4);
+  w.ac = take(n * 4);
+  w.total = off;
+  return w;
+}
+
 inline PrefillWs prefill_ws(const spatten_layer_desc& d) {
   PrefillWs w{};
   const int64_t B = d.batch, n = d.n_tokens, h = d.n_heads_kept, dh = d.head_dim;

@@ -84,6 +84,22 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
   return SPATTEN_OK;
 }
 
+int check_ada(const float* x, int32_t batch, int32_t T, int32_t d, float tau,
+              const int32_t* flags, const void* workspace, const size_t* workspace_bytes) {
+  if (!workspace_bytes) return SPATTEN_EINVAL;
+  if (batch < 0 || T < 1 || d < 1) return SPATTEN_EINVAL;
+  if (!(tau >= 0.0f && tau <= 1.0f)) return SPATTEN_EINVAL;  // also rejects NaN
+  if (d % 32 != 0) return SPATTEN_EUNSUPPORTED;
+  if (int64_t(T) * d > (int64_t(1) << 31)) return SPATTEN_EUNSUPPORTED;
+  if (!workspace) return SPATTEN_OK;  // size query
+  if (!aligned(workspace, 256)) return SPATTEN_EINVAL;
+  if (*workspace_bytes < ada_ws(batch, T).total) return SPATTEN_EWORKSPACE;
+  if (batch == 0) return SPATTEN_OK;
+  if (!x || !flags) return SPATTEN_EINVAL;
+  if (!aligned(x, 16) || !aligned(flags, 4)) return SPATTEN_EINVAL;
+  return SPATTEN_OK;
+}
+
 int check_topk(const float* scores, int32_t batch, int32_t n, int64_t row_stride, int32_t k,
                const int32_t* out_idx) {
   if (batch < 0 || n < 1 || k < 1 || k > n || row_stride < n) return SPATTEN_EINVAL;

@@ -20,6 +20,9 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
                 const uint8_t* v_lsb, const float* v_scale, const void* workspace,
                 const size_t* workspace_bytes);
 
+int check_ada(const float* x, int32_t batch, int32_t T, int32_t d, float tau,
+              const int32_t* flags, const void* workspace, const size_t* workspace_bytes);
+
 int check_topk(const float* scores, int32_t batch, int32_t n, int64_t row_stride, int32_t k,
                const int32_t* out_idx);
 

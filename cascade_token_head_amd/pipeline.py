@@ -279,3 +279,30 @@ class DecodeStack:
         S.compact(pairs, self.cache_sel, k)
         self.side ^= 1
         self.len = k
+
+
+class AdaStack:
+    """Representative-token selection over a stack of layer activations
+    (page 5, "Cascade Token Selection for Transformer Attention
+    Acceleration"): the first layer takes the full-Gram selection, every
+    later one a cascade step from the previous layer's set. All buffers are
+    allocated here; run() only enqueues library calls."""
+
+    def __init__(self, n_layers: int, batch: int, seq_len: int, dim: int, tau: float,
+                 device="cuda"):
+        self.L, self.B, self.T, self.d, self.tau = n_layers, batch, seq_len, dim, tau
+        self.flags = torch.zeros(n_layers, batch, seq_len, dtype=torch.int32, device=device)
+        self.maxcos = torch.empty(n_layers, batch, seq_len, dtype=torch.float32, device=device)
+        self.counts = torch.zeros(n_layers, batch, 4, dtype=torch.int32, device=device)
+        self.ws = torch.empty(max(S.ada_workspace_bytes(batch, seq_len, dim), 256),
+                              dtype=torch.uint8, device=device)
+
+    def run(self, layers, full_every_layer: bool = False):
+        """layers: per-layer activations [B, T, d] fp32 device tensors.
+        full_every_layer selects every layer independently (the baseline
+        the cascade is compared with)."""
+        for l, x in enumerate(layers):
+            prev = None if (l == 0 or full_every_layer) else self.flags[l - 1]
+            S.ada_select(x, self.tau, self.flags[l], self.ws, prev=prev, maxcos=self.maxcos[l],
+                         counts=self.counts[l])
+        return self.flags

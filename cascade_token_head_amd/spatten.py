@@ -22,7 +22,7 @@ PREFILL, DECODE = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("spatten_layer_forward", "spatten_layer_forward_noalloc", "spatten_topk", "spatten_compact", "spatten_compact_inplace",
-            "spatten_quantize_kv", "spatten_status_string")
+            "spatten_quantize_kv", "spatten_ada_select", "spatten_status_string")
 
 
 class SpattenError(RuntimeError):
@@ -70,6 +70,9 @@ def _lib():
                                                 i32, i32, i32, vp]
         lib.spatten_quantize_kv.restype = ctypes.c_int
         lib.spatten_quantize_kv.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, i64, vp]
+        lib.spatten_ada_select.restype = ctypes.c_int
+        lib.spatten_ada_select.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp,
+                                           ctypes.POINTER(ctypes.c_size_t), vp]
         lib.spatten_status_string.restype = ctypes.c_char_p
         lib.spatten_status_string.argtypes = [ctypes.c_int]
         _L = lib
@@ -212,3 +215,25 @@ def compact_inplace(tensors: Sequence, idx: torch.Tensor, n: int, k: int, stream
     B = idx.shape[0]
     st = _lib().spatten_compact_inplace(m, base, rb, rp, bs, _p(idx), B, n, k, _stream(stream))
     _check("spatten_compact_inplace", st)
+
+
+def ada_workspace_bytes(batch: int, T: int, d: int) -> int:
+    nb = ctypes.c_size_t(0)
+    st = _lib().spatten_ada_select(None, batch, T, d, ctypes.c_float(0.3), None, None, None, None,
+                                   None, ctypes.byref(nb), None)
+    _check("spatten_ada_select(query)", st)
+    return nb.value
+
+
+def ada_select(x: torch.Tensor, tau: float, flags: torch.Tensor, workspace: torch.Tensor,
+               prev: Optional[torch.Tensor] = None, maxcos: Optional[torch.Tensor] = None,
+               counts: Optional[torch.Tensor] = None, stream=None):
+    """Representative tokens of one layer: x [B, T, d] fp32; flags [B, T]
+    int32 out; prev [B, T] int32 (None = full-Gram selection)."""
+    assert x.dtype == torch.float32 and x.dim() == 3 and x.is_contiguous()
+    B, T, d = x.shape
+    nb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    st = _lib().spatten_ada_select(_p(x), B, T, d, ctypes.c_float(tau), _p(prev), _p(flags),
+                                   _p(maxcos), _p(counts), _p(workspace), ctypes.byref(nb),
+                                   _stream(stream))
+    _check("spatten_ada_select", st)

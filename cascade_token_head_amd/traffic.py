@@ -49,6 +49,8 @@ KERNEL_SOURCE = {
     "decode_importance": "decode.hip",
     "topk": "topk.hip", "compact": "compact.hip", "compact_inplace": "compact.hip",
     "quantize": "quant.hip",
+    "ada_gram": "ada.hip", "ada_invnorm": "ada.hip", "ada_lists": "ada.hip",
+    "ada_valid": "ada.hip", "ada_finish": "ada.hip",
 }
 SHARED_HEADERS = ("common.hpp", "importance.hpp", "kernels.hpp", "layout.hpp", "timing.hpp")
 

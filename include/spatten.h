@@ -226,6 +226,33 @@ int spatten_quantize_kv(const void* kv, int32_t dtype, int32_t batch, int32_t n,
                         int64_t kv_batch_stride, uint8_t* msb, uint8_t* lsb, float* scale,
                         int64_t plane_batch_stride, void* stream);
 
+/*
+ * spatten_ada_select - representative tokens of one layer by a Gram
+ * threshold, and their cascade across layers ("Cascade Token Selection for
+ * Transformer Attention Acceleration": "Probleemstelling" defines a
+ * representative token, "Methodologie: Het Cascade-mechanisme" the cascade
+ * steps 1-3). With theta = 1 - tau^2 and cos(t, s) the cosine of rows t and
+ * s of x[b] (a zero row has cosine 0 with every row), computed in fp32:
+ *   prev == NULL (full selection): flags[b, t] = 1 iff the largest cos(t,
+ *     s) over s < t is below theta (token 0 always);
+ *   prev != NULL (cascade step from the inherited set R = {t: prev[b, t] !=
+ *     0}): a member t of R stays iff its largest cosine with a preceding
+ *     member of R is below theta (the r x r product); a token u outside R
+ *     joins iff its largest cosine with a preceding member that stayed is
+ *     below theta (the (T - r) x r product); flags = stayed or joined.
+ * x: [batch, T, d] fp32, 16-byte aligned, d a multiple of 32. prev, flags:
+ *   [batch, T] int32 (flags is written whole; it must not alias prev).
+ * maxcos (optional, [batch, T] fp32): the cosine each token's decision was
+ *   taken on (-inf where no token precedes it in the set compared with).
+ * counts (optional, [batch, 4] int32): set size, removed members, added
+ *   tokens, and Gram entries evaluated (pairs s < t; saturates at 2^31-1).
+ * tau in [0, 1] (else SPATTEN_EINVAL). workspace as spatten_layer_forward
+ * (NULL: size query).
+ */
+int spatten_ada_select(const float* x, int32_t batch, int32_t T, int32_t d, float tau,
+                       const int32_t* prev, int32_t* flags, float* maxcos, int32_t* counts,
+                       void* workspace, size_t* workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* spatten_status_string(int status);
 

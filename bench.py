@@ -20,8 +20,11 @@ algorithmic and executed MFMA work; decode: attention bytes) and
 layer's tokens/s including its selection and compaction. `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
 Without --config the line also carries `workloads`: the same measurements
-(no CPU baseline) for bert_base, gpt2_decode and pq_decode, the last with
-the fraction of rows the progressive quantization recomputed.
+(no CPU baseline) for bert_base, gpt2_decode and pq_decode (the last with
+the fraction of rows the progressive quantization recomputed), and for the
+cascade representative-token selection workloads ada_gpt2 and ada_long
+(fp32 Gram products; their line compares the cascade with a full-Gram
+selection at every layer).
 
 With --graph the timed steps replay one pass captured into a HIP graph (the
 stacks allocate nothing and only enqueue kernels; replays match the eager
@@ -37,6 +40,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -456,8 +461,118 @@ def measure(cfg, args, lib, with_cpu: bool) -> dict:
             "cpu_baseline": cpu}
 
 
+PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (MFMA and vector)
+
+
+def measure_ada(cfg, args, lib, with_cpu: bool) -> dict:
+    """Cascade representative-token selection (page 5) over a stack of
+    synthetic layer activations: a step is one pass over every layer (the
+    full-Gram selection of layer 1, then a cascade step per layer)."""
+    import torch
+
+    from cascade_token_head_amd import pipeline
+    from workloads import ada_batch_layers
+
+    layers = [torch.from_numpy(x).cuda() for x in ada_batch_layers(cfg)]
+    st = pipeline.AdaStack(cfg.n_layers, cfg.batch, cfg.seq_len, cfg.dim, cfg.tau)
+    for _ in range(args.warmup):
+        st.run(layers)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        st.run(layers)
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / args.steps
+    value = cfg.token_layers() / (ms_per_step / 1e3)
+    counts = st.counts.cpu().numpy().astype(np.int64)   # [L, B, 4]
+    pairs = counts[:, :, 3].sum(axis=1)                  # Gram entries per layer
+    sizes = counts[:, :, 0].sum(axis=1)
+    # per-layer times, and the same layers selected independently (full
+    # Gram product at every layer) for comparison
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(cfg.n_layers + 1)]
+    from cascade_token_head_amd import spatten as S
+    marks[0].record()
+    for l, x in enumerate(layers):
+        S.ada_select(x, cfg.tau, st.flags[l], st.ws, prev=None if l == 0 else st.flags[l - 1],
+                     maxcos=st.maxcos[l], counts=st.counts[l])
+        marks[l + 1].record()
+    torch.cuda.synchronize()
+    per_layer = []
+    for l in range(cfg.n_layers):
+        us = marks[l].elapsed_time(marks[l + 1]) * 1e3
+        n = cfg.batch * cfg.seq_len
+        per_layer.append({"layer": l + 1, "tokens": n, "representatives": int(sizes[l]),
+                          "gram_pairs": int(pairs[l]), "us": round(us, 2),
+                          "tokens_per_s": round(n / (us / 1e6), 1)})
+    full = pipeline.AdaStack(cfg.n_layers, cfg.batch, cfg.seq_len, cfg.dim, cfg.tau)
+    full.run(layers, full_every_layer=True)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        full.run(layers, full_every_layer=True)
+    f1.record()
+    torch.cuda.synchronize()
+    full_ms = f0.elapsed_time(f1) / args.steps
+    full_pairs = cfg.batch * cfg.n_layers * cfg.seq_len * (cfg.seq_len - 1) // 2
+    # per-kernel times over the same steps
+    _read_kernel_times(lib)
+    lib.spatten_debug_timing(1)
+    for _ in range(args.steps):
+        st.run(layers)
+    torch.cuda.synchronize()
+    lib.spatten_debug_timing(0)
+    ktimes = _read_kernel_times(lib)
+    gram_flops = 2.0 * cfg.dim * float(pairs.sum())   # per step
+    per_kernel = {n: {"total_ms": round(ms / args.steps, 4), "launches_per_step": c // args.steps,
+                      "avg_us": round(ms * 1e3 / max(c, 1), 3)} for n, (ms, c) in ktimes.items()}
+    gms, gcnt = ktimes["ada_gram"]
+    achieved = gram_flops * args.steps / (gms / 1e3) / 1e12
+    per_kernel["ada_gram"]["tflops"] = round(achieved, 2)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "kernel": "ada_gram",
+            "dtype": "f32", "avg_us": round(gms * 1e3 / max(gcnt, 1), 3),
+            "launches_per_step": gcnt // args.steps,
+            "traffic": _traffic("ada_gram", cfg.name, gcnt // args.steps),
+            "step": {"gram_tflop": round(gram_flops / 1e12, 5),
+                     "achieved": round(gram_flops / (ms_per_step / 1e3) / 1e12, 2)}}
+    cpu = None
+    if with_cpu:
+        from oracle import ada_ref as R
+        from workloads import ada_layers
+        t0 = time.perf_counter()
+        done = 0
+        while done < cfg.batch and time.perf_counter() - t0 < args.cpu_seconds:
+            R.run_cascade(ada_layers(cfg, done), cfg.tau)
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(done * cfg.seq_len * cfg.n_layers / el, 1), "unit": "tokens/s",
+               "cores": os.cpu_count(), "kind": "oracle",
+               "sample": "sequences 0..%d of %d, all %d layers" % (done - 1, cfg.batch,
+                                                                   cfg.n_layers),
+               "seconds": round(el, 2)}
+    del layers, st, full
+    torch.cuda.empty_cache()
+    return {"value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
+            "gpu_ms_per_step": round(gpu_ms, 4), "dtype": "f32",
+            "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len,
+                       "dim": cfg.dim, "layers": cfg.n_layers, "tau": cfg.tau},
+            "roofline": roof, "per_layer": per_layer, "kernels": per_kernel,
+            "cascade_vs_full": {"gram_pairs": int(pairs.sum()), "full_gram_pairs": full_pairs,
+                                "pair_ratio": round(float(pairs.sum()) / full_pairs, 4),
+                                "full_ms_per_step": round(full_ms, 4),
+                                "speedup": round(full_ms / gpu_ms, 3)},
+            "cpu_baseline": cpu}
+
+
 HEADLINE = "long_causal"
-OTHERS = ("bert_base", "gpt2_decode", "pq_decode")
+OTHERS = ("bert_base", "gpt2_decode", "pq_decode", "ada_gpt2", "ada_long")
 
 
 def main():
@@ -488,7 +603,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     head = args.config or HEADLINE
     print("measuring %s" % head, file=sys.stderr, flush=True)
-    r = measure(BY_NAME[head], args, lib, with_cpu=not args.no_cpu)
+    run = measure_ada if BY_NAME[head].kind == "ada" else measure
+    r = run(BY_NAME[head], args, lib, with_cpu=not args.no_cpu)
     out = {"metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
            "gpu_ms_per_step": r["gpu_ms_per_step"],
@@ -497,11 +613,14 @@ def main():
            "config": r["config"], "launch": "hip_graph" if args.graph else "eager",
            "roofline": r["roofline"], "per_layer": r["per_layer"], "kernels": r["kernels"],
            "cpu_baseline": r["cpu_baseline"]}
+    if "cascade_vs_full" in r:
+        out["cascade_vs_full"] = r["cascade_vs_full"]
     if args.config is None:
         out["workloads"] = {}
         for name in OTHERS:
             print("measuring %s" % name, file=sys.stderr, flush=True)
-            o = measure(BY_NAME[name], args, lib, with_cpu=False)
+            cfg = BY_NAME[name]
+            o = (measure_ada if cfg.kind == "ada" else measure)(cfg, args, lib, with_cpu=False)
             o.pop("cpu_baseline")
             out["workloads"][name] = o
     print(json.dumps(out))

@@ -16,6 +16,10 @@
 // the raw activations; the cosine is the dot scaled by both rows' inverse
 // norms.
 //
+// The range of B tiles a row tile needs is split over workgroups, which
+// combine their row maxima with an integer atomicMax on order-preserving
+// keys of the fp32 cosines (a maximum does not depend on the order).
+//
 // Lists and decisions: ada_lists turns the inherited flags into the
 // ascending member list R and the list N of the other tokens (an ordered
 // compaction: per-thread counts, a block scan, then writes), ada_valid
@@ -52,6 +56,22 @@ ada_invnorm(const float* __restrict__ x, int64_t rows, int d, float* __restrict_
   if (lane == 0) inv[row] = s > 0.0f ? 1.0f / sqrtf(s) : 0.0f;
 }
 
+// Order-preserving map of fp32 to uint32 (larger value -> larger key), so
+// that workgroups can combine maxima with an integer atomicMax.
+__device__ __forceinline__ uint32_t max_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+constexpr uint32_t kKeyNegInf = 0x007fffffu;  // max_key(-inf)
+
+// Every entry of a [B, T] key array to kKeyNegInf.
+__device__ __forceinline__ void clear_keys(uint32_t* keys, int T, int b) {
+  for (int t = threadIdx.x; t < T; t += blockDim.x) keys[int64_t(b) * T + t] = kKeyNegInf;
+}
+
 // Exclusive block scan of one count per thread (kAdaThreads threads).
 __device__ __forceinline__ int block_scan(int v, int* total) {
   __shared__ int wsum[kAdaThreads / 64];
@@ -79,8 +99,9 @@ __device__ __forceinline__ int block_scan(int v, int* total) {
 // null), N = the others, both ascending; cnt[b*4 + 0] = |R|, [1] = |N|.
 __global__ void __launch_bounds__(kAdaThreads)
 ada_lists(const int32_t* __restrict__ prev, int T, int32_t* __restrict__ listR,
-          int32_t* __restrict__ listN, int32_t* __restrict__ cnt) {
+          int32_t* __restrict__ listN, int32_t* __restrict__ cnt, uint32_t* __restrict__ rkeys) {
   const int b = blockIdx.x, tid = threadIdx.x;
+  clear_keys(rkeys, T, b);
   const int per = (T + kAdaThreads - 1) / kAdaThreads;
   const int t0 = tid * per, t1 = t0 + per < T ? t0 + per : T;
   const int32_t* pf = prev ? prev + int64_t(b) * T : nullptr;
@@ -104,34 +125,43 @@ ada_lists(const int32_t* __restrict__ prev, int T, int32_t* __restrict__ listR,
   }
 }
 
-// For i < nA[b]: out[b*T + i] = max over j < nB[b] with B[j] < A[i] of
-// cos(A[i], B[j]) (-inf when there is none). grid (T / 64 rounded up,
-// batch); four waves, each a 32 x 32 block of the 64 x 64 tile.
+constexpr int kGJ = 4;  // B tiles per workgroup
+
+// For i < nA[b]: keys[b*T + i] = max(keys[b*T + i], key of the largest
+// cos(A[i], B[j]) over j < nB[b] with B[j] < A[i]). grid (T / 64 tiles of
+// A, T / (64 kGJ) ranges of B, batch): each workgroup takes one 64-row A
+// tile and up to kGJ 64-row B tiles of its range that precede the tile's
+// last token, four waves each computing a 32 x 32 block per B tile. The
+// feature chunks stream through LDS with the next chunk's rows requested
+// before the current chunk's MFMAs. keys must hold kKeyNegInf (or an
+// earlier maximum) on entry.
 __global__ void __launch_bounds__(256)
 ada_gram_max(const float* __restrict__ x, const float* __restrict__ inv, int T, int d,
              const int32_t* __restrict__ listA, const int32_t* __restrict__ cntA, int ia,
              const int32_t* __restrict__ listB, const int32_t* __restrict__ cntB, int ib,
-             float* __restrict__ out) {
-  __shared__ float As[kGT][kGK + 1];
-  __shared__ float Bs[kGT][kGK + 1];
+             uint32_t* __restrict__ keys) {
+  constexpr int LDK = kGK + 4;  // padded row: 16-byte stores, spread banks
+  __shared__ __attribute__((aligned(16))) float As[kGT][LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[kGT][LDK];
   __shared__ int posA[kGT], posB[kGT];
   __shared__ float invA[kGT], invB[kGT];
   __shared__ float rmax[2][kGT];
   __shared__ int jend_s;
-  const int b = blockIdx.y;
+  const int b = blockIdx.z;
   const int nA = cntA[b * 4 + ia], nB = cntB[b * 4 + ib];
   const int i0 = blockIdx.x * kGT;
-  if (i0 >= nA) return;
+  const int jr0 = blockIdx.y * (kGJ * kGT);
+  if (i0 >= nA || jr0 >= nB) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* A = listA + int64_t(b) * T;
   const int32_t* B = listB + int64_t(b) * T;
   const float* xb = x + int64_t(b) * T * d;
-  const float* ib_ = inv + int64_t(b) * T;
+  const float* ivb_ = inv + int64_t(b) * T;
   const int last = (i0 + kGT < nA ? i0 + kGT : nA) - 1;
   if (tid < kGT) {
     const int i = i0 + tid <= last ? i0 + tid : last;  // rows past the list repeat the last
     posA[tid] = A[i];
-    invA[tid] = ib_[A[i]];
+    invA[tid] = ivb_[A[i]];
   }
   if (tid == 0) {
     // B entries before the tile's last token: a prefix of B (binary search)
@@ -144,38 +174,46 @@ ada_gram_max(const float* __restrict__ x, const float* __restrict__ inv, int T, 
     jend_s = lo;
   }
   __syncthreads();
-  const int jend = jend_s;
+  const int jend = jend_s < jr0 + kGJ * kGT ? jend_s : jr0 + kGJ * kGT;
+  if (jr0 >= jend) return;  // uniform
   const int mt = wave >> 1, nt = wave & 1;  // this wave's 32 x 32 block
   const int l32 = lane & 31, hi = lane >> 5;
-  // staging: 64 rows x 32 floats per operand, two float4 per thread each
+  // staging: 64 rows x 32 features per operand, two float4 per thread each
   const int sr = tid >> 2, sc = (tid & 3) * 8;
-  float best[4][4];  // running max for this lane's rows (C layout), per register group
+  float best[4][4];  // running max of this lane's rows (C layout)
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
     for (int q = 0; q < 4; ++q) best[g][q] = -INFINITY;
-  for (int j0 = 0; j0 < jend; j0 += kGT) {
+  const float* arow = xb + int64_t(posA[sr]) * d + sc;
+  for (int j0 = jr0; j0 < jend; j0 += kGT) {
     __syncthreads();  // the previous tile's posB / invB readers are done
     if (tid < kGT) {
       const int j = j0 + tid < jend ? j0 + tid : jend - 1;
-      posB[tid] = j0 + tid < jend ? B[j] : 0x7fffffff;  // past the prefix: never precedes
-      invB[tid] = ib_[B[j]];
+      posB[tid] = j0 + tid < jend ? B[j] : 0x7fffffff;  // past the range: never precedes
+      invB[tid] = ivb_[B[j]];
     }
     __syncthreads();
-    const float* arow = xb + int64_t(posA[sr]) * d + sc;
-    const float* brow = xb + int64_t(posB[sr] == 0x7fffffff ? B[jend - 1] : posB[sr]) * d + sc;
+    const int jr = j0 + sr < jend ? j0 + sr : jend - 1;
+    const float* brow = xb + int64_t(B[jr]) * d + sc;
+    float4 a0 = *reinterpret_cast<const float4*>(arow);
+    float4 a1 = *reinterpret_cast<const float4*>(arow + 4);
+    float4 b0 = *reinterpret_cast<const float4*>(brow);
+    float4 b1 = *reinterpret_cast<const float4*>(brow + 4);
     floatx16 acc = {};
     for (int k0 = 0; k0 < d; k0 += kGK) {
-      const float4 a0 = *reinterpret_cast<const float4*>(arow + k0);
-      const float4 a1 = *reinterpret_cast<const float4*>(arow + k0 + 4);
-      const float4 b0 = *reinterpret_cast<const float4*>(brow + k0);
-      const float4 b1 = *reinterpret_cast<const float4*>(brow + k0 + 4);
       __syncthreads();  // the previous chunk's MFMA reads are done
-      As[sr][sc + 0] = a0.x; As[sr][sc + 1] = a0.y; As[sr][sc + 2] = a0.z; As[sr][sc + 3] = a0.w;
-      As[sr][sc + 4] = a1.x; As[sr][sc + 5] = a1.y; As[sr][sc + 6] = a1.z; As[sr][sc + 7] = a1.w;
-      Bs[sr][sc + 0] = b0.x; Bs[sr][sc + 1] = b0.y; Bs[sr][sc + 2] = b0.z; Bs[sr][sc + 3] = b0.w;
-      Bs[sr][sc + 4] = b1.x; Bs[sr][sc + 5] = b1.y; Bs[sr][sc + 6] = b1.z; Bs[sr][sc + 7] = b1.w;
+      *reinterpret_cast<float4*>(&As[sr][sc]) = a0;
+      *reinterpret_cast<float4*>(&As[sr][sc + 4]) = a1;
+      *reinterpret_cast<float4*>(&Bs[sr][sc]) = b0;
+      *reinterpret_cast<float4*>(&Bs[sr][sc + 4]) = b1;
       __syncthreads();
+      if (k0 + kGK < d) {  // next chunk in flight during this one's MFMAs
+        a0 = *reinterpret_cast<const float4*>(arow + k0 + kGK);
+        a1 = *reinterpret_cast<const float4*>(arow + k0 + kGK + 4);
+        b0 = *reinterpret_cast<const float4*>(brow + k0 + kGK);
+        b1 = *reinterpret_cast<const float4*>(brow + k0 + kGK + 4);
+      }
 #pragma unroll
       for (int kk = 0; kk < kGK; kk += 2) {
         // A operand: row l32 of the wave's A block, feature kk + hi; B
@@ -199,8 +237,8 @@ ada_gram_max(const float* __restrict__ x, const float* __restrict__ inv, int T, 
       }
     }
   }
-  // reduce each row over the 32 columns of the half-wave, then over the
-  // two waves that share the rows
+  // each row over the 32 columns of the half-wave, then over the two waves
+  // that share the rows, then across workgroups
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -218,28 +256,32 @@ ada_gram_max(const float* __restrict__ x, const float* __restrict__ inv, int T, 
       for (int q = 0; q < 4; ++q) rmax[nt][mt * 32 + 8 * g + 4 * hi + q] = best[g][q];
   }
   __syncthreads();
-  if (tid < kGT && i0 + tid <= last)
-    out[int64_t(b) * T + i0 + tid] = fmaxf(rmax[0][tid], rmax[1][tid]);
+  if (tid < kGT && i0 + tid <= last) {
+    const float m = fmaxf(rmax[0][tid], rmax[1][tid]);
+    if (m > -INFINITY) atomicMax(keys + int64_t(b) * T + i0 + tid, max_key(m));
+  }
 }
 
 // Members of R whose removal cosine is below the threshold, in order:
 // listV and cnt[b*4 + 2].
 __global__ void __launch_bounds__(kAdaThreads)
-ada_valid(const int32_t* __restrict__ listR, const float* __restrict__ rc, int T, float theta,
-          int32_t* __restrict__ listV, int32_t* __restrict__ cnt) {
+ada_valid(const int32_t* __restrict__ listR, const uint32_t* __restrict__ rkeys, int T,
+          float theta, int32_t* __restrict__ listV, int32_t* __restrict__ cnt,
+          uint32_t* __restrict__ akeys) {
   const int b = blockIdx.x, tid = threadIdx.x;
+  clear_keys(akeys, T, b);
   const int nR = cnt[b * 4 + 0];
   const int per = (nR + kAdaThreads - 1) / kAdaThreads;
   const int i0 = tid * per, i1 = i0 + per < nR ? i0 + per : nR;
-  const float* c = rc + int64_t(b) * T;
+  const uint32_t* ck = rkeys + int64_t(b) * T;
   int nv = 0;
-  for (int i = i0; i < i1; ++i) nv += c[i] < theta ? 1 : 0;
+  for (int i = i0; i < i1; ++i) nv += key_value(ck[i]) < theta ? 1 : 0;
   int tot;
   int o = block_scan(nv, &tot);
   const int32_t* R = listR + int64_t(b) * T;
   int32_t* V = listV + int64_t(b) * T;
   for (int i = i0; i < i1; ++i)
-    if (c[i] < theta) V[o++] = R[i];
+    if (key_value(ck[i]) < theta) V[o++] = R[i];
   if (tid == 0) cnt[b * 4 + 2] = tot;
 }
 
@@ -249,8 +291,8 @@ ada_valid(const int32_t* __restrict__ listR, const float* __restrict__ rc, int T
 // counts[b*4 + 0..3] = set size, removed, added, Gram pairs evaluated.
 __global__ void __launch_bounds__(kAdaThreads)
 ada_finish(const int32_t* __restrict__ listR, const int32_t* __restrict__ listN,
-           const int32_t* __restrict__ listV, const float* __restrict__ rc,
-           const float* __restrict__ ac, const int32_t* __restrict__ cnt, int T, float theta,
+           const int32_t* __restrict__ listV, const uint32_t* __restrict__ rkeys,
+           const uint32_t* __restrict__ akeys, const int32_t* __restrict__ cnt, int T, float theta,
            int cascade, int32_t* __restrict__ flags, float* __restrict__ maxcos,
            int32_t* __restrict__ counts) {
   __shared__ int red[2];
@@ -269,7 +311,7 @@ ada_finish(const int32_t* __restrict__ listR, const int32_t* __restrict__ listN,
   int nsel = 0, nadd = 0;
   unsigned long long pairs = 0;
   for (int i = tid; i < nR; i += kAdaThreads) {
-    const float c = rc[base + i];
+    const float c = key_value(rkeys[base + i]);
     if (maxcos) maxcos[base + R[i]] = c;
     if (!cascade && c < theta) {
       f[R[i]] = 1;
@@ -279,7 +321,7 @@ ada_finish(const int32_t* __restrict__ listR, const int32_t* __restrict__ listN,
   if (cascade) {
     for (int i = tid; i < nV; i += kAdaThreads) f[V[i]] = 1;
     for (int i = tid; i < nN; i += kAdaThreads) {
-      const float c = ac[base + i];
+      const float c = key_value(akeys[base + i]);
       if (maxcos) maxcos[base + N[i]] = c;
       if (c < theta) {
         f[N[i]] = 1;
@@ -319,9 +361,10 @@ int launch_ada_select(const AdaArgs& a, hipStream_t stream) {
   SPATTEN_LAUNCH_CHECK();
   SPATTEN_TIMED("ada_lists", stream,
                 ada_lists<<<a.batch, kAdaThreads, 0, stream>>>(a.prev, a.T, a.listR, a.listN,
-                                                              a.cnt));
+                                                              a.cnt, a.rc));
   SPATTEN_LAUNCH_CHECK();
-  const dim3 gg(unsigned(ceil_div(a.T, kGT)), unsigned(a.batch));
+  const dim3 gg(unsigned(ceil_div(a.T, kGT)), unsigned(ceil_div(a.T, kGT * kGJ)),
+                unsigned(a.batch));
   // r x r (every token against every preceding one for the full selection)
   SPATTEN_TIMED("ada_gram", stream,
                 ada_gram_max<<<gg, 256, 0, stream>>>(a.x, a.inv, a.T, a.d, a.listR, a.cnt, 0,
@@ -332,7 +375,7 @@ int launch_ada_select(const AdaArgs& a, hipStream_t stream) {
   if (cascade) {
     SPATTEN_TIMED("ada_valid", stream,
                   ada_valid<<<a.batch, kAdaThreads, 0, stream>>>(a.listR, a.rc, a.T, theta,
-                                                                a.listV, a.cnt));
+                                                                a.listV, a.cnt, a.ac));
     SPATTEN_LAUNCH_CHECK();
     // (T - r) x r: the other tokens against the members that stayed
     SPATTEN_TIMED("ada_gram", stream,

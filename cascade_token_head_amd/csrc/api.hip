@@ -275,8 +275,8 @@ int spatten_ada_select(const float* x, int32_t batch, int32_t T, int32_t d, floa
   a.listN = reinterpret_cast<int32_t*>(ws + w.listN);
   a.listV = reinterpret_cast<int32_t*>(ws + w.listV);
   a.cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
-  a.rc = reinterpret_cast<float*>(ws + w.rc);
-  a.ac = reinterpret_cast<float*>(ws + w.ac);
+  a.rc = reinterpret_cast<uint32_t*>(ws + w.rc);
+  a.ac = reinterpret_cast<uint32_t*>(ws + w.ac);
   return launch_ada_select(a, as_stream(stream));
 }
 

@@ -139,8 +139,8 @@ struct AdaArgs {
   int32_t* listN;
   int32_t* listV;
   int32_t* cnt;          // [B, 4]
-  float* rc;             // [B, T] removal (full: selection) cosines, by R position
-  float* ac;             // [B, T] addition cosines, by N position
+  uint32_t* rc;          // [B, T] removal (full: selection) cosine keys, by R position
+  uint32_t* ac;          // [B, T] addition cosine keys, by N position
 };
 int launch_ada_select(const AdaArgs& a, hipStream_t stream);
 

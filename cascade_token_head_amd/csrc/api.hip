@@ -68,6 +68,7 @@ int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const vo
   aa.a = a;
   aa.g = g;
   aa.lse_out = lse_out;
+  aa.v_threshold = d.v_threshold;
   SPATTEN_TRY(launch_attention(aa, st));
   OutArgs oa{};
   oa.dtype = d.dtype;

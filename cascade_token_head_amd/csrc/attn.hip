@@ -19,6 +19,9 @@
 // permuted so each lane's 16 scores are 16 consecutive keys, which is
 // exactly the k-slot order the P V MFMA wants - P never leaves registers.
 // fp32 path: plain VALU kernels for the fp32 workload.
+// Local value pruning (a threshold on each exact probability before P V)
+// adds a second forward pass that reads the first pass's LSE (bf16), or is
+// applied to the normalised scores in LDS (fp32).
 #include <type_traits>
 
 #include "common.hpp"
@@ -57,8 +60,13 @@ inline unsigned xcd_grid(int64_t total) { return unsigned(8 * ((total + 7) / 8))
 
 // NU 32-query groups per wave; a workgroup covers QB queries with
 // QB / (32 NU) waves sharing each K/V tile. MINW: waves per SIMD the
-// register budget is sized for.
-template <int DH, bool CAUSAL, int NU, int MINW>
+// register budget is sized for. VP: local value pruning ("A. Cascade Token
+// Pruning", bullet "Local Value Pruning"), a second pass once the first
+// has written every row's log2-sum-exp: the exp2 reference is that LSE, so
+// each probability is exact when formed, those below a.v_threshold are
+// zeroed before the P V MFMA, and O needs no normalisation. It rewrites O
+// and the |O| partials and leaves the LSE as it was.
+template <int DH, bool CAUSAL, int NU, int MINW, bool VP = false>
 __global__ void __launch_bounds__(2 * attn_qblock(DH) / NU, MINW)
 attn_fwd_bf16(AttnArgs a) {
   // dh 128: K/V loads run two tiles ahead (the register budget allows a
@@ -107,11 +115,14 @@ attn_fwd_bf16(AttnArgs a) {
   const float sc = kLog2e / sqrtf(float(DH));
   float mref[NU];  // max used as the exp2 reference (raw score units)
   float lsum[NU];
+  float lse2[NU];  // VP: the row's log2-sum-exp from the first pass
   floatx16 o[DH / 32][NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     mref[u] = -INFINITY;
     lsum[u] = 0.0f;
+    const int my_q = wq0 + 32 * u + col;
+    lse2[u] = VP && my_q < a.n ? a.lse[bs * a.n_pad + my_q] : 0.0f;
   }
 #pragma unroll
   for (int dt = 0; dt < DH / 32; ++dt)
@@ -221,6 +232,25 @@ attn_fwd_bf16(AttnArgs a) {
     bf16x8 pb[2][NU];  // [s2][u]
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      if constexpr (VP) {
+        // exact probabilities against the known LSE; below the threshold
+        // a V row does not enter this query's output
+        const float tau = a.v_threshold;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float p0 = fast_exp2(fmaf(st[u][8 * s2 + 2 * j], sc, -lse2[u]));
+            float p1 = fast_exp2(fmaf(st[u][8 * s2 + 2 * j + 1], sc, -lse2[u]));
+            p0 = p0 >= tau ? p0 : 0.0f;
+            p1 = p1 >= tau ? p1 : 0.0f;
+            w[j] = pack_bf16x2(p0, p1);
+          }
+          pb[s2][u] = as_bf16x8(w);
+        }
+        continue;
+      }
       float m4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -327,7 +357,7 @@ attn_fwd_bf16(AttnArgs a) {
   for (int u = 0; u < NU; ++u) {
     const int my_q = wq0 + 32 * u + col;
     const float l = lsum[u] + __shfl_xor(lsum[u], 32, 64);
-    const float inv = 1.0f / l;
+    const float inv = VP ? 1.0f : 1.0f / l;
     if (my_q < n) {
       bf16_t* orow = static_cast<bf16_t*>(a.o) + (int64_t(b) * n + my_q) * (a.h_kept * DH) + s * DH;
 #pragma unroll
@@ -345,7 +375,7 @@ attn_fwd_bf16(AttnArgs a) {
                               (uint64_t(pack_bf16x2(v[2], v[3])) << 32);
           *reinterpret_cast<uint64_t*>(orow + d0) = pk;
         }
-      if (G == 0) a.lse[bs * n_pad + my_q] = mref[u] * sc + log2f(l);
+      if (!VP && G == 0) a.lse[bs * n_pad + my_q] = mref[u] * sc + log2f(l);
     }
   }
   gsum = wave_sum(gsum);
@@ -526,7 +556,12 @@ attn_fwd_f32(AttnArgs a) {
     }
     sum = wave_sum(sum);
     const float inv = qi < n ? 1.0f / sum : 0.0f;
-    for (int j = lane; j < n; j += 64) S[r * n_pad + j] *= inv;
+    // local value pruning: probabilities below the threshold leave P V
+    const float tau = a.v_threshold;
+    for (int j = lane; j < n; j += 64) {
+      const float p = S[r * n_pad + j] * inv;
+      S[r * n_pad + j] = p >= tau ? p : 0.0f;
+    }
     if (lane == 0 && qi < n) a.lse[bs * n_pad + qi] = (mx + logf(sum)) * kLog2e;
   }
   __syncthreads();
@@ -600,6 +635,11 @@ int run_bf16(const AttnArgs& a, hipStream_t stream) {
   SPATTEN_TIMED("attn_fwd", stream,
                 attn_fwd_bf16<DH, CAUSAL, NU, MINW><<<g1, 2 * QB / NU, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
+  if (a.v_threshold > 0.0f) {
+    SPATTEN_TIMED("attn_fwd_vprune", stream,
+                  (attn_fwd_bf16<DH, CAUSAL, NU, MINW, true><<<g1, 2 * QB / NU, 0, stream>>>(a)));
+    SPATTEN_LAUNCH_CHECK();
+  }
   const dim3 g2(xcd_grid(ceil_div(a.n, kAttnKBlock) * a.h_kept * a.batch));
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_bf16<DH, CAUSAL><<<g2, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();

@@ -86,6 +86,7 @@ struct AttnArgs {
   float* a;         // [B, n]
   float* g;         // [B, H]
   float* lse_out;   // optional [B, h, n] (natural log)
+  float v_threshold;  // local value pruning (0 = off)
 };
 int launch_attention(const AttnArgs& a, hipStream_t stream);
 

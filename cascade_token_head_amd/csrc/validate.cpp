@@ -44,8 +44,7 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
   if (d->per_head != 0 && d->per_head != 1) return SPATTEN_EINVAL;
   if (d->per_head && (d->mode != SPATTEN_DECODE || d->kv_quantized)) return SPATTEN_EUNSUPPORTED;
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return SPATTEN_EUNSUPPORTED;
-  if (d->v_threshold > 0.0f && (d->mode != SPATTEN_DECODE || d->kv_quantized))
-    return SPATTEN_EUNSUPPORTED;
+  if (d->v_threshold > 0.0f && d->kv_quantized) return SPATTEN_EUNSUPPORTED;
   if (d->mode == SPATTEN_PREFILL) {
     if (d->n_tokens < 1 || d->kv_quantized != 0) return SPATTEN_EINVAL;
     if (d->dtype == SPATTEN_BF16 && d->head_dim == 32) return SPATTEN_EUNSUPPORTED;

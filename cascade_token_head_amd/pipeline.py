@@ -37,7 +37,8 @@ def weights_to_device(layers: List[dict], dtype: torch.dtype, device="cuda") -> 
 
 class PrefillStack:
     def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, tokens, heads,
-                 dtype: torch.dtype, causal: bool, weights: List[dict], device="cuda"):
+                 dtype: torch.dtype, causal: bool, weights: List[dict], device="cuda",
+                 v_threshold: float = 0.0):
         assert len(tokens) == n_layers and len(heads) == n_layers
         self.L, self.B, self.H, self.dh = n_layers, batch, n_heads, head_dim
         self.D = n_heads * head_dim
@@ -55,7 +56,8 @@ class PrefillStack:
         self.tok_idx = torch.empty(B * T, dtype=torch.int32, device=dev)
         self.head_sel = torch.empty(B * H, dtype=torch.int32, device=dev)
         self.descs = [S.make_desc(S.PREFILL, S.dtype_code(dtype), causal, B, tokens[l], H,
-                                  heads[l], head_dim) for l in range(n_layers)]
+                                  heads[l], head_dim, v_threshold=v_threshold)
+                      for l in range(n_layers)]
         ws = max(S.workspace_bytes(d) for d in self.descs)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.lse = None

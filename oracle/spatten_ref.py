@@ -58,10 +58,15 @@ def softmax_rows(S: np.ndarray) -> np.ndarray:
     return E / np.sum(E, axis=-1, keepdims=True)
 
 
-def head_attention(Q, K, V, causal: bool, row_block: int = 512):
+def head_attention(Q, K, V, causal: bool, row_block: int = 512, v_threshold: float = 0.0):
     """One head: S = Q K^T / sqrt(dh), causal mask j > i (indices are in
     ascending original-position order, so this is the positional mask),
     P = row softmax(S), O = P V.
+
+    v_threshold > 0 applies local value pruning ("A. Cascade Token
+    Pruning", bullet "Local Value Pruning") to every query row: V row j
+    enters O[i] only when P[i, j] >= v_threshold, with no renormalisation;
+    the column sums still take every probability.
 
     Returns O [n, dh], column sums of P [n], row log-sum-exp [n].
     Works in row blocks so that n x n is never held for long sequences.
@@ -82,20 +87,21 @@ def head_attention(Q, K, V, causal: bool, row_block: int = 512):
         E = np.exp(S - m)
         l = np.sum(E, axis=1, keepdims=True)
         P = E / l
-        O[r0:r1] = P @ V
+        O[r0:r1] = (np.where(P >= v_threshold, P, 0.0) if v_threshold > 0 else P) @ V
         col += P.sum(axis=0)
         lse[r0:r1] = (m + np.log(l))[:, 0]
     return O, col, lse
 
 
-def attention_rows(Q, K, V, rows, causal: bool):
+def attention_rows(Q, K, V, rows, causal: bool, v_threshold: float = 0.0):
     """Selected query rows of one head, each from its own full row of scores
     (the definition head_attention applies to every row): for query i,
     S_i = Q_i K^T / sqrt(dh) over the keys it sees (j <= i when causal),
     P_i = softmax(S_i), O_i = P_i V.
 
     Returns O [len(rows), dh] and the natural-log LSE [len(rows)]. Used to
-    check long sequences on a sample of rows.
+    check long sequences on a sample of rows. v_threshold as in
+    head_attention.
     """
     rows = np.asarray(rows, dtype=np.int64)
     dh = Q.shape[1]
@@ -105,7 +111,10 @@ def attention_rows(Q, K, V, rows, causal: bool):
     m = np.max(S, axis=1, keepdims=True)
     E = np.exp(S - m)
     l = np.sum(E, axis=1, keepdims=True)
-    return (E / l) @ np.asarray(V, np.float64), (m + np.log(l))[:, 0]
+    P = E / l
+    if v_threshold > 0:
+        P = np.where(P >= v_threshold, P, 0.0)
+    return P @ np.asarray(V, np.float64), (m + np.log(l))[:, 0]
 
 
 def column_sums(Q, K, lse, cols, causal: bool):
@@ -133,7 +142,7 @@ def column_sums(Q, K, lse, cols, causal: bool):
 
 
 def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool,
-                  extras: Optional[dict] = None):
+                  extras: Optional[dict] = None, v_threshold: float = 0.0):
     """One attention-only residual layer over the kept tokens and heads of
     one sequence.
 
@@ -144,7 +153,9 @@ def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool,
     Returns (x_new [n, D], token-importance increment [n] = sum over kept
     heads and queries of P, head-importance increment {h: sum |O_h|},
     per-head LSE {h: [n]}). If `extras` is given it also receives the
-    stored per-head Q, K, V and O under extras[h].
+    stored per-head Q, K, V and O under extras[h]. v_threshold > 0 applies
+    local value pruning inside every head; head importance then takes the
+    pruned output (the output the head hands on).
     """
     x = np.asarray(x, dtype=np.float64)
     n, D = x.shape
@@ -158,7 +169,7 @@ def prefill_layer(x, w: dict, heads, head_dim: int, causal: bool, bf16: bool,
         Q = _store(x @ w["wq"][:, c].astype(np.float64), bf16)
         K = _store(x @ w["wk"][:, c].astype(np.float64), bf16)
         V = _store(x @ w["wv"][:, c].astype(np.float64), bf16)
-        O, col, l = head_attention(Q, K, V, causal)
+        O, col, l = head_attention(Q, K, V, causal, v_threshold=v_threshold)
         if extras is not None:
             extras[h] = {"q": Q, "k": K, "v": V, "o": _store(O, bf16)}
         dcol += col
@@ -330,7 +341,8 @@ def run_prefill(cfg, inputs: dict, seqs=None,
         trace = []
         for l in range(cfg.n_layers):
             assert x.shape[0] == cfg.tokens[l] and len(heads) == cfg.heads[l]
-            x, dcol, dg, lse = prefill_layer(x, inputs["layers"][l], heads, dh, cfg.causal, bf16)
+            x, dcol, dg, lse = prefill_layer(x, inputs["layers"][l], heads, dh, cfg.causal, bf16,
+                                             v_threshold=getattr(cfg, "v_threshold", 0.0))
             a = a + dcol
             for h, v in dg.items():
                 g[h] += v

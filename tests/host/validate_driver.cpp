@@ -67,7 +67,7 @@ int main() {
   d.cache_cap = 2048;
   EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_EINVAL);
-  // local value pruning: unquantized decode only; NaN and negative rejected
+  // local value pruning: not with quantized caches; NaN and negative rejected
   d.cache_cap = 2049;
   d.v_threshold = 1e-4f;
   EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
@@ -82,6 +82,25 @@ int main() {
   EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, P, &got), SPATTEN_EINVAL);
   d.v_threshold = 0.0f;
+  // representative-token selection
+  {
+    size_t need_a = ada_ws(4, 512).total, got_a = need_a;
+    int32_t* fl = reinterpret_cast<int32_t*>(P);
+    EXPECT(check_ada(fp, 4, 512, 768, 0.3f, fl, P, &got_a), SPATTEN_OK);
+    EXPECT(check_ada(fp, 4, 512, 770, 0.3f, fl, P, &got_a), SPATTEN_EUNSUPPORTED);
+    EXPECT(check_ada(fp, 4, 512, 768, 1.5f, fl, P, &got_a), SPATTEN_EINVAL);
+    EXPECT(check_ada(fp, 4, 512, 768, __builtin_nanf(""), fl, P, &got_a), SPATTEN_EINVAL);
+    EXPECT(check_ada(fp, 4, 0, 768, 0.3f, fl, P, &got_a), SPATTEN_EINVAL);
+    got_a = need_a - 1;
+    EXPECT(check_ada(fp, 4, 512, 768, 0.3f, fl, P, &got_a), SPATTEN_EWORKSPACE);
+    EXPECT(check_ada(nullptr, 4, 512, 768, 0.3f, nullptr, nullptr, &got_a), SPATTEN_OK);
+    got_a = need_a;
+    EXPECT(check_ada(nullptr, 4, 512, 768, 0.3f, fl, P, &got_a), SPATTEN_EINVAL);
+    EXPECT(check_ada(fp, 4, 512, 768, 0.3f, fl, P, nullptr), SPATTEN_EINVAL);
+    // extreme sizes must not overflow the workspace arithmetic
+    EXPECT(check_ada(nullptr, 1 << 30, 1 << 30, 32, 0.3f, nullptr, nullptr, &got_a),
+           SPATTEN_EUNSUPPORTED);
+  }
   // top-k
   EXPECT(check_topk(fp, 4, 100, 100, 100, hi), SPATTEN_OK);
   EXPECT(check_topk(fp, 4, 100, 100, 101, hi), SPATTEN_EINVAL);

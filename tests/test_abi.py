@@ -120,14 +120,15 @@ def test_decode_rejections(S):
     d = S.make_desc(**{**base, "kv_quantized": True})
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL     # planes missing, caches given
     # local value pruning: a threshold must be a non-negative number, and is
-    # taken by unquantized decode only
+    # taken by unquantized caches and by prefill
     for bad in (-1e-3, float("nan")):
         d = S.make_desc(**{**base, "v_threshold": bad})
         assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(**{**base, "v_threshold": 1e-3, "kv_quantized": True, "pq_threshold": 0.1})
     assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, v_threshold=1e-3)
-    assert _call_layer(S, d, 1 << 40, **_prefill_ptrs()) == S.EUNSUPPORTED
+    assert S.workspace_bytes(d) == S.workspace_bytes(
+        S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64))
     # per-head importance: a flag, for unquantized decode only
     d = S.make_desc(**base)
     d.per_head = 2

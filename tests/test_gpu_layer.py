@@ -130,6 +130,92 @@ def test_prefill_layer(S, dt, B, n, H, hk, dh, causal):
             assert go[b, h] == g0[b, h]
 
 
+VPRUNE_PREFILL_CASES = [
+    # (dtype, B, n, H, h_kept, dh, causal, tau)
+    ("bf16", 2, 300, 12, 10, 64, False, 1e-3),
+    ("bf16", 2, 333, 6, 6, 64, True, 2e-3),
+    ("bf16", 1, 300, 4, 3, 128, True, 1e-3),
+    ("bf16", 2, 257, 4, 4, 128, False, 5e-3),
+    ("bf16", 1, 1, 4, 1, 64, False, 0.5),
+    ("f32", 2, 70, 4, 3, 32, True, 1e-2),
+    ("f32", 1, 64, 4, 4, 32, False, 0.05),
+]
+
+
+@pytest.mark.parametrize("dt,B,n,H,hk,dh,causal,tau", VPRUNE_PREFILL_CASES)
+def test_prefill_layer_value_pruning(S, dt, B, n, H, hk, dh, causal, tau):
+    """Local value pruning in prefill ("A. Cascade Token Pruning", bullet
+    "Local Value Pruning"): on the GPU's own Q, K, V every head output must
+    equal sum over P[i, j] >= tau of P[i, j] V[j] (fp64 P), up to the
+    storage tolerance plus, per element, the weight of the V rows whose
+    probability lies within 1e-4 (relative) of tau, where the fp32 and fp64
+    decisions may differ; token importance still takes every probability,
+    head importance the pruned output."""
+    print("prefill vprune case", dt, B, n, H, hk, dh, causal, tau, flush=True)
+    bf16 = dt == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    es = 2 if bf16 else 4
+    rng = np.random.default_rng(B * 7000 + n + H)
+    D = H * dh
+    x = rng.standard_normal((B, n, D)).astype(np.float32)
+    x[:, ::13] *= 3
+    if bf16:
+        x = R.bf16_round(x).astype(np.float32)
+    w = _weights(rng, D, bf16)
+    heads = np.stack([np.sort(rng.choice(H, hk, replace=False)) for _ in range(B)]).astype(np.int32)
+    a0 = np.zeros((B, n), np.float32)
+    g0 = np.zeros((B, H), np.float32)
+    desc = S.make_desc(S.PREFILL, S.BF16 if bf16 else S.F32, causal, B, n, H, hk, dh,
+                       v_threshold=tau)
+    ws = torch.zeros(S.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    xd, wd = to_dev(x, tdt), _dev_w(w, tdt)
+    ad, gd = to_dev(a0, torch.float32), to_dev(g0, torch.float32)
+    S.layer_forward(desc, xd, wd["wq"], wd["wk"], wd["wv"], wd["wo"], to_dev(heads, torch.int32),
+                    ad, gd, ws)
+    torch.cuda.synchronize()
+    xo, ao, go = to_np(xd), to_np(ad), to_np(gd)
+    lay = PrefillWs(B, n, hk, dh, es, bf16)
+    npd = lay.n_pad
+    o_all = to_np(ws[lay.o: lay.o + B * n * hk * dh * es].view(tdt).view(B, n, hk, dh))
+    q_all = to_np(ws[lay.q: lay.q + B * hk * npd * dh * es].view(tdt).view(B, hk, npd, dh))
+    k_all = to_np(ws[lay.k: lay.k + B * hk * npd * dh * es].view(tdt).view(B, hk, npd, dh))
+    vt_all = to_np(ws[lay.vt: lay.vt + B * hk * npd * dh * es].view(tdt).view(B, hk, dh, npd))
+    kept = total = 0
+    for b in range(B):
+        col = np.zeros(n)
+        xr = x[b].astype(np.float64)
+        delta = np.zeros((n, D))
+        for s_, h in enumerate(heads[b]):
+            Q, K = q_all[b, s_, :n], k_all[b, s_, :n]
+            V = vt_all[b, s_, :, :n].T
+            masked = causal & (np.arange(n)[None, :] > np.arange(n)[:, None])
+            P = R.softmax_rows(np.where(masked, -np.inf, Q @ K.T / math.sqrt(dh)))
+            keepm = P >= tau
+            kept += int(keepm.sum())
+            total += int((P > 0).sum())
+            Oref = np.where(keepm, P, 0.0) @ V
+            band = np.abs(P - tau) <= 1e-4 * tau
+            allow = (np.where(band, P, 0.0) @ np.abs(V)) if band.any() else 0.0
+            got = o_all[b, :, s_]
+            stor = (np.abs(Oref) * 2.0 ** -8 + 1e-6) if bf16 else 1e-5
+            err = np.abs(got - Oref) - allow - stor
+            assert np.all(err <= 2e-2 * np.sqrt(np.mean(Oref ** 2)) + 1e-6), (
+                "O b%d h%d: max excess %.3g" % (b, h, err.max()))
+            col += P.sum(axis=0)
+            gh = go[b, h] - g0[b, h]
+            assert abs(gh - np.abs(got).sum()) <= 1e-3 * max(np.abs(got).sum(), 1e-6), (b, h)
+            delta += (R.bf16_round(got) if bf16 else got) @ w["wo"][h * dh:(h + 1) * dh, :]
+        np.testing.assert_allclose(ao[b] - a0[b], col, rtol=1e-4, atol=2e-5 * max(col.max(), 1))
+        xref = R.bf16_round(xr + delta) if bf16 else xr + delta
+        if bf16:
+            check_bf16_output(xo[b], xref, what="x_out b=%d" % b)
+        else:
+            assert np.max(np.abs(xo[b] - xref)) <= 1e-4
+    print("V entries kept %d of %d" % (kept, total), flush=True)
+    if tau < 0.5:
+        assert 0 < kept < total
+
+
 def _decode_setup(rng, B, H, dh, L0, cap, quantized):
     D = H * dh
     K0 = R.bf16_round(rng.standard_normal((B, L0, D)) * rng.choice([1.0, 3.0], (B, L0, 1)))

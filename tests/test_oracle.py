@@ -842,3 +842,65 @@ def test_run_decode_pq_importance_accumulates_recomputed_probabilities():
     msb = sum(torch.softmax(t(km[:, h] @ q[h] / math.sqrt(dh)), 0).numpy() for h in range(H))
     assert np.max(np.abs(want - msb)) > 1e-4
     np.testing.assert_allclose(a_pre, want, rtol=1e-10, atol=1e-14)
+
+
+# ----------------------------------------------------------------- value pruning in prefill
+# ("A. Cascade Token Pruning", bullet "Local Value Pruning": after the
+# softmax, a head drops its low-probability V vectors for the current head;
+# reading: for every query row, V row j enters only when P[i, j] >= tau)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_value_pruning_one_hot_values(causal):
+    """V = identity rows: O[i, j] is P[i, j] when it reaches the threshold
+    and 0 otherwise, with P from torch's softmax; the column sums keep every
+    probability."""
+    rng = np.random.default_rng(51)
+    n, dh = 24, 32
+    Q, K = rng.standard_normal((n, dh)) * 1.5, rng.standard_normal((n, dh)) * 1.5
+    V = np.eye(n, dh)
+    P, _ = _torch_probs(Q, K, causal)
+    for tau in (1e-3, 0.05, 0.2):
+        O, col, _ = R.head_attention(Q, K, V, causal, v_threshold=tau)
+        np.testing.assert_allclose(O[:, :n], np.where(P >= tau, P, 0.0), atol=1e-14)
+        np.testing.assert_allclose(col, P.sum(axis=0), atol=1e-12)
+        rows = np.array([0, 5, n - 1])
+        Or, _ = R.attention_rows(Q, K, V, rows, causal, v_threshold=tau)
+        np.testing.assert_allclose(Or[:, :n], np.where(P[rows] >= tau, P[rows], 0.0), atol=1e-14)
+
+
+def test_prefill_value_pruning_extremes():
+    rng = np.random.default_rng(52)
+    n, dh = 17, 8
+    Q, K, V = (rng.standard_normal((n, dh)) for _ in range(3))
+    # a threshold below every probability keeps torch's attention
+    O, _, _ = R.head_attention(Q, K, V, True, v_threshold=1e-300)
+    np.testing.assert_allclose(O, _sdpa(Q, K, V, True), atol=1e-12)
+    # above one nothing is kept, except nothing: O = 0
+    O, col, _ = R.head_attention(Q, K, V, False, v_threshold=1.01)
+    np.testing.assert_array_equal(O, 0.0)
+    assert abs(col.sum() - n) < 1e-9
+    # causal row 0 has p = 1 on key 0, kept for any threshold <= 1
+    O, _, _ = R.head_attention(Q, K, V, True, v_threshold=1.0)
+    np.testing.assert_allclose(O[0], V[0], atol=1e-15)
+    # uniform rows (Q = 0): p = 1/n, kept at tau = 1/n exactly, dropped above
+    Z = np.zeros((n, dh))
+    O, _, _ = R.head_attention(Z, K, V, False, v_threshold=1.0 / n)
+    np.testing.assert_allclose(O, np.tile(V.mean(axis=0), (n, 1)), atol=1e-12)
+    O, _, _ = R.head_attention(Z, K, V, False, v_threshold=np.nextafter(1.0 / n, 1.0))
+    np.testing.assert_array_equal(O, 0.0)
+
+
+def test_prefill_layer_value_pruning_head_importance_takes_pruned_output():
+    rng = np.random.default_rng(53)
+    D, dh, n = 32, 8, 12
+    w = _tiny_weights(D, rng)
+    x = rng.standard_normal((n, D))
+    ex = {}
+    _, dcol, dg, _ = R.prefill_layer(x, w, range(4), dh, False, False, extras=ex, v_threshold=0.1)
+    _, dcol0, _, _ = R.prefill_layer(x, w, range(4), dh, False, False)
+    np.testing.assert_allclose(dcol, dcol0, atol=1e-12)
+    for h in range(4):
+        P, _ = _torch_probs(ex[h]["q"], ex[h]["k"], False)
+        O = np.where(P >= 0.1, P, 0.0) @ ex[h]["v"]
+        assert abs(dg[h] - np.abs(O).sum()) < 1e-12

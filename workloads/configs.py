@@ -132,9 +132,12 @@ LONG_CAUSAL = Config(
 GPT2_DECODE_VPRUNE = replace(GPT2_DECODE, name="gpt2_decode_vprune", v_threshold=1e-4)
 GPT2_DECODE_ROLLING = replace(GPT2_DECODE, name="gpt2_decode_rolling", prune_every=1)
 GPT2_DECODE_PERHEAD = replace(GPT2_DECODE, name="gpt2_decode_perhead", per_head=True)
+# Local value pruning in prefill: the bert_base stack with a probability
+# threshold of 1e-3 (about half of a 512-token row's uniform share).
+BERT_BASE_VPRUNE = replace(BERT_BASE, name="bert_base_vprune", v_threshold=1e-3)
 
 CONFIGS = [TINY, BERT_BASE, GPT2_DECODE, PQ_DECODE, LONG_CAUSAL]
-EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD]
+EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD, BERT_BASE_VPRUNE]
 BY_NAME = {c.name: c for c in CONFIGS + EXTENSIONS}
 
 

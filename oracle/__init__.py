@@ -43,6 +43,18 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       threshold 0 -> torch attention; threshold > 1 -> 0;
                       uniform rows at and just above 1/n.
   prune_after_step    truth table for r = 0, 1, 3.
+  head_attention /    value pruning in prefill: one-hot V rows expose every
+  attention_rows      kept probability (torch softmax), extremes, causal
+                      row 0, uniform rows at and just above 1/n.
+  perhead_prefill_    per-head token pruning in prefill: each head's output
+  layer               is torch SDPA over its own keys; one kept key takes all
+                      the mass; keeping every key reproduces the dense stack.
+  run_prefill_perhead every per-head cut keeps that head's largest
+                      importance among its own keys and never revives one;
+                      heads choose different keys.
+  ada_ref (module)    see tests/test_ada_oracle.py: brute force, closed
+                      forms, cascade from all / no tokens, a hand-worked
+                      case, Proposition 4.
   run_prefill /       parity unpinned beyond the composition of the pinned
   run_decode          parts (the pages print no worked example). Invariants
                       checked: total importance per layer, value pruning
@@ -53,4 +65,4 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       the shared cut for one head and for identical heads,
                       and each head's cut keeps that head's largest entries.
 """
-from . import spatten_ref, topk_engine  # noqa: F401
+from . import ada_ref, spatten_ref, topk_engine  # noqa: F401

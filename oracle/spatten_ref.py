@@ -366,6 +366,92 @@ def run_prefill(cfg, inputs: dict, seqs=None,
     return out
 
 
+def perhead_prefill_layer(x, w: dict, heads, keys: dict, head_dim: int, bf16: bool,
+                          extras: Optional[dict] = None):
+    """One attention-only residual layer with per-head token pruning
+    (section "A. Neural Networks Pruning and Quantization", bullet "Token
+    Pruning": each head keeps its own tokens). Reading: head h attends over
+    its own kept tokens keys[h] (ascending token indices) as keys and
+    values; every token still queries every head, so O_h has a row for
+    every token and x keeps all rows. Bidirectional.
+
+    Returns (x_new [n, D], {h: column sums of P_h over its keys [len(keys[h])]},
+    {h: sum |O_h|}). extras, if given, receives each head's stored Q, K, V
+    (all tokens) and O."""
+    x = np.asarray(x, dtype=np.float64)
+    n, D = x.shape
+    dh = head_dim
+    delta = np.zeros((n, D))
+    cols, dg = {}, {}
+    for h in heads:
+        c = slice(h * dh, (h + 1) * dh)
+        Q = _store(x @ w["wq"][:, c].astype(np.float64), bf16)
+        K = _store(x @ w["wk"][:, c].astype(np.float64), bf16)
+        V = _store(x @ w["wv"][:, c].astype(np.float64), bf16)
+        kk = np.asarray(keys[h], dtype=np.int64)
+        S = (Q @ K[kk].T) / math.sqrt(dh)
+        P = softmax_rows(S)
+        O = P @ V[kk]
+        if extras is not None:
+            extras[h] = {"q": Q, "k": K, "v": V, "o": _store(O, bf16), "p": P}
+        cols[h] = P.sum(axis=0)
+        dg[h] = float(np.abs(O).sum())
+        delta += _store(O, bf16) @ w["wo"][c, :].astype(np.float64)
+    return _store(x + delta, bf16), cols, dg
+
+
+def run_prefill_perhead(cfg, inputs: dict, seqs=None,
+                        adopt: Optional[Callable] = None) -> dict:
+    """Per-head token pruning over a prefill stack (bidirectional). Every
+    token keeps its row of x; head h keeps its own key/value tokens: all
+    of them at layer 1, then after layer l the top cfg.key_keep[l+1] of its
+    own cumulative importance a_h among the tokens it kept so far (a token
+    a head dropped stays dropped for that head). a_h[j] accumulates the
+    probability mass head h gives token j. When the head count drops, kept
+    heads are re-ranked by cumulative head importance as in run_prefill.
+
+    adopt(kind, b, l, idx, scores) may return another valid selection.
+    Returns per sequence the final x, heads, {h: keys} and {h: a_h} and a
+    per-layer trace."""
+    bf16 = cfg.dtype == "bf16"
+    seqs = range(cfg.batch) if seqs is None else seqs
+    n, dh, H = cfg.tokens[0], cfg.head_dim, cfg.n_heads
+    out = {}
+    for b in seqs:
+        x = np.asarray(inputs["x"][b], dtype=np.float64)
+        heads = np.arange(H, dtype=np.int32)
+        keys = {h: np.arange(n, dtype=np.int64) for h in range(H)}
+        a = {h: np.zeros(n) for h in range(H)}
+        g = np.zeros(H)
+        trace = []
+        for l in range(cfg.n_layers):
+            assert len(heads) == cfg.heads[l]
+            assert all(len(keys[h]) == cfg.key_keep[l] for h in heads)
+            x, cols, dg = perhead_prefill_layer(x, inputs["layers"][l], heads, keys, dh, bf16)
+            for h in heads:
+                a[h][keys[h]] += cols[h]
+                g[h] += dg[h]
+            rec = {"heads": heads.copy(), "keys": {h: keys[h].copy() for h in heads},
+                   "a": {h: a[h].copy() for h in heads}, "g": g.copy(), "x": x.copy()}
+            if l + 1 < cfg.n_layers:
+                if cfg.heads[l + 1] != len(heads):
+                    gk = g[heads].astype(np.float32)
+                    sel = topk(gk, cfg.heads[l + 1])
+                    if adopt is not None:
+                        sel = adopt("head", b, l, sel, gk)
+                    heads = heads[sel]
+                m = cfg.key_keep[l + 1]
+                for h in heads:
+                    sc = a[h][keys[h]].astype(np.float32)
+                    sel = topk(sc, m)
+                    if adopt is not None:
+                        sel = adopt("key", b, (l, int(h)), sel, sc)
+                    keys[h] = keys[h][sel]
+            trace.append(rec)
+        out[b] = {"x": x, "heads": heads, "keys": keys, "a": a, "g": g, "trace": trace}
+    return out
+
+
 def value_pruned_output(p, V, tau: float):
     """Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning"): once the
     softmax has produced a head's probabilities p [Lc], the V rows whose

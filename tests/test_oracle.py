@@ -904,3 +904,75 @@ def test_prefill_layer_value_pruning_head_importance_takes_pruned_output():
         P, _ = _torch_probs(ex[h]["q"], ex[h]["k"], False)
         O = np.where(P >= 0.1, P, 0.0) @ ex[h]["v"]
         assert abs(dg[h] - np.abs(O).sum()) < 1e-12
+
+
+# ----------------------------------------------------------------- per-head token pruning, prefill
+# (section "A. Neural Networks Pruning and Quantization", bullet "Token
+# Pruning"; reading: each head attends over its own kept tokens as keys and
+# values, every token keeps its row and queries every head)
+
+
+def _perhead_cfg(**kw):
+    from workloads.configs import BERT_BASE_PERHEAD
+    base = dict(n_layers=3, batch=1, n_heads=3, head_dim=8, tokens=(24,) * 3, heads=(3, 3, 3),
+                key_keep=(24, 16, 10), dtype="f32")
+    base.update(kw)
+    return scaled(BERT_BASE_PERHEAD, **base)
+
+
+def test_perhead_prefill_keeping_every_key_is_the_dense_stack():
+    cfg = _perhead_cfg(key_keep=(24, 24, 24))
+    inp = make_prefill_inputs(cfg)
+    ph = R.run_prefill_perhead(cfg, inp)[0]
+    dense = R.run_prefill(scaled(cfg, per_head=False, key_keep=()), inp)[0]
+    np.testing.assert_allclose(ph["x"], dense["x"], atol=1e-12)
+    # the summed per-head importance is the shared importance
+    np.testing.assert_allclose(sum(ph["a"][h] for h in range(3)), dense["a"], atol=1e-12)
+
+
+def test_perhead_prefill_layer_matches_torch_attention_over_each_heads_keys():
+    rng = np.random.default_rng(61)
+    D, dh, n = 24, 8, 15
+    w = _tiny_weights(D, rng)
+    x = rng.standard_normal((n, D))
+    keys = {0: np.array([0, 3, 4, 9, 14]), 1: np.arange(n), 2: np.array([7])}
+    ex = {}
+    xn, cols, dg = R.perhead_prefill_layer(x, w, [0, 1, 2], keys, dh, False, extras=ex)
+    delta = np.zeros((n, D))
+    for h in range(3):
+        c = slice(h * dh, (h + 1) * dh)
+        Q, K, V = x @ w["wq"][:, c], x @ w["wk"][:, c], x @ w["wv"][:, c]
+        q = torch.from_numpy(Q)[None, None]
+        k = torch.from_numpy(K[keys[h]])[None, None]
+        v = torch.from_numpy(V[keys[h]])[None, None]
+        O = torch.nn.functional.scaled_dot_product_attention(q, k, v)[0, 0].numpy()
+        np.testing.assert_allclose(ex[h]["o"], O, atol=1e-12)
+        assert abs(cols[h].sum() - n) < 1e-9          # every query row sums to one
+        assert abs(dg[h] - np.abs(O).sum()) < 1e-9
+        delta += O @ w["wo"][c, :]
+    np.testing.assert_allclose(cols[2], [n], atol=1e-12)   # one key takes all the mass
+    np.testing.assert_allclose(ex[2]["o"], np.tile(x[7] @ w["wv"][:, 16:24], (n, 1)), atol=1e-12)
+    np.testing.assert_allclose(xn, x + delta, atol=1e-12)
+
+
+def test_perhead_prefill_cuts_keep_each_heads_largest_and_never_revive():
+    cfg = _perhead_cfg(n_layers=4, tokens=(30,) * 4, key_keep=(30, 20, 12, 7), heads=(3, 3, 2, 2))
+    out = R.run_prefill_perhead(cfg, make_prefill_inputs(cfg))[0]
+    tr = out["trace"]
+    differ = False
+    for l in range(cfg.n_layers - 1):
+        nxt_heads = tr[l + 1]["heads"]
+        for h in nxt_heads:
+            before, after = tr[l]["keys"][h], tr[l + 1]["keys"][h]
+            assert np.all(np.isin(after, before)) and np.all(np.diff(after) > 0)
+            a = tr[l]["a"][h][before].astype(np.float32)
+            kept = np.isin(before, after)
+            assert a[kept].min() >= a[~kept].max()
+        ks = [tuple(tr[l + 1]["keys"][h]) for h in nxt_heads]
+        differ |= len(set(ks)) > 1
+    assert differ, "heads never chose different keys"
+    # the head cut before layer 3 keeps the largest cumulative |O|
+    g = tr[1]["g"]
+    assert len(tr[2]["heads"]) == 2
+    rest = np.setdiff1d(tr[1]["heads"], tr[2]["heads"])
+    assert g[tr[2]["heads"]].min() >= g[rest].max()

@@ -69,6 +69,9 @@ class Config:
     # per-head token pruning: each head keeps its own cache entries by its
     # own cumulative importance (unquantized decode)
     per_head: bool = False
+    # prefill per-head token pruning: keys (and values) each head keeps per
+    # layer (empty: no per-head pruning); every token keeps its row of x
+    key_keep: tuple = ()
     heavy_frac: float = 0.05
     heavy_scale: float = 3.0
 
@@ -87,6 +90,7 @@ class Config:
 
     def token_layers(self) -> int:
         """Tokens processed summed over layers (and steps for decode)."""
+        # (per-head pruning keeps every token's row: tokens stays n per layer)
         if self.kind == "prefill":
             return self.batch * sum(self.tokens)
         return self.batch * self.n_layers * self.steps
@@ -135,9 +139,15 @@ GPT2_DECODE_PERHEAD = replace(GPT2_DECODE, name="gpt2_decode_perhead", per_head=
 # Local value pruning in prefill: the bert_base stack with a probability
 # threshold of 1e-3 (about half of a 512-token row's uniform share).
 BERT_BASE_VPRUNE = replace(BERT_BASE, name="bert_base_vprune", v_threshold=1e-3)
+# Per-head token pruning in prefill: every token keeps its row (512 per
+# layer) and each head keeps its own keys and values, falling from 512 to
+# 256 like bert_base's token schedule; heads 12 -> 10 from layer 4.
+BERT_BASE_PERHEAD = replace(BERT_BASE, name="bert_base_perhead", per_head=True,
+                            tokens=(512,) * 12, key_keep=BERT_BASE.tokens)
 
 CONFIGS = [TINY, BERT_BASE, GPT2_DECODE, PQ_DECODE, LONG_CAUSAL]
-EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD, BERT_BASE_VPRUNE]
+EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD, BERT_BASE_VPRUNE,
+              BERT_BASE_PERHEAD]
 BY_NAME = {c.name: c for c in CONFIGS + EXTENSIONS}
 
 

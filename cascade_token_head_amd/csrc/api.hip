@@ -23,8 +23,9 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
   } while (0)
 
 int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const void* wk,
-                  const void* wv, const void* wo, const int32_t* head_idx, float* a, float* g,
-                  float* lse_out, char* ws, hipStream_t st) {
+                  const void* wv, const void* wo, const int32_t* head_idx,
+                  const int32_t* head_keys, float* a, float* g, float* lse_out, char* ws,
+                  hipStream_t st) {
   const PrefillWs w = prefill_ws(d);
   const int D = d.n_heads * d.head_dim;
   QkvArgs qa{};
@@ -69,6 +70,11 @@ int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const vo
   aa.g = g;
   aa.lse_out = lse_out;
   aa.v_threshold = d.v_threshold;
+  aa.head_keys = head_keys;
+  aa.kk = head_keys ? ws + w.kk : aa.k;
+  aa.vtk = head_keys ? ws + w.vtk : aa.vt;
+  aa.nk = int(w.nk);
+  aa.nk_pad = int(w.nk_pad);
   SPATTEN_TRY(launch_attention(aa, st));
   OutArgs oa{};
   oa.dtype = d.dtype;
@@ -203,13 +209,15 @@ int device_scratch(char** out) {
 extern "C" {
 
 int spatten_layer_forward(const spatten_layer_desc* d, void* x, const void* wq, const void* wk,
-                          const void* wv, const void* wo, const int32_t* head_idx, float* a,
-                          float* g, void* k_cache, void* v_cache, uint8_t* k_msb, uint8_t* k_lsb,
-                          float* k_scale, uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
-                          int32_t* recompute, int32_t* v_kept, float* lse, void* workspace,
-                          size_t* workspace_bytes, void* stream) {
-  const int st = check_layer(d, x, wq, wk, wv, wo, head_idx, a, g, k_cache, v_cache, k_msb, k_lsb,
-                             k_scale, v_msb, v_lsb, v_scale, workspace, workspace_bytes);
+                          const void* wv, const void* wo, const int32_t* head_idx,
+                          const int32_t* head_keys, float* a, float* g, void* k_cache,
+                          void* v_cache, uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
+                          uint8_t* v_msb, uint8_t* v_lsb, float* v_scale, int32_t* recompute,
+                          int32_t* v_kept, float* lse, void* workspace, size_t* workspace_bytes,
+                          void* stream) {
+  const int st = check_layer(d, x, wq, wk, wv, wo, head_idx, head_keys, a, g, k_cache, v_cache,
+                             k_msb, k_lsb, k_scale, v_msb, v_lsb, v_scale, workspace,
+                             workspace_bytes);
   if (st != SPATTEN_OK) return st;
   if (!workspace) {
     *workspace_bytes = layer_workspace_bytes(*d);
@@ -218,33 +226,35 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x, const void* wq, 
   if (d->batch == 0) return SPATTEN_OK;
   char* ws = static_cast<char*>(workspace);
   if (d->mode == SPATTEN_PREFILL)
-    return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, a, g, lse, ws, as_stream(stream));
+    return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, head_keys, a, g, lse, ws,
+                         as_stream(stream));
   return layer_decode(*d, x, wq, wk, wv, wo, head_idx, a, k_cache, v_cache, k_msb, k_lsb, k_scale,
                       v_msb, v_lsb, v_scale, recompute, v_kept, ws, as_stream(stream));
 }
 
 int spatten_layer_forward_noalloc(const spatten_layer_desc* d, void* x, const void* wq,
                                   const void* wk, const void* wv, const void* wo,
-                                  const int32_t* head_idx, float* a, float* g, void* k_cache,
-                                  void* v_cache, uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
-                                  uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
-                                  int32_t* recompute, int32_t* v_kept, float* lse,
-                                  void* stream) {
+                                  const int32_t* head_idx, const int32_t* head_keys, float* a,
+                                  float* g, void* k_cache, void* v_cache, uint8_t* k_msb,
+                                  uint8_t* k_lsb, float* k_scale, uint8_t* v_msb,
+                                  uint8_t* v_lsb, float* v_scale, int32_t* recompute,
+                                  int32_t* v_kept, float* lse, void* stream) {
   size_t bytes = SPATTEN_NOALLOC_SCRATCH_BYTES;
   // descriptor first (no workspace: only *d is checked), then the size
-  int st = check_layer(d, x, wq, wk, wv, wo, head_idx, a, g, k_cache, v_cache, k_msb, k_lsb,
-                       k_scale, v_msb, v_lsb, v_scale, nullptr, &bytes);
+  int st = check_layer(d, x, wq, wk, wv, wo, head_idx, head_keys, a, g, k_cache, v_cache, k_msb,
+                       k_lsb, k_scale, v_msb, v_lsb, v_scale, nullptr, &bytes);
   if (st != SPATTEN_OK) return st;
   if (layer_workspace_bytes(*d) > SPATTEN_NOALLOC_SCRATCH_BYTES) return SPATTEN_EWORKSPACE;
   if (d->batch == 0) return SPATTEN_OK;
   char* ws = nullptr;
   st = device_scratch(&ws);
   if (st != SPATTEN_OK) return st;
-  st = check_layer(d, x, wq, wk, wv, wo, head_idx, a, g, k_cache, v_cache, k_msb, k_lsb, k_scale,
-                   v_msb, v_lsb, v_scale, ws, &bytes);
+  st = check_layer(d, x, wq, wk, wv, wo, head_idx, head_keys, a, g, k_cache, v_cache, k_msb,
+                   k_lsb, k_scale, v_msb, v_lsb, v_scale, ws, &bytes);
   if (st != SPATTEN_OK) return st;
   if (d->mode == SPATTEN_PREFILL)
-    return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, a, g, lse, ws, as_stream(stream));
+    return layer_prefill(*d, x, wq, wk, wv, wo, head_idx, head_keys, a, g, lse, ws,
+                         as_stream(stream));
   return layer_decode(*d, x, wq, wk, wv, wo, head_idx, a, k_cache, v_cache, k_msb, k_lsb, k_scale,
                       v_msb, v_lsb, v_scale, recompute, v_kept, ws, as_stream(stream));
 }

@@ -21,7 +21,11 @@
 // fp32 path: plain VALU kernels for the fp32 workload.
 // Local value pruning (a threshold on each exact probability before P V)
 // adds a second forward pass that reads the first pass's LSE (bf16), or is
-// applied to the normalised scores in LDS (fp32).
+// applied to the normalised scores in LDS (fp32). Per-head token pruning
+// (bf16, bidirectional): each head's kept tokens are gathered into its own
+// K / V^T slabs and serve as the keys of that head, every token as a query;
+// the column sums are added at each kept token's position of the head
+// slot's own importance row.
 #include <type_traits>
 
 #include "common.hpp"
@@ -97,10 +101,13 @@ attn_fwd_bf16(AttnArgs a) {
   const int q0 = qb * QB;
   const int wq0 = q0 + QW * wave;        // first query of this wave
   const int n = a.n, n_pad = a.n_pad;
+  // keys: the layer's tokens, or (per-head pruning) the head's own kept
+  // tokens gathered into their own K / V^T slabs
+  const int nk = a.nk, nk_pad = a.nk_pad;
   const int64_t bs = int64_t(b) * a.h_kept + s;
   const bf16_t* Q = static_cast<const bf16_t*>(a.q) + bs * n_pad * DH;
-  const bf16_t* K = static_cast<const bf16_t*>(a.k) + bs * n_pad * DH;
-  const bf16_t* VT = static_cast<const bf16_t*>(a.vt) + bs * DH * n_pad;
+  const bf16_t* K = static_cast<const bf16_t*>(a.kk) + bs * nk_pad * DH;
+  const bf16_t* VT = static_cast<const bf16_t*>(a.vtk) + bs * DH * nk_pad;
   const bool wave_live = wq0 < n;
 
   // Q operand (B of S^T = K Q^T): lane holds Q[query][16kk + 8G .. +8]
@@ -131,9 +138,9 @@ attn_fwd_bf16(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][u][r] = 0.0f;
 
-  const int kend = CAUSAL ? min(n, q0 + QB) : n;
+  const int kend = CAUSAL ? min(n, q0 + QB) : nk;
   const int ntiles = int(ceil_div(kend, KT));
-  const int wave_kend = CAUSAL ? min(n, wq0 + QW) : n;   // keys this wave can see
+  const int wave_kend = CAUSAL ? min(n, wq0 + QW) : nk;   // keys this wave can see
 
   // register staging: one set, or two when loads run two tiles ahead
   constexpr int NSET = DEEP ? 2 : 1;
@@ -149,14 +156,14 @@ attn_fwd_bf16(AttnArgs a) {
     for (int i = 0; i < NVC; ++i) {
       const int c = tid + NT * i;
       const int row = c >> 3, k8 = (c & 7) * 8;
-      rv[set][i] = *reinterpret_cast<const u32x4*>(VT + int64_t(row) * n_pad + k0 + k8);
+      rv[set][i] = *reinterpret_cast<const u32x4*>(VT + int64_t(row) * nk_pad + k0 + k8);
       // keys past the end get exact zeros (their probabilities are 0, and
       // the padding itself is never written)
-      if (k0 + KT > n) {
+      if (k0 + KT > nk) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + k8 + 2 * e;
-          const uint32_t lo = key < n ? 0xffffu : 0u, hi = key + 1 < n ? 0xffff0000u : 0u;
+          const uint32_t lo = key < nk ? 0xffffu : 0u, hi = key + 1 < nk ? 0xffff0000u : 0u;
           rv[set][i][e] &= lo | hi;
         }
       }
@@ -223,7 +230,7 @@ attn_fwd_bf16(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + 32 * t + 16 * G + i;
-        const bool m = key >= n || (CAUSAL && key > my_q);
+        const bool m = key >= nk || (CAUSAL && key > my_q);
         st[u][i] = m ? -INFINITY : st[u][i];
       }
     }
@@ -308,11 +315,11 @@ attn_fwd_bf16(AttnArgs a) {
     if (live0) qk(buf, 0, st0);
     if (live1) qk(buf, 1, st1);
     if (live0) {
-      if ((k0 + 32 > n) || (CAUSAL && k0 + 31 > wq0)) mask(st0, k0, 0);
+      if ((k0 + 32 > nk) || (CAUSAL && k0 + 31 > wq0)) mask(st0, k0, 0);
       soft_pv(st0, buf, 0);
     }
     if (live1) {
-      if ((k0 + 64 > n) || (CAUSAL && k0 + 63 > wq0)) mask(st1, k0, 1);
+      if ((k0 + 64 > nk) || (CAUSAL && k0 + 63 > wq0)) mask(st1, k0, 1);
       soft_pv(st1, buf, 1);
     }
   };
@@ -402,14 +409,14 @@ attn_colsum_bf16(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, col = lane & 31;
-  const XcdItem item = xcd_item(int(ceil_div(a.n, kAttnKBlock)), a.h_kept, a.batch);
+  const XcdItem item = xcd_item(int(ceil_div(a.nk, kAttnKBlock)), a.h_kept, a.batch);
   if (!item.valid) return;
   const int b = item.b, s = item.s;
   const int k0 = item.blk * kAttnKBlock;
-  const int n = a.n, n_pad = a.n_pad;
+  const int n = a.n, n_pad = a.n_pad, nk = a.nk, nk_pad = a.nk_pad;
   const int64_t bs = int64_t(b) * a.h_kept + s;
   const bf16_t* Q = static_cast<const bf16_t*>(a.q) + bs * n_pad * DH;
-  const bf16_t* K = static_cast<const bf16_t*>(a.k) + bs * n_pad * DH;
+  const bf16_t* K = static_cast<const bf16_t*>(a.kk) + bs * nk_pad * DH;
   const float* L = a.lse + bs * n_pad;
   const int kw = k0 + 64 * wave;
 
@@ -417,7 +424,7 @@ attn_colsum_bf16(AttnArgs a) {
   bf16x8 kf[2][DH / 16];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int key = min(kw + 32 * t + col, n_pad - 1);
+    const int key = min(kw + 32 * t + col, nk_pad - 1);
 #pragma unroll
     for (int kk = 0; kk < DH / 16; ++kk)
       kf[t][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(K + int64_t(key) * DH + 16 * kk + 8 * G));
@@ -509,7 +516,7 @@ attn_colsum_bf16(AttnArgs a) {
   for (int t = 0; t < 2; ++t) {
     const float v = xor32_sum((acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]));
     const int key = kw + 32 * t + col;
-    if (G == 0 && key < n) a.colsum[bs * n_pad + key] = v;
+    if (G == 0 && key < nk) a.colsum[bs * n_pad + key] = v;
   }
 }
 
@@ -609,10 +616,19 @@ __global__ void __launch_bounds__(256)
 importance_kernel(AttnArgs a) {
   const int b = blockIdx.y;
   const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j < a.n) {
+  if (a.head_keys) {
+    // per-head pruning: a[b, s, token] += column sum of key j of slot s
+    if (j < a.nk)
+      for (int s = 0; s < a.h_kept; ++s) {
+        const int64_t bs = int64_t(b) * a.h_kept + s;
+        a.a[bs * a.n + a.head_keys[bs * a.nk + j]] += a.colsum[bs * a.n_pad + j];
+      }
+  } else if (j < a.n) {
     float acc = 0.0f;
     for (int s = 0; s < a.h_kept; ++s) acc += a.colsum[(int64_t(b) * a.h_kept + s) * a.n_pad + j];
     a.a[int64_t(b) * a.n + j] += acc;
+  }
+  if (j < a.n) {
     if (a.lse_out)
       for (int s = 0; s < a.h_kept; ++s)
         a.lse_out[(int64_t(b) * a.h_kept + s) * a.n + j] =
@@ -626,8 +642,51 @@ importance_kernel(AttnArgs a) {
   }
 }
 
+// Per-head pruning: the kept tokens of slot s (head_keys[b, s, 0 .. nk-1])
+// gathered from the layer's K [.., n_pad, DH] and V^T [.., DH, n_pad] into
+// the slot's own K [.., nk_pad, DH] and V^T [.., DH, nk_pad] (columns past
+// nk of a gathered 64-key tile are zero). grid (nk / 64, h_kept, batch).
+template <int DH>
+__global__ void __launch_bounds__(256)
+gather_keys_bf16(AttnArgs a) {
+  __shared__ int tok[64];
+  const int j0 = blockIdx.x * 64, s = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t bs = int64_t(b) * a.h_kept + s;
+  if (tid < 64) tok[tid] = j0 + tid < a.nk ? a.head_keys[bs * a.nk + j0 + tid] : -1;
+  __syncthreads();
+  const bf16_t* K = static_cast<const bf16_t*>(a.k) + bs * a.n_pad * DH;
+  const bf16_t* VT = static_cast<const bf16_t*>(a.vt) + bs * DH * a.n_pad;
+  bf16_t* Kc = static_cast<bf16_t*>(const_cast<void*>(a.kk)) + bs * a.nk_pad * DH;
+  bf16_t* VTc = static_cast<bf16_t*>(const_cast<void*>(a.vtk)) + bs * DH * a.nk_pad;
+  for (int c = tid; c < 64 * DH / 8; c += 256) {
+    const int r = c / (DH / 8), c8 = (c % (DH / 8)) * 8;
+    if (tok[r] >= 0)
+      *reinterpret_cast<u32x4*>(Kc + int64_t(j0 + r) * DH + c8) =
+          *reinterpret_cast<const u32x4*>(K + int64_t(tok[r]) * DH + c8);
+  }
+  for (int c = tid; c < DH * 8; c += 256) {
+    const int d = c >> 3, j8 = (c & 7) * 8;
+    bf16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = tok[j8 + e];
+      v[e] = t >= 0 ? VT[int64_t(d) * a.n_pad + t] : bf16_t(0);
+    }
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = uint32_t(v[2 * e]) | (uint32_t(v[2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4*>(VTc + int64_t(d) * a.nk_pad + j0 + j8) = w;
+  }
+}
+
 template <int DH, bool CAUSAL>
 int run_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.head_keys) {
+    const dim3 gk(unsigned(ceil_div(a.nk, 64)), a.h_kept, a.batch);
+    SPATTEN_TIMED("gather_keys", stream, gather_keys_bf16<DH><<<gk, 256, 0, stream>>>(a));
+    SPATTEN_LAUNCH_CHECK();
+  }
   // 32 queries per wave: more resident waves hide the MFMA -> softmax ->
   // MFMA latency chain better than larger per-wave tiles
   constexpr int QB = attn_qblock(DH), NU = 1, MINW = DH == 64 ? 3 : 1;
@@ -640,7 +699,7 @@ int run_bf16(const AttnArgs& a, hipStream_t stream) {
                   (attn_fwd_bf16<DH, CAUSAL, NU, MINW, true><<<g1, 2 * QB / NU, 0, stream>>>(a)));
     SPATTEN_LAUNCH_CHECK();
   }
-  const dim3 g2(xcd_grid(ceil_div(a.n, kAttnKBlock) * a.h_kept * a.batch));
+  const dim3 g2(xcd_grid(ceil_div(a.nk, kAttnKBlock) * a.h_kept * a.batch));
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_bf16<DH, CAUSAL><<<g2, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
   const dim3 g3(unsigned(ceil_div(a.n, 256)), a.batch);

@@ -83,10 +83,16 @@ struct AttnArgs {
   float* gpart;     // [B, h, nqb]
   int nqb, nkb;
   const int32_t* head_idx;
-  float* a;         // [B, n]
+  float* a;         // [B, n], or [B, h, n] with per-head pruning
   float* g;         // [B, H]
   float* lse_out;   // optional [B, h, n] (natural log)
   float v_threshold;  // local value pruning (0 = off)
+  // keys: the layer's tokens (kk = k, vtk = vt, nk = n, nk_pad = n_pad), or
+  // with per-head pruning each slot's gathered kept tokens
+  const int32_t* head_keys;  // [B, h, nk] token of each kept key, or null
+  const void* kk;            // [B, h, nk_pad, dh]
+  const void* vtk;           // [B, h, dh, nk_pad]
+  int nk, nk_pad;
 };
 int launch_attention(const AttnArgs& a, hipStream_t stream);
 

@@ -46,7 +46,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct PrefillWs {
   int64_t n_pad, nqb;
   int64_t nkb;
-  size_t q, k, vt, o, lse, colsum, gpart, total;
+  int64_t nk, nk_pad;  // keys per head (per-head pruning: the kept ones)
+  size_t q, k, vt, o, lse, colsum, gpart, kk, vtk, total;
 };
 
 struct DecodeWs {
@@ -92,7 +93,12 @@ inline PrefillWs prefill_ws(const spatten_layer_desc& d) {
   w.lse = take(B * h * w.n_pad * 4);
   w.colsum = take(B * h * w.n_pad * 4);
   w.gpart = take(B * h * w.nqb * 4);
-  w.nkb = ceil_div(n, kAttnKBlock);
+  const bool per_head = d.per_head != 0;
+  w.nk = per_head ? d.n_keys : n;
+  w.nk_pad = round_up(w.nk, kTokPad);
+  w.kk = take(per_head ? B * h * w.nk_pad * dh * es : 0);
+  w.vtk = take(per_head ? B * h * w.nk_pad * dh * es : 0);
+  w.nkb = ceil_div(w.nk, kAttnKBlock);
   w.total = off;
   return w;
 }

@@ -26,8 +26,9 @@ size_t layer_workspace_bytes(const spatten_layer_desc& d) {
 }
 
 int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, const void* wk,
-                const void* wv, const void* wo, const int32_t* head_idx, const float* a,
-                const float* g, const void* k_cache, const void* v_cache, const uint8_t* k_msb,
+                const void* wv, const void* wo, const int32_t* head_idx,
+                const int32_t* head_keys, const float* a, const float* g,
+                const void* k_cache, const void* v_cache, const uint8_t* k_msb,
                 const uint8_t* k_lsb, const float* k_scale, const uint8_t* v_msb,
                 const uint8_t* v_lsb, const float* v_scale, const void* workspace,
                 const size_t* workspace_bytes) {
@@ -42,7 +43,15 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
   if (int64_t(d->n_heads) * d->head_dim > (1 << 20)) return SPATTEN_EINVAL;
   if (!(d->v_threshold >= 0.0f)) return SPATTEN_EINVAL;  // negative or NaN
   if (d->per_head != 0 && d->per_head != 1) return SPATTEN_EINVAL;
-  if (d->per_head && (d->mode != SPATTEN_DECODE || d->kv_quantized)) return SPATTEN_EUNSUPPORTED;
+  if (d->per_head && d->kv_quantized) return SPATTEN_EUNSUPPORTED;
+  const bool keys_per_head = d->per_head && d->mode == SPATTEN_PREFILL;
+  if (keys_per_head) {
+    if (d->n_keys < 1 || d->n_keys > d->n_tokens) return SPATTEN_EINVAL;
+    if (d->dtype != SPATTEN_BF16 || d->causal || d->v_threshold > 0.0f)
+      return SPATTEN_EUNSUPPORTED;
+  } else if (d->n_keys != 0) {
+    return SPATTEN_EINVAL;
+  }
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return SPATTEN_EUNSUPPORTED;
   if (d->v_threshold > 0.0f && d->kv_quantized) return SPATTEN_EUNSUPPORTED;
   if (d->mode == SPATTEN_PREFILL) {
@@ -63,6 +72,7 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
   if (d->batch == 0) return SPATTEN_OK;
   // tensors
   if (!x || !wq || !wk || !wv || !wo || !head_idx || !a) return SPATTEN_EINVAL;
+  if (bool(head_keys) != keys_per_head || !aligned(head_keys, 4)) return SPATTEN_EINVAL;
   if (d->mode == SPATTEN_PREFILL && !g) return SPATTEN_EINVAL;
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(wk, 16) || !aligned(wv, 16) ||
       !aligned(wo, 16) || !aligned(a, 4) || !aligned(g, 4) || !aligned(head_idx, 4))

@@ -14,8 +14,9 @@ namespace spatten {
 size_t layer_workspace_bytes(const spatten_layer_desc& d);
 
 int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, const void* wk,
-                const void* wv, const void* wo, const int32_t* head_idx, const float* a,
-                const float* g, const void* k_cache, const void* v_cache, const uint8_t* k_msb,
+                const void* wv, const void* wo, const int32_t* head_idx,
+                const int32_t* head_keys, const float* a, const float* g,
+                const void* k_cache, const void* v_cache, const uint8_t* k_msb,
                 const uint8_t* k_lsb, const float* k_scale, const uint8_t* v_msb,
                 const uint8_t* v_lsb, const float* v_scale, const void* workspace,
                 const size_t* workspace_bytes);

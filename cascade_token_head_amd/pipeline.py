@@ -10,11 +10,17 @@ positions are compacted together, so pruned tokens are gone from every
 later layer. When the head count drops, the kept heads are re-ranked by
 cumulative head importance.
 
+Per-head token pruning in prefill ("A. Neural Networks Pruning and
+Quantization", bullet "Token Pruning"): every token keeps its row of x;
+each kept head attends over its own kept tokens and cuts them by its own
+cumulative importance after every layer.
+
 Decode (section II, generation): one token per step against per-layer K/V
 caches; after every layer of step 1 the caches of all layers are pruned to
 the top cache_keep entries by cumulative importance, and with prune_every
 = r > 0 cut back to cache_keep again after every r-th later step. Local
-value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning") is a per-layer option of the attention call.
+value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning")
+is a per-layer option of the attention call.
 """
 from __future__ import annotations
 
@@ -129,6 +135,115 @@ class PrefillStack:
                       self.pbuf[cur_t][: B * nL].view(B, nL),
                       self.hbuf[cur_h][: B * hL].view(B, hL),
                       self.abuf[cur_t][: B * nL].view(B, nL))
+        return self.final
+
+
+class PerHeadPrefillStack:
+    """Prefill stack with per-head token pruning (bf16, bidirectional):
+    every token keeps its row of x through all layers; each kept head slot
+    attends over its own kept tokens, key_keep[l] of them at layer l, and
+    after each layer keeps the top key_keep[l + 1] of them by its own
+    cumulative importance a[b, slot, token]. Heads are cut by cumulative
+    head importance as in PrefillStack; the slot rows of a and of the key
+    lists follow the kept heads."""
+
+    def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, n_tokens: int,
+                 heads, key_keep, weights: List[dict], device="cuda"):
+        assert len(heads) == n_layers and len(key_keep) == n_layers
+        assert all(1 <= m <= n_tokens for m in key_keep)
+        assert all(b <= a for a, b in zip(key_keep, key_keep[1:]))
+        self.L, self.B, self.H, self.dh, self.n = n_layers, batch, n_heads, head_dim, n_tokens
+        self.D = n_heads * head_dim
+        self.heads, self.keep, self.w = list(heads), list(key_keep), weights
+        B, H, n, dev = batch, n_heads, n_tokens, device
+        self.x = torch.empty(B, n, self.D, dtype=torch.bfloat16, device=dev)
+        self.abuf = [torch.zeros(B * H * n, dtype=torch.float32, device=dev) for _ in range(2)]
+        self.kbuf = [torch.empty(B * H * n, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.hbuf = [torch.empty(B * H, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.g = torch.zeros(B, H, dtype=torch.float32, device=dev)
+        self.g_kept = torch.empty(B * H, dtype=torch.float32, device=dev)
+        self.head_sel = torch.empty(B * H, dtype=torch.int32, device=dev)
+        self.key_scores = torch.empty(B * H * n, dtype=torch.float32, device=dev)
+        self.key_sel = torch.empty(B * H * n, dtype=torch.int32, device=dev)
+        self.descs = [S.make_desc(S.PREFILL, S.BF16, False, B, n, H, heads[l], head_dim,
+                                  per_head=True, n_keys=key_keep[l]) for l in range(n_layers)]
+        ws = max(S.workspace_bytes(d) for d in self.descs)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.trace: Optional[list] = None
+
+    def load(self, x: torch.Tensor):
+        """Reset the cascade state and load x [B, n, D]; every head keeps
+        every token at the first layer."""
+        B, H, n = self.B, self.H, self.n
+        self.x.copy_(x.reshape(B, n, self.D))
+        self.abuf[0].zero_()
+        self.g.zero_()
+        dev = self.g.device
+        self.hbuf[0].copy_(torch.arange(H, dtype=torch.int32, device=dev).repeat(B))
+        m = self.keep[0]
+        self.kbuf[0][: B * H * m].copy_(
+            torch.arange(m, dtype=torch.int32, device=dev).repeat(B * H))
+
+    def run(self, record: bool = False, layer_hook=None):
+        """Run all layers; returns (x [B, n, D], heads [B, h_L], keys
+        [B, h_L, m_L], a [B, h_L, n])."""
+        B, n, D = self.B, self.n, self.D
+        cur_a, cur_h, cur_k = 0, 0, 0
+        self.trace = [] if record else None
+        for l in range(self.L):
+            h, m = self.heads[l], self.keep[l]
+            a = self.abuf[cur_a][: B * h * n].view(B, h, n)
+            keys = self.kbuf[cur_k][: B * h * m].view(B, h, m)
+            hidx = self.hbuf[cur_h][: B * h].view(B, h)
+            lse = None
+            if record:
+                lse = torch.empty(B, h, n, dtype=torch.float32, device=self.x.device)
+                rec = {"x_in": self.x.clone(), "a_in": a.clone(), "g_in": self.g.clone(),
+                       "heads": hidx.clone(), "keys": keys.clone()}
+            w = self.w[l]
+            S.layer_forward(self.descs[l], self.x, w["wq"], w["wk"], w["wv"], w["wo"], hidx, a,
+                            self.g, self.ws, lse=lse, head_keys=keys)
+            if record:
+                rec.update({"x_out": self.x.clone(), "a_out": a.clone(),
+                            "g_out": self.g.clone(), "lse": lse, "ws": self.ws.clone()})
+            if l + 1 < self.L:
+                h2, m2 = self.heads[l + 1], self.keep[l + 1]
+                if h2 != h:
+                    gk = self.g_kept[: B * h].view(B, h)
+                    S.compact([(self.g, gk, 4, self.H * 4, h * 4)], hidx, h)
+                    sel = self.head_sel[: B * h2].view(B, h2)
+                    S.topk(gk, h2, out=sel)
+                    hnew = self.hbuf[cur_h ^ 1][: B * h2].view(B, h2)
+                    anew = self.abuf[cur_a ^ 1][: B * h2 * n].view(B, h2, n)
+                    knew = self.kbuf[cur_k ^ 1][: B * h2 * m].view(B, h2, m)
+                    S.compact([(hidx, hnew, 4, h * 4, h2 * 4),
+                               (a, anew, n * 4, h * n * 4, h2 * n * 4),
+                               (keys, knew, m * 4, h * m * 4, h2 * m * 4)], sel, h2)
+                    hidx, a, keys = hnew, anew, knew
+                    cur_h, cur_a, cur_k = cur_h ^ 1, cur_a ^ 1, cur_k ^ 1
+                    if record:
+                        rec["head_sel"] = sel.clone()
+                if m2 != m:
+                    # each slot's importance at its own kept tokens, top m2 of
+                    # those (positions in the key list), then the key list cut
+                    rows = B * h2
+                    sc = self.key_scores[: rows * m].view(rows, m)
+                    S.compact([(a, sc, 4, n * 4, m * 4)], keys.view(rows, m), m)
+                    ksel = self.key_sel[: rows * m2].view(rows, m2)
+                    S.topk(sc, m2, out=ksel)
+                    knew = self.kbuf[cur_k ^ 1][: rows * m2].view(B, h2, m2)
+                    S.compact([(keys, knew, 4, m * 4, m2 * 4)], ksel, m2)
+                    cur_k ^= 1
+                    if record:
+                        rec["key_sel"] = ksel.view(B, h2, m2).clone()
+            if record:
+                self.trace.append(rec)
+            if layer_hook is not None:
+                layer_hook(l)
+        hL, mL = self.heads[-1], self.keep[-1]
+        self.final = (self.x, self.hbuf[cur_h][: B * hL].view(B, hL),
+                      self.kbuf[cur_k][: B * hL * mL].view(B, hL, mL),
+                      self.abuf[cur_a][: B * hL * n].view(B, hL, n))
         return self.final
 
 

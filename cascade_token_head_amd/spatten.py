@@ -40,6 +40,7 @@ class LayerDesc(ctypes.Structure):
         ("cache_len", ctypes.c_int32), ("cache_cap", ctypes.c_int32),
         ("kv_quantized", ctypes.c_int32), ("pq_threshold", ctypes.c_float),
         ("v_threshold", ctypes.c_float), ("per_head", ctypes.c_int32),
+        ("n_keys", ctypes.c_int32),
     ]
 
 
@@ -54,10 +55,10 @@ def _lib():
         lib = ctypes.CDLL(LIB_PATH)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         lib.spatten_layer_forward.restype = ctypes.c_int
-        lib.spatten_layer_forward.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 20 + \
+        lib.spatten_layer_forward.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 21 + \
             [ctypes.POINTER(ctypes.c_size_t), vp]
         lib.spatten_layer_forward_noalloc.restype = ctypes.c_int
-        lib.spatten_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 20
+        lib.spatten_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc)] + [vp] * 21
         lib.spatten_topk.restype = ctypes.c_int
         lib.spatten_topk.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp]
         lib.spatten_compact.restype = ctypes.c_int
@@ -112,17 +113,17 @@ def dtype_code(dt: torch.dtype) -> int:
 
 def make_desc(mode=PREFILL, dtype=BF16, causal=False, batch=1, n_tokens=1, n_heads=1,
               n_heads_kept=None, head_dim=64, cache_len=0, cache_cap=0, kv_quantized=False,
-              pq_threshold=0.0, v_threshold=0.0, per_head=False) -> LayerDesc:
+              pq_threshold=0.0, v_threshold=0.0, per_head=False, n_keys=0) -> LayerDesc:
     return LayerDesc(mode, dtype, int(causal), batch, n_tokens, n_heads,
                      n_heads if n_heads_kept is None else n_heads_kept, head_dim, cache_len,
                      cache_cap, int(kv_quantized), float(pq_threshold), float(v_threshold),
-                     int(per_head))
+                     int(per_head), int(n_keys))
 
 
 def workspace_bytes(desc: LayerDesc) -> int:
     """Workspace size the library needs for `desc` (query mode)."""
     nb = ctypes.c_size_t(0)
-    st = _lib().spatten_layer_forward(ctypes.byref(desc), *([None] * 20), ctypes.byref(nb), None)
+    st = _lib().spatten_layer_forward(ctypes.byref(desc), *([None] * 21), ctypes.byref(nb), None)
     _check("spatten_layer_forward(query)", st)
     return nb.value
 
@@ -130,10 +131,11 @@ def workspace_bytes(desc: LayerDesc) -> int:
 def layer_forward(desc: LayerDesc, x, wq, wk, wv, wo, head_idx, a, g, workspace,
                   k_cache=None, v_cache=None, k_msb=None, k_lsb=None, k_scale=None,
                   v_msb=None, v_lsb=None, v_scale=None, recompute=None, v_kept=None, lse=None,
-                  stream=None):
+                  head_keys=None, stream=None):
     nb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     st = _lib().spatten_layer_forward(
-        ctypes.byref(desc), _p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(head_idx), _p(a), _p(g),
+        ctypes.byref(desc), _p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(head_idx), _p(head_keys),
+        _p(a), _p(g),
         _p(k_cache), _p(v_cache), _p(k_msb), _p(k_lsb), _p(k_scale), _p(v_msb), _p(v_lsb),
         _p(v_scale), _p(recompute), _p(v_kept), _p(lse), _p(workspace), ctypes.byref(nb),
         _stream(stream))
@@ -143,10 +145,11 @@ def layer_forward(desc: LayerDesc, x, wq, wk, wv, wo, head_idx, a, g, workspace,
 def layer_forward_noalloc(desc: LayerDesc, x, wq, wk, wv, wo, head_idx, a, g,
                           k_cache=None, v_cache=None, k_msb=None, k_lsb=None, k_scale=None,
                           v_msb=None, v_lsb=None, v_scale=None, recompute=None, v_kept=None,
-                          lse=None, stream=None):
+                          lse=None, head_keys=None, stream=None):
     """layer_forward in the library's fixed per-device scratch (no workspace)."""
     st = _lib().spatten_layer_forward_noalloc(
-        ctypes.byref(desc), _p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(head_idx), _p(a), _p(g),
+        ctypes.byref(desc), _p(x), _p(wq), _p(wk), _p(wv), _p(wo), _p(head_idx), _p(head_keys),
+        _p(a), _p(g),
         _p(k_cache), _p(v_cache), _p(k_msb), _p(k_lsb), _p(k_scale), _p(v_msb), _p(v_lsb),
         _p(v_scale), _p(recompute), _p(v_kept), _p(lse), _stream(stream))
     _check("spatten_layer_forward_noalloc", st)

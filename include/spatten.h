@@ -61,7 +61,9 @@ typedef struct {
   int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
   float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
   float v_threshold;     /* decode, unquantized: local value pruning threshold (0 = off) */
-  int32_t per_head;      /* decode, unquantized: 1 = per-head importance, a is [B, H, cache_cap] */
+  int32_t per_head;      /* 1 = per-head token pruning (decode, unquantized: a is [B, H, cache_cap];
+                            prefill, bf16 bidirectional: see n_keys) */
+  int32_t n_keys;        /* prefill with per_head: tokens each kept head keeps as keys and values */
 } spatten_layer_desc;
 
 /*
@@ -108,7 +110,16 @@ typedef struct {
  *   with spatten_compact_inplace on the head's 128-byte slice of each row).
  *   g is not used in decode and may be NULL. Decode needs head_dim 64,
  *   H <= 32, bf16 and every head kept.
+ *   Per-head token pruning in prefill (per_head = 1; bf16, bidirectional;
+ *   section "A. Neural Networks Pruning and Quantization", bullet "Token
+ *   Pruning"): kept head slot s of sequence b attends over its own kept
+ *   tokens head_keys[b, s, 0 .. n_keys-1] (strictly ascending indices into
+ *   the layer's n_tokens tokens) as keys and values, while every token
+ *   queries every kept head, so x keeps all n_tokens rows; a is [B, h_kept,
+ *   n_tokens] and a[b, s, t] takes slot s's probabilities only (its kept
+ *   tokens' column sums). 1 <= n_keys <= n_tokens.
  * head_idx: [B, h_kept] int32, strictly ascending head ids per sequence.
+ * head_keys: per-head pruning in prefill only (else NULL), as above.
  * workspace: device scratch of *workspace_bytes bytes, 256-byte aligned;
  *   its contents are overwritten by every call, so calls that share one
  *   workspace must be ordered on one stream (or otherwise serialised).
@@ -123,7 +134,7 @@ typedef struct {
  */
 int spatten_layer_forward(const spatten_layer_desc* d, void* x,
                           const void* wq, const void* wk, const void* wv, const void* wo,
-                          const int32_t* head_idx, float* a, float* g,
+                          const int32_t* head_idx, const int32_t* head_keys, float* a, float* g,
                           void* k_cache, void* v_cache,
                           uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
                           uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,
@@ -148,7 +159,8 @@ int spatten_layer_forward(const spatten_layer_desc* d, void* x,
 #define SPATTEN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int spatten_layer_forward_noalloc(const spatten_layer_desc* d, void* x,
                                   const void* wq, const void* wk, const void* wv, const void* wo,
-                                  const int32_t* head_idx, float* a, float* g,
+                                  const int32_t* head_idx, const int32_t* head_keys, float* a,
+                                  float* g,
                                   void* k_cache, void* v_cache,
                                   uint8_t* k_msb, uint8_t* k_lsb, float* k_scale,
                                   uint8_t* v_msb, uint8_t* v_lsb, float* v_scale,

@@ -33,12 +33,12 @@ int main() {
   size_t got = need;
   const int32_t* hi = reinterpret_cast<const int32_t*>(P);
   const float* fp = reinterpret_cast<const float*>(P);
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, fp, nullptr, nullptr, nullptr, nullptr, nullptr,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, fp, nullptr, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, P, &got), SPATTEN_OK);
   got = need - 1;
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, fp, nullptr, nullptr, nullptr, nullptr, nullptr,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, fp, nullptr, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, P, &got), SPATTEN_EWORKSPACE);
-  EXPECT(check_layer(nullptr, P, P, P, P, P, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+  EXPECT(check_layer(nullptr, P, P, P, P, P, hi, nullptr, fp, fp, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);
   // extreme sizes must not overflow the workspace arithmetic
   d.batch = 1 << 30;
@@ -46,7 +46,7 @@ int main() {
   got = 0;
   EXPECT(check_layer(&d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, &got), SPATTEN_OK);
+                     nullptr, nullptr, &got), SPATTEN_OK);
   d.batch = 2;
   d.n_tokens = 100;
   // decode
@@ -60,28 +60,62 @@ int main() {
   need = layer_workspace_bytes(d);
   got = need;
   const uint8_t* u8 = reinterpret_cast<const uint8_t*>(P);
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_OK);
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, nullptr, u8, u8, fp, u8, u8, fp, P,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, P, nullptr, u8, u8, fp, u8, u8, fp, P,
                      &got), SPATTEN_EINVAL);
   d.cache_cap = 2048;
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_EINVAL);
   // local value pruning: not with quantized caches; NaN and negative rejected
   d.cache_cap = 2049;
   d.v_threshold = 1e-4f;
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_EUNSUPPORTED);
   d.kv_quantized = 0;
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, P, &got), SPATTEN_OK);
   d.v_threshold = -1e-4f;
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, P, &got), SPATTEN_EINVAL);
   d.v_threshold = __builtin_nanf("");
-  EXPECT(check_layer(&d, P, P, P, P, P, hi, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, P, &got), SPATTEN_EINVAL);
   d.v_threshold = 0.0f;
+  // per-head token pruning in prefill: bf16 bidirectional, 1 <= n_keys <= n_tokens,
+  // head_keys given exactly then
+  d.mode = SPATTEN_PREFILL;
+  d.n_tokens = 300;
+  d.cache_len = d.cache_cap = 0;
+  d.per_head = 1;
+  d.n_keys = 120;
+  need = layer_workspace_bytes(d);
+  got = need;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_OK);
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);
+  d.n_keys = 301;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);
+  d.n_keys = 0;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);
+  d.n_keys = 120;
+  d.causal = 1;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EUNSUPPORTED);
+  d.causal = 0;
+  d.dtype = SPATTEN_F32;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EUNSUPPORTED);
+  d.dtype = SPATTEN_BF16;
+  d.per_head = 0;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);  // n_keys set
+  d.n_keys = 0;
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, hi, fp, fp, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, nullptr, P, &got), SPATTEN_EINVAL);  // stray keys
   // representative-token selection
   {
     size_t need_a = ada_ws(4, 512).total, got_a = need_a;

@@ -68,8 +68,9 @@ FAKE = 1 << 20   # 256-aligned fake address: the validator never dereferences
 
 def _call_layer(S, desc, ws_bytes, **kw):
     vp = ctypes.c_void_p
-    names = ["x", "wq", "wk", "wv", "wo", "head_idx", "a", "g", "k_cache", "v_cache", "k_msb",
-             "k_lsb", "k_scale", "v_msb", "v_lsb", "v_scale", "recompute", "v_kept", "lse"]
+    names = ["x", "wq", "wk", "wv", "wo", "head_idx", "head_keys", "a", "g", "k_cache", "v_cache",
+             "k_msb", "k_lsb", "k_scale", "v_msb", "v_lsb", "v_scale", "recompute", "v_kept",
+             "lse"]
     args = [vp(kw[n]) if kw.get(n) else None for n in names]
     nb = ctypes.c_size_t(ws_bytes)
     return S.load().spatten_layer_forward(ctypes.byref(desc), *args, vp(kw.get("ws", FAKE)),
@@ -106,6 +107,28 @@ def test_layer_rejects_small_workspace_and_nulls(S):
     assert _call_layer(S, desc, need, ws=FAKE + 16, **_prefill_ptrs()) == S.EINVAL
 
 
+def test_prefill_per_head_pruning_rejections(S):
+    """Per-head token pruning in prefill: bf16 bidirectional only, with
+    1 <= n_keys <= n_tokens and the head_keys array given exactly then."""
+    ok = S.make_desc(S.PREFILL, S.BF16, False, 2, 300, 12, 8, 64, per_head=True, n_keys=120)
+    ptrs = dict(_prefill_ptrs(), head_keys=FAKE)
+    # a valid call would launch; the size query stops after the descriptor
+    assert _call_layer(S, ok, 0, ws=0) == S.OK
+    assert S.workspace_bytes(ok) > S.workspace_bytes(
+        S.make_desc(S.PREFILL, S.BF16, False, 2, 300, 12, 8, 64))
+    assert _call_layer(S, ok, 1 << 40, **_prefill_ptrs()) == S.EINVAL
+    for field, value, code in (("n_keys", 0, S.EINVAL), ("n_keys", 301, S.EINVAL),
+                               ("causal", 1, S.EUNSUPPORTED), ("dtype", S.F32, S.EUNSUPPORTED),
+                               ("v_threshold", 1e-3, S.EUNSUPPORTED)):
+        d = S.make_desc(S.PREFILL, S.BF16, False, 2, 300, 12, 8, 64, per_head=True, n_keys=120)
+        setattr(d, field, value)
+        assert _call_layer(S, d, 1 << 40, **ptrs) == code, field
+    plain = S.make_desc(S.PREFILL, S.BF16, False, 2, 300, 12, 8, 64)
+    assert _call_layer(S, plain, 1 << 40, **ptrs) == S.EINVAL
+    plain.n_keys = 5
+    assert _call_layer(S, plain, 1 << 40, **_prefill_ptrs()) == S.EINVAL
+
+
 def test_decode_rejections(S):
     base = dict(mode=S.DECODE, dtype=S.BF16, causal=False, batch=2, n_tokens=1, n_heads=12,
                 n_heads_kept=12, head_dim=64, cache_len=10, cache_cap=11)
@@ -129,13 +152,18 @@ def test_decode_rejections(S):
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, v_threshold=1e-3)
     assert S.workspace_bytes(d) == S.workspace_bytes(
         S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64))
-    # per-head importance: a flag, for unquantized decode only
+    # per-head importance: a flag, not with quantized caches; in prefill it
+    # also needs the kept key count (bidirectional only)
     d = S.make_desc(**base)
     d.per_head = 2
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(**{**base, "per_head": True, "kv_quantized": True, "pq_threshold": 0.1})
     assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
+    d = S.make_desc(**{**base, "per_head": True, "n_keys": 5})
+    assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, per_head=True)
+    assert _call_layer(S, d, 1 << 40, **_prefill_ptrs()) == S.EINVAL
+    d = S.make_desc(S.PREFILL, S.BF16, True, 2, 100, 12, 12, 64, per_head=True, n_keys=50)
     assert _call_layer(S, d, 1 << 40, **_prefill_ptrs()) == S.EUNSUPPORTED
 
 
@@ -209,10 +237,10 @@ def test_noalloc_rejects_oversized_and_malformed_calls_on_the_host(S):
     lib = S.load()
     big = S.make_desc(S.PREFILL, S.BF16, False, 32, 512, 12, 12, 64)
     assert S.workspace_bytes(big) > S.NOALLOC_SCRATCH_BYTES
-    args = [ctypes.byref(big)] + [None] * 20
+    args = [ctypes.byref(big)] + [None] * 21
     assert lib.spatten_layer_forward_noalloc(*args) == S.EWORKSPACE
     bad = S.make_desc(S.PREFILL, S.BF16, False, 2, 64, 12, 13, 64)   # more kept heads than H
-    assert lib.spatten_layer_forward_noalloc(ctypes.byref(bad), *([None] * 20)) == S.EINVAL
+    assert lib.spatten_layer_forward_noalloc(ctypes.byref(bad), *([None] * 21)) == S.EINVAL
     dec = S.make_desc(S.DECODE, S.BF16, False, 64, 1, 12, 12, 64, 1024, 1056)
     assert S.workspace_bytes(dec) <= S.NOALLOC_SCRATCH_BYTES
     with open(HEADER) as f:

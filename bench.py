@@ -65,6 +65,11 @@ def _cache_lengths(cfg):
     return out
 
 
+def _keys(cfg, l):
+    """Keys each head attends over at prefill layer l."""
+    return cfg.key_keep[l] if cfg.key_keep else cfg.tokens[l]
+
+
 def _kernel_work(cfg, v_kept=None, recompute_frac=None):
     """Algorithmic work per kernel name for one step: (flops, bytes).
     v_kept[s][l]: V rows read at step s, layer l (value pruning);
@@ -82,11 +87,19 @@ def _kernel_work(cfg, v_kept=None, recompute_frac=None):
     if cfg.kind == "prefill":
         for l in range(cfg.n_layers):
             n, h = cfg.tokens[l], cfg.heads[l]
-            pairs = n * (n + 1) / 2 if cfg.causal else float(n) * n
-            add("qkv_gemm", 2.0 * B * n * 3 * h * dh * D, es * (B * n * D + 3 * h * dh * D + 3 * B * n * h * dh))
-            add("out_gemm", 2.0 * B * n * D * h * dh, es * (B * n * h * dh + D * h * dh + 2 * B * n * D))
-            add("attn_fwd", 4.0 * B * h * dh * pairs, es * 4 * B * h * n * dh)
-            add("attn_colsum", 2.0 * B * h * dh * pairs, es * 2 * B * h * n * dh + 4 * B * h * n)
+            m = _keys(cfg, l)
+            pairs = n * (n + 1) / 2 if cfg.causal else float(n) * m
+            add("qkv_gemm", 2.0 * B * n * 3 * h * dh * D,
+                es * (B * n * D + 3 * h * dh * D + 3 * B * n * h * dh))
+            add("out_gemm", 2.0 * B * n * D * h * dh,
+                es * (B * n * h * dh + D * h * dh + 2 * B * n * D))
+            # Q and O per query, K and V per key
+            add("attn_fwd", 4.0 * B * h * dh * pairs, es * 2 * B * h * (n + m) * dh)
+            add("attn_colsum", 2.0 * B * h * dh * pairs,
+                es * B * h * (n + m) * dh + 4 * B * h * m)
+            if cfg.key_keep:
+                # each head's kept K rows and V columns, read and written
+                add("gather_keys", 0.0, es * 4 * B * h * m * dh)
     else:
         for s, lc in enumerate(_cache_lengths(cfg)):
             for l in range(cfg.n_layers):
@@ -207,7 +220,7 @@ def _cpu_baseline(cfg, inputs, budget_s: float):
 
 
 ATTN_KERNELS = {
-    "prefill": ("attn_fwd", "attn_colsum", "importance"),
+    "prefill": ("gather_keys", "attn_fwd", "attn_fwd_vprune", "attn_colsum", "importance"),
     "decode": ("decode_attn", "pq_attn", "decode_vrow", "decode_scores", "decode_vprune",
                "decode_vsum", "decode_importance"),
 }
@@ -224,11 +237,11 @@ def _attention_roof(cfg, ktimes, work, steps):
         alg = 0.0
         for l in range(cfg.n_layers):
             n, h = cfg.tokens[l], cfg.heads[l]
-            pairs = n * (n + 1) / 2 if cfg.causal else float(n) * n
+            pairs = n * (n + 1) / 2 if cfg.causal else float(n) * _keys(cfg, l)
             alg += 4.0 * B * h * dh * pairs
         # the column-sum pass recomputes Q K^T: 6 instead of 4 flops per
-        # (pair, dim)
-        executed = 1.5 * alg
+        # (pair, dim); value pruning runs the forward pass twice (8)
+        executed = (2.0 if cfg.v_threshold > 0 else 1.5) * alg
         a = alg / (ms / 1e3) / 1e12
         e = executed / (ms / 1e3) / 1e12
         return {"kernels": names, "ms_per_step": round(ms, 4), "bound": "mfma", "unit": "TFLOP/s",
@@ -266,8 +279,14 @@ def measure(cfg, args, lib, with_cpu: bool) -> dict:
     w = pipeline.weights_to_device(inputs["layers"], dtype)
 
     if cfg.kind == "prefill":
-        stack = pipeline.PrefillStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim,
-                                      cfg.tokens, cfg.heads, dtype, cfg.causal, w)
+        if cfg.key_keep:
+            stack = pipeline.PerHeadPrefillStack(cfg.n_layers, cfg.batch, cfg.n_heads,
+                                                 cfg.head_dim, cfg.tokens[0], cfg.heads,
+                                                 cfg.key_keep, w)
+        else:
+            stack = pipeline.PrefillStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim,
+                                          cfg.tokens, cfg.heads, dtype, cfg.causal, w,
+                                          v_threshold=cfg.v_threshold)
         x0 = torch.from_numpy(inputs["x"]).to(dtype).cuda()
 
         def reset():
@@ -444,6 +463,10 @@ def measure(cfg, args, lib, with_cpu: bool) -> dict:
                 "layers": cfg.n_layers, "heads": cfg.n_heads, "head_dim": cfg.head_dim,
                 "tokens_per_layer": list(cfg.tokens), "heads_per_layer": list(cfg.heads),
                 "causal": cfg.causal}
+        if cfg.key_keep:
+            conf["keys_per_head_per_layer"] = list(cfg.key_keep)
+        if cfg.v_threshold > 0:
+            conf["v_threshold"] = cfg.v_threshold
     else:
         conf = {"workload": cfg.name, "batch": cfg.batch, "cache_len": cfg.cache_len,
                 "cache_keep": cfg.cache_keep, "decode_steps": cfg.steps, "layers": cfg.n_layers,
@@ -572,7 +595,7 @@ def measure_ada(cfg, args, lib, with_cpu: bool) -> dict:
 
 
 HEADLINE = "long_causal"
-OTHERS = ("bert_base", "gpt2_decode", "pq_decode", "ada_gpt2", "ada_long")
+OTHERS = ("bert_base", "bert_base_perhead", "gpt2_decode", "pq_decode", "ada_gpt2", "ada_long")
 
 
 def main():
@@ -582,7 +605,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=None,
                     help="measure only this workload (default: long_causal as the headline, "
-                         "plus bert_base, gpt2_decode and pq_decode)")
+                         "plus " + ", ".join(OTHERS) + ")")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--graph", action="store_true",

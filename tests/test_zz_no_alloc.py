@@ -11,6 +11,7 @@ from cascade_token_head_amd import pipeline
 from cascade_token_head_amd import spatten as S
 from workloads import BERT_BASE, GPT2_DECODE, PQ_DECODE, make_decode_inputs, make_prefill_inputs
 from workloads import scaled
+from workloads.configs import BERT_BASE_PERHEAD
 
 pytestmark = pytest.mark.gpu
 
@@ -20,16 +21,27 @@ def _prefill_pair(cfg, noalloc):
     w = pipeline.weights_to_device(inp["layers"][:1], torch.bfloat16)[0]
     B, n, H, dh = cfg.batch, cfg.tokens[0], cfg.n_heads, cfg.head_dim
     x = torch.from_numpy(inp["x"]).to(torch.bfloat16).cuda()
-    a = torch.linspace(0, 1, B * n, device="cuda").reshape(B, n).contiguous()
+    ashape = (B, H, n) if cfg.per_head else (B, n)
+    a = torch.linspace(0, 1, int(np.prod(ashape)), device="cuda").reshape(ashape).contiguous()
     g = torch.ones(B, H, device="cuda")
     hidx = torch.arange(H, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
     lse = torch.empty(B, H, n, device="cuda")
-    desc = S.make_desc(S.PREFILL, S.BF16, cfg.causal, B, n, H, H, dh)
+    keys, m = None, 0
+    if cfg.per_head:
+        m = cfg.key_keep[0]
+        rng = np.random.default_rng(n)
+        keys = torch.from_numpy(np.stack([np.sort(rng.choice(n, m, replace=False))
+                                          for _ in range(B * H)]).astype(np.int32))
+        keys = keys.reshape(B, H, m).cuda()
+    desc = S.make_desc(S.PREFILL, S.BF16, cfg.causal, B, n, H, H, dh,
+                       v_threshold=cfg.v_threshold, per_head=cfg.per_head, n_keys=m)
     if noalloc:
-        S.layer_forward_noalloc(desc, x, w["wq"], w["wk"], w["wv"], w["wo"], hidx, a, g, lse=lse)
+        S.layer_forward_noalloc(desc, x, w["wq"], w["wk"], w["wv"], w["wo"], hidx, a, g, lse=lse,
+                                head_keys=keys)
     else:
         ws = torch.empty(S.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
-        S.layer_forward(desc, x, w["wq"], w["wk"], w["wv"], w["wo"], hidx, a, g, ws, lse=lse)
+        S.layer_forward(desc, x, w["wq"], w["wk"], w["wv"], w["wo"], hidx, a, g, ws, lse=lse,
+                        head_keys=keys)
     torch.cuda.synchronize()
     return [t.cpu() for t in (x, a, g, lse)]
 
@@ -87,6 +99,12 @@ CASES = [
     ("prefill_causal", scaled(BERT_BASE, batch=2, n_layers=1, tokens=(500,), heads=(12,),
                               causal=True),
      scaled(BERT_BASE, batch=1, n_layers=1, tokens=(130,), heads=(12,), causal=True)),
+    ("prefill_vprune", scaled(BERT_BASE, batch=3, n_layers=1, tokens=(260,), heads=(12,),
+                              v_threshold=1e-3),
+     scaled(BERT_BASE, batch=2, n_layers=1, tokens=(64,), heads=(12,), v_threshold=1e-3)),
+    ("prefill_perhead", scaled(BERT_BASE_PERHEAD, batch=3, n_layers=1, tokens=(300,),
+                               heads=(12,), key_keep=(140,)),
+     scaled(BERT_BASE_PERHEAD, batch=2, n_layers=1, tokens=(90,), heads=(12,), key_keep=(33,))),
     ("decode", scaled(GPT2_DECODE, batch=8, n_layers=1, cache_len=700, steps=1),
      scaled(GPT2_DECODE, batch=3, n_layers=1, cache_len=90, steps=1)),
     ("decode_pq", scaled(PQ_DECODE, batch=4, n_layers=1, cache_len=900, steps=1),

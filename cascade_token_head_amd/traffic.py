@@ -3,11 +3,14 @@
     # a plain device-to-device copy of known size, for the counter scale
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o copy_fetch -- \\
         python3 -m cascade_token_head_amd.traffic copy --mib 1024
-    # the same with WRITE_SIZE, then both counters on the benchmark command
+    # the same with WRITE_SIZE; the same pair on a second known-traffic
+    # kernel (`triad`, c = a + b) to cross-check the scales; then both
+    # counters on the benchmark command
     python3 -m cascade_token_head_amd.traffic summarize --label qkv_gemm \\
         --workload bert_base --kernel-regex 'gemm_tile_kernel<0,' \\
         --fetch run_fetch.csv --write run_write.csv \\
         --copy-fetch copy_fetch.csv --copy-write copy_write.csv \\
+        --triad-fetch triad_fetch.csv --triad-write triad_write.csv \\
         --command '...' --out profiles/
 
 The mfma subcommand reads SQ_INSTS_MFMA (wave-level MFMA instructions per
@@ -44,6 +47,7 @@ COPY_KERNEL = r"copyBuffer"
 KERNEL_SOURCE = {
     "qkv_gemm": "gemm.hip", "out_gemm": "gemm.hip",
     "attn_fwd": "attn.hip", "attn_colsum": "attn.hip", "importance": "attn.hip",
+    "attn_fwd_vprune": "attn.hip", "gather_keys": "attn.hip",
     "decode_attn": "decode.hip", "pq_attn": "decode.hip", "decode_vrow": "decode.hip",
     "decode_scores": "decode.hip", "decode_vprune": "decode.hip", "decode_vsum": "decode.hip",
     "decode_importance": "decode.hip",
@@ -93,18 +97,48 @@ def copy_main(mib: int) -> None:
     print(json.dumps({"copy_bytes": n, "copies": 3}))
 
 
+def triad_main(mib: int) -> None:
+    """c = a + b over fp32 vectors of `mib` MiB each: a second kernel of
+    known traffic (2 x mib read, mib written per dispatch)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.ones(n, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.add(a, b, out=c)
+    torch.cuda.synchronize()
+    print(json.dumps({"triad_bytes_each": n * 4, "dispatches": 3}))
+
+
+TRIAD_KERNEL = r"CUDAFunctor_add|AddFunctor|add_kernel"
+
+
+def _scale(path, counter, regex, expected):
+    """known bytes / counted bytes over the dispatches that carry the bulk
+    (at least half the expected bytes; fills and small copies excluded)."""
+    vals = per_dispatch(path, counter, regex)
+    big = [v for v in vals.values() if v * 1024 > 0.5 * expected]
+    if not big:
+        sys.exit("no %s dispatch of the expected size in %s" % (counter, path))
+    return expected / (sum(big) / len(big) * 1024)
+
+
 def summarize_main(a) -> None:
     copy_bytes = a.copy_mib * (1 << 20)
-    cf = per_dispatch(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
-    cw = per_dispatch(a.copy_write, "WRITE_SIZE", COPY_KERNEL)
-    # the copy kernel moves copy_bytes in and out per dispatch; take the
-    # dispatches that carry the bulk (fills and small copies excluded)
-    big_f = [v for v in cf.values() if v * 1024 > 0.5 * copy_bytes]
-    big_w = [v for v in cw.values() if v * 1024 > 0.5 * copy_bytes]
-    if not big_f or not big_w:
-        sys.exit("no copy dispatch of the expected size in the calibration runs")
-    f_scale = copy_bytes / (sum(big_f) / len(big_f) * 1024)
-    w_scale = copy_bytes / (sum(big_w) / len(big_w) * 1024)
+    # the copy kernel moves copy_bytes in and out per dispatch
+    f_scale = _scale(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL, copy_bytes)
+    w_scale = _scale(a.copy_write, "WRITE_SIZE", COPY_KERNEL, copy_bytes)
+    check = None
+    if a.triad_fetch and a.triad_write:
+        # a second known-traffic kernel: the scales must agree
+        tb = a.triad_mib * (1 << 20)
+        tf = _scale(a.triad_fetch, "FETCH_SIZE", TRIAD_KERNEL, 2 * tb)
+        tw = _scale(a.triad_write, "WRITE_SIZE", TRIAD_KERNEL, tb)
+        check = {"triad_fetch_scale": round(tf, 4), "triad_write_scale": round(tw, 4),
+                 "fetch_scale_rel_diff": round(abs(tf - f_scale) / f_scale, 4),
+                 "write_scale_rel_diff": round(abs(tw - w_scale) / w_scale, 4)}
     kf = per_dispatch(a.fetch, "FETCH_SIZE", a.kernel_regex)
     kw = per_dispatch(a.write, "WRITE_SIZE", a.kernel_regex)
     if not kf or not kw:
@@ -116,7 +150,8 @@ def summarize_main(a) -> None:
            "write_bytes_per_launch": round(write),
            "hbm_bytes_per_launch": round(fetch + write),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-           "copy_bytes": copy_bytes, "source_sha1": source_sha1(a.label), "command": a.command}
+           "copy_bytes": copy_bytes, "calibration_check": check,
+           "source_sha1": source_sha1(a.label), "command": a.command}
     os.makedirs(a.out, exist_ok=True)
     base = os.path.join(a.out, "pmc_%s_%s" % (a.label, a.workload))
     with open(base + ".json", "w") as f:
@@ -131,6 +166,12 @@ def summarize_main(a) -> None:
         for k in ("dispatches", "fetch_bytes_per_launch", "write_bytes_per_launch",
                   "hbm_bytes_per_launch", "fetch_scale", "write_scale"):
             f.write("| %s | %s |\n" % (k, rec[k]))
+        if check:
+            f.write("\nCalibration cross-check with a second kernel of known traffic "
+                    "(c = a + b, %d MiB per vector: 2x read, 1x written):\n\n"
+                    "| quantity | value |\n|---|---|\n" % a.triad_mib)
+            for k, v in check.items():
+                f.write("| %s | %s |\n" % (k, v))
         f.write("\nkernel symbol regex: `%s`\n\nsource sha1: `%s`\n\ncommand:\n\n```\n%s\n```\n"
                 % (a.kernel_regex, rec["source_sha1"], a.command))
     print(json.dumps(rec))
@@ -182,11 +223,43 @@ def mfma_main(a) -> None:
     print(json.dumps(rec))
 
 
+def trace_main(a) -> None:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: the
+    kernels by share of GPU time, with the command that produced it."""
+    rows = list(csv.DictReader(open(a.stats, newline="")))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    os.makedirs(a.out, exist_ok=True)
+    path = os.path.join(a.out, "%s_%s_kernel_trace.md" % (a.label, a.workload))
+    with open(path, "w") as f:
+        f.write("# Kernel trace: %s workload (dominant kernel %s)\n\n" % (a.workload, a.label))
+        f.write("rocprofv3 kernel-trace statistics: every dispatch of the command (the "
+                "warm-up, timed and instrumented passes bench.py runs).\n\nCommand:\n\n"
+                "```\n%s\n```\n\n" % a.command)
+        f.write("| kernel | calls | avg us | min us | max us | share |\n|---|---|---|---|---|---|\n")
+        for r in rows[: a.top]:
+            name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+            f.write("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |\n" % (
+                name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+        f.write("\nsource sha1 of %s: `%s`\n" % (a.label, source_sha1(a.label)))
+    print(path)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
+    t = sub.add_parser("triad")
+    t.add_argument("--mib", type=int, default=512)
+    tr = sub.add_parser("trace")
+    tr.add_argument("--label", required=True)
+    tr.add_argument("--workload", required=True)
+    tr.add_argument("--stats", required=True)
+    tr.add_argument("--top", type=int, default=12)
+    tr.add_argument("--command", default="")
+    tr.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     s = sub.add_parser("summarize")
     s.add_argument("--label", required=True)
     s.add_argument("--workload", required=True)
@@ -196,6 +269,9 @@ def main() -> None:
     s.add_argument("--copy-fetch", required=True)
     s.add_argument("--copy-write", required=True)
     s.add_argument("--copy-mib", type=int, default=1024)
+    s.add_argument("--triad-fetch", default=None)
+    s.add_argument("--triad-write", default=None)
+    s.add_argument("--triad-mib", type=int, default=512)
     s.add_argument("--command", default="")
     s.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     m = sub.add_parser("mfma")
@@ -210,6 +286,10 @@ def main() -> None:
     a = ap.parse_args()
     if a.cmd == "copy":
         copy_main(a.mib)
+    elif a.cmd == "triad":
+        triad_main(a.mib)
+    elif a.cmd == "trace":
+        trace_main(a)
     elif a.cmd == "mfma":
         mfma_main(a)
     else:

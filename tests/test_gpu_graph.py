@@ -123,3 +123,49 @@ def test_decode_pass_graph_replays_match_eager(name):
     assert np.isfinite(outs.float().cpu().numpy()).all()
     g = _capture(pass_, reset)
     _replays_match(g, reset, outputs, ref)
+
+
+def test_perhead_prefill_graph_replays_match_eager():
+    """Per-head token pruning in prefill: the head cut, each slot's key cut
+    and the layer calls of a whole pass replay from one graph."""
+    from workloads.configs import BERT_BASE_PERHEAD
+    cfg = scaled(BERT_BASE_PERHEAD, batch=3, n_layers=4, n_heads=6, tokens=(300,) * 4,
+                 heads=(6, 6, 4, 4), key_keep=(300, 200, 120, 120))
+    print("graph per-head prefill", flush=True)
+    inputs = make_prefill_inputs(cfg)
+    w = pipeline.weights_to_device(inputs["layers"], torch.bfloat16)
+    st = pipeline.PerHeadPrefillStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim,
+                                      cfg.tokens[0], cfg.heads, cfg.key_keep, w)
+    x0 = torch.from_numpy(inputs["x"]).to(torch.bfloat16).cuda()
+    st.load(x0)
+    st.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in st.final] + [st.g.clone()]
+    g = _capture(st.run, lambda: st.load(x0))
+    _replays_match(g, lambda: st.load(x0), lambda: list(st.final) + [st.g], ref)
+
+
+def test_selection_stack_graph_replays_match_eager():
+    """Page-5 representative selection over a stack of layers (full Gram
+    product at layer 1, cascade steps after) replays from one graph."""
+    from workloads import ada_batch_layers
+    from workloads.configs import ADA_SMALL
+    cfg = scaled(ADA_SMALL, batch=3, seq_len=300, dim=64, n_layers=4)
+    print("graph selection", flush=True)
+    layers = [torch.from_numpy(x).cuda() for x in ada_batch_layers(cfg)]
+    st = pipeline.AdaStack(cfg.n_layers, cfg.batch, cfg.seq_len, cfg.dim, cfg.tau)
+
+    def reset():
+        st.flags.zero_()
+        st.counts.zero_()
+
+    def pass_():
+        st.run(layers)
+
+    reset()
+    pass_()
+    torch.cuda.synchronize()
+    ref = [st.flags.clone(), st.maxcos.clone(), st.counts.clone()]
+    assert 0 < int(ref[2][:, :, 0].min()) < cfg.seq_len
+    g = _capture(pass_, reset)
+    _replays_match(g, reset, lambda: [st.flags, st.maxcos, st.counts], ref)

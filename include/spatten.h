@@ -120,6 +120,9 @@ typedef struct {
  *   tokens' column sums). 1 <= n_keys <= n_tokens.
  * head_idx: [B, h_kept] int32, strictly ascending head ids per sequence.
  * head_keys: per-head pruning in prefill only (else NULL), as above.
+ *   Device index arrays are not read on the host: ids or token indices
+ *   outside their ranges are not detected and make the call's reads and
+ *   writes undefined.
  * workspace: device scratch of *workspace_bytes bytes, 256-byte aligned;
  *   its contents are overwritten by every call, so calls that share one
  *   workspace must be ordered on one stream (or otherwise serialised).

@@ -162,6 +162,21 @@ def _traffic(kernel, workload, launches):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _mfma_counters(kernel, workload):
+    """Executed MFMA rate of a kernel from a committed SQ_INSTS_MFMA summary
+    for this workload (counter-measured), if its source hash still matches."""
+    path = os.path.join(ROOT, "profiles", "mfma_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    from cascade_token_head_amd.traffic import source_sha1
+    if rec.get("source_sha1") != source_sha1(kernel):
+        return None
+    return {"executed_tflops": rec["executed_tflops"], "executed_frac": rec["executed_frac"],
+            "avg_us": rec["avg_duration_us"]}
+
+
 def _cpu_baseline(cfg, inputs, budget_s: float):
     """Time the fp64 oracle on whole sequences until `budget_s` is spent."""
     from oracle import spatten_ref as R
@@ -450,11 +465,19 @@ def measure(cfg, args, lib, with_cpu: bool) -> dict:
         achieved = by * args.steps / (dms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof.update({"kernel": dom, "avg_us": round(dms * 1e3 / max(dcnt, 1), 3),
+    traffic = _traffic(dom, cfg.name, dcnt // args.steps)
+    avg_us = dms * 1e3 / max(dcnt, 1)
+    roof.update({"kernel": dom, "avg_us": round(avg_us, 3),
                  "launches_per_step": dcnt // args.steps,
-                 "traffic": _traffic(dom, cfg.name, dcnt // args.steps),
+                 "traffic": traffic,
                  "attention": _attention_roof(cfg, ktimes, work, args.steps),
                  "step": _step_roof(cfg, work, ms_per_step)})
+    if traffic is not None and cfg.kind == "decode":
+        # the same launch's HBM rate from counter-measured bytes
+        roof["frac_counters"] = round(traffic / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    if cfg.kind == "prefill" and roof["attention"] is not None:
+        roof["attention"]["mfma_counters"] = {
+            k: _mfma_counters(k, cfg.name) for k in ("attn_fwd", "attn_colsum")}
 
     cpu = _cpu_baseline(cfg, inputs, args.cpu_seconds) if with_cpu else None
 

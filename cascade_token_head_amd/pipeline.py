@@ -150,6 +150,7 @@ class PerHeadPrefillStack:
     def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, n_tokens: int,
                  heads, key_keep, weights: List[dict], device="cuda"):
         assert len(heads) == n_layers and len(key_keep) == n_layers
+        assert key_keep[0] == n_tokens, "every head starts with every token"
         assert all(1 <= m <= n_tokens for m in key_keep)
         assert all(b <= a for a, b in zip(key_keep, key_keep[1:]))
         self.L, self.B, self.H, self.dh, self.n = n_layers, batch, n_heads, head_dim, n_tokens
@@ -180,9 +181,8 @@ class PerHeadPrefillStack:
         self.g.zero_()
         dev = self.g.device
         self.hbuf[0].copy_(torch.arange(H, dtype=torch.int32, device=dev).repeat(B))
-        m = self.keep[0]
-        self.kbuf[0][: B * H * m].copy_(
-            torch.arange(m, dtype=torch.int32, device=dev).repeat(B * H))
+        self.kbuf[0][: B * H * n].copy_(
+            torch.arange(n, dtype=torch.int32, device=dev).repeat(B * H))
 
     def run(self, record: bool = False, layer_hook=None):
         """Run all layers; returns (x [B, n, D], heads [B, h_L], keys

@@ -129,11 +129,15 @@ typedef struct {
  *   If workspace is NULL only *d is checked, the required size is stored in
  *   *workspace_bytes and SPATTEN_OK is returned without enqueuing anything
  *   (tensor pointers may then be NULL).
- * Supported: prefill bf16 with head_dim 64 or 128, prefill fp32 with
- *   n_tokens <= 1024; other shapes return SPATTEN_EUNSUPPORTED, as does a
- *   non-zero v_threshold in prefill or with a quantized cache. A NaN or
- *   negative v_threshold is SPATTEN_EINVAL; per_head is 0 or 1 and, when 1,
- *   needs an unquantized decode (else SPATTEN_EUNSUPPORTED).
+ * Supported (else SPATTEN_EUNSUPPORTED): prefill bf16 with head_dim 64 or
+ *   128; prefill fp32 with head_dim 32, 64 or 128 and n_tokens <= 1024;
+ *   decode bf16 with head_dim 64, n_heads <= 32 and every head kept. A
+ *   v_threshold > 0 is taken by prefill and by unquantized decode, not by
+ *   quantized caches or per-head prefill; a NaN or negative one is
+ *   SPATTEN_EINVAL. per_head is 0 or 1 (else SPATTEN_EINVAL); 1 needs an
+ *   unquantized decode, or a bf16 bidirectional prefill with
+ *   1 <= n_keys <= n_tokens; n_keys must be 0 in every other case
+ *   (SPATTEN_EINVAL).
  */
 int spatten_layer_forward(const spatten_layer_desc* d, void* x,
                           const void* wq, const void* wk, const void* wv, const void* wo,

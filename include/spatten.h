@@ -5,7 +5,9 @@
  * The operations follow "SpAtten: Efficient Sparse Attention Architecture
  * with Cascade Token and Head Pruning" (Wang, Zhang, Han, arXiv 2012.09852)
  * as summarised on its paperlayer.ai page; section names below are that
- * page's.
+ * page's, except for spatten_ada_select, which follows "Cascade Token
+ * Selection for Transformer Attention Acceleration" (gist.science summary)
+ * and names that page's sections.
  *
  * Conventions for every entry point
  *  - Tensor pointers are DEVICE pointers owned by the caller; the library
@@ -60,7 +62,7 @@ typedef struct {
   int32_t cache_cap;     /* decode: cache rows allocated per sequence */
   int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
   float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
-  float v_threshold;     /* decode, unquantized: local value pruning threshold (0 = off) */
+  float v_threshold;     /* local value pruning threshold (0 = off): prefill, unquantized decode */
   int32_t per_head;      /* 1 = per-head token pruning (decode, unquantized: a is [B, H, cache_cap];
                             prefill, bf16 bidirectional: see n_keys) */
   int32_t n_keys;        /* prefill with per_head: tokens each kept head keeps as keys and values */

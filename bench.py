@@ -20,8 +20,9 @@ algorithmic and executed MFMA work; decode: attention bytes) and
 layer's tokens/s including its selection and compaction. `cpu_baseline`
 times the fp64 CPU oracle on a bounded sample of the same workload.
 Without --config the line also carries `workloads`: the same measurements
-(no CPU baseline) for bert_base, gpt2_decode and pq_decode (the last with
-the fraction of rows the progressive quantization recomputed), and for the
+(no CPU baseline) for bert_base, bert_base_perhead, gpt2_decode and
+pq_decode (the last with the fraction of rows the progressive quantization
+recomputed), and for the
 cascade representative-token selection workloads ada_gpt2 and ada_long
 (fp32 Gram products; their line compares the cascade with a full-Gram
 selection at every layer).
@@ -109,11 +110,13 @@ def _kernel_work(cfg, v_kept=None, recompute_frac=None):
                 add("out_gemm", 2.0 * B * D * D, es * D * D + 8.0 * B * lc)
                 if cfg.quantized:
                     # MSB planes and scales of K and V; a recomputed
-                    # (sequence, head) row also reads both planes of its head
-                    # slice of K and V, and the two scales
+                    # (sequence, head) row also needs the LSB halves of its
+                    # head slice of K and V (dh / 2 bytes each; the kernel
+                    # re-reads the MSB halves too, which the method does not
+                    # need)
                     r = recompute_frac or 0.0
                     add("pq_attn", 4.0 * B * H * dh * lc * (1 + r),
-                        2 * B * lc * (D // 2 + 4) + r * B * H * lc * (2 * dh + 8))
+                        2 * B * lc * (D // 2 + 4) + r * B * H * lc * dh)
                 elif cfg.v_threshold > 0:
                     # K rows once, the kept V rows (a 128-byte head slice
                     # each) and the fp32 scores the importance pass reads

@@ -244,6 +244,25 @@ def trace_main(a) -> None:
             f.write("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |\n" % (
                 name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / total))
+        if a.bench_json:
+            # bench.py's own HIP-event average for the same kernel, printed
+            # by the traced run itself
+            with open(a.bench_json) as bj:
+                line = json.loads(bj.read().strip().splitlines()[-1])
+            rec = line if line["config"]["workload"] == a.workload else \
+                line.get("workloads", {}).get(a.workload)
+            if rec is not None and rec["roofline"].get("kernel") == a.label:
+                tr = [r for r in rows if re.search(a.kernel_regex, r["Name"])] if \
+                    a.kernel_regex else []
+                f.write("\nbench.py's HIP-event average for %s in the traced run: %.2f us "
+                        "over %d launches per step" % (a.label, rec["roofline"]["avg_us"],
+                                                        rec["roofline"]["launches_per_step"]))
+                if tr:
+                    calls = sum(int(r["Calls"]) for r in tr)
+                    avg = sum(float(r["TotalDurationNs"]) for r in tr) / calls / 1e3
+                    f.write("; the trace's average for `%s`: %.2f us over %d dispatches"
+                            % (a.kernel_regex, avg, calls))
+                f.write(".\n")
         f.write("\nsource sha1 of %s: `%s`\n" % (a.label, source_sha1(a.label)))
     print(path)
 
@@ -261,6 +280,10 @@ def main() -> None:
     tr.add_argument("--stats", required=True)
     tr.add_argument("--top", type=int, default=12)
     tr.add_argument("--command", default="")
+    tr.add_argument("--bench-json", default=None,
+                    help="bench.py's output line from the traced run")
+    tr.add_argument("--kernel-regex", default=None,
+                    help="symbol regex of the dominant kernel in the trace")
     tr.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     s = sub.add_parser("summarize")
     s.add_argument("--label", required=True)

@@ -140,7 +140,7 @@ def test_trace_summary_orders_kernels_by_time(tmp_path):
 
     class A:
         label, workload, stats, top, command = "attn_fwd", "synthetic", str(path), 12, "cmd"
-        out = str(tmp_path)
+        out, bench_json, kernel_regex = str(tmp_path), None, None
     traffic.trace_main(A)
     text = open(tmp_path / "attn_fwd_synthetic_kernel_trace.md").read()
     assert text.index("big_kernel") < text.index("small_kernel")

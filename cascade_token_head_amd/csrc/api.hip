@@ -321,13 +321,13 @@ int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t*
 }
 
 int spatten_quantize_kv(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,
-                        int64_t kv_batch_stride, uint8_t* msb, uint8_t* lsb, float* scale,
-                        int64_t plane_batch_stride, void* stream) {
-  const int st = check_quantize(kv, dtype, batch, n, dim, kv_batch_stride, msb, lsb, scale,
-                                plane_batch_stride);
+                        int32_t head_dim, int64_t kv_batch_stride, uint8_t* msb, uint8_t* lsb,
+                        float* scale, int64_t plane_rows, void* stream) {
+  const int st = check_quantize(kv, dtype, batch, n, dim, head_dim, kv_batch_stride, msb, lsb,
+                                scale, plane_rows);
   if (st != SPATTEN_OK) return st;
-  return launch_quantize(kv, dtype, batch, n, dim, kv_batch_stride, msb, lsb, scale,
-                         plane_batch_stride, as_stream(stream));
+  return launch_quantize(kv, dtype, batch, n, dim, head_dim, kv_batch_stride, msb, lsb, scale,
+                         plane_rows, as_stream(stream));
 }
 
 const char* spatten_status_string(int status) {

@@ -134,15 +134,21 @@ __device__ __forceinline__ void load8_f32(const float* x, float* v) {
 // LSB nibble planes (byte p: element 2p in the low nibble, 2p+1 in the high
 // one) and its scale. Rows of up to 2048 values in 8-value groups are held
 // in registers, so every load is issued before the first use.
+// The row's dim/2 plane bytes go out in segments of seg bytes, segment i
+// at byte i * seg_stride of mrow / lrow (seg = dim/2: one contiguous row;
+// seg = head_dim/2 with seg_stride = one head's slab: head-major planes).
 template <typename T>
 __device__ __forceinline__ void quantize_row_wave(const T* x, int dim, uint8_t* mrow,
-                                                  uint8_t* lrow, float* scale) {
+                                                  uint8_t* lrow, float* scale, int seg,
+                                                  int64_t seg_stride) {
   const int lane = threadIdx.x & 63;
   const int nch = dim >> 3;
-  const bool grouped = (dim & 7) == 0 && nch <= 4 * 64 &&
+  const bool grouped = (dim & 7) == 0 && nch <= 4 * 64 && (seg & 3) == 0 &&
+                       (seg_stride & 3) == 0 &&
                        (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                        (reinterpret_cast<uintptr_t>(mrow) & 3) == 0 &&
                        (reinterpret_cast<uintptr_t>(lrow) & 3) == 0;
+  auto at = [&](int p) { return int64_t(p / seg) * seg_stride + p % seg; };
   if (grouped) {
     float v[4][8];
     float amax = 0.0f;
@@ -171,8 +177,8 @@ __device__ __forceinline__ void quantize_row_wave(const T* x, int dim, uint8_t* 
           mw |= uint32_t((qc >> 4) & 15) << (4 * e);
           lw |= uint32_t(qc & 15) << (4 * e);
         }
-        reinterpret_cast<uint32_t*>(mrow)[ch] = mw;
-        reinterpret_cast<uint32_t*>(lrow)[ch] = lw;
+        *reinterpret_cast<uint32_t*>(mrow + at(4 * ch)) = mw;
+        *reinterpret_cast<uint32_t*>(lrow + at(4 * ch)) = lw;
       }
     }
     if (lane == 0) *scale = s;
@@ -189,8 +195,8 @@ __device__ __forceinline__ void quantize_row_wave(const T* x, int dim, uint8_t* 
   for (int p = lane; p < half; p += 64) {
     const int q0 = quant_code(load_elem<T>(x, 2 * p), s);
     const int q1 = quant_code(load_elem<T>(x, 2 * p + 1), s);
-    mrow[p] = uint8_t(((q0 >> 4) & 15) | (((q1 >> 4) & 15) << 4));
-    lrow[p] = uint8_t((q0 & 15) | ((q1 & 15) << 4));
+    mrow[at(p)] = uint8_t(((q0 >> 4) & 15) | (((q1 >> 4) & 15) << 4));
+    lrow[at(p)] = uint8_t((q0 & 15) | ((q1 & 15) << 4));
   }
   if (lane == 0) *scale = s;
 }

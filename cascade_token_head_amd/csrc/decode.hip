@@ -5,36 +5,33 @@
 // "E. ... Progressive Quantization": MSBs first, LSBs fetched and the row
 // recomputed when its largest probability is below a threshold).
 //
-// The cache is token-major [B, cap, D], so one cache row holds every head
-// of one token. decode_partial: a workgroup owns (sequence, 32-entry chunk)
-// and streams the chunk's K rows, then its V rows, once and coalesced. Each
-// thread owns one 8-dim column group (one head's slice) of every R-th row of
-// the chunk and issues all of its row loads before using any of them, so a
-// thread keeps up to 16 loads in flight; partial dots are reduced with the 7
-// neighbouring lanes of the same head. Chunks are combined per (sequence,
-// head): split-K over the cache length, so a few hundred rows still fill 256
-// CUs. Scores stay in a small fp32 stash so the importance pass can form the
-// exact normalised probabilities.
+// The bf16 cache is token-major [B, cap, D], so one cache row holds every
+// head of one token; the quantized planes are head-major [B, H, cap, dh/2],
+// so one (sequence, head) slab is contiguous. Three families of kernels:
 //
-// Quantized caches: the MSB pass first codes this step's k and v rows into
-// the planes (in the workgroup that owns the new row), then scores and
-// accumulates with 16 * msb; decode_flag marks each (sequence, head) row
-// whose largest MSB-pass probability is below the threshold and appends it
-// to the recompute queue; decode_recompute runs one workgroup per (queued
-// row, chunk) over both planes of that head only. decode_finish combines
-// what is left, writes O and adds the probabilities that produced O to the
-// token importance.
+// decode_bh (dense and quantized): one workgroup per (sequence, head) row
+// streams that head's slice of the whole cache with an online softmax per
+// row group and writes the normalised output and the row's log2-sum-exp;
+// no cross-workgroup combine. Quantized caches code this step's k and v
+// rows into the planes first, score with 16 * msb, and recompute the whole
+// row from both planes in the same workgroup when its largest MSB-pass
+// probability is below the threshold.
 //
-// Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning": after the softmax
-// a head drops its low-probability V vectors). A V row can only be skipped
-// once the row's exact probabilities are known, i.e. after the softmax over
-// the whole cache. decode_vrow gives each (sequence, head) row one
-// workgroup that keeps all of the row's scores in LDS, so it reads K, forms
-// the probabilities and then fetches only the V head slices (128 bytes of a
-// cache row) that reach the threshold; decode_finish adds the importance.
-// Caches too long for LDS take a split path: a K-only scores pass with
-// per-chunk statistics, decode_vprune (exact probabilities per chunk,
-// importance, kept V rows) and decode_vsum (sum of the chunk outputs).
+// Local value pruning ("A. Cascade Token Pruning", bullet "Local Value
+// Pruning": after the softmax a head drops its low-probability V vectors).
+// A V row can only be skipped once the row's exact probabilities are known,
+// i.e. after the softmax over the whole cache. decode_vrow gives each
+// (sequence, head) row one workgroup that keeps all of the row's scores in
+// LDS, so it reads K, forms the probabilities and then fetches only the V
+// head slices (128 bytes of a cache row) that reach the threshold. Caches
+// too long for LDS take a split path over 32-row chunks: decode_scores
+// (K only, scores and per-chunk statistics), decode_vprune (exact
+// probabilities per chunk, importance, kept V rows) and decode_vsum (sum of
+// the chunk outputs).
+//
+// Token importance: every path leaves its fp32 scores in a stash; the
+// importance pass (in the output projection's launch, or decode_importance)
+// adds sum over heads of exp2(s - lse) to each kept token's score.
 #include "common.hpp"
 #include "importance.hpp"
 #include "kernels.hpp"
@@ -45,8 +42,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int CH = kDecChunk;  // cache entries per chunk
-// one 32-lane half-wave holds a head's chunk statistics, and the recompute
-// kernel maps its 64 threads to 32 rows x 2 halves of a head
+// one 32-lane half-wave of decode_vprune holds a head's chunk statistics
 static_assert(CH == 32, "decode kernels are written for 32-row chunks");
 constexpr int KB = 16;         // rows per load batch
 constexpr int kMaxHeads = 32;
@@ -287,7 +283,7 @@ decode_vrow(DecodeArgs a) {
 }
 
 // Local value pruning, after the K-only scores pass. grid (nchunk, B), the
-// thread layout of decode_partial. Each half-wave combines one head's chunk
+// thread layout of decode_scores. Each half-wave combines one head's chunk
 // statistics into its log2-sum-exp, forms the chunk's 32 probabilities and
 // counts the kept rows; the workgroup then adds the chunk's importance
 // (it owns those a entries) and accumulates p V over the kept rows only.
@@ -416,7 +412,9 @@ decode_vsum(DecodeArgs a) {
 //
 // Dense and progressive-quantization decode: the workgroup streams its
 // head's slice of every cache row (bf16: 128 bytes of K and of V;
-// quantized: 32 bytes of each plane it reads plus the row scales), with K
+// quantized: the 32-byte rows of its own slab of each plane it reads - the
+// planes are head-major, so a workgroup's reads fill whole cache lines -
+// plus the row scales), with K
 // and V of a row requested together, and keeps an online softmax per row
 // group: each load batch raises the group's reference maximum once and
 // rescales its running sum and output. The groups then meet in LDS, so the
@@ -565,17 +563,17 @@ __device__ __forceinline__ float bh_q_dot(const float* q, float qsum, const floa
   return d * ks * (kLog2e * 0.125f);
 }
 
-// Quantized cache: rows r0..r1-1 of head h read from the planes (row r0 +
-// g + 128 i belongs to row group g), MSB only or (FULL) both planes.
+// Quantized cache: rows r0..r1-1 of head h read from the head-major planes
+// (row r0 + g + 128 i belongs to row group g), MSB only or (FULL) both.
 template <bool FULL>
 __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int g, int cl,
                                           int r0, int r1, const float* q, float qsum,
                                           BhState<16>& st) {
   constexpr int LPR = BhCfg<kMsb>::LPR, NG = BhCfg<kMsb>::NT / LPR;
   constexpr int KBq = FULL ? BhCfg<kMsb>::KBF : BhCfg<kMsb>::KB;
-  const int D = a.H * 64;
   const int64_t rowb = int64_t(b) * a.cap;
-  const int64_t off = h * 32 + 8 * cl;  // byte offset of this lane's 16 nibbles in a row
+  // head-major planes: this head's slab of 32-byte rows, this lane's 8 bytes
+  const int64_t slab = (int64_t(b) * a.H + h) * a.cap * 32 + 8 * cl;
   float* srow = a.scores + (int64_t(b) * a.H + h) * a.lc_pad;
   const float kmul = FULL ? 1.0f : 16.0f;
   const int nit = (r1 - r0 + NG - 1) / NG;
@@ -585,17 +583,18 @@ __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int u = 0; u < KBq; ++u) {
       const int j = r0 + g + NG * (i0 + u);
-      const int64_t row = rowb + (j < r1 ? j : r0);  // past the range: a valid row, masked
-      km[u] = *reinterpret_cast<const uint2*>(a.k_msb + row * (D / 2) + off);
-      vm[u] = *reinterpret_cast<const uint2*>(a.v_msb + row * (D / 2) + off);
+      const int jr = j < r1 ? j : r0;  // past the range: a valid row, masked
+      const int64_t po = slab + int64_t(jr) * 32;
+      km[u] = *reinterpret_cast<const uint2*>(a.k_msb + po);
+      vm[u] = *reinterpret_cast<const uint2*>(a.v_msb + po);
       if constexpr (FULL) {
-        kl[u] = *reinterpret_cast<const uint2*>(a.k_lsb + row * (D / 2) + off);
-        vl[u] = *reinterpret_cast<const uint2*>(a.v_lsb + row * (D / 2) + off);
+        kl[u] = *reinterpret_cast<const uint2*>(a.k_lsb + po);
+        vl[u] = *reinterpret_cast<const uint2*>(a.v_lsb + po);
       } else {
         kl[u] = vl[u] = uint2{0u, 0u};
       }
-      ks[u] = a.k_scale[row];
-      vs[u] = a.v_scale[row];
+      ks[u] = a.k_scale[rowb + jr];
+      vs[u] = a.v_scale[rowb + jr];
     }
     float s[KBq];
     float bm = -INFINITY;
@@ -785,8 +784,9 @@ decode_bh(DecodeArgs a) {
         const int w = lane >> 3;
         nw[wave][w] = mn;
         nlw[wave][w] = ln;
-        uint8_t* mp = (wave == 0 ? a.k_msb : a.v_msb) + nrow * (D / 2) + h * 32 + 4 * w;
-        uint8_t* lp = (wave == 0 ? a.k_lsb : a.v_lsb) + nrow * (D / 2) + h * 32 + 4 * w;
+        const int64_t po = ((int64_t(b) * a.H + h) * a.cap + a.lc - 1) * 32 + 4 * w;
+        uint8_t* mp = (wave == 0 ? a.k_msb : a.v_msb) + po;
+        uint8_t* lp = (wave == 0 ? a.k_lsb : a.v_lsb) + po;
         *reinterpret_cast<uint32_t*>(mp) = mn;
         *reinterpret_cast<uint32_t*>(lp) = ln;
       }

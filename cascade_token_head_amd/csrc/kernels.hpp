@@ -21,8 +21,9 @@ int launch_compact_inplace(int n_tensors, void* const* base, const int64_t* row_
                            const int64_t* row_pitch, const int64_t* bs, const int32_t* idx,
                            int batch, int n, int k, hipStream_t stream);
 
-int launch_quantize(const void* kv, int dtype, int batch, int n, int dim, int64_t kv_bs,
-                    uint8_t* msb, uint8_t* lsb, float* scale, int64_t pbs, hipStream_t stream);
+int launch_quantize(const void* kv, int dtype, int batch, int n, int dim, int head_dim,
+                    int64_t kv_bs, uint8_t* msb, uint8_t* lsb, float* scale, int64_t pbs,
+                    hipStream_t stream);
 
 // Projections. QKV: for each kept head slot s of sequence b the rows
 // head_idx[b, s]*dh .. +dh of wq/wk/wv (output-major) produce Q, K and V.

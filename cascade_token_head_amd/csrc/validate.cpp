@@ -158,12 +158,16 @@ int check_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* r
 }
 
 int check_quantize(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,
-                   int64_t kv_batch_stride, const uint8_t* msb, const uint8_t* lsb,
-                   const float* scale, int64_t plane_batch_stride) {
+                   int32_t head_dim, int64_t kv_batch_stride, const uint8_t* msb,
+                   const uint8_t* lsb, const float* scale, int64_t plane_rows) {
   if (!valid_dtype(dtype)) return SPATTEN_EINVAL;
   if (batch < 0 || n < 0 || dim < 2 || (dim & 1)) return SPATTEN_EINVAL;
-  if (batch > 1 && (kv_batch_stride < int64_t(n) * dim || plane_batch_stride < n))
+  if (head_dim < 0 || (head_dim > 0 && ((head_dim & 1) || dim % head_dim != 0)))
     return SPATTEN_EINVAL;
+  if (batch > 1 && kv_batch_stride < int64_t(n) * dim) return SPATTEN_EINVAL;
+  // sequences (and, head-major, the heads' slabs) must not overlap
+  const bool slabs = batch > 1 || (head_dim > 0 && dim / head_dim > 1);
+  if (slabs && plane_rows < n) return SPATTEN_EINVAL;
   if (batch == 0 || n == 0) return SPATTEN_OK;
   if (!kv || !msb || !lsb || !scale) return SPATTEN_EINVAL;
   if (!aligned(kv, dtype_bytes(dtype)) || !aligned(scale, 4)) return SPATTEN_EINVAL;

@@ -36,7 +36,7 @@ int check_compact_inplace(int32_t n_tensors, void* const* base, const int64_t* r
                           const int32_t* idx, int32_t batch, int32_t n, int32_t k);
 
 int check_quantize(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,
-                   int64_t kv_batch_stride, const uint8_t* msb, const uint8_t* lsb,
-                   const float* scale, int64_t plane_batch_stride);
+                   int32_t head_dim, int64_t kv_batch_stride, const uint8_t* msb,
+                   const uint8_t* lsb, const float* scale, int64_t plane_rows);
 
 }  // namespace spatten

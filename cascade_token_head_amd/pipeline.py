@@ -247,6 +247,14 @@ class PerHeadPrefillStack:
         return self.final
 
 
+def _row_views(t: torch.Tensor):
+    """Views of t whose dim 1 is the cache row: t itself for [B, cap, ...],
+    one [B, cap, dh/2] view per head for head-major planes [B, H, cap, dh/2]."""
+    if t.dim() == 4:
+        return [t[:, h] for h in range(t.shape[1])]
+    return [t]
+
+
 class DecodeStack:
     def __init__(self, n_layers: int, batch: int, n_heads: int, head_dim: int, cache_len: int,
                  cache_keep: int, steps: int, weights: List[dict], quantized: bool = False,
@@ -268,11 +276,13 @@ class DecodeStack:
         for side in range(sides):
             for _ in range(n_layers):
                 if quantized:
-                    c = {"k_msb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
-                         "k_lsb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
+                    # head-major planes: each (sequence, head) slab contiguous
+                    pl = (B, n_heads, cap, head_dim // 2)
+                    c = {"k_msb": torch.empty(pl, dtype=torch.uint8, device=dev),
+                         "k_lsb": torch.empty(pl, dtype=torch.uint8, device=dev),
                          "k_scale": torch.empty(B, cap, dtype=torch.float32, device=dev),
-                         "v_msb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
-                         "v_lsb": torch.empty(B, cap, D // 2, dtype=torch.uint8, device=dev),
+                         "v_msb": torch.empty(pl, dtype=torch.uint8, device=dev),
+                         "v_lsb": torch.empty(pl, dtype=torch.uint8, device=dev),
                          "v_scale": torch.empty(B, cap, dtype=torch.float32, device=dev)}
                 else:
                     c = {"k_cache": torch.empty(B, cap, D, dtype=dtype, device=dev),
@@ -377,8 +387,10 @@ class DecodeStack:
             tensors = [(a, 4, cap * 4)]
             for c in self.caches[0]:
                 for t in c.values():
-                    rb = t.stride(1) * t.element_size() if t.dim() == 3 else t.element_size()
-                    tensors.append((t, rb, t.stride(0) * t.element_size()))
+                    for v in _row_views(t):
+                        es = v.element_size()
+                        rb = v.stride(1) * es if v.dim() == 3 else es
+                        tensors.append((v, rb, v.stride(0) * es))
             S.compact_inplace(tensors, self.cache_sel, self.len, k)
             # rows past the kept range take the next entries, whose
             # importance starts at 0
@@ -390,9 +402,10 @@ class DecodeStack:
         for l in range(self.L):
             src, dst = self.caches[self.side][l], self.caches[self.side ^ 1][l]
             for name, t in src.items():
-                rb = t.stride(1) * t.element_size() if t.dim() == 3 else t.element_size()
-                bs = t.stride(0) * t.element_size()
-                pairs.append((t, dst[name], rb, bs, bs))
+                for v, w in zip(_row_views(t), _row_views(dst[name])):
+                    es = v.element_size()
+                    rb = v.stride(1) * es if v.dim() == 3 else es
+                    pairs.append((v, w, rb, v.stride(0) * es, w.stride(0) * es))
         S.compact(pairs, self.cache_sel, k)
         self.side ^= 1
         self.len = k

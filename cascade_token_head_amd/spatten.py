@@ -70,7 +70,7 @@ def _lib():
                                                 ctypes.POINTER(i64), ctypes.POINTER(i64), vp,
                                                 i32, i32, i32, vp]
         lib.spatten_quantize_kv.restype = ctypes.c_int
-        lib.spatten_quantize_kv.argtypes = [vp, i32, i32, i32, i32, i64, vp, vp, vp, i64, vp]
+        lib.spatten_quantize_kv.argtypes = [vp, i32, i32, i32, i32, i32, i64, vp, vp, vp, i64, vp]
         lib.spatten_ada_select.restype = ctypes.c_int
         lib.spatten_ada_select.argtypes = [vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(ctypes.c_size_t), vp]
@@ -193,11 +193,27 @@ def compact(pairs: Sequence, idx: torch.Tensor, k: int, stream=None):
 
 def quantize_kv(kv: torch.Tensor, msb: torch.Tensor, lsb: torch.Tensor, scale: torch.Tensor,
                 n: Optional[int] = None, stream=None):
-    """kv [B, n, D] (bf16/fp32) -> msb/lsb [B, cap, D/2] u8, scale [B, cap] (rows 0..n-1)."""
+    """kv [B, n, D] (bf16/fp32) -> planes and scale [B, cap] (rows 0..n-1).
+
+    Planes [B, H, cap, dh/2] u8 are head-major (the layout the quantized
+    decode reads); [B, cap, D/2] u8 planes are token-major.
+    """
     B, rows, D = kv.shape
     n = rows if n is None else n
-    st = _lib().spatten_quantize_kv(_p(kv), dtype_code(kv.dtype), B, n, D, kv.stride(0), _p(msb),
-                                    _p(lsb), _p(scale), scale.stride(0), _stream(stream))
+    if msb.dim() == 4:
+        H, hd2 = msb.shape[1], msb.shape[3]
+        head_dim = 2 * hd2
+        plane_rows = msb.stride(1) // msb.stride(2)
+        assert msb.stride(3) == 1 and msb.stride(2) == hd2 and H * head_dim == D
+        assert msb.stride(0) == H * msb.stride(1) and lsb.stride() == msb.stride()
+    else:
+        head_dim = 0
+        plane_rows = msb.stride(0) // msb.stride(1)
+        assert msb.stride(2) == 1 and msb.stride(1) == D // 2 and lsb.stride() == msb.stride()
+    assert scale.stride(0) == plane_rows or B == 1
+    st = _lib().spatten_quantize_kv(_p(kv), dtype_code(kv.dtype), B, n, D, head_dim,
+                                    kv.stride(0), _p(msb), _p(lsb), _p(scale), plane_rows,
+                                    _stream(stream))
     _check("spatten_quantize_kv", st)
 
 

@@ -91,8 +91,10 @@ typedef struct {
  *   for those rows. Unquantized: k_cache, v_cache are [B, cache_cap, D]
  *   in dtype. Quantized (progressive quantization, "A. Cascade
  *   Token Pruning" and "E. ... Progressive Quantization"): k_msb, k_lsb, v_msb, v_lsb are
- *   [B, cache_cap, D/2] u8 and k_scale, v_scale [B, cache_cap] fp32 as
- *   written by spatten_quantize_kv; this step's k and v rows are coded into
+ *   head-major [B, H, cache_cap, head_dim/2] u8 (each head's rows
+ *   contiguous, so a (sequence, head) row reads whole cache lines) and
+ *   k_scale, v_scale [B, cache_cap] fp32, as spatten_quantize_kv writes
+ *   them with head_dim set; this step's k and v rows are coded into
  *   row cache_len of the planes and scales with that function's arithmetic
  *   (bit for bit) before they are read; each (b, h) row is scored with MSB-only
  *   values (scale*16*msb) and, when its largest probability is below
@@ -239,13 +241,18 @@ int spatten_compact_inplace(int32_t n_tensors, void* const* base, const int64_t*
  *   msb = q >> 4 (arithmetic, -8..7), lsb = q & 15 (0..15)
  *   msb byte j = (msb[2j] & 15) | (msb[2j+1] & 15) << 4, lsb likewise.
  * kv: [batch, n, dim] in dtype with batch stride kv_batch_stride elements.
- * msb, lsb: [batch, *, dim/2] u8 with batch stride plane_batch_stride rows;
- * scale: [batch, *] fp32 with the same batch stride in rows. dim must be
- * even. Pointers may be pre-offset to the first row to write.
+ * msb, lsb: head_dim = 0 - token-major [batch, plane_rows, dim/2] u8;
+ *   head_dim > 0 (even, dividing dim) - head-major [batch, dim/head_dim,
+ *   plane_rows, head_dim/2] u8: each head's rows are contiguous, the
+ *   layout spatten_layer_forward takes for quantized caches. Row r of
+ *   sequence b is written at row r of its sequence's (and head's) slab.
+ * scale: [batch, plane_rows] fp32. dim must be even; plane_rows >= n when
+ * the slabs are more than one. Pointers may be pre-offset by the same
+ * number of rows (to the first row to write).
  */
 int spatten_quantize_kv(const void* kv, int32_t dtype, int32_t batch, int32_t n, int32_t dim,
-                        int64_t kv_batch_stride, uint8_t* msb, uint8_t* lsb, float* scale,
-                        int64_t plane_batch_stride, void* stream);
+                        int32_t head_dim, int64_t kv_batch_stride, uint8_t* msb, uint8_t* lsb,
+                        float* scale, int64_t plane_rows, void* stream);
 
 /*
  * spatten_ada_select - representative tokens of one layer by a Gram

@@ -170,9 +170,17 @@ int main() {
   hbs[0] = 1 << 20;
   EXPECT(check_compact_inplace(1, base, hrb, hpitch, hbs, hi, 2, 100, 10), SPATTEN_EINVAL);
   // quantize
-  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 5 * 1024, u8, u8, fp, 5), SPATTEN_OK);
-  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1023, 5 * 1023, u8, u8, fp, 5), SPATTEN_EINVAL);
-  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 4 * 1024, u8, u8, fp, 5), SPATTEN_EINVAL);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 0, 5 * 1024, u8, u8, fp, 5), SPATTEN_OK);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1023, 0, 5 * 1023, u8, u8, fp, 5), SPATTEN_EINVAL);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 1024, 0, 4 * 1024, u8, u8, fp, 5), SPATTEN_EINVAL);
+  // head-major planes: head_dim even and dividing dim; slabs of plane_rows >= n rows
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 768, 64, 5 * 768, u8, u8, fp, 9), SPATTEN_OK);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 1, 5, 768, 64, 5 * 768, u8, u8, fp, 5), SPATTEN_OK);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 1, 5, 768, 64, 5 * 768, u8, u8, fp, 4), SPATTEN_EINVAL);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 1, 5, 768, 768, 5 * 768, u8, u8, fp, 1), SPATTEN_OK);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 768, 63, 5 * 768, u8, u8, fp, 5), SPATTEN_EINVAL);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 768, 96 * 5, 5 * 768, u8, u8, fp, 5), SPATTEN_EINVAL);
+  EXPECT(check_quantize(P, SPATTEN_BF16, 2, 5, 768, -2, 5 * 768, u8, u8, fp, 5), SPATTEN_EINVAL);
   if (failures) return 1;
   std::printf("all validator cases passed\n");
   return 0;

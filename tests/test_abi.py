@@ -182,11 +182,17 @@ def test_topk_compact_quantize_rejections(S):
     assert lib.spatten_compact(1, VP(FAKE), VP(FAKE * 4), I64(16), I64(1600), I64(32),
                                vp(FAKE * 2), 2, 10, None) == S.EINVAL
     assert lib.spatten_compact(0, None, None, None, None, None, None, 2, 10, None) == S.OK
-    assert lib.spatten_quantize_kv(vp(FAKE), 1, 2, 3, 7, 21, vp(FAKE), vp(FAKE), vp(FAKE), 3,
+    assert lib.spatten_quantize_kv(vp(FAKE), 1, 2, 3, 7, 0, 21, vp(FAKE), vp(FAKE), vp(FAKE), 3,
                                    None) == S.EINVAL       # odd dim
-    assert lib.spatten_quantize_kv(vp(FAKE), 3, 2, 3, 8, 24, vp(FAKE), vp(FAKE), vp(FAKE), 3,
+    assert lib.spatten_quantize_kv(vp(FAKE), 3, 2, 3, 8, 0, 24, vp(FAKE), vp(FAKE), vp(FAKE), 3,
                                    None) == S.EINVAL       # bad dtype
-    assert lib.spatten_quantize_kv(None, 1, 0, 3, 8, 24, None, None, None, 3, None) == S.OK
+    assert lib.spatten_quantize_kv(vp(FAKE), 1, 2, 3, 8, 3, 24, vp(FAKE), vp(FAKE), vp(FAKE), 3,
+                                   None) == S.EINVAL       # odd head_dim
+    assert lib.spatten_quantize_kv(vp(FAKE), 1, 2, 3, 12, 8, 36, vp(FAKE), vp(FAKE), vp(FAKE), 3,
+                                   None) == S.EINVAL       # head_dim does not divide dim
+    assert lib.spatten_quantize_kv(vp(FAKE), 1, 1, 3, 8, 4, 24, vp(FAKE), vp(FAKE), vp(FAKE), 2,
+                                   None) == S.EINVAL       # head slabs overlap
+    assert lib.spatten_quantize_kv(None, 1, 0, 3, 8, 0, 24, None, None, None, 3, None) == S.OK
 
 
 def test_compact_inplace_rejections(S):

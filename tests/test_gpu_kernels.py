@@ -231,6 +231,55 @@ def test_quantize_bit_exact(S, dtype, B, n, D):
     assert int(msb[:, n:].abs().sum()) == 0
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("B,n,H,dh", [(1, 1, 1, 2), (2, 5, 4, 8), (3, 17, 12, 64), (2, 33, 3, 6)])
+def test_quantize_head_major(S, dtype, B, n, H, dh):
+    """Head-major planes [B, H, cap, dh/2] hold, head by head, the bytes of
+    the token-major planes of the same rows (the row scale still covers the
+    whole row of H * dh values)."""
+    rng = np.random.default_rng(B * 977 + n * 31 + H * 7 + dh)
+    D = H * dh
+    x = (rng.standard_normal((B, n, D)) * rng.choice([1e-2, 1.0, 50.0], (B, n, 1))).astype(np.float32)
+    x[0, 0] = 0.0
+    xt = torch.from_numpy(x).to(dtype)
+    rm, rl, rs = R.quantize_kv(xt.float().numpy())
+    cap = n + 2
+    msb = torch.full((B, H, cap, dh // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    lsb = torch.full_like(msb, 0xA5)
+    sc = torch.full((B, cap), -1.0, device="cuda")
+    S.quantize_kv(xt.cuda(), msb, lsb, sc)
+    got_m = msb[:, :, :n].permute(0, 2, 1, 3).reshape(B, n, D // 2).cpu().numpy()
+    got_l = lsb[:, :, :n].permute(0, 2, 1, 3).reshape(B, n, D // 2).cpu().numpy()
+    np.testing.assert_array_equal(got_m, rm)
+    np.testing.assert_array_equal(got_l, rl)
+    np.testing.assert_array_equal(sc[:, :n].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    # rows past n are untouched in every head's slab
+    assert int((msb[:, :, n:] != 0x5A).sum()) == 0 and int((lsb[:, :, n:] != 0xA5).sum()) == 0
+    assert int((sc[:, n:] != -1).sum()) == 0
+
+
+def test_quantize_head_major_offset_rows(S):
+    """The decode append into head-major planes: one row written at a row
+    offset of every head's slab, the other rows left alone."""
+    rng = np.random.default_rng(19)
+    B, H, dh, cap, row = 3, 12, 64, 10, 7
+    D = H * dh
+    x = rng.standard_normal((B, 1, D)).astype(np.float32)
+    msb = torch.full((B, H, cap, dh // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    lsb = torch.full_like(msb, 0xCD)
+    sc = torch.full((B, cap), -1.0, device="cuda")
+    S.quantize_kv(torch.from_numpy(x).cuda(), msb[:, :, row:], lsb[:, :, row:], sc[:, row:])
+    rm, rl, rs = R.quantize_kv(x)
+    np.testing.assert_array_equal(msb[:, :, row].reshape(B, 1, D // 2).cpu().numpy(), rm)
+    np.testing.assert_array_equal(lsb[:, :, row].reshape(B, 1, D // 2).cpu().numpy(), rl)
+    np.testing.assert_array_equal(sc[:, row:row + 1].cpu().numpy().view(np.uint32),
+                                  rs.view(np.uint32))
+    keep = torch.ones(cap, dtype=torch.bool)
+    keep[row] = False
+    assert int((msb[:, :, keep] != 0xAB).sum()) == 0 and int((lsb[:, :, keep] != 0xCD).sum()) == 0
+    assert int((sc[:, keep] != -1).sum()) == 0
+
+
 def test_quantize_offset_rows(S):
     """Writing at a row offset (the decode append) leaves other rows alone."""
     rng = np.random.default_rng(9)

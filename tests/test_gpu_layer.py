@@ -277,7 +277,7 @@ def test_decode_layer(S, B, H, L0, quantized, thr, vthr, per_head):
     kw = {}
     if quantized:
         for name, arr in (("k", K0), ("v", V0)):
-            msb = torch.zeros(B, cap, D // 2, dtype=torch.uint8, device="cuda")
+            msb = torch.zeros(B, H, cap, dh // 2, dtype=torch.uint8, device="cuda")
             lsb = torch.zeros_like(msb)
             sc = torch.zeros(B, cap, device="cuda")
             S.quantize_kv(to_dev(arr, torch.bfloat16), msb, lsb, sc)

@@ -341,14 +341,15 @@ def test_prefill_stack_long_causal_full_size():
 
 def _cache_np(c, b, rows, quantized, H, dh):
     if quantized:
-        return {k: v[b, :rows].cpu().numpy() for k, v in c.items()}
+        return {k: _rows_np(v, b, rows) for k, v in c.items()}
     return {"k": to_np(c["k_cache"][b, :rows]).reshape(rows, H, dh),
             "v": to_np(c["v_cache"][b, :rows]).reshape(rows, H, dh)}
 
 
 def _rows_np(t, b, n):
-    """Rows 0..n-1 of sequence b of a cache tensor, exact (bf16 as fp32)."""
-    v = t[b, :n]
+    """Rows 0..n-1 of sequence b of a cache tensor, exact (bf16 as fp32);
+    head-major planes [B, H, cap, dh/2] come back token-major [n, H dh/2]."""
+    v = t[b, :, :n].permute(1, 0, 2).reshape(n, -1) if t.dim() == 4 else t[b, :n]
     return (v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy()
 
 
@@ -445,7 +446,8 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
         for b in seqs:
             per_b[b] = {}
             for name, t in c.items():
-                store = np.zeros((cap,) + tuple(t.shape[2:]), dtype=_rows_np(t, b, 1).dtype)
+                one = _rows_np(t, b, 1)
+                store = np.zeros((cap,) + one.shape[1:], dtype=one.dtype)
                 store[:cfg.cache_len] = _rows_np(t, b, cfg.cache_len)
                 per_b[b][name] = store
         rows.append(per_b)

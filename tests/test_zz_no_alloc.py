@@ -62,7 +62,7 @@ def _decode_pair(cfg, noalloc):
     rec = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     kept = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     if cfg.quantized:
-        c = {n: torch.zeros(B, cap, D // 2, dtype=torch.uint8, device="cuda")
+        c = {n: torch.zeros(B, H, cap, D // H // 2, dtype=torch.uint8, device="cuda")
              for n in ("k_msb", "k_lsb", "v_msb", "v_lsb")}
         c["k_scale"] = torch.zeros(B, cap, device="cuda")
         c["v_scale"] = torch.zeros(B, cap, device="cuda")

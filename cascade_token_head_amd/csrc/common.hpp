@@ -152,17 +152,22 @@ __device__ __forceinline__ void quantize_row_wave(const T* x, int dim, uint8_t* 
   if (grouped) {
     float v[4][8];
     float amax = 0.0f;
+    // every lane loads all four groups (past the row: its last group again,
+    // then zeroed), with no branch between the loads, so the four requests
+    // are in flight together
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = lane + 64 * i;
-      if (ch < nch) {
-        load8_f32(x + 8 * ch, v[i]);
-      } else {
+      load8_f32(x + 8 * (ch < nch ? ch : nch - 1), v[i]);
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const bool in = lane + 64 * i < nch;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = in ? v[i][e] : 0.0f;
+        amax = fmaxf(amax, fabsf(v[i][e]));
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
     }
     amax = wave_max(amax);
     const float s = amax / 127.0f;

@@ -231,6 +231,61 @@ def test_quantize_bit_exact(S, dtype, B, n, D):
     assert int(msb[:, n:].abs().sum()) == 0
 
 
+def _tie_rows(D, rng):
+    """fp32 rows whose quotients x / s sit on or near the rounding ties of
+    the int8 code (k + 1/2), around the kernel's near-tie band and on both
+    sides of the smallest normal scale."""
+    rows = []
+    k = np.arange(-127, 127) + 0.5
+    rows.append(np.resize(np.concatenate([[127.0], k]), D))          # s = 1: exact ties
+    for amax in (3.0, 0.7134, 5.5e3, 1.0e-30):
+        s = np.float32(np.float32(amax) / np.float32(127.0))
+        vals = [np.float32(amax)]
+        for d in (0.0, 1e-5, -1e-5, 2.2e-5, -2.2e-5, 4e-5, -4e-5, 5e-5, -5e-5, 6e-5, -6e-5):
+            x = ((k + d) * np.float64(s)).astype(np.float32)
+            vals += list(x) + list(np.nextafter(x, np.float32(np.inf))) + \
+                list(np.nextafter(x, np.float32(-np.inf)))
+        v = np.array(vals, dtype=np.float32)
+        v = np.clip(v, -np.float32(amax), np.float32(amax))
+        rows.append(np.resize(v, D))
+    # scales around the smallest normal float (1.18e-38): amax / 127 below,
+    # at and above it
+    for amax in (1.0e-37, 127 * 1.17549435e-38, 2.0e-36):
+        v = (rng.uniform(-1, 1, D) * amax).astype(np.float32)
+        v[0] = np.float32(amax)
+        rows.append(v)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("D,H", [(1024, 0), (1024, 16), (768, 12)])
+def test_quantize_ties(S, D, H):
+    """Bit-exact codes where the rounding of x / s is decided by its last
+    bits: exact ties (half to even), quotients within a few ulps of a tie,
+    and scales at the smallest normal float."""
+    rng = np.random.default_rng(D + H)
+    rows = _tie_rows(D, rng)
+    n = rows.shape[0]
+    B = 2
+    x = np.stack([rows, rows[::-1]])                                 # [B, n, D]
+    rm, rl, rs = R.quantize_kv(x)
+    cap = n + 1
+    if H:
+        msb = torch.zeros(B, H, cap, D // H // 2, dtype=torch.uint8, device="cuda")
+    else:
+        msb = torch.zeros(B, cap, D // 2, dtype=torch.uint8, device="cuda")
+    lsb = torch.zeros_like(msb)
+    sc = torch.zeros(B, cap, device="cuda")
+    S.quantize_kv(torch.from_numpy(x).cuda(), msb, lsb, sc)
+    if H:
+        gm = msb[:, :, :n].permute(0, 2, 1, 3).reshape(B, n, D // 2).cpu().numpy()
+        gl = lsb[:, :, :n].permute(0, 2, 1, 3).reshape(B, n, D // 2).cpu().numpy()
+    else:
+        gm, gl = msb[:, :n].cpu().numpy(), lsb[:, :n].cpu().numpy()
+    np.testing.assert_array_equal(sc[:, :n].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(gm, rm)
+    np.testing.assert_array_equal(gl, rl)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("B,n,H,dh", [(1, 1, 1, 2), (2, 5, 4, 8), (3, 17, 12, 64), (2, 33, 3, 6)])
 def test_quantize_head_major(S, dtype, B, n, H, dh):

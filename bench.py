@@ -92,8 +92,10 @@ def _kernel_work(cfg, v_kept=None, recompute_frac=None):
             pairs = n * (n + 1) / 2 if cfg.causal else float(n) * m
             add("qkv_gemm", 2.0 * B * n * 3 * h * dh * D,
                 es * (B * n * D + 3 * h * dh * D + 3 * B * n * h * dh))
+            # the output projection's launch also runs the importance
+            # reduction (bf16): column sums read, a read and written
             add("out_gemm", 2.0 * B * n * D * h * dh,
-                es * (B * n * h * dh + D * h * dh + 2 * B * n * D))
+                es * (B * n * h * dh + D * h * dh + 2 * B * n * D) + 4.0 * B * h * m + 8.0 * B * n)
             # Q and O per query, K and V per key
             add("attn_fwd", 4.0 * B * h * dh * pairs, es * 2 * B * h * (n + m) * dh)
             add("attn_colsum", 2.0 * B * h * dh * pairs,

@@ -75,8 +75,12 @@ int layer_prefill(const spatten_layer_desc& d, void* x, const void* wq, const vo
   aa.vtk = head_keys ? ws + w.vtk : aa.vt;
   aa.nk = int(w.nk);
   aa.nk_pad = int(w.nk_pad);
+  // the importance pass rides in the output projection's launch
+  PrefillImp pimp{};
+  aa.imp_out = &pimp;
   SPATTEN_TRY(launch_attention(aa, st));
   OutArgs oa{};
+  oa.pimp = &pimp;
   oa.dtype = d.dtype;
   oa.o = ws + w.o;
   oa.wo = wo;

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "importance.hpp"
 #include "kernels.hpp"
 #include "timing.hpp"
 
@@ -36,7 +37,6 @@ namespace spatten {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // Workgroup i runs on XCD i % 8. Attention grids are 1-D over (block,
 // head, sequence) with the block index fastest; each XCD takes a contiguous
@@ -610,36 +610,42 @@ attn_colsum_f32(AttnArgs a) {
   }
 }
 
-// a[b, j] += sum_s colsum[b, s, j] (heads in order: deterministic);
-// g[b, head_idx[b, s]] += sum_q gpart[b, s, q]; optional natural-log LSE copy.
+// The importance reduction alone (when no tiled output projection follows
+// to carry it): one workgroup per 256 entries of a sequence.
 __global__ void __launch_bounds__(256)
-importance_kernel(AttnArgs a) {
-  const int b = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (a.head_keys) {
-    // per-head pruning: a[b, s, token] += column sum of key j of slot s
-    if (j < a.nk)
-      for (int s = 0; s < a.h_kept; ++s) {
-        const int64_t bs = int64_t(b) * a.h_kept + s;
-        a.a[bs * a.n + a.head_keys[bs * a.nk + j]] += a.colsum[bs * a.n_pad + j];
-      }
-  } else if (j < a.n) {
-    float acc = 0.0f;
-    for (int s = 0; s < a.h_kept; ++s) acc += a.colsum[(int64_t(b) * a.h_kept + s) * a.n_pad + j];
-    a.a[int64_t(b) * a.n + j] += acc;
+importance_kernel(PrefillImp p) {
+  prefill_importance_block(p, int(blockIdx.x));
+}
+
+PrefillImp prefill_imp(const AttnArgs& a) {
+  PrefillImp p{};
+  p.colsum = a.colsum;
+  p.gpart = a.gpart;
+  p.lse = a.lse;
+  p.lse_out = a.lse_out;
+  p.a = a.a;
+  p.g = a.g;
+  p.head_idx = a.head_idx;
+  p.head_keys = a.head_keys;
+  p.batch = a.batch;
+  p.h_kept = a.h_kept;
+  p.H = a.H;
+  p.n = a.n;
+  p.n_pad = a.n_pad;
+  p.nk = a.nk;
+  p.nqb = a.nqb;
+  p.pieces = int(ceil_div(a.n, 256));
+  p.pending = 1;
+  return p;
+}
+
+// After the column sums: hand the importance pass to the caller, or run it.
+int finish_importance(const AttnArgs& a, hipStream_t stream) {
+  if (a.imp_out) {
+    *a.imp_out = prefill_imp(a);
+    return SPATTEN_OK;
   }
-  if (j < a.n) {
-    if (a.lse_out)
-      for (int s = 0; s < a.h_kept; ++s)
-        a.lse_out[(int64_t(b) * a.h_kept + s) * a.n + j] =
-            a.lse[(int64_t(b) * a.h_kept + s) * a.n_pad + j] * kLn2;
-  }
-  if (blockIdx.x == 0 && int(threadIdx.x) < a.h_kept) {
-    const int s = threadIdx.x;
-    float acc = 0.0f;
-    for (int q = 0; q < a.nqb; ++q) acc += a.gpart[(int64_t(b) * a.h_kept + s) * a.nqb + q];
-    a.g[int64_t(b) * a.H + a.head_idx[b * a.h_kept + s]] += acc;
-  }
+  return launch_prefill_importance(prefill_imp(a), stream);
 }
 
 // Per-head pruning: the kept tokens of slot s (head_keys[b, s, 0 .. nk-1])
@@ -702,10 +708,7 @@ int run_bf16(const AttnArgs& a, hipStream_t stream) {
   const dim3 g2(xcd_grid(ceil_div(a.nk, kAttnKBlock) * a.h_kept * a.batch));
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_bf16<DH, CAUSAL><<<g2, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
-  const dim3 g3(unsigned(ceil_div(a.n, 256)), a.batch);
-  SPATTEN_TIMED("importance", stream, importance_kernel<<<g3, 256, 0, stream>>>(a));
-  SPATTEN_LAUNCH_CHECK();
-  return SPATTEN_OK;
+  return finish_importance(a, stream);
 }
 
 template <bool CAUSAL>
@@ -717,13 +720,18 @@ int run_f32(const AttnArgs& a, hipStream_t stream) {
   const dim3 g2(unsigned(ceil_div(a.n, 256)), a.h_kept, a.batch);
   SPATTEN_TIMED("attn_colsum", stream, attn_colsum_f32<CAUSAL><<<g2, 256, 0, stream>>>(a));
   SPATTEN_LAUNCH_CHECK();
-  const dim3 g3(unsigned(ceil_div(a.n, 256)), a.batch);
-  SPATTEN_TIMED("importance", stream, importance_kernel<<<g3, 256, 0, stream>>>(a));
-  SPATTEN_LAUNCH_CHECK();
-  return SPATTEN_OK;
+  return finish_importance(a, stream);
 }
 
 }  // namespace
+
+int launch_prefill_importance(const PrefillImp& p, hipStream_t stream) {
+  if (!p.pending || p.batch == 0 || p.pieces == 0) return SPATTEN_OK;
+  SPATTEN_TIMED("importance", stream,
+                importance_kernel<<<unsigned(p.pieces * p.batch), 256, 0, stream>>>(p));
+  SPATTEN_LAUNCH_CHECK();
+  return SPATTEN_OK;
+}
 
 int launch_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.dtype == SPATTEN_F32) return a.causal ? run_f32<true>(a, stream) : run_f32<false>(a, stream);

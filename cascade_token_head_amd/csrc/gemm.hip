@@ -228,9 +228,11 @@ gemm_bf16_kernel(GemmParams p) {
 // stages of a 256 x 256 tile fit in 128 KB. Epilogue index math is hoisted:
 // column terms once per MFMA column tile, row terms advanced incrementally.
 
+// pimp (output projection): workgroups past the tiles run the prefill
+// importance pass when pimp.pending; the grid then holds its workgroups.
 template <int MODE, int BM, int BN, int NW>
 __global__ void __launch_bounds__(64 * NW, (BM * BN <= 128 * 128) ? 2 : 1)
-gemm_tile_kernel(GemmParams p) {
+gemm_tile_kernel(GemmParams p, PrefillImp pimp) {
   constexpr int BKT = 64;
   constexpr int NT = 64 * NW;                 // threads
   constexpr int WGN = NW == 8 ? 4 : 2;        // waves across N (2 or 4) x 2 across M
@@ -249,6 +251,11 @@ gemm_tile_kernel(GemmParams p) {
   const int ntx = int(ceil_div(p.N, BN));
   const int total = ntx * p.tiles_y;
   const int per_xcd = int(ceil_div(total, 8));
+  if (MODE == kOut && int(blockIdx.x) >= 8 * per_xcd) {
+    // dispatched after every tile, so they run beside the last round
+    prefill_importance_block(pimp, int(blockIdx.x) - 8 * per_xcd);
+    return;
+  }
   const int t = (int(blockIdx.x) & 7) * per_xcd + (int(blockIdx.x) >> 3);
   if (t >= total) return;
   const int grp = t / (GM * ntx), in_grp = t - grp * (GM * ntx);
@@ -656,7 +663,7 @@ gemm_f32_kernel(GemmParams p) {
 }
 
 template <int MODE, int BMt, int BNt, int NW = 4>
-int run_tile(GemmParams& p, hipStream_t stream, const char* name) {
+int run_tile(GemmParams& p, const PrefillImp& pimp, hipStream_t stream, const char* name) {
   if (!p.seq_tiled && p.M_total >= (1 << 24)) p.seq_tiled = 1;
   int tiles_y;
   if (p.seq_tiled) {
@@ -668,9 +675,10 @@ int run_tile(GemmParams& p, hipStream_t stream, const char* name) {
   }
   p.tiles_y = tiles_y;
   const int64_t total = ceil_div(p.N, BNt) * int64_t(tiles_y);
-  const dim3 grid(unsigned(8 * ceil_div(total, 8)));
+  const int64_t imp_blocks = MODE == kOut && pimp.pending ? int64_t(pimp.pieces) * pimp.batch : 0;
+  const dim3 grid(unsigned(8 * ceil_div(total, 8) + imp_blocks));
   SPATTEN_TIMED(name, stream,
-                (gemm_tile_kernel<MODE, BMt, BNt, NW><<<grid, 64 * NW, 0, stream>>>(p)));
+                (gemm_tile_kernel<MODE, BMt, BNt, NW><<<grid, 64 * NW, 0, stream>>>(p, pimp)));
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;
 }
@@ -684,27 +692,39 @@ inline double tile_rounds(const GemmParams& p, int bm, int bn, int per_cu) {
   return std::ceil(tiles / (256.0 * per_cu));
 }
 
+// pimp (output projection, optional): the prefill importance pass, carried
+// by the tiled kernel's launch or run alone before the projection.
 template <int MODE>
-int run_gemm(GemmParams& p, int dtype, hipStream_t stream) {
+int run_gemm(GemmParams& p, int dtype, hipStream_t stream, const PrefillImp* pimp_in = nullptr) {
+  PrefillImp pimp{};
+  if (pimp_in) pimp = *pimp_in;
   const char* name = MODE == kOut ? "out_gemm" : "qkv_gemm";
   const int kt = skinny_kt(p.K);
-  if (MODE != kQkvPrefill && dtype == SPATTEN_BF16 && !p.seq_tiled && p.M_total <= 64 &&
-      p.N % 16 == 0 && kt > 0)
-    return run_skinny<MODE>(p, kt, stream, name);
+  const bool skinny = MODE != kQkvPrefill && dtype == SPATTEN_BF16 && !p.seq_tiled &&
+                      p.M_total <= 64 && p.N % 16 == 0 && kt > 0;
+  const bool tiled = !skinny && dtype == SPATTEN_BF16 && MODE != kQkvDecode;
+  if (pimp.pending && !tiled) {
+    // only the tiled kernel carries the prefill importance pass
+    const int st = launch_prefill_importance(pimp, stream);
+    if (st != SPATTEN_OK) return st;
+    pimp.pending = 0;
+  }
+  if (skinny) return run_skinny<MODE>(p, kt, stream, name);
   if (p.imp.pending) {
     // the projection takes a tiled path: the importance pass runs alone
     const int st = launch_importance(p.imp, stream);
     if (st != SPATTEN_OK) return st;
   }
-  if (dtype == SPATTEN_BF16 && MODE != kQkvDecode) {
+  if (tiled) {
     // 128x128 tiles of four 64x64 waves run two workgroups per CU; 256x256
     // tiles of eight 128x64 waves run one, read a quarter fewer LDS bytes
     // per MFMA and finish a round in ~1.67x the time of a 128x128 round
     // (measured on MI355X: ~20% faster on 4096-deep projections). The
     // larger tile wins when its coarser rounds do not waste more than that.
     const double r128 = tile_rounds(p, 128, 128, 2), r256 = tile_rounds(p, 256, 256, 1);
-    if (p.K >= 256 && 1.67 * r256 < 0.97 * r128) return run_tile<MODE, 256, 256, 8>(p, stream, name);
-    return run_tile<MODE, 128, 128>(p, stream, name);
+    if (p.K >= 256 && 1.67 * r256 < 0.97 * r128)
+      return run_tile<MODE, 256, 256, 8>(p, pimp, stream, name);
+    return run_tile<MODE, 128, 128>(p, pimp, stream, name);
   }
   const int tm = dtype == SPATTEN_BF16 ? BM : FT;
   const int tn = dtype == SPATTEN_BF16 ? BN : FT;
@@ -776,7 +796,7 @@ int launch_out(const OutArgs& a, hipStream_t stream) {
   p.D = a.D;
   p.out0 = a.x;
   if (a.imp) p.imp = *a.imp;
-  return run_gemm<kOut>(p, a.dtype, stream);
+  return run_gemm<kOut>(p, a.dtype, stream, a.pimp);
 }
 
 }  // namespace spatten

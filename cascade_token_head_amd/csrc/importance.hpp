@@ -1,8 +1,10 @@
-// Decode token importance (SpAtten, "B. Motivation": a token's importance
+// Token and head importance (SpAtten, "B. Motivation": a token's importance
 // is the probability mass it receives, summed over heads and queries, and
-// cumulative over layers and steps), applied once every score and row
-// log2-sum-exp of the layer is in the stash. It runs as extra workgroups of
-// the output projection (or alone), so it costs no launch of its own.
+// cumulative over layers and steps; a head's is the magnitude of its
+// output). Decode applies it once every score and row log2-sum-exp of the
+// layer is in the stash; prefill once the column sums and |O| partials are
+// written. Both run as extra workgroups of the output projection's launch
+// (or alone), so they cost no launch of their own.
 #pragma once
 
 #include "common.hpp"
@@ -58,6 +60,37 @@ __device__ __forceinline__ void importance_block(const ImpArgs& p, int blk) {
         if (h0 + u < p.H) acc += fast_exp2(sv[u] - lp[h0 + u]);
     }
     ab[j] = old + acc;
+  }
+}
+
+// Prefill importance, workgroup blk (sequence blk / pieces, entries
+// 256 * piece ..): the reduction the attention's column sums and |O|
+// partials feed. Threads past 256 have nothing to do.
+__device__ __forceinline__ void prefill_importance_block(const PrefillImp& p, int blk) {
+  const int b = blk / p.pieces, piece = blk - b * p.pieces;
+  const int t = threadIdx.x;
+  if (t >= 256) return;
+  const int j = piece * 256 + t;
+  if (p.head_keys) {
+    // per-head pruning: a[b, s, token] += column sum of key j of slot s
+    if (j < p.nk)
+      for (int s = 0; s < p.h_kept; ++s) {
+        const int64_t bs = int64_t(b) * p.h_kept + s;
+        p.a[bs * p.n + p.head_keys[bs * p.nk + j]] += p.colsum[bs * p.n_pad + j];
+      }
+  } else if (j < p.n) {
+    float acc = 0.0f;
+    for (int s = 0; s < p.h_kept; ++s) acc += p.colsum[(int64_t(b) * p.h_kept + s) * p.n_pad + j];
+    p.a[int64_t(b) * p.n + j] += acc;
+  }
+  if (j < p.n && p.lse_out)
+    for (int s = 0; s < p.h_kept; ++s)
+      p.lse_out[(int64_t(b) * p.h_kept + s) * p.n + j] =
+          p.lse[(int64_t(b) * p.h_kept + s) * p.n_pad + j] * 0.6931471805599453f;
+  if (piece == 0 && t < p.h_kept) {
+    float acc = 0.0f;
+    for (int q = 0; q < p.nqb; ++q) acc += p.gpart[(int64_t(b) * p.h_kept + t) * p.nqb + q];
+    p.g[int64_t(b) * p.H + p.head_idx[b * p.h_kept + t]] += acc;
   }
 }
 

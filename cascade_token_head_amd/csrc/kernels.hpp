@@ -55,9 +55,29 @@ struct ImpArgs {
 };
 int launch_importance(const ImpArgs& p, hipStream_t stream);
 
+// Prefill token and head importance from the attention's column sums and
+// |O| partials: a[b, j] += sum over kept heads of colsum (heads in order),
+// g[b, head] += sum of the head's partials, optional natural-log LSE copy.
+// Workgroup blk covers 256 entries of sequence blk / pieces.
+struct PrefillImp {
+  const float* colsum;      // [B, h, n_pad]
+  const float* gpart;       // [B, h, nqb]
+  const float* lse;         // [B, h, n_pad] (log2 units)
+  float* lse_out;           // optional [B, h, n]
+  float* a;                 // [B, n], or [B, h, n] with per-head pruning
+  float* g;                 // [B, H]
+  const int32_t* head_idx;  // [B, h]
+  const int32_t* head_keys; // per-head pruning: [B, h, nk], else null
+  int batch, h_kept, H, n, n_pad, nk, nqb;
+  int pieces;   // ceil(n / 256)
+  int pending;  // 1: still to run
+};
+int launch_prefill_importance(const PrefillImp& p, hipStream_t stream);
+
 // Output projection with residual: x[b, m, :] += O[b, m, :] wo[:, gathered]^T.
-// imp (decode, optional): the layer's importance pass, run by extra
-// workgroups of the projection when it takes the skinny path, else alone.
+// imp (decode) / pimp (prefill), optional: the layer's importance pass, run
+// by extra workgroups of the projection's launch (decode: skinny path;
+// prefill: tiled path), else alone before it.
 struct OutArgs {
   int dtype;
   const void* o;  // [B, n, h_kept*dh]
@@ -66,6 +86,7 @@ struct OutArgs {
   int batch, n, h_kept, dh, D;
   void* x;
   const ImpArgs* imp;
+  const PrefillImp* pimp;
 };
 int launch_out(const OutArgs& a, hipStream_t stream);
 
@@ -94,6 +115,9 @@ struct AttnArgs {
   const void* kk;            // [B, h, nk_pad, dh]
   const void* vtk;           // [B, h, dh, nk_pad]
   int nk, nk_pad;
+  // non-null: the importance pass is not launched but described here, for
+  // the output projection's launch to run
+  PrefillImp* imp_out;
 };
 int launch_attention(const AttnArgs& a, hipStream_t stream);
 
@@ -104,7 +128,7 @@ struct DecodeArgs {
   const void* q;  // [B, D] bf16
   const void* k_cache;
   const void* v_cache;  // [B, cap, D] bf16
-  uint8_t* k_msb;  // quantized planes [B, cap, D/2] and scales [B, cap]
+  uint8_t* k_msb;  // quantized planes [B, H, cap, dh/2] and scales [B, cap]
   uint8_t* k_lsb;
   float* k_scale;
   uint8_t* v_msb;

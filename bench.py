@@ -27,11 +27,16 @@ cascade representative-token selection workloads ada_gpt2 and ada_long
 (fp32 Gram products; their line compares the cascade with a full-Gram
 selection at every layer).
 
-With --graph the timed steps replay one pass captured into a HIP graph (the
-stacks allocate nothing and only enqueue kernels; replays match the eager
-pass bit for bit). The per-kernel pass is always eager.
+Launch mode (--launch): decode workloads replay one pass captured into a
+HIP graph by default (the stacks allocate nothing and only enqueue kernels;
+replays match the eager pass bit for bit), since a decode pass is thousands
+of short launches and the host would otherwise pace the quantized one;
+prefill and selection passes launch eagerly. --launch graph / eager forces
+one mode for every workload (--graph = --launch graph). Each workload's
+object names its mode in `launch`. The per-kernel pass is always eager.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu] [--graph]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+                    [--launch auto|graph|eager]
 """
 from __future__ import annotations
 
@@ -288,6 +293,11 @@ def _step_roof(cfg, work, ms_per_step):
             "achieved": round(a, 1), "frac": round(a / PEAK_HBM_GBS, 4)}
 
 
+def use_graph(cfg, args) -> bool:
+    """Whether the timed passes of this workload replay a captured graph."""
+    return args.launch == "graph" or (args.launch == "auto" and cfg.kind == "decode")
+
+
 def measure(cfg, args, lib, with_cpu: bool) -> dict:
     import torch
 
@@ -357,7 +367,7 @@ def measure(cfg, args, lib, with_cpu: bool) -> dict:
     # nothing and only enqueue kernels once constructed) and each timed step
     # replays it from a freshly loaded state.
     graph = None
-    if args.graph:
+    if use_graph(cfg, args):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -507,6 +517,7 @@ def measure(cfg, args, lib, with_cpu: bool) -> dict:
     torch.cuda.empty_cache()
     return {"value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
             "gpu_ms_per_step": round(gpu_ms / args.steps, 4),
+            "launch": "hip_graph" if use_graph(cfg, args) else "eager",
             "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "config": conf,
             "roofline": roof, "per_layer": per_layer, "kernels": per_kernel,
             "cpu_baseline": cpu}
@@ -611,7 +622,7 @@ def measure_ada(cfg, args, lib, with_cpu: bool) -> dict:
     del layers, st, full
     torch.cuda.empty_cache()
     return {"value": round(value, 1), "ms_per_step": round(ms_per_step, 4),
-            "gpu_ms_per_step": round(gpu_ms, 4), "dtype": "f32",
+            "gpu_ms_per_step": round(gpu_ms, 4), "launch": "eager", "dtype": "f32",
             "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len,
                        "dim": cfg.dim, "layers": cfg.n_layers, "tau": cfg.tau},
             "roofline": roof, "per_layer": per_layer, "kernels": per_kernel,
@@ -636,10 +647,13 @@ def main():
                          "plus " + ", ".join(OTHERS) + ")")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of one pass captured into a HIP graph instead of "
-                         "launching every kernel from the host")
+    ap.add_argument("--launch", choices=("auto", "graph", "eager"), default="auto",
+                    help="auto: decode passes replay a captured HIP graph, the others launch "
+                         "every kernel from the host; graph / eager: that mode everywhere")
+    ap.add_argument("--graph", action="store_true", help="same as --launch graph")
     args = ap.parse_args()
+    if args.graph:
+        args.launch = "graph"
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(sequences are independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
@@ -661,7 +675,7 @@ def main():
            "gpu_ms_per_step": r["gpu_ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": r["dtype"], "data": "synthetic (seeded)",
-           "config": r["config"], "launch": "hip_graph" if args.graph else "eager",
+           "config": r["config"], "launch": r["launch"],
            "roofline": r["roofline"], "per_layer": r["per_layer"], "kernels": r["kernels"],
            "cpu_baseline": r["cpu_baseline"]}
     if "cascade_vs_full" in r:

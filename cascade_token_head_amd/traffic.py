@@ -225,6 +225,71 @@ def mfma_main(a) -> None:
     print(json.dumps(rec))
 
 
+# Issue-level SQ counters summarised per kernel, and the ratios read from
+# them (counts are summed over the shader engines; the ratios of two counts
+# of one run do not depend on that).
+SQ_RATIOS = (
+    ("valu_insts_per_mfma", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"),
+    ("trans_insts_per_mfma", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA"),
+    ("lds_insts_per_mfma", "SQ_INSTS_LDS", "SQ_INSTS_MFMA"),
+    ("wave_cycles_waiting_on_dependencies", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("wave_cycles_issuing_valu", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+    ("wave_cycles_issuing_lds", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("wave_cycles_waiting_on_lds", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("mfma_busy_with_valu_coissued", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES"),
+    ("lds_bank_conflicts_per_lds_inst", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"),
+)
+
+
+def sq_main(a) -> None:
+    kernels = [kv.split("=", 1) for kv in a.kernel]
+    per = {}
+    for label, rx in kernels:
+        vals = {}
+        for path in a.counters:
+            names = set()
+            with open(path, newline="") as f:
+                for row in csv.DictReader(f):
+                    names.add(row["Counter_Name"])
+            for c in sorted(names):
+                d = per_dispatch(path, c, rx)
+                if d:
+                    vals[c] = sum(d.values()) / len(d)
+        if not vals:
+            sys.exit("kernel %r not found in the counter runs" % rx)
+        per[label] = vals
+    rec = {"workload": a.workload, "kernels": {k: v for k, v in per.items()},
+           "ratios": {}, "command": a.command,
+           "source_sha1": {label: source_sha1(label) for label, _ in kernels}}
+    for label, vals in per.items():
+        rec["ratios"][label] = {name: round(vals[n] / vals[d], 4)
+                                for name, n, d in SQ_RATIOS if n in vals and vals.get(d)}
+    os.makedirs(a.out, exist_ok=True)
+    base = os.path.join(a.out, "sq_%s_%s" % (a.name, a.workload))
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    labels = [k for k, _ in kernels]
+    with open(base + ".md", "w") as f:
+        f.write("# Issue counters: %s on %s\n\n" % (", ".join(labels), a.workload))
+        f.write("SQ counters per dispatch (averages over the matching dispatches of each "
+                "rocprofv3 --pmc pass; counts summed over the shader engines), and the "
+                "ratios read from them.\n\n")
+        f.write("| ratio | " + " | ".join(labels) + " |\n|---|" + "---|" * len(labels) + "\n")
+        for name, _, _ in SQ_RATIOS:
+            f.write("| %s | %s |\n" % (name, " | ".join(
+                str(rec["ratios"][l].get(name, "")) for l in labels)))
+        f.write("\n| counter | " + " | ".join(labels) + " |\n|---|" + "---|" * len(labels) + "\n")
+        names = sorted(set().union(*[set(v) for v in per.values()]))
+        for c in names:
+            f.write("| %s | %s |\n" % (c, " | ".join(
+                "%.4g" % per[l][c] if c in per[l] else "" for l in labels)))
+        f.write("\nkernel symbol regexes: %s\n\nsource sha1: %s\n\ncommand:\n\n```\n%s\n```\n"
+                % (", ".join("%s `%s`" % (l, r) for l, r in kernels),
+                   ", ".join("%s `%s`" % (l, rec["source_sha1"][l]) for l in labels), a.command))
+    print(json.dumps(rec["ratios"]))
+
+
 def trace_main(a) -> None:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run: the
     kernels by share of GPU time, with the command that produced it."""
@@ -308,6 +373,13 @@ def main() -> None:
     m.add_argument("--shape", default="32x32x16", choices=sorted(MFMA_FLOPS))
     m.add_argument("--command", default="")
     m.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    q = sub.add_parser("sq")
+    q.add_argument("--name", required=True, help="file name stem, e.g. attention")
+    q.add_argument("--workload", required=True)
+    q.add_argument("--kernel", action="append", required=True, help="label=symbol regex")
+    q.add_argument("--counters", nargs="+", required=True, help="counter CSVs, one per pass")
+    q.add_argument("--command", default="")
+    q.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
     if a.cmd == "copy":
         copy_main(a.mib)
@@ -317,6 +389,8 @@ def main() -> None:
         trace_main(a)
     elif a.cmd == "mfma":
         mfma_main(a)
+    elif a.cmd == "sq":
+        sq_main(a)
     else:
         summarize_main(a)
 

@@ -146,3 +146,35 @@ def test_trace_summary_orders_kernels_by_time(tmp_path):
     assert text.index("big_kernel") < text.index("small_kernel")
     assert "| `big_kernel` | 3 | 3.00 | 2.90 | 3.10 | 90.0% |" in text
     assert "cmd" in text
+
+
+def test_issue_counter_summary_ratios(tmp_path):
+    """SQ counters average over a kernel's dispatches across several pass
+    files, and the ratios are quotients of those averages."""
+    _counter_csv(tmp_path / "p1.csv", [
+        {"Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v}
+        for d, k, c, v in [
+            (1, "attn_fwd_bf16<128, true, 1, 1, false>", "SQ_INSTS_MFMA", 100),
+            (2, "attn_fwd_bf16<128, true, 1, 1, false>", "SQ_INSTS_MFMA", 300),
+            (1, "attn_fwd_bf16<128, true, 1, 1, false>", "SQ_WAVE_CYCLES", 1000),
+            (2, "attn_fwd_bf16<128, true, 1, 1, false>", "SQ_WAVE_CYCLES", 3000),
+            (3, "other_kernel", "SQ_INSTS_MFMA", 7)]])
+    _counter_csv(tmp_path / "p2.csv", [
+        {"Dispatch_Id": d, "Kernel_Name": "attn_fwd_bf16<128, true, 1, 1, false>",
+         "Counter_Name": c, "Counter_Value": v}
+        for d, c, v in [(4, "SQ_INSTS_VALU", 1400), (5, "SQ_INSTS_VALU", 1400),
+                        (4, "SQ_WAIT_INST_ANY", 500), (5, "SQ_WAIT_INST_ANY", 700)]])
+    class A:
+        name, workload, kernel = "attention", "w", ["attn_fwd=attn_fwd_bf16<128, true"]
+        counters = [str(tmp_path / "p1.csv"), str(tmp_path / "p2.csv")]
+        command, out = "cmd", str(tmp_path)
+    traffic.sq_main(A)
+    rec = json.load(open(tmp_path / "sq_attention_w.json"))
+    k = rec["kernels"]["attn_fwd"]
+    assert k["SQ_INSTS_MFMA"] == 200 and k["SQ_WAVE_CYCLES"] == 2000 and k["SQ_INSTS_VALU"] == 1400
+    rt = rec["ratios"]["attn_fwd"]
+    assert rt["valu_insts_per_mfma"] == 7.0
+    assert rt["wave_cycles_waiting_on_dependencies"] == 0.3
+    assert "trans_insts_per_mfma" not in rt      # its counter was not collected
+    md = open(tmp_path / "sq_attention_w.md").read()
+    assert "| valu_insts_per_mfma | 7.0 |" in md and "cmd" in md

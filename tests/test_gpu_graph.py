@@ -81,6 +81,9 @@ DECODE = {
     "perhead_rolling_vprune": scaled(GPT2_DECODE, batch=3, n_layers=3, cache_len=200,
                                      cache_keep=80, steps=5, prune_every=1, per_head=True,
                                      v_threshold=1e-3),
+    # the configurations bench.py times as graph replays, at full size
+    "gpt2_decode": GPT2_DECODE,
+    "pq_decode": PQ_DECODE,
 }
 
 

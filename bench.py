@@ -655,8 +655,9 @@ def main():
     if args.graph:
         args.launch = "graph"
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sequences are independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(the sequences of a batch are independent, so a batch would shard by sequence)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -646,7 +646,7 @@ def main():
                     help="measure only this workload (default: long_causal as the headline, "
                          "plus " + ", ".join(OTHERS) + ")")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--launch", choices=("auto", "graph", "eager"), default="auto",
                     help="auto: decode passes replay a captured HIP graph, the others launch "
                          "every kernel from the host; graph / eager: that mode everywhere")

@@ -42,6 +42,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // head, sequence) with the block index fastest; each XCD takes a contiguous
 // run of that order, so the blocks of one head run on one XCD together and
 // re-read that head's K/V (forward) or Q (column sums) from its own L2.
+// Block 0 is the longest one (causal). When an XCD holds whole (head,
+// sequence) groups but only a few blocks per CU, its groups are dispatched
+// interleaved by block (every group's longest block first) instead of one
+// group after another, which would leave the last group's long blocks to
+// start late and run alone.
 struct XcdItem {
   bool valid;
   int blk, s, b;
@@ -49,7 +54,12 @@ struct XcdItem {
 __device__ __forceinline__ XcdItem xcd_item(int nblk, int h, int batch) {
   const int total = nblk * h * batch;
   const int per = (total + 7) / 8;
-  const int t = (int(blockIdx.x) & 7) * per + (int(blockIdx.x) >> 3);
+  const int x = int(blockIdx.x) & 7, u = int(blockIdx.x) >> 3;
+  int t = x * per + u;
+  if ((h * batch) % 8 == 0 && per <= 128) {
+    const int groups = per / nblk;  // whole groups per XCD
+    t = x * per + (u % groups) * nblk + u / groups;
+  }
   XcdItem it;
   it.valid = t < total;
   it.blk = t % nblk;

@@ -40,21 +40,26 @@ template <> struct VecT<4> { using T = uint32_t; };
 template <> struct VecT<2> { using T = uint16_t; };
 template <> struct VecT<1> { using T = uint8_t; };
 
-template <int V>
+// Unit u of the tensor's batch * k rows: row u / upr, sequence row / k.
+// I is the index type: 32-bit unsigned when every unit index of the launch
+// fits (its divisions are a few instructions), 64-bit otherwise.
+template <int V, typename I>
 __device__ __forceinline__ void copy_units(const CompactTensor& t, const int32_t* __restrict__ idx,
                                            int k, int64_t total, int64_t start, int64_t step) {
   using T = typename VecT<V>::T;
-  const int64_t upr = t.row_bytes / V;
-  for (int64_t u = start; u < total; u += step) {
-    const int64_t row = u / upr, part = u - row * upr;
-    const int64_t b = row / k, r = row - b * k;
-    const int64_t sr = idx[b * k + r];
-    const T* s = reinterpret_cast<const T*>(t.src + b * t.sbs + sr * t.row_bytes) + part;
-    T* d = reinterpret_cast<T*>(t.dst + b * t.dbs + r * t.row_bytes) + part;
+  const I upr = I(t.row_bytes / V), kk = I(k);
+  for (int64_t u64 = start; u64 < total; u64 += step) {
+    const I u = I(u64);
+    const I row = u / upr, part = u - row * upr;
+    const I b = row / kk, r = row - b * kk;
+    const int64_t sr = idx[int64_t(row)];
+    const T* s = reinterpret_cast<const T*>(t.src + int64_t(b) * t.sbs + sr * t.row_bytes) + part;
+    T* d = reinterpret_cast<T*>(t.dst + int64_t(b) * t.dbs + int64_t(r) * t.row_bytes) + part;
     *d = *s;
   }
 }
 
+template <typename I>
 __global__ void __launch_bounds__(256)
 compact_kernel(CompactParams p, const int32_t* __restrict__ idx, int batch, int k) {
   const CompactTensor& t = p.t[blockIdx.y];
@@ -62,11 +67,11 @@ compact_kernel(CompactParams p, const int32_t* __restrict__ idx, int batch, int 
   const int64_t start = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t step = int64_t(gridDim.x) * blockDim.x;
   switch (t.vec_shift) {
-    case 4: copy_units<16>(t, idx, k, total, start, step); break;
-    case 3: copy_units<8>(t, idx, k, total, start, step); break;
-    case 2: copy_units<4>(t, idx, k, total, start, step); break;
-    case 1: copy_units<2>(t, idx, k, total, start, step); break;
-    default: copy_units<1>(t, idx, k, total, start, step); break;
+    case 4: copy_units<16, I>(t, idx, k, total, start, step); break;
+    case 3: copy_units<8, I>(t, idx, k, total, start, step); break;
+    case 2: copy_units<4, I>(t, idx, k, total, start, step); break;
+    case 1: copy_units<2, I>(t, idx, k, total, start, step); break;
+    default: copy_units<1, I>(t, idx, k, total, start, step); break;
   }
 }
 
@@ -221,9 +226,15 @@ int launch_compact(int n_tensors, const void* const* src, void* const* dst,
     }
     int64_t blocks = ceil_div(max_units, 256);
     if (blocks > 8192) blocks = 8192;
-    SPATTEN_TIMED("compact", stream,
-                  compact_kernel<<<dim3(unsigned(blocks), cnt), dim3(256), 0, stream>>>(p, idx,
-                                                                                    batch, k));
+    // 32-bit unit indices while the largest, plus one grid stride, stay below 2^31
+    if (max_units + blocks * 256 < (int64_t(1) << 31))
+      SPATTEN_TIMED("compact", stream,
+                    compact_kernel<uint32_t><<<dim3(unsigned(blocks), cnt), dim3(256), 0, stream>>>(
+                        p, idx, batch, k));
+    else
+      SPATTEN_TIMED("compact", stream,
+                    compact_kernel<int64_t><<<dim3(unsigned(blocks), cnt), dim3(256), 0, stream>>>(
+                        p, idx, batch, k));
     SPATTEN_LAUNCH_CHECK();
   }
   return SPATTEN_OK;

@@ -56,6 +56,8 @@ topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, i
                   int32_t* __restrict__ out_idx, float* __restrict__ kth_out) {
   __shared__ uint32_t hist[256];
   __shared__ int scan_buf[kMaxWaves];
+  // per (j, wave) counts of > T and == T keys, then their exclusive prefixes
+  __shared__ int pre_gt[PT > 0 ? PT * kMaxWaves : 1], pre_eq[PT > 0 ? PT * kMaxWaves : 1];
   __shared__ uint32_t sh_digit;
   __shared__ int sh_krem;
 
@@ -149,27 +151,88 @@ topk_radix_kernel(const float* __restrict__ scores, int n, int64_t row_stride, i
 
   // ordered selection: key > T, or key == T among the first krem ties
   int32_t* out = out_idx + int64_t(b) * k;
-  int run_sel = 0, run_eq = 0;
+  if constexpr (PT > 0) {
+    // Element i = j * nthreads + 64 * wave + lane, so index order is (j,
+    // wave, lane). Count the > T and == T keys of every (j, wave), turn the
+    // counts into exclusive prefixes in that order (one wave scans them),
+    // and each key's output position is then the number of > T keys before
+    // it plus the number of selected ties before it, min(== T before, krem).
+    const int E = iters * nwaves;  // (j, wave) pairs, at most PT * kMaxWaves
 #pragma unroll
-  for (int j = 0; j < (PT > 0 ? PT : 1 << 20); ++j) {
-    if (j >= iters || run_sel >= k) break;  // uniform
-    const int i = tid + j * nthreads;
-    uint32_t key = 0;
-    if (i < n) key = key_at(j, i);
-    const bool gt = i < n && key > T;
-    const bool eq = i < n && key == T;
-    const uint64_t eqm = __ballot(eq);
-    int eq_tot;
-    const int eq_off = wave_offsets(__popcll(eqm), wave, nwaves, lane, scan_buf, &eq_tot);
-    const int eq_rank = run_eq + eq_off + __popcll(eqm & lanemask_lt(lane));
-    const bool sel = gt || (eq && eq_rank < krem);
-    const uint64_t selm = __ballot(sel);
-    int sel_tot;
-    const int sel_off = wave_offsets(__popcll(selm), wave, nwaves, lane, scan_buf, &sel_tot);
-    const int pos = run_sel + sel_off + __popcll(selm & lanemask_lt(lane));
-    if (sel && pos < k) out[pos] = i;
-    run_sel += sel_tot;
-    run_eq += eq_tot;
+    for (int j = 0; j < PT; ++j) {
+      if (j >= iters) break;  // uniform
+      const int i = tid + j * nthreads;
+      const uint32_t key = keys[j];
+      const uint64_t gtm = __ballot(i < n && key > T);
+      const uint64_t eqm = __ballot(i < n && key == T);
+      if (lane == 0) {
+        pre_gt[j * nwaves + wave] = __popcll(gtm);
+        pre_eq[j * nwaves + wave] = __popcll(eqm);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int per = (E + 63) / 64, e0 = lane * per;
+      int sg = 0, se = 0;
+      for (int e = e0; e < e0 + per && e < E; ++e) {
+        sg += pre_gt[e];
+        se += pre_eq[e];
+      }
+      int ig = sg, ie = se;  // inclusive scans over the lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int yg = __shfl_up(ig, o, 64), ye = __shfl_up(ie, o, 64);
+        if (lane >= o) {
+          ig += yg;
+          ie += ye;
+        }
+      }
+      int rg = ig - sg, re = ie - se;  // this lane's exclusive starts
+      for (int e = e0; e < e0 + per && e < E; ++e) {
+        const int cg = pre_gt[e], ce = pre_eq[e];
+        pre_gt[e] = rg;
+        pre_eq[e] = re;
+        rg += cg;
+        re += ce;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      if (j >= iters) break;  // uniform
+      const int i = tid + j * nthreads;
+      const uint32_t key = keys[j];
+      const bool gt = i < n && key > T;
+      const bool eq = i < n && key == T;
+      const uint64_t lt = lanemask_lt(lane);
+      const int gt_before = pre_gt[j * nwaves + wave] + __popcll(__ballot(gt) & lt);
+      const int eq_before = pre_eq[j * nwaves + wave] + __popcll(__ballot(eq) & lt);
+      const bool sel = gt || (eq && eq_before < krem);
+      const int pos = gt_before + (eq_before < krem ? eq_before : krem);
+      if (sel && pos < k) out[pos] = i;
+    }
+  } else {
+    int run_sel = 0, run_eq = 0;
+    for (int j = 0;; ++j) {
+      if (j >= iters || run_sel >= k) break;  // uniform
+      const int i = tid + j * nthreads;
+      uint32_t key = 0;
+      if (i < n) key = key_at(j, i);
+      const bool gt = i < n && key > T;
+      const bool eq = i < n && key == T;
+      const uint64_t eqm = __ballot(eq);
+      int eq_tot;
+      const int eq_off = wave_offsets(__popcll(eqm), wave, nwaves, lane, scan_buf, &eq_tot);
+      const int eq_rank = run_eq + eq_off + __popcll(eqm & lanemask_lt(lane));
+      const bool sel = gt || (eq && eq_rank < krem);
+      const uint64_t selm = __ballot(sel);
+      int sel_tot;
+      const int sel_off = wave_offsets(__popcll(selm), wave, nwaves, lane, scan_buf, &sel_tot);
+      const int pos = run_sel + sel_off + __popcll(selm & lanemask_lt(lane));
+      if (sel && pos < k) out[pos] = i;
+      run_sel += sel_tot;
+      run_eq += eq_tot;
+    }
   }
 }
 

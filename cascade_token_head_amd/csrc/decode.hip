@@ -482,26 +482,52 @@ __device__ __forceinline__ void bh_raise(BhState<DPL>& st, float bm) {
   }
 }
 
+// Keeps the loads requested before it in front of the code after it: the
+// compiler would otherwise sink a pass's first batch of loads below the
+// wait for the query (into the pass's loop), serialising two round trips.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+// Returns w unchanged, from behind an empty asm statement: code using the
+// result stays below an earlier issue_fence, and so does the wait for w.
+__device__ __forceinline__ u32x4 after_fence(u32x4 w) {
+  asm volatile("" : "+v"(w));
+  return w;
+}
+
 // bf16 cache: rows r0..r1-1 of head h; row r0 + g + 32 i belongs to row group g.
-__device__ __forceinline__ void bh_pass_bf16(const DecodeArgs& a, int b, int h, int g, int cl,
-                                             int r0, int r1, const float* q, BhState<8>& st) {
-  constexpr int LPR = BhCfg<kBf16>::LPR, NG = BhCfg<kBf16>::NT / LPR, KBb = BhCfg<kBf16>::KB;
+// One load batch: this lane's 16-byte slices of K and V of KB rows.
+struct BfRows {
+  u32x4 k[BhCfg<kBf16>::KB], v[BhCfg<kBf16>::KB];
+};
+
+// Requests batch i0 (rows r0 + g + 32 (i0 + u)); past r1 a valid row is
+// read and masked later.
+__device__ __forceinline__ void bh_load_bf16(const DecodeArgs& a, int b, int h, int g, int cl,
+                                             int r0, int r1, int i0, BfRows& t) {
+  constexpr int NG = BhCfg<kBf16>::NT / BhCfg<kBf16>::LPR, KBb = BhCfg<kBf16>::KB;
   const int D = a.H * 64;
   const int64_t rowb = int64_t(b) * a.cap;
   const bf16_t* kc = static_cast<const bf16_t*>(a.k_cache) + h * 64 + 8 * cl;
   const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache) + h * 64 + 8 * cl;
+#pragma unroll
+  for (int u = 0; u < KBb; ++u) {
+    const int j = r0 + g + NG * (i0 + u);
+    const int64_t row = rowb + (j < r1 ? j : r0);
+    t.k[u] = *reinterpret_cast<const u32x4*>(kc + row * D);
+    t.v[u] = *reinterpret_cast<const u32x4*>(vc + row * D);
+  }
+}
+
+// The pass over the rows; t holds batch 0 on entry (requested by the caller
+// before it waited for the query, so the two round trips overlap).
+__device__ __forceinline__ void bh_pass_bf16(const DecodeArgs& a, int b, int h, int g, int cl,
+                                             int r0, int r1, const float* q, BhState<8>& st,
+                                             BfRows& t) {
+  constexpr int NG = BhCfg<kBf16>::NT / BhCfg<kBf16>::LPR, KBb = BhCfg<kBf16>::KB;
   float* srow = a.scores + (int64_t(b) * a.H + h) * a.lc_pad;
   const float sc = kLog2e * 0.125f;  // log2(e) / sqrt(64)
   const int nit = (r1 - r0 + NG - 1) / NG;
   for (int i0 = 0; i0 < nit; i0 += KBb) {
-    u32x4 kr[KBb], vr[KBb];
-#pragma unroll
-    for (int u = 0; u < KBb; ++u) {
-      const int j = r0 + g + NG * (i0 + u);
-      const int64_t row = rowb + (j < r1 ? j : r0);  // past the range: a valid row, masked
-      kr[u] = *reinterpret_cast<const u32x4*>(kc + row * D);
-      vr[u] = *reinterpret_cast<const u32x4*>(vc + row * D);
-    }
+    if (i0 > 0) bh_load_bf16(a, b, h, g, cl, r0, r1, i0, t);
     float s[KBb];
     float bm = -INFINITY;
 #pragma unroll
@@ -509,8 +535,8 @@ __device__ __forceinline__ void bh_pass_bf16(const DecodeArgs& a, int b, int h, 
       float d = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        d = fmaf(q[2 * e], __uint_as_float(kr[u][e] << 16), d);
-        d = fmaf(q[2 * e + 1], __uint_as_float(kr[u][e] & 0xffff0000u), d);
+        d = fmaf(q[2 * e], __uint_as_float(t.k[u][e] << 16), d);
+        d = fmaf(q[2 * e + 1], __uint_as_float(t.k[u][e] & 0xffff0000u), d);
       }
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
@@ -528,8 +554,8 @@ __device__ __forceinline__ void bh_pass_bf16(const DecodeArgs& a, int b, int h, 
       st.l += p;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        st.acc[2 * e] = fmaf(p, __uint_as_float(vr[u][e] << 16), st.acc[2 * e]);
-        st.acc[2 * e + 1] = fmaf(p, __uint_as_float(vr[u][e] & 0xffff0000u), st.acc[2 * e + 1]);
+        st.acc[2 * e] = fmaf(p, __uint_as_float(t.v[u][e] << 16), st.acc[2 * e]);
+        st.acc[2 * e + 1] = fmaf(p, __uint_as_float(t.v[u][e] & 0xffff0000u), st.acc[2 * e + 1]);
       }
     }
   }
@@ -720,21 +746,35 @@ decode_bh(DecodeArgs a) {
   const int D = a.H * 64;
   const bf16_t* qp = static_cast<const bf16_t*>(a.q) + int64_t(b) * D + h * 64 + DPL * cl;
   float q[DPL];
-  load8_f32(qp, q);
-  if constexpr (DPL == 16) load8_f32(qp + 8, q + 8);
   float qsum = 0.0f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) qsum += q[e];
   BhState<DPL> st;
   bh_reset(st);
   float M, L, o;
   float cm;
   bool flag = false;
   if constexpr (KIND == kBf16) {
-    bh_pass_bf16(a, b, h, g, cl, 0, a.lc, q, st);
+    // the query's words are requested first and converted only after the
+    // first batch of cache rows has been requested too
+    const u32x4 qw = *reinterpret_cast<const u32x4*>(qp);
+    BfRows rows;
+    bh_load_bf16(a, b, h, g, cl, 0, a.lc, 0, rows);
+    issue_fence();
+    const u32x4 w = after_fence(qw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[2 * e] = __uint_as_float(w[e] << 16);
+      q[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+    bh_pass_bf16(a, b, h, g, cl, 0, a.lc, q, st, rows);
     bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M, &L, &o);
     cm = 1.0f / L;
   } else {
+    // the query first (requesting the first batch of plane rows before
+    // its wait, as the bf16 path does, measured slower here)
+    load8_f32(qp, q);
+    load8_f32(qp + 8, q + 8);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qsum += q[e];
     // this step's k and v rows: requested now, used after the old rows
     float xk[8], xv[8];
     const bool hasx = t < D / 8;

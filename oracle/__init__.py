@@ -51,18 +51,37 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       the mass; keeping every key reproduces the dense stack.
   run_prefill_perhead every per-head cut keeps that head's largest
                       importance among its own keys and never revives one;
-                      heads choose different keys.
+                      heads choose different keys; on the equal-query
+                      inputs (see run_prefill) the whole per-head cascade
+                      against its closed form (one softmax per head over its
+                      own keys).
   ada_ref (module)    see tests/test_ada_oracle.py: brute force, closed
                       forms, cascade from all / no tokens, a hand-worked
-                      case, Proposition 4.
-  run_prefill /       parity unpinned beyond the composition of the pinned
-  run_decode          parts (the pages print no worked example). Invariants
-                      checked: total importance per layer, value pruning
-                      leaves importance unchanged, every rolling cut keeps
-                      the largest entries (brute force over candidates) and
-                      never revives a pruned one, a budget that never cuts
-                      reproduces the plain run; per-head pruning reduces to
-                      the shared cut for one head and for identical heads,
-                      and each head's cut keeps that head's largest entries.
+                      case, Proposition 4; run_cascade's sets and Gram pair
+                      counts over a four-layer stack against scalar loops
+                      over the three steps.
+  run_prefill         closed form: with every token's query equal (x[:, 0]
+                      = 1, Wq zero outside row 0, Wo writing nothing into
+                      column 0) each head's probability rows are one vector
+                      softmax (bidirectional) or its prefix-normalised form
+                      (causal); the whole cascade - outputs, cumulative token
+                      and head importance, token and head cuts, compacted
+                      positions - is recomputed from that without a score
+                      matrix, on a case where the cumulative and the last
+                      layer's importance choose different sets. Also: total
+                      importance per layer, keep-all = repeated dense layers.
+  run_decode          closed form at q = 0: every cache entry takes 1/Lc per
+                      head, so each layer adds the mean V row times Wo, the
+                      importance is layers x heads / Lc per step and cuts
+                      keep the longest-present entries; checked over five
+                      steps with the cut once, rolling, per head and under
+                      progressive quantization across the threshold. Also:
+                      value pruning leaves importance unchanged, every rolling
+                      cut keeps the largest entries (brute force over
+                      candidates) and never revives a pruned one, a budget
+                      that never cuts reproduces the plain run; per-head
+                      pruning reduces to the shared cut for one head and for
+                      identical heads, and each head's cut keeps that head's
+                      largest entries.
 """
 from . import ada_ref, spatten_ref, topk_engine  # noqa: F401

@@ -151,3 +151,62 @@ def test_synthetic_activations_keep_a_coherent_set():
         union = np.union1d(a["set"], b["set"]).size
         assert inter / union > 0.5
     assert 0 < recs[0]["set"].size < cfg.seq_len
+
+
+def _brute_cos(X, t, s):
+    nt = math.sqrt(sum(v * v for v in X[t]))
+    ns = math.sqrt(sum(v * v for v in X[s]))
+    if nt == 0 or ns == 0:
+        return 0.0
+    return sum(X[t][c] * X[s][c] for c in range(len(X[t]))) / (nt * ns)
+
+
+def _brute_cascade(layers, tau):
+    """The page's three steps over a stack, written as scalar loops: layer 1
+    keeps the full-Gram selection; each later layer drops the inherited
+    members that come close to an earlier inherited member, then adds the
+    other tokens that come close to no earlier member that stayed. Returns
+    per layer (set, Gram pairs read)."""
+    theta = 1.0 - tau * tau
+    out, prev = [], None
+    for X in layers:
+        X = np.asarray(X, dtype=np.float64).tolist()
+        T = len(X)
+        if prev is None:
+            sel = _brute_selection(X, tau)
+            out.append((sel, T * (T - 1) // 2))
+        else:
+            R = sorted(prev)
+            valid = [t for t in R if all(_brute_cos(X, t, s) < theta for s in R if s < t)]
+            others = [u for u in range(T) if u not in R]
+            added = [u for u in others
+                     if all(_brute_cos(X, u, s) < theta for s in valid if s < u)]
+            pairs = sum(1 for t in R for s in R if s < t)
+            pairs += sum(1 for u in others for s in valid if s < u)
+            sel = sorted(valid + added)
+            out.append((sel, pairs))
+        prev = out[-1][0]
+    return out
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_run_cascade_matches_brute_force_loops(seed):
+    """The whole stack: sets and Gram pairs of every layer against scalar
+    loops over the definitions, on clustered activations small enough for
+    them (18 tokens, 4 layers, a drift that turns some tokens over)."""
+    rng = np.random.default_rng(seed)
+    centres = rng.standard_normal((5, 4))
+    X = centres[rng.integers(0, 5, 18)] + 0.25 * rng.standard_normal((18, 4))
+    layers = []
+    for _ in range(4):
+        layers.append(X.copy())
+        X = X + 0.3 * rng.standard_normal(X.shape)
+    recs = A.run_cascade(layers, 0.3)
+    want = _brute_cascade(layers, 0.3)
+    changed = False
+    for l, (r, (sel, pairs)) in enumerate(zip(recs, want)):
+        assert r["set"].tolist() == sel, l
+        assert r["gram_pairs"] == pairs, l
+        if l > 0:
+            changed |= (r["set"].tolist() != recs[l - 1]["set"].tolist())
+    assert changed  # some layer removes or adds a token

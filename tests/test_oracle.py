@@ -976,3 +976,233 @@ def test_perhead_prefill_cuts_keep_each_heads_largest_and_never_revive():
     assert len(tr[2]["heads"]) == 2
     rest = np.setdiff1d(tr[1]["heads"], tr[2]["heads"])
     assert g[tr[2]["heads"]].min() >= g[rest].max()
+
+
+# ------------------------------------------------- closed-form cascades
+#
+# Inputs under which every query of a head sees the same scores: x[:, 0] = 1
+# for every token, Wq is zero outside row 0 and Wo writes nothing into
+# column 0, so column 0 stays 1 through every layer and head h's query is
+# row 0 of its Wq columns for every token. The score of key j is then a
+# function of the key alone, each probability row is one vector softmax
+# (bidirectional) or its prefix-normalised form (causal), and the whole
+# cascade - importance accumulated over layers, token and head cuts,
+# compaction of x, a and positions - has a closed form that never builds a
+# score matrix.
+
+
+def _rank_one_inputs(cfg, seed=0):
+    inp = make_prefill_inputs(cfg, seed=seed)
+    inp["x"][:, :, 0] = 1.0
+    for w in inp["layers"]:
+        w["wq"][1:, :] = 0.0
+        w["wo"][:, 0] = 0.0
+    return inp
+
+
+def _rank_one_head(e, V, causal):
+    """Column sums and output rows of a head whose probability of key j in
+    row i is proportional to e_j (keys j <= i when causal).
+    Bidirectional: every row is e / sum(e), so column j sums to
+    n e_j / sum(e) and every output row is e V / sum(e).
+    Causal: row i is e_j / Z_i with Z_i = e_0 + ... + e_i, so column j sums
+    to e_j (1/Z_j + ... + 1/Z_{n-1}) and output row i is
+    (e_0 V_0 + ... + e_i V_i) / Z_i."""
+    n = e.shape[0]
+    if not causal:
+        Z = e.sum()
+        return n * e / Z, np.broadcast_to(e @ V / Z, V.shape)
+    Z = np.cumsum(e)
+    tail = np.cumsum((1.0 / Z)[::-1])[::-1]
+    return e * tail, np.cumsum(e[:, None] * V, axis=0) / Z[:, None]
+
+
+def _largest(v, k):
+    """Indices of the k largest fp32 values (lower index first on ties),
+    ascending, by a plain sort."""
+    v32 = np.asarray(v, np.float32)
+    order = sorted(range(v32.shape[0]), key=lambda j: (-float(v32[j]), j))
+    return np.sort(np.array(order[:k], dtype=np.int64))
+
+
+def _closed_form_cascade(cfg, inp, b):
+    dh = cfg.head_dim
+    x = inp["x"][b].astype(np.float64)
+    n0 = x.shape[0]
+    pos, heads = np.arange(n0), np.arange(cfg.n_heads)
+    a, g = np.zeros(n0), np.zeros(cfg.n_heads)
+    trace = []
+    for l in range(cfg.n_layers):
+        w = {k_: v_.astype(np.float64) for k_, v_ in inp["layers"][l].items()}
+        delta, dcol, dg = np.zeros_like(x), np.zeros(x.shape[0]), np.zeros(cfg.n_heads)
+        for h in heads:
+            c = slice(h * dh, (h + 1) * dh)
+            s = (x @ w["wk"][:, c]) @ w["wq"][0, c] / math.sqrt(dh)
+            col, O = _rank_one_head(np.exp(s - s.max()), x @ w["wv"][:, c], cfg.causal)
+            dcol += col
+            dg[h] = np.abs(O).sum()
+            delta += O @ w["wo"][c, :]
+        x, a, g = x + delta, a + dcol, g + dg
+        rec = {"pos": pos, "heads": heads, "a": a, "g": g, "x": x, "dcol": dcol, "dg": dg}
+        if l + 1 < cfg.n_layers:
+            if cfg.heads[l + 1] != len(heads):
+                heads = heads[_largest(g[heads], cfg.heads[l + 1])]
+            keep = _largest(a, cfg.tokens[l + 1])
+            x, a, pos = x[keep], a[keep], pos[keep]
+        trace.append(rec)
+    return trace
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_run_prefill_matches_closed_form_cascade(causal):
+    cfg = scaled(TINY, n_layers=4, tokens=(40, 30, 22, 16), heads=(4, 4, 3, 2), causal=causal,
+                 batch=4)
+    inp = _rank_one_inputs(cfg)
+    out = R.run_prefill(cfg, inp)
+    sensitive_tok = sensitive_head = False
+    for b in range(cfg.batch):
+        want = _closed_form_cascade(cfg, inp, b)
+        got = out[b]["trace"]
+        for l, (wr, gr) in enumerate(zip(want, got)):
+            np.testing.assert_array_equal(gr["pos"], wr["pos"])
+            np.testing.assert_array_equal(gr["heads"], wr["heads"])
+            np.testing.assert_allclose(gr["a"], wr["a"], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(gr["g"], wr["g"], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(gr["x"], wr["x"], rtol=1e-10, atol=1e-10)
+            if l + 1 < cfg.n_layers:
+                k = cfg.tokens[l + 1]
+                sensitive_tok |= not np.array_equal(_largest(wr["a"], k),
+                                                    _largest(wr["dcol"], k))
+                if cfg.heads[l + 1] != len(wr["heads"]):
+                    hk = wr["heads"]
+                    sensitive_head |= not np.array_equal(
+                        _largest(wr["g"][hk], cfg.heads[l + 1]),
+                        _largest(wr["dg"][hk], cfg.heads[l + 1]))
+    # the case tells cumulative importance from the last layer's alone (a
+    # causal layer's column sums fall with position so steeply that its own
+    # token ranking already agrees with the cumulative one here)
+    assert sensitive_head and (sensitive_tok or causal)
+
+
+def _uniform_decode(cfg, inp, b):
+    """The decode stack in closed form when every query is zero (Wq = 0):
+    each head spreads probability 1/Lc over the Lc entries of the cache
+    (the new token's entry included), so a layer adds the mean of the cache's
+    V rows times Wo, every entry present gains layers x heads / Lc per step
+    (layers / Lc per head under per-head pruning), and a cut keeps the entries that have been present longest (ties go to
+    the lower cache slot). Quantized caches hold the rows' int8 values;
+    a row whose largest probability 1/Lc is below the threshold reads both
+    planes, otherwise the MSB plane alone."""
+    L0, D = cfg.cache_len, cfg.model_dim
+    vals = []
+    for l in range(cfg.n_layers):
+        V0 = inp["layers"][l]["v_cache"][b].reshape(L0, D)
+        vals.append(R.quantize_kv(V0.astype(np.float32)) if cfg.quantized else V0)
+    full = []
+    a, ids = np.zeros(L0), list(range(L0))
+    xs, kept, flat = [], [], []
+    for s in range(cfg.steps):
+        x = inp["x_steps"][s][b].astype(np.float64)
+        ids.append(L0 + s)
+        a = np.append(a, 0.0)
+        Lc = len(ids)
+        use_full = cfg.quantized and 1.0 / Lc < cfg.pq_threshold
+        for l in range(cfg.n_layers):
+            w = {k_: v_.astype(np.float64) for k_, v_ in inp["layers"][l].items()
+                 if k_ in ("wv", "wo")}
+            v = x @ w["wv"]
+            if cfg.quantized:
+                planes = R.quantize_kv(v.astype(np.float32)[None])
+                vals[l] = tuple(np.concatenate([p_, n_]) for p_, n_ in zip(vals[l], planes))
+                V = R.dequant(*vals[l], use_full)
+            else:
+                vals[l] = np.concatenate([vals[l], v[None]])
+                V = vals[l]
+            x = x + V.mean(axis=0) @ w["wo"]
+        # per-head pruning: head h's importance takes head h's share only
+        a = a + cfg.n_layers * (1 if cfg.per_head else cfg.n_heads) / Lc
+        xs.append(x)
+        flat.append(use_full)
+        if R.prune_after_step(cfg, s) and Lc > cfg.cache_keep:
+            keep = _largest(a, cfg.cache_keep)
+            a, ids = a[keep], [ids[j] for j in keep]
+            vals = [tuple(p_[keep] for p_ in c) if cfg.quantized else c[keep] for c in vals]
+        kept.append(np.array(ids))
+    return np.stack(xs), a, kept, flat
+
+
+@pytest.mark.parametrize("variant", ["once", "rolling", "perhead", "pq"])
+def test_run_decode_matches_zero_query_closed_form(variant):
+    from workloads import GPT2_DECODE, PQ_DECODE, make_decode_inputs
+    base = PQ_DECODE if variant == "pq" else GPT2_DECODE
+    cfg = scaled(base, dtype="f32", n_layers=3, batch=2, n_heads=2, head_dim=8, cache_len=12,
+                 cache_keep=7, steps=5, prune_every=1 if variant == "rolling" else 0,
+                 per_head=variant == "perhead")
+    inp = make_decode_inputs(cfg)
+    for w in inp["layers"]:
+        w["wq"][:] = 0.0
+    out = R.run_decode(cfg, inp)
+    for b in range(cfg.batch):
+        xs, a, kept, flat = _uniform_decode(cfg, inp, b)
+        o = out[b]
+        np.testing.assert_allclose(o["x_steps"], xs, rtol=1e-10, atol=1e-10)
+        for s in range(cfg.steps):
+            ids = np.asarray(o["kept_ids"][s])
+            want = np.broadcast_to(kept[s], ids.shape) if variant == "perhead" else kept[s]
+            np.testing.assert_array_equal(ids, want)
+            if cfg.quantized:
+                assert all(bool(r.all()) == flat[s] and bool(r.any()) == flat[s]
+                           for r, _ in o["recompute"][s])
+        np.testing.assert_allclose(o["a"], np.broadcast_to(a, o["a"].shape), rtol=1e-12)
+    if variant == "pq":
+        # the case crosses the threshold: rows of 12 and 13 entries read both
+        # planes, the pruned cache of 8 entries only the MSBs
+        assert flat[0] and not flat[1]
+
+
+def test_run_prefill_perhead_matches_closed_form_cascade():
+    """Per-head token pruning on the equal-query inputs: head h's rows are
+    one softmax over its own keys, so its column sums are n p_h and every
+    output row is p_h V[keys_h]; each head's cut keeps its own largest
+    cumulative importance, and the head cut ranks cumulative |O_h|."""
+    from workloads.configs import BERT_BASE_PERHEAD
+    cfg = scaled(BERT_BASE_PERHEAD, dtype="f32", n_layers=4, batch=3, n_heads=4, head_dim=8,
+                 tokens=(24,) * 4, key_keep=(24, 17, 12, 9), heads=(4, 4, 3, 2))
+    inp = _rank_one_inputs(cfg)
+    out = R.run_prefill_perhead(cfg, inp)
+    dh, n = cfg.head_dim, cfg.tokens[0]
+    differ = False
+    for b in range(cfg.batch):
+        x = inp["x"][b].astype(np.float64)
+        heads = np.arange(cfg.n_heads)
+        keys = {h: np.arange(n) for h in heads}
+        a = {h: np.zeros(n) for h in heads}
+        g = np.zeros(cfg.n_heads)
+        for l in range(cfg.n_layers):
+            w = {k_: v_.astype(np.float64) for k_, v_ in inp["layers"][l].items()}
+            delta = np.zeros_like(x)
+            for h in heads:
+                c = slice(h * dh, (h + 1) * dh)
+                kk = keys[h]
+                s = (x[kk] @ w["wk"][:, c]) @ w["wq"][0, c] / math.sqrt(dh)
+                e = np.exp(s - s.max())
+                p = e / e.sum()
+                o = p @ (x[kk] @ w["wv"][:, c])
+                a[h][kk] += n * p
+                g[h] += n * np.abs(o).sum()
+                delta += o @ w["wo"][c, :]
+            x = x + delta
+            rec = out[b]["trace"][l]
+            np.testing.assert_array_equal(rec["heads"], heads)
+            np.testing.assert_allclose(rec["x"], x, rtol=1e-10, atol=1e-10)
+            np.testing.assert_allclose(rec["g"], g, rtol=1e-10, atol=1e-12)
+            for h in heads:
+                np.testing.assert_array_equal(rec["keys"][h], keys[h])
+                np.testing.assert_allclose(rec["a"][h], a[h], rtol=1e-10, atol=1e-12)
+            if l + 1 < cfg.n_layers:
+                if cfg.heads[l + 1] != len(heads):
+                    heads = heads[_largest(g[heads], cfg.heads[l + 1])]
+                for h in heads:
+                    keys[h] = keys[h][_largest(a[h][keys[h]], cfg.key_keep[l + 1])]
+                differ |= len({tuple(keys[h]) for h in heads}) > 1
+    assert differ  # the heads keep different tokens

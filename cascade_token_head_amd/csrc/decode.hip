@@ -597,7 +597,9 @@ __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int
                                           BhState<16>& st) {
   constexpr int LPR = BhCfg<kMsb>::LPR, NG = BhCfg<kMsb>::NT / LPR;
   constexpr int KBq = FULL ? BhCfg<kMsb>::KBF : BhCfg<kMsb>::KB;
-  const int64_t rowb = int64_t(b) * a.cap;
+  // row scales: one per token [B, cap], or with per-head pruning one per
+  // (head, slot) [B, H, cap], since each head's slot r holds its own entry
+  const int64_t rowb = (a.per_head ? int64_t(b) * a.H + h : int64_t(b)) * a.cap;
   // head-major planes: this head's slab of 32-byte rows, this lane's 8 bytes
   const int64_t slab = (int64_t(b) * a.H + h) * a.cap * 32 + 8 * cl;
   float* srow = a.scores + (int64_t(b) * a.H + h) * a.lc_pad;
@@ -808,7 +810,9 @@ decode_bh(DecodeArgs a) {
       mv = fmaxf(mv, wred[NW + w]);
     }
     const float sk = mk / 127.0f, sv = mv / 127.0f;
-    const int64_t nrow = int64_t(b) * a.cap + a.lc - 1;
+    // the new row's scale slot: shared by the heads (written once), or per
+    // head under per-head pruning (each head's workgroup writes its own)
+    const int64_t nrow = (a.per_head ? int64_t(b) * a.H + h : int64_t(b)) * a.cap + a.lc - 1;
     if (wave < 2) {
       const bf16_t* src = static_cast<const bf16_t*>(wave == 0 ? a.knew : a.vnew) +
                           int64_t(b) * D + h * 64;
@@ -834,7 +838,7 @@ decode_bh(DecodeArgs a) {
     if (t == 0) {
       nscale[0] = sk;
       nscale[1] = sv;
-      if (h == 0) {
+      if (h == 0 || a.per_head) {
         a.k_scale[nrow] = sk;
         a.v_scale[nrow] = sv;
       }

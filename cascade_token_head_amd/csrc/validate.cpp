@@ -43,7 +43,6 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
   if (int64_t(d->n_heads) * d->head_dim > (1 << 20)) return SPATTEN_EINVAL;
   if (!(d->v_threshold >= 0.0f)) return SPATTEN_EINVAL;  // negative or NaN
   if (d->per_head != 0 && d->per_head != 1) return SPATTEN_EINVAL;
-  if (d->per_head && d->kv_quantized) return SPATTEN_EUNSUPPORTED;
   const bool keys_per_head = d->per_head && d->mode == SPATTEN_PREFILL;
   if (keys_per_head) {
     if (d->n_keys < 1 || d->n_keys > d->n_tokens) return SPATTEN_EINVAL;

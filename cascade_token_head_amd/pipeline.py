@@ -276,18 +276,24 @@ class DecodeStack:
         for side in range(sides):
             for _ in range(n_layers):
                 if quantized:
-                    # head-major planes: each (sequence, head) slab contiguous
+                    # head-major planes: each (sequence, head) slab contiguous;
+                    # per-head pruning keeps a scale per (head, slot)
                     pl = (B, n_heads, cap, head_dim // 2)
+                    sc = (B, n_heads, cap) if per_head else (B, cap)
                     c = {"k_msb": torch.empty(pl, dtype=torch.uint8, device=dev),
                          "k_lsb": torch.empty(pl, dtype=torch.uint8, device=dev),
-                         "k_scale": torch.empty(B, cap, dtype=torch.float32, device=dev),
+                         "k_scale": torch.empty(sc, dtype=torch.float32, device=dev),
                          "v_msb": torch.empty(pl, dtype=torch.uint8, device=dev),
                          "v_lsb": torch.empty(pl, dtype=torch.uint8, device=dev),
-                         "v_scale": torch.empty(B, cap, dtype=torch.float32, device=dev)}
+                         "v_scale": torch.empty(sc, dtype=torch.float32, device=dev)}
                 else:
                     c = {"k_cache": torch.empty(B, cap, D, dtype=dtype, device=dev),
                          "v_cache": torch.empty(B, cap, D, dtype=dtype, device=dev)}
                 self.caches[side].append(c)
+        # per-token scales of the initial cache, copied to every head's slots
+        # when each head keeps its own entries
+        self.scale_tok = (torch.empty(B, cap, dtype=torch.float32, device=dev)
+                          if quantized and per_head else None)
         ashape = (B, n_heads, cap) if per_head else (B, cap)
         self.abuf = [torch.zeros(ashape, dtype=torch.float32, device=dev) for _ in range(sides)]
         self.x = torch.empty(B, 1, D, dtype=dtype, device=dev)
@@ -308,7 +314,13 @@ class DecodeStack:
         B, L0, D = self.B, self.L0, self.D
         for l in range(self.L):
             c = self.caches[0][l]
-            if self.quantized:
+            if self.quantized and self.per_head:
+                for kv, name in ((k0[l], "k"), (v0[l], "v")):
+                    S.quantize_kv(kv.reshape(B, L0, D), c[name + "_msb"], c[name + "_lsb"],
+                                  self.scale_tok)
+                    c[name + "_scale"].copy_(self.scale_tok[:, None, :].expand(B, self.H,
+                                                                                self.cap))
+            elif self.quantized:
                 S.quantize_kv(k0[l].reshape(B, L0, D), c["k_msb"], c["k_lsb"], c["k_scale"])
                 S.quantize_kv(v0[l].reshape(B, L0, D), c["v_msb"], c["v_lsb"], c["v_scale"])
             else:
@@ -367,7 +379,8 @@ class DecodeStack:
         a = self.abuf[self.side]
         if self.per_head:
             # each head: its own top-k, then an in-place cut of its 128-byte
-            # slice of every layer's cache rows and of its importance row
+            # slice of every layer's cache rows (quantized: its slab of plane
+            # rows and its row of scales) and of its importance row
             H, dh, D = self.H, self.dh, self.D
             for h in range(H):
                 sel = self.cache_sel[h]
@@ -376,8 +389,13 @@ class DecodeStack:
                 for c in self.caches[0]:
                     for t in c.values():
                         es = t.element_size()
-                        tensors.append((t[:, :, h * dh:(h + 1) * dh], dh * es, cap * D * es,
-                                        D * es))
+                        if t.dim() == 4:    # planes [B, H, cap, dh/2]
+                            tensors.append((t[:, h], t.shape[3], H * cap * t.shape[3]))
+                        elif t.dim() == 3 and self.quantized:   # scales [B, H, cap]
+                            tensors.append((t[:, h], es, H * cap * es))
+                        else:               # rows [B, cap, D]
+                            tensors.append((t[:, :, h * dh:(h + 1) * dh], dh * es,
+                                            cap * D * es, D * es))
                 S.compact_inplace(tensors, sel, self.len, k)
             a[:, :, k:self.len].zero_()
             self.len = k

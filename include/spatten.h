@@ -63,8 +63,9 @@ typedef struct {
   int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
   float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
   float v_threshold;     /* local value pruning threshold (0 = off): prefill, unquantized decode */
-  int32_t per_head;      /* 1 = per-head token pruning (decode, unquantized: a is [B, H, cache_cap];
-                            prefill, bf16 bidirectional: see n_keys) */
+  int32_t per_head;      /* 1 = per-head token pruning (decode: a is [B, H, cache_cap], and
+                            quantized scales are [B, H, cache_cap]; prefill, bf16
+                            bidirectional: see n_keys) */
   int32_t n_keys;        /* prefill with per_head: tokens each kept head keeps as keys and values */
 } spatten_layer_desc;
 
@@ -94,7 +95,8 @@ typedef struct {
  *   head-major [B, H, cache_cap, head_dim/2] u8 (each head's rows
  *   contiguous, so a (sequence, head) row reads whole cache lines) and
  *   k_scale, v_scale [B, cache_cap] fp32, as spatten_quantize_kv writes
- *   them with head_dim set; this step's k and v rows are coded into
+ *   them with head_dim set (with per_head = 1: [B, H, cache_cap], each
+ *   head holding the scale of the token in each of its own slots); this step's k and v rows are coded into
  *   row cache_len of the planes and scales with that function's arithmetic
  *   (bit for bit) before they are read; each (b, h) row is scored with MSB-only
  *   values (scale*16*msb) and, when its largest probability is below
@@ -108,10 +110,14 @@ typedef struct {
  *   a still takes every probability. v_kept (optional, [B, H] int32)
  *   receives the number of V rows that entered O_h (cache_len + 1 without
  *   value pruning).
- *   Per-head token pruning (section "A. Neural Networks Pruning and Quantization", bullet "Token Pruning"; per_head = 1,
- *   unquantized): a is [B, H, cache_cap] and a[b, h, j] takes head h's
- *   probabilities only, so each head can keep its own cache entries (cut
- *   with spatten_compact_inplace on the head's 128-byte slice of each row).
+ *   Per-head token pruning (section "A. Neural Networks Pruning and Quantization", bullet "Token Pruning"; per_head = 1):
+ *   a is [B, H, cache_cap] and a[b, h, j] takes head h's probabilities
+ *   only, so each head can keep its own cache entries (cut with
+ *   spatten_compact_inplace on the head's 128-byte slice of each row, or
+ *   for quantized caches on the head's slab of plane rows and its row of
+ *   scales). A quantized cache then keeps one scale per (head, slot): the
+ *   new row's per-token scale (taken over the whole row) is written to
+ *   every head's slot cache_len.
  *   g is not used in decode and may be NULL. Decode needs head_dim 64,
  *   H <= 32, bf16 and every head kept.
  *   Per-head token pruning in prefill (per_head = 1; bf16, bidirectional;
@@ -138,8 +144,8 @@ typedef struct {
  *   decode bf16 with head_dim 64, n_heads <= 32 and every head kept. A
  *   v_threshold > 0 is taken by prefill and by unquantized decode, not by
  *   quantized caches or per-head prefill; a NaN or negative one is
- *   SPATTEN_EINVAL. per_head is 0 or 1 (else SPATTEN_EINVAL); 1 needs an
- *   unquantized decode, or a bf16 bidirectional prefill with
+ *   SPATTEN_EINVAL. per_head is 0 or 1 (else SPATTEN_EINVAL); 1 needs a
+ *   decode, or a bf16 bidirectional prefill with
  *   1 <= n_keys <= n_tokens; n_keys must be 0 in every other case
  *   (SPATTEN_EINVAL).
  */

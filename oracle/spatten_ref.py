@@ -469,16 +469,23 @@ def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: boo
                      v_threshold: float = 0.0):
     """Attention of one decode query q [H, dh] over every entry of a cache
     (no mask). Unquantized caches hold k, v [Lc, H, dh]; quantized ones the
-    packed planes and scales of K and V rows. v_threshold > 0 applies local
+    packed planes and scales of K and V rows: planes [Lc, D/2] with scales
+    [Lc] (one scale per token, shared by the heads), or under per-head
+    pruning planes [Lc, H, dh/2] with scales [Lc, H] (slot r of head h holds
+    head h's r-th kept entry and that token's scale). v_threshold > 0 applies local
     value pruning to unquantized caches. Returns (o [H, dh], p [H, Lc],
     recompute flags [H], MSB-pass max probability [H], V rows kept [H])."""
     H, dh = heads_n, head_dim
     if quantized:
         assert v_threshold == 0.0, "value pruning is defined here for unquantized caches"
-        Km = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], False).reshape(-1, H, dh)
-        Kf = dequant(cache["k_msb"], cache["k_lsb"], cache["k_scale"], True).reshape(-1, H, dh)
-        Vm = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], False).reshape(-1, H, dh)
-        Vf = dequant(cache["v_msb"], cache["v_lsb"], cache["v_scale"], True).reshape(-1, H, dh)
+
+        def planes(kv, full):
+            m, l_, sc = cache[kv + "_msb"], cache[kv + "_lsb"], np.asarray(cache[kv + "_scale"])
+            if sc.ndim == 2:  # per-head slots: each head's planes carry their own scale
+                m = np.asarray(m).reshape(sc.shape[0], H, dh // 2)
+                l_ = np.asarray(l_).reshape(sc.shape[0], H, dh // 2)
+            return dequant(m, l_, sc, full).reshape(-1, H, dh)
+        Km, Kf, Vm, Vf = planes("k", False), planes("k", True), planes("v", False), planes("v", True)
         Lc = Km.shape[0]
     else:
         Lc = cache["k"].shape[0]
@@ -516,7 +523,11 @@ def decode_layer(x, w: dict, cache: dict, heads_n: int, head_dim: int, bf16: boo
         vm, vl, vs = quantize_kv(v.astype(np.float32))
         for name, val in (("k_msb", km), ("k_lsb", kl), ("k_scale", ks),
                           ("v_msb", vm), ("v_lsb", vl), ("v_scale", vs)):
-            cache[name] = np.concatenate([cache[name], np.asarray(val)[None]], axis=0)
+            # per-head slots: the row's planes split by head, its scale
+            # copied to every head
+            row = np.broadcast_to(val, cache[name].shape[1:]) if name.endswith("scale") \
+                else np.asarray(val).reshape(cache[name].shape[1:])
+            cache[name] = np.concatenate([cache[name], row[None]], axis=0)
     else:
         cache["k"] = np.concatenate([cache["k"], k.reshape(1, H, dh)], axis=0)
         cache["v"] = np.concatenate([cache["v"], v.reshape(1, H, dh)], axis=0)
@@ -551,7 +562,10 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
     section "A. Neural Networks Pruning and Quantization", bullet "Token Pruning" names it) each head h keeps its own entries:
     a_h[j] accumulates only head h's probabilities and every cut keeps
     topk(a_h, cache_keep) for that head in every layer's K and V. All heads
-    keep the same count, so slot r of head h holds head h's r-th entry.
+    keep the same count, so slot r of head h holds head h's r-th entry; a
+    quantized cache then holds its token scales per head as well (each head
+    keeps a copy of the scale of every token it keeps; the scale itself is
+    still the token's, taken over the whole row).
     pq_adopt(b, s, l, h, c, default) may override a recompute decision.
 
     Per sequence the result holds the step outputs, the final a, the first
@@ -565,7 +579,6 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
     H, dh = cfg.n_heads, cfg.head_dim
     vthr = getattr(cfg, "v_threshold", 0.0)
     per_head = getattr(cfg, "per_head", False)
-    assert not (per_head and cfg.quantized), "per-token scales are shared by all heads"
     out = {}
     for b in seqs:
         caches = []
@@ -576,8 +589,16 @@ def run_decode(cfg, inputs: dict, seqs=None, adopt: Optional[Callable] = None,
             if cfg.quantized:
                 km, kl, ks = quantize_kv(K0.reshape(K0.shape[0], -1).astype(np.float32))
                 vm, vl, vs = quantize_kv(V0.reshape(V0.shape[0], -1).astype(np.float32))
-                caches.append({"k_msb": km, "k_lsb": kl, "k_scale": ks,
-                               "v_msb": vm, "v_lsb": vl, "v_scale": vs})
+                c = {"k_msb": km, "k_lsb": kl, "k_scale": ks,
+                     "v_msb": vm, "v_lsb": vl, "v_scale": vs}
+                if per_head:
+                    # per-head slots: planes [L0, H, dh/2], the token's
+                    # scale copied to every head [L0, H]
+                    L0 = K0.shape[0]
+                    c = {k_: (np.repeat(np.asarray(v_)[:, None], H, axis=1)
+                              if k_.endswith("scale") else
+                              np.asarray(v_).reshape(L0, H, dh // 2)) for k_, v_ in c.items()}
+                caches.append(c)
             else:
                 caches.append({"k": K0, "v": V0})
         shape = (H, cfg.cache_len) if per_head else (cfg.cache_len,)

@@ -152,13 +152,15 @@ def test_decode_rejections(S):
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, v_threshold=1e-3)
     assert S.workspace_bytes(d) == S.workspace_bytes(
         S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64))
-    # per-head importance: a flag, not with quantized caches; in prefill it
-    # also needs the kept key count (bidirectional only)
+    # per-head importance: a flag (quantized caches included: the size query
+    # accepts the descriptor); in prefill it also needs the kept key count
+    # (bidirectional only)
     d = S.make_desc(**base)
     d.per_head = 2
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(**{**base, "per_head": True, "kv_quantized": True, "pq_threshold": 0.1})
-    assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
+    assert S.workspace_bytes(d) == S.workspace_bytes(
+        S.make_desc(**{**base, "kv_quantized": True, "pq_threshold": 0.1}))
     d = S.make_desc(**{**base, "per_head": True, "n_keys": 5})
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, per_head=True)

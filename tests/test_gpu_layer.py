@@ -249,10 +249,16 @@ PERHEAD_CASES = [(3, 12, 100, 0.0), (2, 16, 257, 0.0), (64, 12, 130, 0.0), (1, 5
                  (2, 12, 300, 1e-3), (2, 12, 4200, 1e-4)]
 
 
+# per-head importance with quantized caches, whose scales are then per (head,
+# slot): (B, H, L0, threshold)
+PERHEAD_PQ_CASES = [(3, 16, 200, 0.1), (2, 12, 150, 1.01), (2, 16, 301, 0.0)]
+
+
 @pytest.mark.parametrize("B,H,L0,quantized,thr,vthr,per_head",
                          [c + (0.0, False) for c in DECODE_LAYER_CASES] +
                          [(B, H, L0, False, 0.0, v, False) for B, H, L0, v in VPRUNE_CASES] +
-                         [(B, H, L0, False, 0.0, v, True) for B, H, L0, v in PERHEAD_CASES])
+                         [(B, H, L0, False, 0.0, v, True) for B, H, L0, v in PERHEAD_CASES] +
+                         [(B, H, L0, True, t, 0.0, True) for B, H, L0, t in PERHEAD_PQ_CASES])
 def test_decode_layer(S, B, H, L0, quantized, thr, vthr, per_head):
     print("decode case", B, H, L0, quantized, thr, vthr, per_head, flush=True)
     dh = 64
@@ -275,7 +281,30 @@ def test_decode_layer(S, B, H, L0, quantized, thr, vthr, per_head):
     rec = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     vk = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     kw = {}
-    if quantized:
+    # per-head slots of a quantized cache: head h's slot r holds token
+    # (r + h) mod L0, with that token's planes and scale, so each head reads
+    # its own scale row
+    ph_tok = (np.arange(L0)[:, None] + np.arange(H)[None, :]) % L0     # [slot, head]
+    ph_cache = {}
+    if quantized and per_head:
+        for name, arr in (("k", K0), ("v", V0)):
+            msb = np.zeros((B, H, cap, dh // 2), np.uint8)
+            lsb = np.zeros_like(msb)
+            sc = np.zeros((B, H, cap), np.float32)
+            for b in range(B):
+                m_, l_, s_ = R.quantize_kv(arr[b])
+                m_ = m_.reshape(L0, H, dh // 2)[ph_tok, np.arange(H)[None, :]]   # [L0, H, dh/2]
+                l_ = l_.reshape(L0, H, dh // 2)[ph_tok, np.arange(H)[None, :]]
+                s_ = s_[ph_tok]                                                  # [L0, H]
+                msb[b, :, :L0] = m_.transpose(1, 0, 2)
+                lsb[b, :, :L0] = l_.transpose(1, 0, 2)
+                sc[b, :, :L0] = s_.T
+                ph_cache.setdefault(b, {}).update(
+                    {name + "_msb": m_, name + "_lsb": l_, name + "_scale": s_})
+            kw.update({name + "_msb": torch.from_numpy(msb).cuda(),
+                       name + "_lsb": torch.from_numpy(lsb).cuda(),
+                       name + "_scale": torch.from_numpy(sc).cuda()})
+    elif quantized:
         for name, arr in (("k", K0), ("v", V0)):
             msb = torch.zeros(B, H, cap, dh // 2, dtype=torch.uint8, device="cuda")
             lsb = torch.zeros_like(msb)
@@ -296,7 +325,13 @@ def test_decode_layer(S, B, H, L0, quantized, thr, vthr, per_head):
     assert float(gd.abs().sum()) == 0.0
     n_rec = 0
     for b in range(B):
-        if quantized:
+        if quantized and per_head:
+            cache = dict(ph_cache[b])
+            # the new row's scale went to every head's slot L0
+            for name in ("k_scale", "v_scale"):
+                col = kw[name][b, :, L0].cpu().numpy()
+                assert np.all(col == col[0]) and col[0] > 0, (name, b, col)
+        elif quantized:
             cache = {}
             for name, arr in (("k", K0), ("v", V0)):
                 m_, l_, s_ = R.quantize_kv(arr[b])

@@ -31,7 +31,7 @@ from oracle import spatten_ref as R
 from workloads import (BERT_BASE, GPT2_DECODE, LONG_CAUSAL, PQ_DECODE, TINY, make_decode_inputs,
                        make_prefill_inputs, scaled)
 from workloads.configs import (BERT_BASE_VPRUNE, GPT2_DECODE_PERHEAD, GPT2_DECODE_ROLLING,
-                               GPT2_DECODE_VPRUNE)
+                               GPT2_DECODE_VPRUNE, PQ_DECODE_PERHEAD)
 
 pytestmark = pytest.mark.gpu
 
@@ -348,8 +348,14 @@ def _cache_np(c, b, rows, quantized, H, dh):
 
 def _rows_np(t, b, n):
     """Rows 0..n-1 of sequence b of a cache tensor, exact (bf16 as fp32);
-    head-major planes [B, H, cap, dh/2] come back token-major [n, H dh/2]."""
-    v = t[b, :, :n].permute(1, 0, 2).reshape(n, -1) if t.dim() == 4 else t[b, :n]
+    head-major planes [B, H, cap, dh/2] come back slot-major [n, H dh/2]
+    and per-head scales [B, H, cap] (fp32, per-head pruning) as [n, H]."""
+    if t.dim() == 4:
+        v = t[b, :, :n].permute(1, 0, 2).reshape(n, -1)
+    elif t.dim() == 3 and t.dtype == torch.float32:
+        v = t[b, :, :n].T
+    else:
+        v = t[b, :n]
     return (v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy()
 
 
@@ -394,7 +400,9 @@ def importance_error_bound(q, cache, P, cfg, a_out):
     sc2 = math.log2(math.e) / math.sqrt(dh)
     qa = np.abs(np.asarray(q, np.float64)).reshape(H, dh)
     if cfg.quantized:
-        E = 383.0 * np.asarray(cache["k_scale"], np.float64)[None, :] * qa.sum(axis=1)[:, None]
+        ks = np.asarray(cache["k_scale"], np.float64)
+        ks = ks.T if ks.ndim == 2 else ks[None, :]     # [H or 1, lc]
+        E = 383.0 * ks * qa.sum(axis=1)[:, None]
     else:
         E = np.einsum("hd,jhd->hj", qa, np.abs(cache["k"]))
     lc = P.shape[1]
@@ -480,8 +488,8 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
                     want = rows[l][b][name][ids[b][g]]
                     got = arr[:lc - 1]
                     if cfg.per_head:   # head g's slice of every row
-                        want = want.reshape(lc - 1, H, dh)[:, g]
-                        got = got.reshape(lc - 1, H, dh)[:, g]
+                        want = want.reshape(lc - 1, H, -1)[:, g]
+                        got = got.reshape(lc - 1, H, -1)[:, g]
                     np.testing.assert_array_equal(got, want,
                                                   err_msg="%s l%d b%d g%d" % (name, l, b, g))
                 rows[l][b][name][new_id] = arr[lc - 1]
@@ -495,7 +503,7 @@ def run_decode_checked(cfg, inputs, seqs, steps=None):
                     m_, l_, s_ = R.quantize_kv(row.astype(np.float32)[None])
                     np.testing.assert_array_equal(cache[name + "_msb"][-1], m_[0])
                     np.testing.assert_array_equal(cache[name + "_lsb"][-1], l_[0])
-                    assert cache[name + "_scale"][-1] == s_[0]
+                    assert np.all(cache[name + "_scale"][-1] == s_[0])
                 else:
                     check_bf16_output(cache[name][-1].reshape(-1), ref,
                                       what="%s row l%d b%d" % (name, l, b))
@@ -589,6 +597,10 @@ DECODE_CFGS = {
                           steps=5, prune_every=1), [1]),
     "gpt2_perhead": (scaled(GPT2_DECODE_PERHEAD, batch=4, n_layers=4, cache_len=256,
                             cache_keep=102, steps=4), [0, 3]),
+    "pq_perhead_rolling": (scaled(PQ_DECODE_PERHEAD, batch=3, n_layers=3, cache_len=300,
+                                  cache_keep=150, steps=5, prune_every=1), [0, 2]),
+    "pq_perhead_all": (scaled(PQ_DECODE_PERHEAD, batch=2, n_layers=3, cache_len=200,
+                              cache_keep=100, steps=3, pq_threshold=1.01), [1]),
     "gpt2_perhead_rolling_vprune": (scaled(GPT2_DECODE_PERHEAD, batch=3, n_layers=3,
                                            cache_len=200, cache_keep=80, steps=5, prune_every=1,
                                            v_threshold=1e-3), [2]),
@@ -621,7 +633,7 @@ def most_recomputed_sequence(cfg, inputs):
     w = pipeline.weights_to_device(inputs["layers"], dt)
     st = pipeline.DecodeStack(cfg.n_layers, cfg.batch, cfg.n_heads, cfg.head_dim, cfg.cache_len,
                               cfg.cache_keep, cfg.steps, w, cfg.quantized, cfg.pq_threshold, dt,
-                              prune_every=cfg.prune_every)
+                              prune_every=cfg.prune_every, per_head=cfg.per_head)
     st.load([torch.from_numpy(l["k_cache"]).to(dt).cuda() for l in inputs["layers"]],
             [torch.from_numpy(l["v_cache"]).to(dt).cuda() for l in inputs["layers"]])
     count = torch.zeros(cfg.batch, dtype=torch.int64, device="cuda")
@@ -638,9 +650,9 @@ def most_recomputed_sequence(cfg, inputs):
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [GPT2_DECODE, PQ_DECODE, GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING,
-                                 GPT2_DECODE_PERHEAD],
+                                 GPT2_DECODE_PERHEAD, PQ_DECODE_PERHEAD],
                          ids=["gpt2_decode", "pq_decode", "gpt2_decode_vprune",
-                              "gpt2_decode_rolling", "gpt2_decode_perhead"])
+                              "gpt2_decode_rolling", "gpt2_decode_perhead", "pq_decode_perhead"])
 def test_decode_stack_full_size(cfg):
     """Full batch, cache, layer and step count; per-layer checks of every
     step on the first and last sequence, and for progressive quantization

@@ -602,9 +602,11 @@ def _small_decode(**kw):
     return scaled(GPT2_DECODE, **base)
 
 
-def test_per_head_with_one_head_is_the_shared_cut():
+@pytest.mark.parametrize("quantized", [False, True])
+def test_per_head_with_one_head_is_the_shared_cut(quantized):
     from workloads import make_decode_inputs
-    cfg = _small_decode(n_heads=1, head_dim=16, prune_every=1)
+    cfg = _small_decode(n_heads=1, head_dim=16, prune_every=1, quantized=quantized,
+                        pq_threshold=0.2 if quantized else 0.0)
     inp = make_decode_inputs(cfg)
     shared = R.run_decode(cfg, inp)[0]
     ph = R.run_decode(scaled(cfg, per_head=True), inp)[0]
@@ -612,15 +614,24 @@ def test_per_head_with_one_head_is_the_shared_cut():
     np.testing.assert_array_equal(ph["a"][0], shared["a"])
     for k1, k2 in zip(ph["kept_ids"], shared["kept_ids"]):
         np.testing.assert_array_equal(k1[0], k2)
+    for r1, r2 in zip(ph["recompute"], shared["recompute"]):
+        for (f1, c1), (f2, c2) in zip(r1, r2):
+            np.testing.assert_array_equal(f1, f2)
+            np.testing.assert_array_equal(c1, c2)
+    if quantized:
+        flags = [bool(f.any()) for step in shared["recompute"] for f, _ in step]
+        assert any(flags) and not all(flags)  # the case reaches both sides of the threshold
 
 
-def test_per_head_with_identical_heads_is_the_shared_cut():
+@pytest.mark.parametrize("quantized", [False, True])
+def test_per_head_with_identical_heads_is_the_shared_cut(quantized):
     """Two heads with identical weights and caches see identical
     probabilities: each head's importance is half the shared one (exact in
     binary), so every head keeps the shared selection and the outputs
     match."""
     from workloads import make_decode_inputs
-    cfg = _small_decode(n_heads=2, head_dim=8, prune_every=2)
+    cfg = _small_decode(n_heads=2, head_dim=8, prune_every=2, quantized=quantized,
+                        pq_threshold=0.2 if quantized else 0.0)
     inp = make_decode_inputs(cfg)
     dh = 8
     for L in inp["layers"]:
@@ -1131,13 +1142,13 @@ def _uniform_decode(cfg, inp, b):
     return np.stack(xs), a, kept, flat
 
 
-@pytest.mark.parametrize("variant", ["once", "rolling", "perhead", "pq"])
+@pytest.mark.parametrize("variant", ["once", "rolling", "perhead", "pq", "pq_perhead"])
 def test_run_decode_matches_zero_query_closed_form(variant):
     from workloads import GPT2_DECODE, PQ_DECODE, make_decode_inputs
-    base = PQ_DECODE if variant == "pq" else GPT2_DECODE
+    base = PQ_DECODE if variant.startswith("pq") else GPT2_DECODE
     cfg = scaled(base, dtype="f32", n_layers=3, batch=2, n_heads=2, head_dim=8, cache_len=12,
                  cache_keep=7, steps=5, prune_every=1 if variant == "rolling" else 0,
-                 per_head=variant == "perhead")
+                 per_head=variant.endswith("perhead"))
     inp = make_decode_inputs(cfg)
     for w in inp["layers"]:
         w["wq"][:] = 0.0
@@ -1148,13 +1159,13 @@ def test_run_decode_matches_zero_query_closed_form(variant):
         np.testing.assert_allclose(o["x_steps"], xs, rtol=1e-10, atol=1e-10)
         for s in range(cfg.steps):
             ids = np.asarray(o["kept_ids"][s])
-            want = np.broadcast_to(kept[s], ids.shape) if variant == "perhead" else kept[s]
+            want = np.broadcast_to(kept[s], ids.shape) if cfg.per_head else kept[s]
             np.testing.assert_array_equal(ids, want)
             if cfg.quantized:
                 assert all(bool(r.all()) == flat[s] and bool(r.any()) == flat[s]
                            for r, _ in o["recompute"][s])
         np.testing.assert_allclose(o["a"], np.broadcast_to(a, o["a"].shape), rtol=1e-12)
-    if variant == "pq":
+    if cfg.quantized:
         # the case crosses the threshold: rows of 12 and 13 entries read both
         # planes, the pruned cache of 8 entries only the MSBs
         assert flat[0] and not flat[1]

@@ -122,8 +122,17 @@ def _kernel_work(cfg, v_kept=None, recompute_frac=None):
                     # re-reads the MSB halves too, which the method does not
                     # need)
                     r = recompute_frac or 0.0
-                    add("pq_attn", 4.0 * B * H * dh * lc * (1 + r),
-                        2 * B * lc * (D // 2 + 4) + r * B * H * lc * dh)
+                    if cfg.v_threshold > 0:
+                        # value pruning: K planes and scales, then the MSB
+                        # half (and scale) of each kept V head row only; the
+                        # fp32 scores the importance pass reads
+                        kept = v_kept[s][l] if v_kept is not None else 0
+                        add("pq_attn_vprune", 2.0 * B * H * dh * lc * (1 + r) + 2.0 * dh * kept,
+                            B * lc * (D // 2 + 4) + r * B * H * lc * dh // 2
+                            + kept * (dh // 2 + 4) + 4 * B * H * lc)
+                    else:
+                        add("pq_attn", 4.0 * B * H * dh * lc * (1 + r),
+                            2 * B * lc * (D // 2 + 4) + r * B * H * lc * dh)
                 elif cfg.v_threshold > 0:
                     # K rows once, the kept V rows (a 128-byte head slice
                     # each) and the fp32 scores the importance pass reads
@@ -246,7 +255,8 @@ def _cpu_baseline(cfg, inputs, budget_s: float):
 
 ATTN_KERNELS = {
     "prefill": ("gather_keys", "attn_fwd", "attn_fwd_vprune", "attn_colsum", "importance"),
-    "decode": ("decode_attn", "pq_attn", "decode_vrow", "decode_scores", "decode_vprune",
+    "decode": ("decode_attn", "pq_attn", "pq_attn_vprune", "decode_vrow", "decode_scores",
+               "decode_vprune",
                "decode_vsum", "decode_importance"),
 }
 

@@ -482,6 +482,12 @@ __device__ __forceinline__ void bh_raise(BhState<DPL>& st, float bm) {
   }
 }
 
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 // Keeps the loads requested before it in front of the code after it: the
 // compiler would otherwise sink a pass's first batch of loads below the
 // wait for the query (into the pass's loop), serialising two round trips.
@@ -591,10 +597,12 @@ __device__ __forceinline__ float bh_q_dot(const float* q, float qsum, const floa
 
 // Quantized cache: rows r0..r1-1 of head h read from the head-major planes
 // (row r0 + g + 128 i belongs to row group g), MSB only or (FULL) both.
-template <bool FULL>
+// VP (local value pruning): K only - the scores also go to sS, and V waits
+// for the exact probabilities (bh_vpass_q).
+template <bool FULL, bool VP = false>
 __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int g, int cl,
                                           int r0, int r1, const float* q, float qsum,
-                                          BhState<16>& st) {
+                                          BhState<16>& st, float* sS = nullptr) {
   constexpr int LPR = BhCfg<kMsb>::LPR, NG = BhCfg<kMsb>::NT / LPR;
   constexpr int KBq = FULL ? BhCfg<kMsb>::KBF : BhCfg<kMsb>::KB;
   // row scales: one per token [B, cap], or with per-head pruning one per
@@ -614,15 +622,16 @@ __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int
       const int jr = j < r1 ? j : r0;  // past the range: a valid row, masked
       const int64_t po = slab + int64_t(jr) * 32;
       km[u] = *reinterpret_cast<const uint2*>(a.k_msb + po);
-      vm[u] = *reinterpret_cast<const uint2*>(a.v_msb + po);
+      if constexpr (!VP) vm[u] = *reinterpret_cast<const uint2*>(a.v_msb + po);
       if constexpr (FULL) {
         kl[u] = *reinterpret_cast<const uint2*>(a.k_lsb + po);
-        vl[u] = *reinterpret_cast<const uint2*>(a.v_lsb + po);
+        if constexpr (!VP) vl[u] = *reinterpret_cast<const uint2*>(a.v_lsb + po);
       } else {
-        kl[u] = vl[u] = uint2{0u, 0u};
+        kl[u] = uint2{0u, 0u};
+        if constexpr (!VP) vl[u] = uint2{0u, 0u};
       }
       ks[u] = a.k_scale[rowb + jr];
-      vs[u] = a.v_scale[rowb + jr];
+      if constexpr (!VP) vs[u] = a.v_scale[rowb + jr];
     }
     float s[KBq];
     float bm = -INFINITY;
@@ -633,7 +642,10 @@ __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int
       const float sv = bh_q_dot<FULL>(q, qsum, cu, ks[u]);
       const int j = r0 + g + NG * (i0 + u);
       s[u] = j < r1 ? sv : -INFINITY;
-      if (cl == 0 && j < r1) srow[j] = s[u];
+      if (cl == 0 && j < r1) {
+        srow[j] = s[u];
+        if constexpr (VP) sS[j] = s[u];
+      }
       bm = fmaxf(bm, s[u]);
     }
     bh_raise(st, bm);
@@ -642,23 +654,25 @@ __device__ __forceinline__ void bh_pass_q(const DecodeArgs& a, int b, int h, int
       const int j = r0 + g + NG * (i0 + u);
       const float w = j < r1 ? fast_exp2(s[u] - st.m) : 0.0f;
       st.l += w;
-      const float wv = w * vs[u] * kmul;
-      st.wsum += wv;
-      float cu[16];
-      bh_codes<FULL>(vm[u], vl[u], cu);
+      if constexpr (!VP) {
+        const float wv = w * vs[u] * kmul;
+        st.wsum += wv;
+        float cu[16];
+        bh_codes<FULL>(vm[u], vl[u], cu);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(wv, cu[e], st.acc[e]);
+        for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(wv, cu[e], st.acc[e]);
+      }
     }
   }
 }
 
 // The new row (index lc-1) from its codes in LDS (MSB words, and LSB words
 // for the recompute): enters the state of row group 0.
-template <bool FULL>
+template <bool FULL, bool VP = false>
 __device__ __forceinline__ void bh_new_row_q(const DecodeArgs& a, int b, int h, int g, int cl,
                                              const float* q, float qsum, BhState<16>& st,
                                              const uint32_t (*nw)[8], const uint32_t (*nlw)[8],
-                                             const float* nscale) {
+                                             const float* nscale, float* sS = nullptr) {
   if (g != 0) return;
   const int j = a.lc - 1;
   const float kmul = FULL ? 1.0f : 16.0f;
@@ -669,15 +683,73 @@ __device__ __forceinline__ void bh_new_row_q(const DecodeArgs& a, int b, int h, 
   float cu[16];
   bh_codes<FULL>(km, kl, cu);
   const float s = bh_q_dot<FULL>(q, qsum, cu, nscale[0]);
-  if (cl == 0) a.scores[(int64_t(b) * a.H + h) * a.lc_pad + j] = s;
+  if (cl == 0) {
+    a.scores[(int64_t(b) * a.H + h) * a.lc_pad + j] = s;
+    if constexpr (VP) sS[j] = s;
+  }
   bh_raise(st, s);
   const float w = fast_exp2(s - st.m);
   st.l += w;
+  if constexpr (VP) return;
   const float wv = w * nscale[1] * kmul;
   st.wsum += wv;
   bh_codes<FULL>(vm, vl, cu);
 #pragma unroll
   for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(wv, cu[e], st.acc[e]);
+}
+
+// Local value pruning, quantized: the V rows of the exact probabilities
+// p_j = exp2(sS[j] - lse2) >= tau only (rows 0..lc-2 from the planes, MSB
+// only or FULL, the new row lc-1 from its codes in LDS), p_j V_j summed
+// into st.acc with the code offset tracked in st.wsum; returns this lane's
+// count of kept rows (counted once per row, by lane cl == 0).
+template <bool FULL>
+__device__ __forceinline__ int bh_vpass_q(const DecodeArgs& a, int b, int h, int g, int cl,
+                                          float lse2, const float* sS, BhState<16>& st,
+                                          const uint32_t (*nw)[8], const uint32_t (*nlw)[8],
+                                          const float* nscale) {
+  constexpr int LPR = BhCfg<kMsb>::LPR, NG = BhCfg<kMsb>::NT / LPR, KBV = 8;
+  const float kmul = FULL ? 1.0f : 16.0f;
+  const float tau = a.v_threshold;
+  const int64_t rowb = (a.per_head ? int64_t(b) * a.H + h : int64_t(b)) * a.cap;
+  const int64_t slab = (int64_t(b) * a.H + h) * a.cap * 32 + 8 * cl;
+  int kept = 0;
+  // batches of KBV rows per group: the kept rows' loads are all requested
+  // before the first is used
+  for (int i0 = 0; g + NG * i0 < a.lc; i0 += KBV) {
+    uint2 vm[KBV], vl[KBV];
+    float vs[KBV], pw[KBV];
+#pragma unroll
+    for (int u = 0; u < KBV; ++u) {
+      const int j = g + NG * (i0 + u);
+      const float p = j < a.lc ? fast_exp2(sS[j] - lse2) : 0.0f;
+      const bool keep = j < a.lc && p >= tau;  // uniform over the row group's lanes
+      pw[u] = keep ? p : 0.0f;
+      kept += keep && cl == 0 ? 1 : 0;
+      vm[u] = vl[u] = uint2{0u, 0u};
+      vs[u] = 0.0f;
+      if (keep && j == a.lc - 1) {  // the new row, from its codes in LDS
+        vm[u] = uint2{nw[1][2 * cl], nw[1][2 * cl + 1]};
+        vl[u] = uint2{nlw[1][2 * cl], nlw[1][2 * cl + 1]};
+        vs[u] = nscale[1];
+      } else if (keep) {
+        const int64_t po = slab + int64_t(j) * 32;
+        vm[u] = *reinterpret_cast<const uint2*>(a.v_msb + po);
+        if (FULL) vl[u] = *reinterpret_cast<const uint2*>(a.v_lsb + po);
+        vs[u] = a.v_scale[rowb + j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KBV; ++u) {
+      const float wv = pw[u] * vs[u] * kmul;
+      st.wsum += wv;
+      float cu[16];
+      bh_codes<FULL>(vm[u], vl[u], cu);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(wv, cu[e], st.acc[e]);
+    }
+  }
+  return kept;
 }
 
 // The row groups of the workgroup meet: M = largest reference maximum, L =
@@ -726,12 +798,16 @@ __device__ __forceinline__ void bh_combine(const BhState<DPL>& st, int g, int cl
 }
 
 // grid B * H workgroups of BhCfg<KIND>::NT threads; head_dim 64, H <= 32.
-template <int KIND>
+// VP (quantized only): local value pruning, lc <= kVrowMaxRows.
+template <int KIND, bool VP = false>
 __global__ void __launch_bounds__(BhCfg<KIND>::NT, BhCfg<KIND>::WAVES)
 decode_bh(DecodeArgs a) {
   constexpr int NT = BhCfg<KIND>::NT, LPR = BhCfg<KIND>::LPR, NG = NT / LPR;
   constexpr int DPL = BhCfg<KIND>::DPL, NW = NT / 64;
+  static_assert(!VP || KIND == kMsb, "value pruning here is the quantized variant");
   __shared__ float red[NG][65];
+  __shared__ float sS[VP ? kVrowMaxRows : 1];  // the row's scores (log2 units)
+  __shared__ int kred[NW];
   __shared__ float wred[2 * NW];
   __shared__ uint32_t nw[2][8];   // new row of this head: [k, v] MSB words
   __shared__ uint32_t nlw[2][8];  // and LSB words
@@ -754,6 +830,7 @@ decode_bh(DecodeArgs a) {
   float M, L, o;
   float cm;
   bool flag = false;
+  int vkept = a.lc;
   if constexpr (KIND == kBf16) {
     // the query's words are requested first and converted only after the
     // first batch of cache rows has been requested too
@@ -784,7 +861,7 @@ decode_bh(DecodeArgs a) {
       load8_f32(static_cast<const bf16_t*>(a.knew) + int64_t(b) * D + 8 * t, xk);
       load8_f32(static_cast<const bf16_t*>(a.vnew) + int64_t(b) * D + 8 * t, xv);
     }
-    bh_pass_q<false>(a, b, h, g, cl, 0, a.lc - 1, q, qsum, st);
+    bh_pass_q<false, VP>(a, b, h, g, cl, 0, a.lc - 1, q, qsum, st, sS);
     // code the new row: per-token scale from the whole row, then this
     // head's 64 dims into the planes (the arithmetic of spatten_quantize_kv,
     // so every head's workgroup finds the same scale)
@@ -844,7 +921,7 @@ decode_bh(DecodeArgs a) {
       }
     }
     __syncthreads();
-    bh_new_row_q<false>(a, b, h, g, cl, q, qsum, st, nw, nlw, nscale);
+    bh_new_row_q<false, VP>(a, b, h, g, cl, q, qsum, st, nw, nlw, nscale, sS);
 #pragma unroll
     for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(-8.0f, st.wsum, st.acc[e]);
     bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M, &L, &o);
@@ -855,11 +932,34 @@ decode_bh(DecodeArgs a) {
       // from its codes in LDS (this workgroup wrote its planes; the scale
       // may come from another head's workgroup, so it is not read back)
       bh_reset(st);
-      bh_pass_q<true>(a, b, h, g, cl, 0, a.lc - 1, q, qsum, st);
-      bh_new_row_q<true>(a, b, h, g, cl, q, qsum, st, nw, nlw, nscale);
+      bh_pass_q<true, VP>(a, b, h, g, cl, 0, a.lc - 1, q, qsum, st, sS);
+      bh_new_row_q<true, VP>(a, b, h, g, cl, q, qsum, st, nw, nlw, nscale, sS);
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(-128.0f, st.wsum, st.acc[e]);
       bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M, &L, &o);
+    }
+    if constexpr (VP) {
+      // exact probabilities against the final row log2-sum-exp; the V rows
+      // below the threshold are not read. The groups' sums are already
+      // normalised, so they meet at a common reference of 0 and L = 1.
+      __syncthreads();  // sS complete
+      const float lse2 = M + log2f(L);
+      bh_reset(st);
+      st.m = 0.0f;
+      const int kc = flag ? bh_vpass_q<true>(a, b, h, g, cl, lse2, sS, st, nw, nlw, nscale)
+                          : bh_vpass_q<false>(a, b, h, g, cl, lse2, sS, st, nw, nlw, nscale);
+      const float off = flag ? -128.0f : -8.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[e] = fmaf(off, st.wsum, st.acc[e]);
+      const int kw = wave_sum_int(kc);
+      if (lane == 0) kred[wave] = kw;
+      float M2, L2;
+      bh_combine<NT, NG, DPL>(st, g, cl, red, wred, &M2, &L2, &o);
+      M = lse2;   // the row's statistics as the plain path reports them
+      L = 1.0f;
+      vkept = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) vkept += kred[w];
     }
   }
   if (t < 64) static_cast<bf16_t*>(a.o)[int64_t(b) * D + h * 64 + t] = f32_to_bf16(o / L);
@@ -867,7 +967,7 @@ decode_bh(DecodeArgs a) {
     a.lse[bh] = M + log2f(L);
     a.cmax[bh] = cm;
     if (a.recompute) a.recompute[bh] = flag ? 1 : 0;
-    if (a.v_kept) a.v_kept[bh] = a.lc;
+    if (a.v_kept) a.v_kept[bh] = vkept;
   }
 }
 
@@ -926,7 +1026,14 @@ int launch_decode(const DecodeArgs& a, bool quantized, ImpArgs* imp, hipStream_t
     SPATTEN_TIMED("decode_attn", stream,
                   decode_bh<kBf16><<<blocks, BhCfg<kBf16>::NT, 0, stream>>>(a));
   } else {
-    SPATTEN_TIMED("pq_attn", stream, decode_bh<kMsb><<<blocks, BhCfg<kMsb>::NT, 0, stream>>>(a));
+    if (a.v_threshold > 0.0f) {
+      if (a.lc_pad > kVrowMaxRows) return SPATTEN_EUNSUPPORTED;
+      SPATTEN_TIMED("pq_attn_vprune", stream,
+                    (decode_bh<kMsb, true><<<blocks, BhCfg<kMsb>::NT, 0, stream>>>(a)));
+    } else {
+      SPATTEN_TIMED("pq_attn", stream,
+                    decode_bh<kMsb><<<blocks, BhCfg<kMsb>::NT, 0, stream>>>(a));
+    }
   }
   SPATTEN_LAUNCH_CHECK();
   return SPATTEN_OK;

@@ -52,7 +52,11 @@ int check_layer(const spatten_layer_desc* d, const void* x, const void* wq, cons
     return SPATTEN_EINVAL;
   }
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return SPATTEN_EUNSUPPORTED;
-  if (d->v_threshold > 0.0f && d->kv_quantized) return SPATTEN_EUNSUPPORTED;
+  // quantized value pruning keeps the row's scores in LDS: caches of at most
+  // kVrowMaxRows rows (rounded up to whole chunks)
+  if (d->v_threshold > 0.0f && d->kv_quantized &&
+      round_up(int64_t(d->cache_len) + 1, kDecChunk) > kVrowMaxRows)
+    return SPATTEN_EUNSUPPORTED;
   if (d->mode == SPATTEN_PREFILL) {
     if (d->n_tokens < 1 || d->kv_quantized != 0) return SPATTEN_EINVAL;
     if (d->dtype == SPATTEN_BF16 && d->head_dim == 32) return SPATTEN_EUNSUPPORTED;

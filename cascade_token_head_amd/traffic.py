@@ -48,7 +48,8 @@ KERNEL_SOURCE = {
     "qkv_gemm": "gemm.hip", "out_gemm": "gemm.hip",
     "attn_fwd": "attn.hip", "attn_colsum": "attn.hip", "importance": "attn.hip",
     "attn_fwd_vprune": "attn.hip", "gather_keys": "attn.hip",
-    "decode_attn": "decode.hip", "pq_attn": "decode.hip", "decode_vrow": "decode.hip",
+    "decode_attn": "decode.hip", "pq_attn": "decode.hip", "pq_attn_vprune": "decode.hip",
+    "decode_vrow": "decode.hip",
     "decode_scores": "decode.hip", "decode_vprune": "decode.hip", "decode_vsum": "decode.hip",
     "decode_importance": "decode.hip",
     "topk": "topk.hip", "compact": "compact.hip", "compact_inplace": "compact.hip",

@@ -62,7 +62,8 @@ typedef struct {
   int32_t cache_cap;     /* decode: cache rows allocated per sequence */
   int32_t kv_quantized;  /* decode: 1 = cache held as int8 MSB/LSB nibble planes */
   float pq_threshold;    /* decode, quantized: recompute rows whose max prob < this */
-  float v_threshold;     /* local value pruning threshold (0 = off): prefill, unquantized decode */
+  float v_threshold;     /* local value pruning threshold (0 = off): prefill, decode (quantized:
+                            cache_len + 1 <= 4096) */
   int32_t per_head;      /* 1 = per-head token pruning (decode: a is [B, H, cache_cap], and
                             quantized scales are [B, H, cache_cap]; prefill, bf16
                             bidirectional: see n_keys) */
@@ -103,10 +104,14 @@ typedef struct {
  *   pq_threshold, recomputed with the full code scale*(16*msb + lsb) for
  *   both K and V. recompute (optional, [B, H] int32) receives 1 for
  *   recomputed rows. a accumulates the probabilities that produced O.
- *   Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning"; unquantized
- *   caches, v_threshold > 0): after the softmax, V row j of head h enters
+ *   Local value pruning ("A. Cascade Token Pruning", bullet "Local Value Pruning";
+ *   v_threshold > 0): after the softmax, V row j of head h enters
  *   O_h only when P_h[j] >= v_threshold, O_h = sum over those j of
  *   P_h[j] V_h[j] (no renormalisation); the other V rows are never read.
+ *   Quantized caches apply it to the probabilities of the pass that
+ *   produces O_h (the recomputed ones, with both planes of V, for a
+ *   recomputed row; else the MSB pass's, with MSB-only V) and need
+ *   cache_len + 1 <= 4096.
  *   a still takes every probability. v_kept (optional, [B, H] int32)
  *   receives the number of V rows that entered O_h (cache_len + 1 without
  *   value pruning).
@@ -142,8 +147,8 @@ typedef struct {
  * Supported (else SPATTEN_EUNSUPPORTED): prefill bf16 with head_dim 64 or
  *   128; prefill fp32 with head_dim 32, 64 or 128 and n_tokens <= 1024;
  *   decode bf16 with head_dim 64, n_heads <= 32 and every head kept. A
- *   v_threshold > 0 is taken by prefill and by unquantized decode, not by
- *   quantized caches or per-head prefill; a NaN or negative one is
+ *   v_threshold > 0 is taken by prefill and by decode (quantized caches:
+ *   cache_len + 1 <= 4096), not by per-head prefill; a NaN or negative one is
  *   SPATTEN_EINVAL. per_head is 0 or 1 (else SPATTEN_EINVAL); 1 needs a
  *   decode, or a bf16 bidirectional prefill with
  *   1 <= n_keys <= n_tokens; n_keys must be 0 in every other case

@@ -38,6 +38,10 @@ Parity status of each function (what pins it, in tests/test_oracle.py):
                       sqrt(dh) ln 3 give p = (3/4, 1/4) (the 1/sqrt(dh)
                       scale); under progressive quantization the stack's
                       importance sums the recomputed probabilities.
+  pq_head_attention   with value pruning: V rows 127 e_j (scale 1, code
+  (value pruning)     127) expose each kept probability as 127 p (both
+                      planes) or 112 p (MSB only); thresholds just below the
+                      m-th largest keep m rows; tau = 0 is plain PQ.
   value_pruned_output one-hot V rows expose every kept probability (and
                       thresholds at the m-th largest keep exactly m rows);
                       threshold 0 -> torch attention; threshold > 1 -> 0;

@@ -288,14 +288,16 @@ def dequant(msb_p, lsb_p, scale, full: bool):
 
 
 def pq_head_attention(q, Kmsb, Kfull, Vmsb, Vfull, threshold: float,
-                      decide: Optional[Callable] = None):
+                      decide: Optional[Callable] = None, v_threshold: float = 0.0):
     """One decode query row of one head under progressive quantization.
 
     First pass scores against the MSB-only keys. If the largest probability
     is below the threshold the distribution is flat: the row is recomputed
     with both planes for K and V. Returns (o, p, recomputed, max_p_msb).
     decide(c, default) may override the decision (tests use it to follow
-    the GPU among rows whose confidence is at the threshold).
+    the GPU among rows whose confidence is at the threshold). v_threshold
+    > 0 applies local value pruning to the probabilities that produce o
+    (the recomputed ones for a flat row) and the V values of the same pass.
     """
     dh = q.shape[0]
     p = softmax_rows((Kmsb @ q) / math.sqrt(dh))
@@ -305,8 +307,8 @@ def pq_head_attention(q, Kmsb, Kfull, Vmsb, Vfull, threshold: float,
         flat = decide(c, flat)
     if flat:
         p = softmax_rows((Kfull @ q) / math.sqrt(dh))
-        return p @ Vfull, p, True, c
-    return p @ Vmsb, p, False, c
+        return value_pruned_output(p, Vfull, v_threshold)[0], p, True, c
+    return value_pruned_output(p, Vmsb, v_threshold)[0], p, False, c
 
 
 # --------------------------------------------------------------------------
@@ -473,11 +475,11 @@ def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: boo
     [Lc] (one scale per token, shared by the heads), or under per-head
     pruning planes [Lc, H, dh/2] with scales [Lc, H] (slot r of head h holds
     head h's r-th kept entry and that token's scale). v_threshold > 0 applies local
-    value pruning to unquantized caches. Returns (o [H, dh], p [H, Lc],
+    value pruning (quantized caches: to the probabilities and V values of the
+    pass that produces o, the recomputed one for a flat row). Returns (o [H, dh], p [H, Lc],
     recompute flags [H], MSB-pass max probability [H], V rows kept [H])."""
     H, dh = heads_n, head_dim
     if quantized:
-        assert v_threshold == 0.0, "value pruning is defined here for unquantized caches"
 
         def planes(kv, full):
             m, l_, sc = cache[kv + "_msb"], cache[kv + "_lsb"], np.asarray(cache[kv + "_scale"])
@@ -498,7 +500,8 @@ def decode_attention(q, cache: dict, heads_n: int, head_dim: int, quantized: boo
         if quantized:
             dec = None if decide is None else (lambda c_, d_, h_=h: decide(h_, c_, d_))
             O[h], P[h], rec[h], cmax[h] = pq_head_attention(q[h], Km[:, h], Kf[:, h], Vm[:, h],
-                                                            Vf[:, h], threshold, dec)
+                                                            Vf[:, h], threshold, dec, v_threshold)
+            kept[h] = int(np.sum(P[h] >= v_threshold))
         else:
             P[h] = softmax_rows((cache["k"][:, h] @ q[h]) / math.sqrt(dh))
             O[h], kept[h] = value_pruned_output(P[h], cache["v"][:, h], v_threshold)

@@ -67,11 +67,20 @@ int main() {
   d.cache_cap = 2048;
   EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_EINVAL);
-  // local value pruning: not with quantized caches; NaN and negative rejected
+  // local value pruning: quantized caches up to 4096 rows (the scores of a
+  // row stay in LDS); NaN and negative rejected
   d.cache_cap = 2049;
   d.v_threshold = 1e-4f;
   EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
+                     P, &got), SPATTEN_OK);
+  d.cache_len = 4096;
+  d.cache_cap = 4097;
+  got = layer_workspace_bytes(d);
+  EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, nullptr, nullptr, u8, u8, fp, u8, u8, fp,
                      P, &got), SPATTEN_EUNSUPPORTED);
+  d.cache_len = 2048;
+  d.cache_cap = 2049;
+  got = need;
   d.kv_quantized = 0;
   EXPECT(check_layer(&d, P, P, P, P, P, hi, nullptr, fp, nullptr, P, P, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, P, &got), SPATTEN_OK);

@@ -142,12 +142,18 @@ def test_decode_rejections(S):
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
     d = S.make_desc(**{**base, "kv_quantized": True})
     assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL     # planes missing, caches given
-    # local value pruning: a threshold must be a non-negative number, and is
-    # taken by unquantized caches and by prefill
+    # local value pruning: a threshold must be a non-negative number; it is
+    # taken by prefill, by unquantized caches and by quantized caches of at
+    # most 4096 rows (whose scores one workgroup keeps in LDS)
     for bad in (-1e-3, float("nan")):
         d = S.make_desc(**{**base, "v_threshold": bad})
         assert _call_layer(S, d, 1 << 40, **p) == S.EINVAL
-    d = S.make_desc(**{**base, "v_threshold": 1e-3, "kv_quantized": True, "pq_threshold": 0.1})
+    pq = {**base, "v_threshold": 1e-3, "kv_quantized": True, "pq_threshold": 0.1}
+    assert S.workspace_bytes(S.make_desc(**pq)) == S.workspace_bytes(
+        S.make_desc(**{**pq, "v_threshold": 0.0}))
+    d = S.make_desc(**{**pq, "cache_len": 4095, "cache_cap": 4096})
+    assert S.workspace_bytes(d) > 0
+    d = S.make_desc(**{**pq, "cache_len": 4096, "cache_cap": 4097})
     assert _call_layer(S, d, 1 << 40, **p) == S.EUNSUPPORTED
     d = S.make_desc(S.PREFILL, S.BF16, False, 2, 100, 12, 12, 64, v_threshold=1e-3)
     assert S.workspace_bytes(d) == S.workspace_bytes(

@@ -252,13 +252,19 @@ PERHEAD_CASES = [(3, 12, 100, 0.0), (2, 16, 257, 0.0), (64, 12, 130, 0.0), (1, 5
 # per-head importance with quantized caches, whose scales are then per (head,
 # slot): (B, H, L0, threshold)
 PERHEAD_PQ_CASES = [(3, 16, 200, 0.1), (2, 12, 150, 1.01), (2, 16, 301, 0.0)]
+# value pruning with quantized caches: (B, H, L0, threshold, v_threshold,
+# per_head)
+PQ_VPRUNE_CASES = [(3, 16, 200, 0.1, 1e-3, False), (2, 12, 300, 1.01, 2e-3, False),
+                   (2, 16, 257, 0.0, 1e-2, False), (2, 16, 301, 0.1, 1e-3, True),
+                   (1, 16, 4000, 0.1, 1e-4, False), (2, 16, 0, 0.1, 0.5, False)]
 
 
 @pytest.mark.parametrize("B,H,L0,quantized,thr,vthr,per_head",
                          [c + (0.0, False) for c in DECODE_LAYER_CASES] +
                          [(B, H, L0, False, 0.0, v, False) for B, H, L0, v in VPRUNE_CASES] +
                          [(B, H, L0, False, 0.0, v, True) for B, H, L0, v in PERHEAD_CASES] +
-                         [(B, H, L0, True, t, 0.0, True) for B, H, L0, t in PERHEAD_PQ_CASES])
+                         [(B, H, L0, True, t, 0.0, True) for B, H, L0, t in PERHEAD_PQ_CASES] +
+                         [(B, H, L0, True, t, v, ph) for B, H, L0, t, v, ph in PQ_VPRUNE_CASES])
 def test_decode_layer(S, B, H, L0, quantized, thr, vthr, per_head):
     print("decode case", B, H, L0, quantized, thr, vthr, per_head, flush=True)
     dh = 64

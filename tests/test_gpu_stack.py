@@ -31,7 +31,7 @@ from oracle import spatten_ref as R
 from workloads import (BERT_BASE, GPT2_DECODE, LONG_CAUSAL, PQ_DECODE, TINY, make_decode_inputs,
                        make_prefill_inputs, scaled)
 from workloads.configs import (BERT_BASE_VPRUNE, GPT2_DECODE_PERHEAD, GPT2_DECODE_ROLLING,
-                               GPT2_DECODE_VPRUNE, PQ_DECODE_PERHEAD)
+                               GPT2_DECODE_VPRUNE, PQ_DECODE_PERHEAD, PQ_DECODE_VPRUNE)
 
 pytestmark = pytest.mark.gpu
 
@@ -597,6 +597,11 @@ DECODE_CFGS = {
                           steps=5, prune_every=1), [1]),
     "gpt2_perhead": (scaled(GPT2_DECODE_PERHEAD, batch=4, n_layers=4, cache_len=256,
                             cache_keep=102, steps=4), [0, 3]),
+    "pq_vprune": (scaled(PQ_DECODE_VPRUNE, batch=3, n_layers=3, cache_len=300, cache_keep=150,
+                         steps=4, v_threshold=1e-3), [0, 2]),
+    "pq_vprune_perhead_all": (scaled(PQ_DECODE_VPRUNE, batch=2, n_layers=3, cache_len=200,
+                                     cache_keep=100, steps=4, prune_every=2, per_head=True,
+                                     pq_threshold=1.01, v_threshold=2e-3), [1]),
     "pq_perhead_rolling": (scaled(PQ_DECODE_PERHEAD, batch=3, n_layers=3, cache_len=300,
                                   cache_keep=150, steps=5, prune_every=1), [0, 2]),
     "pq_perhead_all": (scaled(PQ_DECODE_PERHEAD, batch=2, n_layers=3, cache_len=200,
@@ -650,9 +655,10 @@ def most_recomputed_sequence(cfg, inputs):
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [GPT2_DECODE, PQ_DECODE, GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING,
-                                 GPT2_DECODE_PERHEAD, PQ_DECODE_PERHEAD],
+                                 GPT2_DECODE_PERHEAD, PQ_DECODE_PERHEAD, PQ_DECODE_VPRUNE],
                          ids=["gpt2_decode", "pq_decode", "gpt2_decode_vprune",
-                              "gpt2_decode_rolling", "gpt2_decode_perhead", "pq_decode_perhead"])
+                              "gpt2_decode_rolling", "gpt2_decode_perhead", "pq_decode_perhead",
+                              "pq_decode_vprune"])
 def test_decode_stack_full_size(cfg):
     """Full batch, cache, layer and step count; per-layer checks of every
     step on the first and last sequence, and for progressive quantization

@@ -1217,3 +1217,41 @@ def test_run_prefill_perhead_matches_closed_form_cascade():
                     keys[h] = keys[h][_largest(a[h][keys[h]], cfg.key_keep[l + 1])]
                 differ |= len({tuple(keys[h]) for h in heads}) > 1
     assert differ  # the heads keep different tokens
+
+
+@pytest.mark.parametrize("threshold,full", [(0.0, False), (1.01, True)])
+def test_pq_value_pruning_one_hot_values(threshold, full):
+    """Quantized caches: V rows 127 e_j (scale 1, code 127 in one dim) make
+    every kept probability show up in its own output element, as 127 p_j
+    from both planes (a recomputed row) or 16 * 7 p_j = 112 p_j from the MSB
+    plane alone (127 >> 4 = 7); probabilities from torch's softmax of the
+    dequantized keys of the pass. A threshold just below the m-th largest
+    probability keeps exactly m rows."""
+    rng = np.random.default_rng(61)
+    H, dh, Lc = 1, 16, 12
+    K = rng.standard_normal((Lc, dh)).astype(np.float32)
+    V = np.zeros((Lc, dh), np.float32)
+    V[np.arange(Lc), np.arange(Lc)] = 127.0
+    km, kl, ks = R.quantize_kv(K)
+    vm, vl, vs = R.quantize_kv(V)
+    np.testing.assert_array_equal(vs, 1.0)
+    cache = {"k_msb": km, "k_lsb": kl, "k_scale": ks, "v_msb": vm, "v_lsb": vl, "v_scale": vs}
+    q = rng.standard_normal((H, dh)) * 2.0
+    Kd = R.dequant(km, kl, ks, full)
+    p = torch.softmax(torch.from_numpy(Kd @ q[0]) / math.sqrt(dh), dim=0).numpy()
+    amp = 127.0 if full else 112.0
+    for m in (1, 4, Lc):
+        ps = np.sort(p)[::-1]
+        tau = float(ps[m - 1]) * (1 - 1e-9)   # just below the m-th largest
+        assert m == Lc or ps[m] < tau
+        o, P, rec, _, kept = R.decode_attention(q, cache, H, dh, True, threshold, v_threshold=tau)
+        assert bool(rec[0]) == full and kept[0] == m
+        np.testing.assert_allclose(P[0], p, atol=1e-12)
+        want = np.zeros(dh)
+        want[:Lc] = np.where(p >= tau, amp * p, 0.0)
+        np.testing.assert_allclose(o[0], want, atol=1e-10)
+    # tau = 0 is the unpruned progressive quantization
+    o0, _, _, _, kept0 = R.decode_attention(q, cache, H, dh, True, threshold)
+    o1, _, _, _, kept1 = R.decode_attention(q, cache, H, dh, True, threshold, v_threshold=0.0)
+    np.testing.assert_array_equal(o0, o1)
+    assert kept0[0] == kept1[0] == Lc

@@ -23,7 +23,8 @@ Three extensions of gpt2_decode: gpt2_decode_vprune (local value pruning,
 threshold 1e-4), gpt2_decode_rolling (the cache cut back to 410 entries
 after every step) and gpt2_decode_perhead (each head keeps its own 410
 entries by its own importance); pq_decode_perhead does the same for the
-quantized cache (1024 entries per head).
+quantized cache (1024 entries per head) and pq_decode_vprune adds value
+pruning at 1e-4 to it.
 
 This module holds shapes and schedules only. Keep counts follow
 k = floor(f * N + 1/2) with N the original length, so fractions are absolute
@@ -141,6 +142,10 @@ GPT2_DECODE_PERHEAD = replace(GPT2_DECODE, name="gpt2_decode_perhead", per_head=
 # own 1024 entries of the pq_decode cache (with a copy of each kept token's
 # scales), recomputing flat rows from both planes as pq_decode does.
 PQ_DECODE_PERHEAD = replace(PQ_DECODE, name="pq_decode_perhead", per_head=True)
+# Local value pruning under progressive quantization, threshold 1e-4 as in
+# gpt2_decode_vprune: V rows are read (MSB plane, or both for a recomputed
+# row) only where the final probability reaches it.
+PQ_DECODE_VPRUNE = replace(PQ_DECODE, name="pq_decode_vprune", v_threshold=1e-4)
 # Local value pruning in prefill: the bert_base stack with a probability
 # threshold of 1e-3 (about half of a 512-token row's uniform share).
 BERT_BASE_VPRUNE = replace(BERT_BASE, name="bert_base_vprune", v_threshold=1e-3)
@@ -152,7 +157,7 @@ BERT_BASE_PERHEAD = replace(BERT_BASE, name="bert_base_perhead", per_head=True,
 
 CONFIGS = [TINY, BERT_BASE, GPT2_DECODE, PQ_DECODE, LONG_CAUSAL]
 EXTENSIONS = [GPT2_DECODE_VPRUNE, GPT2_DECODE_ROLLING, GPT2_DECODE_PERHEAD, PQ_DECODE_PERHEAD,
-              BERT_BASE_VPRUNE, BERT_BASE_PERHEAD]
+              PQ_DECODE_VPRUNE, BERT_BASE_VPRUNE, BERT_BASE_PERHEAD]
 BY_NAME = {c.name: c for c in CONFIGS + EXTENSIONS}
 
 

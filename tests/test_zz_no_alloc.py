@@ -112,6 +112,9 @@ CASES = [
     ("decode_vprune", scaled(GPT2_DECODE, batch=4, n_layers=1, cache_len=500, steps=1,
                              v_threshold=1e-3),
      scaled(GPT2_DECODE, batch=2, n_layers=1, cache_len=64, steps=1, v_threshold=1e-3)),
+    ("decode_pq_vprune", scaled(PQ_DECODE, batch=4, n_layers=1, cache_len=900, steps=1,
+                                v_threshold=1e-3),
+     scaled(PQ_DECODE, batch=2, n_layers=1, cache_len=200, steps=1, v_threshold=1e-3)),
 ]
 
 
